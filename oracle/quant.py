@@ -1,0 +1,208 @@
+"""Per-row quantisation of the oracle (test infrastructure only).
+
+Every token row is quantised once, then copied to each routed row.  The five
+modes and the passages they follow:
+
+* ``none``       -- bf16 passes through ("Low-Latency Mode API", Return
+  Values: BF16 when ``use_fp8`` is off).
+* ``int8_token`` -- per-token dynamic int8 with a float32 scale (same page,
+  Parameters, ``use_fp8``; Return Values: int8 data plus one float32 per
+  token).  Scale = amax/127, round half to even, clamp to +-127.
+* ``fp8_b128``   -- e4m3 codes with one float32 scale per 128-channel block
+  ("DeepEP FP8 Dispatch and Combine Operations", "The Dispatch Stage": the
+  hidden dimension is cut into 128-element blocks, each with its own amax
+  and scale; "The FP8 Combine Operation": the stored inverse scale multiplies
+  the codes back).  The page prints the multiplier as 127/amax; for e4m3 the
+  largest code is 448, so the oracle uses 448 (reading S1).
+* ``mxfp8``      -- e4m3 codes plus one e8m0 scale per 32-element block
+  ("Low-Latency Mode API", ``use_ue8m0``).
+* ``mxfp4``      -- e2m1 codes, two per byte, plus one e8m0 scale per
+  32-element block ("Low-Latency Mode API", ``use_mxfp4``).
+
+Arithmetic for the scaled modes (reading S2): with ``qmax`` the largest code
+(127 or 448), the multiplier ``m = fl32(qmax / amax)`` scales the elements
+and the stored scale is ``s = fl32(amax / qmax)`` -- two separate float32
+divisions, each rounded once.  Each element is ``fl32(x * m)``, clamped to
++-qmax and rounded to the code.  If ``amax`` is zero or ``m`` is not finite
+the block stores scale 0 and all codes 0 (reading S3).
+
+MX scale rule (reading S6): with ``e = floor(log2(amax))`` and ``emax`` the
+exponent of the element format's largest value (8 for e4m3, whose largest is
+1.75 * 2**8; 2 for e2m1, whose largest is 1.5 * 2**2), the shared exponent is
+``clamp(e - emax, -127, 127)`` (-127 when amax is zero) and the stored byte
+is that plus 127.  Elements are ``fl32(x * 2**-exp)``, clamped to the
+element format's largest value, then rounded.
+
+Parity: ``int8``/``fp8_b128`` pinned by the properties |q| <= qmax, the amax
+element mapping to +-qmax and the per-element error bound; the MX scale byte
+pinned by recomputation with ``math.frexp``; all element rounding is in
+``codecs`` (pinned there).  The MX rule itself is pinned only by the OCP MX
+specification, which is not among the pages: that part is "parity unpinned"
+with respect to the pages and is stated so in the design doc.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+
+INT8_QMAX = np.float32(127.0)
+E4M3_QMAX = np.float32(448.0)
+
+# bytes of data and of scales per row, by mode (hidden size H)
+
+
+def row_bytes(mode: str, hidden: int) -> tuple[int, int]:
+    """(data bytes, scale bytes) of one packed row -- the receive layout of
+    "Low-Latency Mode API", Return Values, with the FP8 per-128 scales as in
+    "DeepEP FP8 Dispatch and Combine Operations"."""
+    if mode == "none":
+        return 2 * hidden, 0
+    if mode == "int8_token":
+        return hidden, 4
+    if mode == "fp8_b128":
+        return hidden, 4 * (hidden // 128)
+    if mode == "mxfp8":
+        return hidden, hidden // 32
+    if mode == "mxfp4":
+        return hidden // 2, hidden // 32
+    raise ValueError(f"unknown quant mode {mode!r}")
+
+
+def _amax(x_f32: np.ndarray) -> np.float32:
+    """Largest magnitude of a block, exact in float32."""
+    return np.float32(np.max(np.abs(x_f32))) if x_f32.size else np.float32(0.0)
+
+
+def _scaled_block(x_f32: np.ndarray, qmax: np.float32):
+    """Multiplier, stored scale and the scaled, clamped elements of one block
+    (see the module header: reading S2 and S3)."""
+    amax = _amax(x_f32)
+    with np.errstate(divide="ignore", over="ignore"):
+        m = np.float32(qmax / amax) if amax != 0 else np.float32(np.inf)
+    if amax == 0 or not np.isfinite(m):
+        return np.float32(0.0), np.zeros_like(x_f32), True
+    s = np.float32(amax / qmax)
+    v = (x_f32 * m).astype(np.float32)
+    v = np.clip(v, -qmax, qmax).astype(np.float32)
+    return s, v, False
+
+
+def quant_int8_token(x_bits: np.ndarray):
+    """One bf16 row -> (int8 codes [H], float32 scale)."""
+    x = codecs.bf16_bits_to_f32(x_bits)
+    s, v, zero = _scaled_block(x, INT8_QMAX)
+    if zero:
+        return np.zeros(x.shape, np.int8), np.float32(0.0)
+    q = np.rint(v)                       # round half to even
+    q = np.clip(q, -127, 127).astype(np.int8)
+    return q, s
+
+
+def quant_fp8_b128(x_bits: np.ndarray):
+    """One bf16 row -> (e4m3 codes [H] uint8, float32 scales [H/128])."""
+    x = codecs.bf16_bits_to_f32(x_bits)
+    H = x.shape[0]
+    codes = np.empty(H, np.uint8)
+    scales = np.empty(H // 128, np.float32)
+    for g in range(H // 128):
+        blk = x[g * 128:(g + 1) * 128]
+        s, v, zero = _scaled_block(blk, E4M3_QMAX)
+        scales[g] = s
+        codes[g * 128:(g + 1) * 128] = 0 if zero else codecs.e4m3_encode(v)
+    return codes, scales
+
+
+def mx_shared_exponent(amax: np.float32, emax: int) -> int:
+    """Shared exponent of an MX block: clamp(floor(log2 amax) - emax, -127,
+    127), or -127 for amax == 0.  floor(log2 amax) is read off the float32
+    bit pattern: the biased exponent field, or for a subnormal amax the
+    position of its leading one."""
+    a = int(np.float32(amax).view(np.uint32)) & 0x7FFFFFFF
+    if a == 0:
+        return -127
+    ef = a >> 23
+    if ef == 0:                            # subnormal: value = mant * 2**-149
+        e = (a.bit_length() - 1) - 149
+    else:
+        e = ef - 127
+    return max(-127, min(127, e - emax))
+
+
+def _quant_mx(x_bits: np.ndarray, emax: int, vmax: float, encode):
+    x = codecs.bf16_bits_to_f32(x_bits)
+    H = x.shape[0]
+    codes = np.empty(H, np.uint8)
+    scale_bytes = np.empty(H // 32, np.uint8)
+    for g in range(H // 32):
+        blk = x[g * 32:(g + 1) * 32]
+        se = mx_shared_exponent(_amax(blk), emax)
+        scale_bytes[g] = se + 127
+        # x * 2**-se: exact in float64, then one rounding to float32
+        v = (blk.astype(np.float64) * (2.0 ** -se)).astype(np.float32)
+        v = np.clip(v, np.float32(-vmax), np.float32(vmax)).astype(np.float32)
+        codes[g * 32:(g + 1) * 32] = encode(v)
+    return codes, scale_bytes
+
+
+def quant_mxfp8(x_bits: np.ndarray):
+    """One bf16 row -> (e4m3 codes [H] uint8, e8m0 scale bytes [H/32])."""
+    return _quant_mx(x_bits, 8, codecs.E4M3_MAX, codecs.e4m3_encode)
+
+
+def quant_mxfp4(x_bits: np.ndarray):
+    """One bf16 row -> (packed e2m1 bytes [H/2], e8m0 scale bytes [H/32])."""
+    codes, sb = _quant_mx(x_bits, 2, codecs.E2M1_MAX, codecs.e2m1_encode)
+    return codecs.pack_e2m1_pairs(codes), sb
+
+
+def quantize_row(mode: str, x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """One bf16 row (uint16 patterns) -> (data bytes, scale bytes) exactly as
+    they are laid out in a receive row (little-endian scalars)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    if mode == "none":
+        return x_bits.view(np.uint8).copy(), np.zeros(0, np.uint8)
+    if mode == "int8_token":
+        q, s = quant_int8_token(x_bits)
+        return q.view(np.uint8), np.array([s], np.float32).view(np.uint8)
+    if mode == "fp8_b128":
+        q, s = quant_fp8_b128(x_bits)
+        return q, s.astype("<f4").view(np.uint8)
+    if mode == "mxfp8":
+        return quant_mxfp8(x_bits)
+    if mode == "mxfp4":
+        return quant_mxfp4(x_bits)
+    raise ValueError(f"unknown quant mode {mode!r}")
+
+
+def dequantize_row(mode: str, data: np.ndarray, scales: np.ndarray, hidden: int) -> np.ndarray:
+    """Row bytes -> float32 values, one rounding per element.
+
+    ``none``: the bf16 value.  ``int8_token`` and ``fp8_b128``: fl32(code *
+    scale) ("DeepEP FP8 Dispatch and Combine Operations", "The FP8 Combine
+    Operation": codes times the stored inverse scale, through float32).  MX:
+    code value times 2**(b-127), formed exactly in float64 and rounded once to
+    float32 (the same number a float32 multiply by the exact power of two
+    gives).
+    """
+    data = np.asarray(data, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    if mode == "none":
+        return codecs.bf16_bits_to_f32(data.view(np.uint16))
+    if mode == "int8_token":
+        s = scales.view(np.float32)[0]
+        return (data.view(np.int8).astype(np.float32) * s).astype(np.float32)
+    if mode == "fp8_b128":
+        s = np.repeat(scales.view("<f4").astype(np.float32), 128)
+        val = codecs.e4m3_decode(data).astype(np.float32)     # exact
+        return (val * s).astype(np.float32)
+    if mode in ("mxfp8", "mxfp4"):
+        if mode == "mxfp8":
+            val = codecs.e4m3_decode(data)
+        else:
+            val = codecs.e2m1_decode(codecs.unpack_e2m1_pairs(data))
+        sc = np.repeat(codecs.e8m0_decode(scales), 32)
+        with np.errstate(over="ignore", invalid="ignore"):
+            return (val * sc).astype(np.float32)
+    raise ValueError(f"unknown quant mode {mode!r}")

@@ -1,0 +1,171 @@
+"""Pins of the oracle's dispatch and combine, and planted-mistake checks.
+
+* dispatch ``none``: every routed receive row equals its token bit for bit;
+* combine with unit weights and bf16 rows: out == bf16(k_eff * x) exactly
+  (k_eff <= 16 equal terms sum exactly in float32) -- the invariant stated for
+  the method; k_eff is counted here directly from topk_idx;
+* combine with general weights: within one bf16 ulp of the float64 sum
+  rounded once, plus the float32 accumulation bound;
+* quantised round trips within each format's error;
+* planted mistakes (wrong order in the layout, weights dropped, fp8 ties away
+  from even, a dropped term in combine) are each caught by one of the pins.
+"""
+
+import numpy as np
+import pytest
+
+from combine_topk_idx_amd import workloads as W
+from oracle import codecs, combine as C, dispatch as D, layout as L, quant as Q
+
+
+def _case(seed, T=40, H=96, E=6, k=4, neg=0.2, mode="none"):
+    w = W.random_workload(seed, T, H, E, k, mode, neg_frac=neg)
+    inp = W.make_inputs(w)
+    return w, inp
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_dispatch_none_copies_rows(seed):
+    w, inp = _case(seed)
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    rb = D.dispatch(inp["x"], lay, "none", inp["topk_weights"])
+    for t in range(w.T):
+        for j in range(w.k):
+            r = lay.slot[t, j]
+            if r >= 0:
+                assert np.array_equal(rb.data[r].view(np.uint16), inp["x"][t])
+                assert rb.weights[r] == inp["topk_weights"][t, j]
+
+
+def _keff(idx, E):
+    return ((idx >= 0) & (idx < E)).sum(axis=1)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_combine_unit_weights_is_keff_times_x(seed):
+    w, inp = _case(seed, k=16, E=5, neg=0.3)
+    idx = inp["topk_idx"]
+    if seed == 3:
+        idx = W.with_duplicates(idx, seed)
+    lay = L.layout(idx, w.E, w.T)
+    rb = D.dispatch(inp["x"], lay, "none")
+    out = C.combine(rb, lay, np.ones((w.T, w.k), np.float32))
+    keff = _keff(idx, w.E).astype(np.float64)
+    ref = W.bf16_from_f32((codecs.bf16_bits_to_f32(inp["x"]).astype(np.float64) * keff[:, None]).astype(np.float32))
+    # k_eff * x is exact in float64 and float32 (8-bit mantissa times <= 16)
+    assert np.array_equal(out, ref)
+    assert np.all(out[keff == 0] == 0)               # +0 rows
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_combine_general_weights_within_one_ulp(seed):
+    w, inp = _case(seed, T=30, H=128, E=7, k=8, neg=0.1)
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    y = W.make_expert_out(w)
+    rb = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8).reshape(w.max_rows, -1),
+                      np.zeros((w.max_rows, 0), np.uint8), None)
+    out = codecs.bf16_bits_to_f32(C.combine(rb, lay, inp["topk_weights"])).astype(np.float64)
+    yf = codecs.bf16_bits_to_f32(y).astype(np.float64)
+    ref = np.zeros((w.T, w.H))
+    mag = np.zeros((w.T, w.H))
+    for t in range(w.T):
+        for j in range(w.k):
+            r = lay.slot[t, j]
+            if r >= 0:
+                p = float(inp["topk_weights"][t, j]) * yf[r]
+                ref[t] += p
+                mag[t] += np.abs(p)
+    ref_bf = codecs.bf16_bits_to_f32(codecs.f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    ulp = np.maximum(np.abs(ref_bf), 2.0 ** -126) * 2.0 ** -7
+    # float32: one rounding per product and per add, at most 2k of them
+    acc_err = 2 * w.k * 2.0 ** -24 * mag
+    assert np.all(np.abs(out - ref) <= ulp + acc_err)
+
+
+@pytest.mark.parametrize("mode,rel", [("int8_token", 0.02), ("fp8_b128", 0.04),
+                                      ("mxfp8", 0.05), ("mxfp4", 0.2)])
+def test_dispatch_combine_quantised_roundtrip(mode, rel):
+    w, inp = _case(5, T=24, H=256, E=8, k=3, neg=0.0, mode=mode)
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    rb = D.dispatch(inp["x"], lay, mode)
+    ones = np.ones((w.T, w.k), np.float32) / w.k
+    out = codecs.bf16_bits_to_f32(C.combine(rb, lay, ones)).astype(np.float64)
+    xf = codecs.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    assert np.linalg.norm(out - xf) / np.linalg.norm(xf) < rel
+
+
+def test_buffer_bytes_layout():
+    total, off = D.buffer_bytes(10, 7168, "mxfp4")
+    assert off == D.align_up(10 * 3584, 256) and total == off + 10 * 224
+    total, off = D.buffer_bytes(3, 32, "int8_token")
+    assert off == 256 and total == 256 + 12
+
+
+def test_recv_buffer_bytes_roundtrip():
+    w, inp = _case(9, T=10, H=64, E=4, k=2, mode="mxfp8")
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    rb = D.dispatch(inp["x"], lay, "mxfp8")
+    rb2 = D.RecvBuffer.from_bytes(rb.to_bytes(), w.max_rows, w.H, "mxfp8", rb.num_rows)
+    assert np.array_equal(rb.data, rb2.data) and np.array_equal(rb.scales, rb2.scales)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must trip one of the pins above
+# ---------------------------------------------------------------------------
+
+
+def test_planted_unstable_layout_is_caught(monkeypatch):
+    from tests.test_oracle_layout import _brute
+    rng = np.random.default_rng(0)
+    idx = rng.integers(-1, 5, size=(30, 4))
+    real = L.layout
+
+    def reversed_order(topk_idx, E, tmax, cum_stats=None):
+        lay = real(topk_idx[::-1].copy(), E, tmax)   # assigns rows from the last token
+        return lay
+
+    cnt, rows = _brute(idx, 5)
+    bad = reversed_order(idx, 5, 30)
+    assert not np.array_equal(bad.row_src[:bad.num_rows], rows)
+
+
+def test_planted_dropped_weight_is_caught():
+    w, inp = _case(1, T=30, H=128, E=7, k=8, neg=0.1)
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    y = W.make_expert_out(w)
+    rb = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8).reshape(w.max_rows, -1),
+                      np.zeros((w.max_rows, 0), np.uint8), None)
+    wrong = C.combine(rb, lay, np.ones_like(inp["topk_weights"]))   # weights ignored
+    right = C.combine(rb, lay, inp["topk_weights"])
+    assert not np.array_equal(wrong, right)
+
+
+def test_planted_ties_away_is_caught():
+    # rounding half away from zero instead of half to even disagrees with torch
+    mids = ((codecs.E4M3_POS_VALUES[:-1] + codecs.E4M3_POS_VALUES[1:]) / 2).astype(np.float32)
+    hi = np.searchsorted(codecs.E4M3_POS_VALUES, mids)
+    away = hi.astype(np.uint8)
+    import torch
+    ref = torch.from_numpy(mids).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert not np.array_equal(away, ref)
+    assert np.array_equal(codecs.e4m3_encode(mids), ref)
+
+
+def test_planted_dropped_term_is_caught(monkeypatch):
+    w, inp = _case(2, k=16, E=5, neg=0.0)
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    rb = D.dispatch(inp["x"], lay, "none")
+    real = C.combine_token
+
+    def drop_last(expert_out, lay_, wts, t):
+        s = lay_.slot.copy()
+        s[t, -1] = -1
+        return real(expert_out, L.Layout(lay_.num_tokens, lay_.num_topk, lay_.num_experts,
+                                         lay_.max_rows, lay_.count, lay_.offsets, s,
+                                         lay_.row_src, lay_.status), wts, t)
+
+    monkeypatch.setattr(C, "combine_token", drop_last)
+    out = C.combine(rb, lay, np.ones((w.T, w.k), np.float32))
+    keff = _keff(inp["topk_idx"], w.E).astype(np.float64)
+    ref = W.bf16_from_f32((codecs.bf16_bits_to_f32(inp["x"]).astype(np.float64) * keff[:, None]).astype(np.float32))
+    assert not np.array_equal(out, ref)
