@@ -1,0 +1,269 @@
+"""Benchmark of MoE dispatch + combine on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path over one batch: ep_layout (routing
+layout), ep_dispatch (quantise + scatter) and ep_combine (gather + dequantise
++ weighted reduce), all launched on one stream with inputs resident in HBM.
+Buffer sets rotate between steps so that no step finds its inputs in the
+256 MB last-level cache.  The default workload is "large": 16384 tokens,
+hidden 7168, top-8 of 256 experts with 5% of the pairs unrouted, MXFP4
+dispatch and a bf16 combine.
+
+Prints one JSON line: tokens/s over the timed steps, the algorithmic bytes
+and GB/s of the whole step, the roofline entry of the dominant kernel
+(combine) with its duration measured by HIP events on the launch stream, and
+the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), H=7168 k=8"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_large_traffic.json")
+KERNEL_SOURCES = ["combine_topk_idx_amd/csrc/combine.hip", "combine_topk_idx_amd/csrc/formats.hpp",
+                  "combine_topk_idx_amd/csrc/common.hpp"]
+
+
+def algorithmic_bytes(w, R: int) -> dict:
+    """Bytes the method has to move, per phase (Measurement).
+
+    layout:   read ids, write counts/offsets, slot map and row sources
+    dispatch: read x once and the slot map, write every routed packed row
+    combine:  read every routed row, the slot map and the weights, write out
+    """
+    b_idx = 4 if w.idx_dtype == "int32" else 8
+    H, T, k, E = w.H, w.T, w.k, w.E
+    dq, sq = _row_bytes(w.mode, H)
+    cin = w.mode if w.combine_input == "identity" else "none"
+    dc, sc = _row_bytes(cin, H)
+    lay = T * k * b_idx + E * 8 + (E + 1) * 4 + T * k * 4 + R * 4
+    disp = 2 * T * H + T * k * 4 + R * (dq + sq)
+    comb = R * (dc + sc) + T * k * (4 + 4) + 2 * T * H
+    return {"layout": lay, "dispatch": disp, "combine": comb, "total": lay + disp + comb}
+
+
+def _row_bytes(mode: str, H: int):
+    return {"none": (2 * H, 0), "int8_token": (H, 4), "fp8_b128": (H, 4 * (H // 128)),
+            "mxfp8": (H, H // 32), "mxfp4": (H // 2, H // 32)}[mode]
+
+
+def _source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per combine launch from the committed rocprofv3 counter
+    summary, or None if it is missing, for another workload, or was taken
+    on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != _source_hash() or d.get("workload") != workload:
+        return None
+    return d.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle leg (runs in a child process pinned to one core)
+# ---------------------------------------------------------------------------
+
+
+def cpu_baseline_child(name: str, tokens: int) -> None:
+    os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    import numpy as np
+    from combine_topk_idx_amd import workloads as W
+    from oracle import combine as C, dispatch as D, layout as L
+
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w)
+    x = inp["x"][:tokens]
+    idx = inp["topk_idx"][:tokens]
+    wts = inp["topk_weights"][:tokens]
+    y = None
+    if w.combine_input == "normal":
+        y = W.make_expert_out(w, rows=tokens * w.k)
+    t0 = time.perf_counter()
+    lay = L.layout(idx, w.E, tokens)
+    rb = D.dispatch(x, lay, w.mode)
+    if w.combine_input == "identity":
+        cin = rb
+    else:
+        cin = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8).reshape(tokens * w.k, -1),
+                           np.zeros((tokens * w.k, 0), np.uint8), None)
+    C.combine(cin, lay, wts)
+    dt = time.perf_counter() - t0
+    print(json.dumps({"tokens": tokens, "seconds": dt, "cores": len(os.sched_getaffinity(0))}))
+
+
+def cpu_baseline(name: str, tokens: int) -> dict:
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", name,
+                        "--cpu-tokens", str(tokens)], capture_output=True, text=True, env=dict(
+                            os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+                            HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES=""))
+    if r.returncode != 0:
+        raise RuntimeError(f"cpu baseline failed:\n{r.stderr}")
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"value": d["tokens"] / d["seconds"], "unit": "tokens/s", "cores": d["cores"], "kind": "oracle",
+            "sample": f"first {d['tokens']} tokens of the workload as one batch (layout + dispatch + "
+                      f"combine), {d['seconds']:.1f} s on one host core"}
+
+
+# ---------------------------------------------------------------------------
+# GPU leg
+# ---------------------------------------------------------------------------
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large")
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough to exceed 1 GB)")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: workload default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
+    args = ap.parse_args()
+
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args.cpu_baseline_child, args.cpu_tokens)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path has no "
+              f"multi-GPU exchange)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from combine_topk_idx_amd import ep, workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} {w.mode}", file=sys.stderr, flush=True)
+    inp = W.make_inputs(w)
+    y_host = W.make_expert_out(w) if w.combine_input == "normal" else None
+
+    total_recv, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    per_set = (w.T * w.H * 2 * 2 + total_recv + (w.max_rows * w.H * 2 if y_host is not None else 0))
+    nsets = args.sets or max(2, -(-(1 << 30) // max(per_set, 1)))
+    nsets = min(nsets, 64)
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    sets = []
+    for i in range(nsets):
+        s = {
+            "x": dev_bf16(inp["x"]),
+            "idx": torch.from_numpy(inp["topk_idx"]).to(dev),
+            "w": torch.from_numpy(inp["topk_weights"]).to(dev),
+            "ws": torch.empty(ep.ep_workspace_bytes(w.t_max, w.k, w.E), dtype=torch.uint8, device=dev),
+            "rc": torch.empty(w.E, dtype=torch.int64, device=dev),
+            "recv": torch.empty(total_recv, dtype=torch.uint8, device=dev),
+            "out": torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev),
+        }
+        if y_host is not None:
+            s["y"] = dev_bf16(y_host).view(torch.uint8).reshape(-1) if i == 0 else sets[0]["y"].clone()
+        sets.append(s)
+    del y_host
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        h = ep.ep_layout(s["idx"], w.E, w.t_max, s["rc"], s["ws"], stream=stream)
+        ep.ep_dispatch(h, s["x"], w.H, w.mode, s["recv"], stream=stream)
+        if w.combine_input == "identity":
+            ep.ep_combine(h, s["recv"], w.mode, w.H, s["w"], s["out"], stream=stream)
+        else:
+            ep.ep_combine(h, s["y"], "none", w.H, s["w"], s["out"], stream=stream)
+        return h
+
+    print(f"[bench] {nsets} buffer sets, warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    h = step(sets[0])
+    torch.cuda.synchronize()
+    R = int(sets[0]["rc"].sum().item())
+
+    # timed region: events around each phase, on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        s = sets[i % nsets]
+        e = ev[i]
+        e[0].record(stream)
+        hh = ep.ep_layout(s["idx"], w.E, w.t_max, s["rc"], s["ws"], stream=stream)
+        e[1].record(stream)
+        ep.ep_dispatch(hh, s["x"], w.H, w.mode, s["recv"], stream=stream)
+        e[2].record(stream)
+        if w.combine_input == "identity":
+            ep.ep_combine(hh, s["recv"], w.mode, w.H, s["w"], s["out"], stream=stream)
+        else:
+            ep.ep_combine(hh, s["y"], "none", w.H, s["w"], s["out"], stream=stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    total_ms = ev[0][0].elapsed_time(ev[-1][3])
+    lay_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    disp_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    comb_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    ms_per_step = total_ms / args.steps
+
+    b = algorithmic_bytes(w, R)
+    gbps = b["total"] / (ms_per_step * 1e-3) / 1e9
+    comb_gbps = b["combine"] / (comb_ms * 1e-3) / 1e9
+    traffic = _traffic(w.name)
+    roof = {"bound": "hbm", "kernel": "combine", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(comb_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "alg_bytes_per_launch": b["combine"], "avg_launch_ms": round(comb_ms, 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        tokens = args.cpu_tokens or {"large": 1536, "prefill": 1024}.get(w.name, w.T)
+        print(f"[bench] cpu oracle on {tokens} tokens", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w.name, tokens)
+
+    line = {
+        "metric": METRIC, "value": round(w.T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E} k={w.k} ids={w.idx_dtype} "
+                               f"dispatch={w.mode} routing={w.routing} unrouted={w.neg_frac} "
+                               f"combine_input={w.combine_input}",
+                   "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R, "buffer_sets": nsets},
+        "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "alg_bytes_per_step": b["total"],
+        "phase_ms": {"layout": round(lay_ms, 5), "dispatch": round(disp_ms, 5), "combine": round(comb_ms, 5)},
+        "phase_gbps": {"dispatch": round(b["dispatch"] / (disp_ms * 1e-3) / 1e9, 1),
+                       "combine": round(comb_gbps, 1)},
+        "wall_s": round(wall_s, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

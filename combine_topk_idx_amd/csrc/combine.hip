@@ -1,0 +1,148 @@
+// Combine kernel for gfx950: gather each token's expert-output rows,
+// dequantise them and reduce them weighted by topk_weights.
+//
+// ("Low-Latency Mode API", low_latency_combine: the result is the bf16
+// weighted sum over the token's experts; "DeepEP FP8 Dispatch and Combine
+// Operations", The FP8 Combine Operation: codes times the stored inverse
+// scale, through float32.)  Per element:
+//   acc = +0;  for j = 0..k-1 with slot[t, j] >= 0:  acc = acc + fl(w[t, j] * y_j)
+//   out = bf16_rne(acc)
+// in float32 with one rounding per multiply and per add (the library is built
+// with -ffp-contract=off, so no fused multiply-add and no reassociation).
+//
+// Mapping: a workgroup handles one token and a span of its row; a lane owns 8
+// consecutive output elements.  Slots and weights are workgroup-uniform
+// (scalar loads).  All k row loads of a lane are issued before the first add,
+// so a lane has up to k independent 4-16 byte loads in flight; the adds then
+// run in ascending j.
+#include "common.hpp"
+#include "formats.hpp"
+
+namespace ep {
+
+namespace {
+
+template <int Q> struct Raw;
+template <> struct Raw<EP_QUANT_NONE> { using T = u32x4; };
+template <> struct Raw<EP_QUANT_INT8_TOKEN> { using T = u32x2; };
+template <> struct Raw<EP_QUANT_FP8_B128> { using T = u32x2; };
+template <> struct Raw<EP_QUANT_MXFP8> { using T = u32x2; };
+template <> struct Raw<EP_QUANT_MXFP4> { using T = uint32_t; };
+
+template <int Q> constexpr int kBytesPerVec = sizeof(typename Raw<Q>::T);
+
+// dequantised 8 elements of one row vector
+template <int Q>
+__device__ __forceinline__ void dequant8(const typename Raw<Q>::T &r, float scale, float (&y)[8]) {
+  if constexpr (Q == EP_QUANT_NONE) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[2 * i] = bf16_lo(r[i]);
+      y[2 * i + 1] = bf16_hi(r[i]);
+    }
+  } else if constexpr (Q == EP_QUANT_INT8_TOKEN) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = (int)(int8_t)((r[i >> 2] >> (8 * (i & 3))) & 0xffu);
+      y[i] = (float)q * scale;
+    }
+  } else if constexpr (Q == EP_QUANT_FP8_B128 || Q == EP_QUANT_MXFP8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = e4m3_decode((r[i >> 2] >> (8 * (i & 3))) & 0xffu) * scale;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = e2m1_decode((r >> (4 * i)) & 0xfu) * scale;
+  }
+}
+
+template <int Q, int NT, int VPT>
+__global__ __launch_bounds__(NT) void combine_kernel(const char *__restrict__ data, const char *__restrict__ scales,
+                                                     int64_t dq, int64_t sq, int nvec, int k, int chunks,
+                                                     const int *__restrict__ slot, const float *__restrict__ w,
+                                                     u32x4 *__restrict__ out) {
+  using RawT = typename Raw<Q>::T;
+  const int t = blockIdx.x / chunks;
+  const int c = blockIdx.x - t * chunks;
+  const int64_t pair0 = (int64_t)t * k;
+
+  int s[kMaxTopk];
+  float wt[kMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {
+    s[j] = j < k ? slot[pair0 + j] : -1;
+    wt[j] = j < k ? w[pair0 + j] : 0.0f;
+  }
+  // per-row int8 scales are workgroup-uniform
+  float rs[kMaxTopk];
+  if constexpr (Q == EP_QUANT_INT8_TOKEN) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) rs[j] = s[j] >= 0 ? *(const float *)(scales + s[j] * sq) : 0.0f;
+  }
+
+  const int v0 = c * NT * VPT + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = v0 + i * NT;
+    if (v >= nvec) continue;
+    RawT raw[kMaxTopk];
+    float sc[kMaxTopk];
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (s[j] < 0) continue;
+      raw[j] = *(const RawT *)(data + s[j] * dq + (int64_t)v * kBytesPerVec<Q>);
+      if constexpr (Q == EP_QUANT_NONE) {
+        sc[j] = 1.0f;
+      } else if constexpr (Q == EP_QUANT_INT8_TOKEN) {
+        sc[j] = rs[j];
+      } else if constexpr (Q == EP_QUANT_FP8_B128) {
+        sc[j] = *(const float *)(scales + s[j] * sq + (int64_t)(v >> 4) * 4);
+      } else {
+        sc[j] = e8m0_decode(*(const uint8_t *)(scales + s[j] * sq + (int64_t)(v >> 2)));
+      }
+    }
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (s[j] < 0) continue;
+      float y[8];
+      dequant8<Q>(raw[j], sc[j], y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + wt[j] * y[e];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    out[(int64_t)t * nvec + v] = o;
+  }
+}
+
+template <int Q, int NT, int VPT>
+hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out, hipStream_t s) {
+  size_t dq, sq;
+  row_bytes(Q, hidden, &dq, &sq);
+  const size_t scale_off = align_up((size_t)h.max_rows * dq, kScaleAlign);
+  const int nvec = hidden / 8;
+  const int chunks = (nvec + NT * VPT - 1) / (NT * VPT);
+  const int64_t blocks = h.num_tokens * chunks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((combine_kernel<Q, NT, VPT>), dim3((unsigned)blocks), dim3(NT), 0, s, in, in + scale_off,
+                     (int64_t)dq, (int64_t)sq, nvec, h.num_topk, chunks, h.slot, w, (u32x4 *)out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const float *w, void *out,
+                          hipStream_t s) {
+  switch (quant) {
+    case EP_QUANT_NONE: return launch_q<EP_QUANT_NONE, 128, 1>(h, in, hidden, w, out, s);
+    case EP_QUANT_INT8_TOKEN: return launch_q<EP_QUANT_INT8_TOKEN, 128, 1>(h, in, hidden, w, out, s);
+    case EP_QUANT_FP8_B128: return launch_q<EP_QUANT_FP8_B128, 128, 1>(h, in, hidden, w, out, s);
+    case EP_QUANT_MXFP8: return launch_q<EP_QUANT_MXFP8, 128, 1>(h, in, hidden, w, out, s);
+    default: return launch_q<EP_QUANT_MXFP4, 128, 1>(h, in, hidden, w, out, s);
+  }
+}
+
+}  // namespace ep

@@ -1,0 +1,84 @@
+// Shared definitions of the HIP library: vector types, wave64 helpers and the
+// internal launcher interface between the C ABI (ep_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ep.h"
+
+namespace ep {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 512;
+constexpr size_t kScaleAlign = 256;   // scale region alignment inside a receive buffer
+constexpr size_t kWsAlign = 256;      // alignment of each workspace sub-array
+
+__host__ __device__ constexpr size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+// Per-row byte sizes of the receive format (see include/ep.h).
+__host__ __device__ inline void row_bytes(int quant, int hidden, size_t *dq, size_t *sq) {
+  const size_t H = (size_t)hidden;
+  switch (quant) {
+    case EP_QUANT_NONE: *dq = 2 * H; *sq = 0; break;
+    case EP_QUANT_INT8_TOKEN: *dq = H; *sq = 4; break;
+    case EP_QUANT_FP8_B128: *dq = H; *sq = 4 * (H / 128); break;
+    case EP_QUANT_MXFP8: *dq = H; *sq = H / 32; break;
+    default: *dq = H / 2; *sq = H / 32; break;   // EP_QUANT_MXFP4
+  }
+}
+
+// DPP lane exchanges (wave64, no LDS traffic).  Controls: quad_perm
+// [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E; row_ror:n = 0x120 + n (rotate within a
+// row of 16 lanes).
+__device__ __forceinline__ uint32_t dpp_quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_row_ror4(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+}
+
+// max over the 4 lanes of a quad / the 16 lanes of a row, on unsigned values
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, dpp_quad_xor1(v));
+  return max(v, dpp_quad_xor2(v));
+}
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = quad_max(v);
+  v = max(v, dpp_row_ror4(v));
+  return max(v, dpp_row_ror8(v));
+}
+
+// ---------------------------------------------------------------------------
+// internal launchers (defined in layout.hip / dispatch.hip / combine.hip)
+// ---------------------------------------------------------------------------
+
+struct WsLayout {      // byte offsets of the workspace sub-arrays
+  size_t offsets, slot, row_src, status, hist, bstat, total;
+  int64_t nblocks;     // blocks of the multi-block layout path (0 = single block)
+};
+
+WsLayout workspace_layout(int64_t max_tokens, int32_t k, int32_t E);
+
+hipError_t launch_layout(const void *idx, int idx64, int64_t T, int32_t k, int32_t E, int64_t max_rows,
+                         int64_t *recv_count, int32_t *cum, char *ws, const WsLayout &wl,
+                         hipStream_t s);
+
+hipError_t launch_dispatch(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant,
+                           char *recv, float *recv_w, hipStream_t s);
+
+hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const float *w,
+                          void *out, hipStream_t s);
+
+}  // namespace ep

@@ -1,0 +1,306 @@
+// Dispatch kernel for gfx950: read each bf16 token row once, quantise it once,
+// write the packed row (and its scales) to every receive row it is routed to.
+//
+// Quantisation ("Low-Latency Mode API", Parameters use_fp8 / use_ue8m0 /
+// use_mxfp4; "DeepEP FP8 Dispatch and Combine Operations", The Dispatch
+// Stage), all in float32 with one rounding per operation:
+//   INT8_TOKEN  amax over the row;  m = 127/amax, scale = amax/127,
+//               code = clamp(rint(x*m), +-127)
+//   FP8_B128    the same per 128 channels with 448, code = e4m3(clamp(x*m))
+//   MXFP8/MXFP4 per 32 elements: shared exponent clamp(floor(log2 amax) -
+//               emax, +-127) (emax 8 for e4m3, 2 for e2m1), byte = exp+127,
+//               code = enc(clamp(x * 2^-exp, +-max))
+// A block whose amax is 0, or whose multiplier overflows, stores scale 0 and
+// zero codes.
+//
+// Mapping: a workgroup handles one token and a contiguous span of its row; a
+// lane owns 8 consecutive elements (one 16-byte load).  An MX block is 4
+// adjacent lanes and a 128-channel block 16 adjacent lanes, so block maxima
+// are DPP exchanges inside a quad or a 16-lane row; the int8 row maximum is a
+// workgroup reduction.  Routed rows and weights are read once per workgroup
+// (scalar loads).  Stores are non-temporal: the receive buffer is written
+// once and not read back by this kernel.
+#include "common.hpp"
+#include "formats.hpp"
+
+namespace ep {
+
+namespace {
+
+// largest |x| of the 8 bf16 elements of a vector, as the bits of a
+// non-negative bf16 (unsigned order == float order for these)
+__device__ __forceinline__ uint32_t vec_absmax_bits(const u32x4 &r) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, r[i] & 0x7fffu);
+    m = max(m, (r[i] >> 16) & 0x7fffu);
+  }
+  return m;
+}
+
+__device__ __forceinline__ void unpack8(const u32x4 &r, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(r[i]);
+    f[2 * i + 1] = bf16_hi(r[i]);
+  }
+}
+
+// Scaled-integer style block (INT8 / FP8_B128): multiplier and stored scale.
+struct ScaledBlock {
+  float m, scale;
+  bool zero;
+};
+__device__ __forceinline__ ScaledBlock scaled_block(uint32_t amax_bits, float qmax) {
+  const float amax = __uint_as_float(amax_bits << 16);
+  ScaledBlock b;
+  b.m = qmax / amax;
+  b.scale = amax / qmax;
+  b.zero = (amax_bits == 0) || __builtin_isinf(b.m);
+  if (b.zero) b.scale = 0.0f;
+  return b;
+}
+
+__device__ __forceinline__ u32x2 codes_int8(const float (&f)[8], const ScaledBlock &b) {
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v = fminf(fmaxf(f[i] * b.m, -127.0f), 127.0f);
+    const int q = b.zero ? 0 : (int)__builtin_rintf(v);
+    w[i >> 2] |= ((uint32_t)q & 0xffu) << (8 * (i & 3));
+  }
+  return u32x2{w[0], w[1]};
+}
+
+__device__ __forceinline__ u32x2 codes_e4m3_scaled(const float (&f)[8], const ScaledBlock &b) {
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = fminf(fmaxf(f[i] * b.m, -448.0f), 448.0f);
+    const uint32_t c = b.zero ? 0u : e4m3_encode(v);
+    w[i >> 2] |= c << (8 * (i & 3));
+  }
+  return u32x2{w[0], w[1]};
+}
+
+// MX shared exponent of a block from its amax bits (bf16 pattern); returns the
+// e8m0 byte and the float32 multiplier 2^-exp.
+__device__ __forceinline__ uint32_t mx_scale(uint32_t amax_bits, int emax, float &mult) {
+  int se = -127;
+  if (amax_bits != 0) {
+    se = floor_log2_bits(amax_bits << 16) - emax;
+    se = se < -127 ? -127 : (se > 127 ? 127 : se);
+  }
+  // 2^-se with se in [-127, 126] is a normal float32 (se = 127 cannot occur
+  // for finite bf16 input because floor(log2) <= 127 and emax >= 2)
+  mult = __uint_as_float((uint32_t)(127 - se) << 23);
+  return (uint32_t)(se + 127);
+}
+
+__device__ __forceinline__ u32x2 codes_mxfp8(const float (&f)[8], float mult) {
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = fminf(fmaxf(f[i] * mult, -448.0f), 448.0f);
+    w[i >> 2] |= e4m3_encode(v) << (8 * (i & 3));
+  }
+  return u32x2{w[0], w[1]};
+}
+
+__device__ __forceinline__ uint32_t codes_mxfp4(const float (&f)[8], float mult) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = fminf(fmaxf(f[i] * mult, -6.0f), 6.0f);
+    w |= e2m1_encode(v) << (4 * i);
+  }
+  return w;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_nt(char *p, const T &v) {
+  __builtin_nontemporal_store(v, (T *)p);
+}
+
+// Workgroup max of one unsigned per thread (NT threads).
+template <int NT>
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d));
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) m = max(m, red[i]);
+  return m;
+}
+
+template <int Q, int NT, int VPT, bool PACK>
+__global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ x, int nvec, int k, int chunks,
+                                                      const int *__restrict__ slot,
+                                                      const float *__restrict__ w, float *__restrict__ recv_w,
+                                                      char *__restrict__ data, char *__restrict__ scales,
+                                                      int64_t dq, int64_t sq) {
+  const int t = blockIdx.x / chunks;
+  const int c = blockIdx.x - t * chunks;
+  const int64_t pair0 = (int64_t)t * k;
+
+  int s[kMaxTopk];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {
+    s[j] = j < k ? slot[pair0 + j] : -1;
+    any |= s[j] >= 0;
+  }
+  if (!any) return;   // uniform: the token is routed nowhere
+  if (recv_w != nullptr && c == 0 && threadIdx.x < k) {
+    const int r = slot[pair0 + threadIdx.x];
+    if (r >= 0) recv_w[r] = w[pair0 + threadIdx.x];
+  }
+
+  const u32x4 *xr = x + (int64_t)t * nvec;
+  const int v0 = c * NT * VPT + threadIdx.x;
+  u32x4 raw[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = v0 + i * NT;
+    raw[i] = v < nvec ? xr[v] : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  if constexpr (Q == EP_QUANT_NONE) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = v0 + i * NT;
+      if (v >= nvec) continue;
+#pragma unroll
+      for (int j = 0; j < kMaxTopk; ++j)
+        if (s[j] >= 0) st_nt(data + s[j] * dq + (int64_t)v * 16, raw[i]);
+    }
+  } else if constexpr (Q == EP_QUANT_INT8_TOKEN) {
+    __shared__ uint32_t red[NT / kWave];
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) am = max(am, vec_absmax_bits(raw[i]));
+    const ScaledBlock b = scaled_block(block_max<NT>(am, red), 127.0f);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = v0 + i * NT;
+      if (v >= nvec) continue;
+      float f[8];
+      unpack8(raw[i], f);
+      const u32x2 q = codes_int8(f, b);
+#pragma unroll
+      for (int j = 0; j < kMaxTopk; ++j)
+        if (s[j] >= 0) st_nt(data + s[j] * dq + (int64_t)v * 8, q);
+    }
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int j = 0; j < kMaxTopk; ++j)
+        if (s[j] >= 0) st_nt(scales + s[j] * sq, b.scale);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = v0 + i * NT;
+      float f[8];
+      unpack8(raw[i], f);
+      const uint32_t am = vec_absmax_bits(raw[i]);
+      if constexpr (Q == EP_QUANT_FP8_B128) {
+        const ScaledBlock b = scaled_block(row16_max(am), 448.0f);   // all 16 lanes
+        if (v >= nvec) continue;
+        const u32x2 q = codes_e4m3_scaled(f, b);
+        const bool lead = (v & 15) == 0;
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j) {
+          if (s[j] < 0) continue;
+          st_nt(data + s[j] * dq + (int64_t)v * 8, q);
+          if (lead) st_nt(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
+        }
+      } else {
+        constexpr int emax = Q == EP_QUANT_MXFP8 ? 8 : 2;
+        float mult;
+        const uint32_t sbyte = mx_scale(quad_max(am), emax, mult);
+        uint32_t sword = sbyte;
+        if constexpr (PACK) {
+          // gather the scale bytes of 4 consecutive blocks (lanes 0, 4, 8, 12
+          // of each 16-lane row) into one dword held by the row's first lane;
+          // only used when every 16-lane row is fully inside the row
+          // (hidden % 128 == 0), which also makes the dword store aligned
+          const int lane = threadIdx.x & (kWave - 1);
+          const int rbase = lane & ~15;
+          const uint32_t b1 = (uint32_t)__shfl((int)sbyte, rbase + 4);
+          const uint32_t b2 = (uint32_t)__shfl((int)sbyte, rbase + 8);
+          const uint32_t b3 = (uint32_t)__shfl((int)sbyte, rbase + 12);
+          sword = sbyte | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+        if (v >= nvec) continue;
+        const bool lead = PACK ? (v & 15) == 0 : (v & 3) == 0;
+#pragma unroll
+        for (int j = 0; j < kMaxTopk; ++j) {
+          if (s[j] < 0) continue;
+          char *drow = data + s[j] * dq;
+          if constexpr (Q == EP_QUANT_MXFP8) {
+            st_nt(drow + (int64_t)v * 8, codes_mxfp8(f, mult));
+          } else {
+            st_nt(drow + (int64_t)v * 4, codes_mxfp4(f, mult));
+          }
+          if (lead) {
+            char *sp = scales + s[j] * sq + (int64_t)(v >> 2);
+            if constexpr (PACK) st_nt(sp, sword);
+            else st_nt(sp, (uint8_t)sbyte);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int Q, int NT, int VPT, bool PACK = false>
+hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *w, char *recv, float *recv_w,
+                    int64_t dq, int64_t sq, size_t scale_off, hipStream_t s) {
+  const int chunks = (nvec + NT * VPT - 1) / (NT * VPT);
+  const int64_t blocks = h.num_tokens * chunks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((dispatch_kernel<Q, NT, VPT, PACK>), dim3((unsigned)blocks), dim3(NT), 0, s, (const u32x4 *)x,
+                     nvec, h.num_topk, chunks, h.slot, w, recv_w, recv, recv + scale_off, dq, sq);
+  return hipGetLastError();
+}
+
+template <int Q>
+hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const float *w, char *recv,
+                       float *recv_w, hipStream_t s) {
+  size_t dq, sq;
+  row_bytes(Q, hidden, &dq, &sq);
+  const size_t scale_off = align_up((size_t)h.max_rows * dq, kScaleAlign);
+  const int nvec = hidden / 8;
+  if constexpr (Q == EP_QUANT_INT8_TOKEN) {
+    // the whole row must sit in one workgroup (its amax is a row reduction)
+    if (nvec <= 256) return launch_q<Q, 256, 1>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (nvec <= 512) return launch_q<Q, 256, 2>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (nvec <= 1024) return launch_q<Q, 256, 4>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (nvec <= 2048) return launch_q<Q, 256, 8>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    return launch_q<Q, 1024, 8>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+  } else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) {
+    if (hidden % 128 == 0) return launch_q<Q, 128, 1, true>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    return launch_q<Q, 128, 1, false>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+  } else {
+    return launch_q<Q, 128, 1>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant,
+                           char *recv, float *recv_w, hipStream_t s) {
+  switch (quant) {
+    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE>(h, x, hidden, w, recv, recv_w, s);
+    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN>(h, x, hidden, w, recv, recv_w, s);
+    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128>(h, x, hidden, w, recv, recv_w, s);
+    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8>(h, x, hidden, w, recv, recv_w, s);
+    default: return launch_mode<EP_QUANT_MXFP4>(h, x, hidden, w, recv, recv_w, s);
+  }
+}
+
+}  // namespace ep

@@ -1,0 +1,202 @@
+// C ABI of libep.so: argument checks, workspace carving and kernel launches.
+//
+// Every check runs on the host before anything is launched; a failed check
+// returns an error code and records a message for ep_last_error() ("DeepEP
+// topk_idx_t Custom Dtype Requirements", Runtime Validation: validation halts
+// before any GPU work).  The numeric limits are those of the "Low-Latency
+// Mode API" page, Constraints: top-k in (0, 16], experts in (0, 512], hidden a
+// positive multiple of 32; the token count may not exceed the capacity.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ep_status_t fail(ep_status_t code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+ep_status_t hip_fail(hipError_t e, const char *where) {
+  return fail(EP_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_quant(int q) { return q >= EP_QUANT_NONE && q <= EP_QUANT_MXFP4; }
+
+constexpr int32_t kMaxHidden = 65536;
+
+ep_status_t check_hidden(int32_t hidden, int quant, const char *fn) {
+  if (!valid_quant(quant)) return fail(EP_ERR_INVALID_ARG, "%s: unknown quant mode %d", fn, quant);
+  if (hidden <= 0 || hidden % 32 != 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: hidden must be a positive multiple of 32 (got %d)", fn, hidden);
+  if (hidden > kMaxHidden) return fail(EP_ERR_UNSUPPORTED, "%s: hidden %d exceeds %d", fn, hidden, kMaxHidden);
+  if (quant == EP_QUANT_FP8_B128 && hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: per-128 e4m3 needs hidden %% 128 == 0 (got %d)", fn, hidden);
+  return EP_OK;
+}
+
+ep_status_t check_handle(const ep_handle_t *h, const char *fn) {
+  if (!h) return fail(EP_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  if (h->num_topk <= 0 || h->num_topk > ep::kMaxTopk || h->num_experts <= 0 ||
+      h->num_experts > ep::kMaxExperts || h->num_tokens < 0 || h->num_tokens > h->num_max_tokens ||
+      h->max_rows != h->num_max_tokens * h->num_topk || h->max_rows > INT32_MAX)
+    return fail(EP_ERR_INVALID_ARG, "%s: handle fields are inconsistent (not made by ep_layout?)", fn);
+  if (!h->offsets || !h->slot || !h->row_src || !h->status)
+    return fail(EP_ERR_INVALID_ARG, "%s: handle holds NULL pointers", fn);
+  return EP_OK;
+}
+
+size_t buffer_bytes(int64_t rows, int32_t hidden, int quant, size_t *scale_off) {
+  size_t dq, sq;
+  ep::row_bytes(quant, hidden, &dq, &sq);
+  const size_t off = ep::align_up((size_t)rows * dq, ep::kScaleAlign);
+  if (scale_off) *scale_off = off;
+  return off + (size_t)rows * sq;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ep_abi_version(void) { return EP_ABI_VERSION; }
+
+const char *ep_last_error(void) { return g_err; }
+
+size_t ep_workspace_bytes(int64_t num_max_dispatch_tokens, int32_t num_topk, int32_t num_experts) {
+  if (num_max_dispatch_tokens < 0 || num_topk <= 0 || num_topk > ep::kMaxTopk || num_experts <= 0 ||
+      num_experts > ep::kMaxExperts || num_max_dispatch_tokens * num_topk > INT32_MAX)
+    return 0;
+  return ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts).total;
+}
+
+ep_status_t ep_buffer_bytes(int64_t rows, int32_t hidden, ep_quant_t quant, size_t *total_bytes,
+                            size_t *scale_offset) {
+  if (rows < 0 || rows > INT32_MAX) return fail(EP_ERR_INVALID_ARG, "ep_buffer_bytes: rows out of range");
+  const ep_status_t st = check_hidden(hidden, quant, "ep_buffer_bytes");
+  if (st != EP_OK) return st;
+  const size_t total = buffer_bytes(rows, hidden, quant, scale_offset);
+  if (total_bytes) *total_bytes = total;
+  return EP_OK;
+}
+
+ep_status_t ep_layout(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens, int32_t num_topk,
+                      int64_t num_max_dispatch_tokens, int32_t num_experts, int64_t *recv_count,
+                      int32_t *cumulative_recv_stats, void *workspace, size_t workspace_bytes,
+                      ep_handle_t *handle, void *stream) {
+  const char *fn = "ep_layout";
+  if (idx_dtype != EP_IDX_INT32 && idx_dtype != EP_IDX_INT64)
+    return fail(EP_ERR_INVALID_ARG, "%s: topk_idx dtype must be int32 or int64", fn);
+  if (num_topk <= 0 || num_topk > ep::kMaxTopk)
+    return fail(EP_ERR_INVALID_ARG, "%s: num_topk must be in (0, 16] (got %d)", fn, num_topk);
+  if (num_experts <= 0 || num_experts > ep::kMaxExperts)
+    return fail(EP_ERR_INVALID_ARG, "%s: num_experts must be in (0, 512] (got %d)", fn, num_experts);
+  if (num_tokens < 0 || num_max_dispatch_tokens < 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: negative token count", fn);
+  if (num_tokens > num_max_dispatch_tokens)
+    return fail(EP_ERR_INVALID_ARG, "%s: num_tokens %lld exceeds num_max_dispatch_tokens %lld", fn,
+                (long long)num_tokens, (long long)num_max_dispatch_tokens);
+  if (num_max_dispatch_tokens > INT32_MAX / num_topk)
+    return fail(EP_ERR_INVALID_ARG, "%s: num_max_dispatch_tokens * num_topk exceeds 2^31-1", fn);
+  if (num_tokens > 0 && !topk_idx) return fail(EP_ERR_INVALID_ARG, "%s: topk_idx is NULL", fn);
+  if (topk_idx && !aligned(topk_idx, idx_dtype == EP_IDX_INT64 ? 8 : 4))
+    return fail(EP_ERR_INVALID_ARG, "%s: topk_idx is not aligned to its dtype", fn);
+  if (!recv_count || !aligned(recv_count, 8))
+    return fail(EP_ERR_INVALID_ARG, "%s: recv_count is NULL or misaligned", fn);
+  if (cumulative_recv_stats && !aligned(cumulative_recv_stats, 4))
+    return fail(EP_ERR_INVALID_ARG, "%s: cumulative_recv_stats is misaligned", fn);
+  if (!workspace || !aligned(workspace, ep::kWsAlign))
+    return fail(EP_ERR_INVALID_ARG, "%s: workspace is NULL or not 256-byte aligned", fn);
+  if (!handle) return fail(EP_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const ep::WsLayout wl = ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts);
+  if (workspace_bytes < wl.total)
+    return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, wl.total);
+
+  char *ws = (char *)workspace;
+  ep_handle_t h;
+  h.num_tokens = num_tokens;
+  h.num_max_tokens = num_max_dispatch_tokens;
+  h.max_rows = num_max_dispatch_tokens * num_topk;
+  h.num_topk = num_topk;
+  h.num_experts = num_experts;
+  h.offsets = (int32_t *)(ws + wl.offsets);
+  h.slot = (int32_t *)(ws + wl.slot);
+  h.row_src = (int32_t *)(ws + wl.row_src);
+  h.status = (uint32_t *)(ws + wl.status);
+  const hipError_t e = ep::launch_layout(topk_idx, idx_dtype == EP_IDX_INT64, num_tokens, num_topk, num_experts,
+                                         h.max_rows, recv_count, cumulative_recv_stats, ws, wl,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  *handle = h;
+  return EP_OK;
+}
+
+ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden, const float *topk_weights,
+                        ep_quant_t quant, void *recv_buf, size_t recv_buf_bytes, float *recv_weights,
+                        void *stream) {
+  const char *fn = "ep_dispatch";
+  ep_status_t st = check_handle(handle, fn);
+  if (st != EP_OK) return st;
+  st = check_hidden(hidden, quant, fn);
+  if (st != EP_OK) return st;
+  if (handle->num_tokens > 0 && !x) return fail(EP_ERR_INVALID_ARG, "%s: x is NULL", fn);
+  if (x && !aligned(x, 16)) return fail(EP_ERR_INVALID_ARG, "%s: x is not 16-byte aligned", fn);
+  if (!recv_buf || !aligned(recv_buf, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: recv_buf is NULL or not 16-byte aligned", fn);
+  const size_t need = buffer_bytes(handle->max_rows, hidden, quant, nullptr);
+  if (recv_buf_bytes < need)
+    return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: recv_buf has %zu bytes, needs %zu", fn, recv_buf_bytes, need);
+  if (recv_weights && !topk_weights)
+    return fail(EP_ERR_INVALID_ARG, "%s: recv_weights given without topk_weights", fn);
+  if ((topk_weights && !aligned(topk_weights, 4)) || (recv_weights && !aligned(recv_weights, 4)))
+    return fail(EP_ERR_INVALID_ARG, "%s: weights are misaligned", fn);
+  const hipError_t e = ep::launch_dispatch(*handle, x, hidden, topk_weights, quant, (char *)recv_buf,
+                                           recv_weights, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return EP_OK;
+}
+
+ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t expert_out_bytes,
+                       ep_quant_t in_quant, int32_t hidden, const float *topk_weights, void *out, void *stream) {
+  const char *fn = "ep_combine";
+  ep_status_t st = check_handle(handle, fn);
+  if (st != EP_OK) return st;
+  st = check_hidden(hidden, in_quant, fn);
+  if (st != EP_OK) return st;
+  if (!expert_out || !aligned(expert_out, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: expert_out is NULL or not 16-byte aligned", fn);
+  const size_t need = buffer_bytes(handle->max_rows, hidden, in_quant, nullptr);
+  if (expert_out_bytes < need)
+    return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: expert_out has %zu bytes, needs %zu", fn, expert_out_bytes, need);
+  if (handle->num_tokens > 0 && (!topk_weights || !aligned(topk_weights, 4)))
+    return fail(EP_ERR_INVALID_ARG, "%s: topk_weights is NULL or misaligned (it is required)", fn);
+  if (handle->num_tokens > 0 && (!out || !aligned(out, 16)))
+    return fail(EP_ERR_INVALID_ARG, "%s: out is NULL or not 16-byte aligned", fn);
+  const hipError_t e = ep::launch_combine(*handle, (const char *)expert_out, in_quant, hidden, topk_weights, out,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return EP_OK;
+}
+
+ep_status_t ep_read_status(const ep_handle_t *handle, uint32_t *flags, void *stream) {
+  const char *fn = "ep_read_status";
+  if (!handle || !handle->status) return fail(EP_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  if (!flags) return fail(EP_ERR_INVALID_ARG, "%s: flags is NULL", fn);
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  e = hipMemcpy(flags, handle->status, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return EP_OK;
+}
+
+}  // extern "C"

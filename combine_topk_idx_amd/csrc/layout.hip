@@ -1,0 +1,317 @@
+// Routing layout kernels: expert histogram, exclusive scan and stable
+// token-order slot assignment for gfx950.
+//
+// What is computed ("Low-Latency Mode API", Parameters topk_idx and
+// cumulative_local_expert_recv_stats, Return Values recv_count): for the T*k
+// (token, j) pairs in (t, j) order, pair f = t*k + j with a valid expert e
+// gets receive row offsets[e] + (number of earlier pairs with expert e).
+//
+// How: a workgroup of 16 wave64s owns a contiguous chunk of pairs; each wave
+// walks its sub-range 64 pairs at a time.  For one step, the lanes holding the
+// same expert find each other with one ballot per key bit (the AND of the
+// matching ballots is the set of lanes with an equal key), so a lane's rank
+// among equal lanes is the popcount of that set below it.  A per-wave LDS
+// counter per expert carries the count across steps (the wave's LDS
+// operations complete in program order, so every lane reads the counter
+// before the leader of its group bumps it).  Per-wave counts are then turned
+// into per-wave bases by a prefix over the 16 waves.  Nothing depends on the
+// order in which atomics or waves happen to run: the result is deterministic.
+//
+// Small problems (pairs <= 16384) run in one workgroup that also does the
+// scan over experts and writes every output: one launch.  Larger ones run
+// rank -> scan -> finalize over 4096-pair chunks.
+#include "common.hpp"
+
+namespace ep {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kSingleItems = 16;                   // 16 * 1024 pairs in one workgroup
+constexpr int kMultiItems = 4;                     // 4096-pair chunks
+constexpr int kMultiChunk = kMultiItems * kThreads;
+constexpr int64_t kSingleMaxPairs = (int64_t)kSingleItems * kThreads;
+constexpr int64_t kSingleMaxRows = 65536;          // single workgroup also clears row_src tail
+constexpr int kFinalizeThreads = 256;
+
+// Expert of pair f, or -1 for -1 / out-of-range ids / f past the end.
+template <typename IdxT>
+__device__ __forceinline__ int expert_of(const IdxT *__restrict__ idx, int f, int n, int E, bool &bad) {
+  if (f >= n) return -1;
+  const int64_t v = (int64_t)idx[f];
+  if (v >= 0 && v < (int64_t)E) return (int)v;
+  if (v != -1) bad = true;
+  return -1;
+}
+
+// Stable rank of each of this thread's ITEMS pairs among the equal-expert
+// pairs of its wave's sub-range [begin + w*ITEMS*64, ...).  On return,
+// cnt[w*E + e] is the number of wave-w pairs with expert e; ex[i] is the
+// expert (or -1) and lr[i] the rank within the wave.
+template <typename IdxT, int ITEMS>
+__device__ __forceinline__ void wave_rank(const IdxT *__restrict__ idx, int begin, int n, int E, int nbits,
+                                          int *cnt, int (&ex)[ITEMS], int (&lr)[ITEMS], bool &bad) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int *my = cnt + w * E;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int wbegin = begin + w * ITEMS * kWave;
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int f = wbegin + it * kWave + lane;
+    const int e = expert_of(idx, f, n, E, bad);
+    const int key = e < 0 ? E : e;
+    uint64_t same = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(same & below);
+    const int tot = __popcll(same);
+    int r = 0;
+    if (e >= 0) r = my[e] + rank;
+    if (e >= 0 && rank == 0) my[e] = r + tot;
+    ex[it] = e;
+    lr[it] = r;
+  }
+}
+
+// cnt[w*E + e] (counts) -> per-wave exclusive bases; total[e] = block count.
+__device__ __forceinline__ void wave_bases(int *cnt, int *total, int E) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+    total[e] = run;
+  }
+}
+
+// Exclusive scan of one int per thread over a 1024-thread block.  Returns the
+// exclusive prefix; *sum (LDS) receives the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int *sum) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < kWaves; ++i) {
+      const int c = wsum[i];
+      wsum[i] = run;
+      run += c;
+    }
+    *sum = run;
+  }
+  __syncthreads();
+  return wsum[w] + x - v;
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kThreads) void layout_single_kernel(
+    const IdxT *__restrict__ idx, int n, int E, int max_rows, int64_t *__restrict__ recv_count,
+    int *__restrict__ cum, int *__restrict__ offsets, int *__restrict__ slot, int *__restrict__ row_src,
+    uint32_t *__restrict__ status) {
+  __shared__ int cnt[kWaves * kMaxExperts];
+  __shared__ int total[kMaxExperts];
+  __shared__ int excl[kMaxExperts];
+  __shared__ int wsum[kWaves];
+  __shared__ int nrows;
+  __shared__ uint32_t sbad;
+  for (int i = threadIdx.x; i < kWaves * E; i += kThreads) cnt[i] = 0;
+  if (threadIdx.x == 0) sbad = 0;
+  __syncthreads();
+
+  const int nbits = 32 - __builtin_clz((unsigned)E);   // keys 0..E
+  int ex[kSingleItems], lr[kSingleItems];
+  bool bad = false;
+  wave_rank<IdxT, kSingleItems>(idx, 0, n, E, nbits, cnt, ex, lr, bad);
+  __syncthreads();
+  wave_bases(cnt, total, E);
+  __syncthreads();
+
+  const int c = threadIdx.x < E ? total[threadIdx.x] : 0;
+  const int pre = block_exclusive_scan(c, wsum, &nrows);
+  if (threadIdx.x < E) {
+    excl[threadIdx.x] = pre;
+    recv_count[threadIdx.x] = c;
+    offsets[threadIdx.x] = pre;
+    if (cum) cum[threadIdx.x] += c;
+  }
+  if (threadIdx.x == 0) offsets[E] = nrows;
+  if (bad) atomicOr(&sbad, 1u);
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int it = 0; it < kSingleItems; ++it) {
+    const int f = w * kSingleItems * kWave + it * kWave + lane;
+    if (f >= n) continue;
+    const int e = ex[it];
+    if (e >= 0) {
+      const int r = excl[e] + cnt[w * E + e] + lr[it];
+      slot[f] = r;
+      row_src[r] = f;
+    } else {
+      slot[f] = -1;
+    }
+  }
+  for (int r = nrows + threadIdx.x; r < max_rows; r += kThreads) row_src[r] = -1;
+  if (threadIdx.x == 0) *status = sbad;
+}
+
+// Multi-block pass 1: per-chunk counts and chunk-local ranks (kept in slot[]).
+template <typename IdxT>
+__global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__restrict__ idx, int n, int E,
+                                                               int *__restrict__ hist,
+                                                               uint32_t *__restrict__ bstat,
+                                                               int *__restrict__ slot) {
+  __shared__ int cnt[kWaves * kMaxExperts];
+  __shared__ int total[kMaxExperts];
+  __shared__ uint32_t sbad;
+  for (int i = threadIdx.x; i < kWaves * E; i += kThreads) cnt[i] = 0;
+  if (threadIdx.x == 0) sbad = 0;
+  __syncthreads();
+
+  const int nbits = 32 - __builtin_clz((unsigned)E);
+  const int begin = blockIdx.x * kMultiChunk;
+  int ex[kMultiItems], lr[kMultiItems];
+  bool bad = false;
+  wave_rank<IdxT, kMultiItems>(idx, begin, n, E, nbits, cnt, ex, lr, bad);
+  __syncthreads();
+  wave_bases(cnt, total, E);
+  if (bad) atomicOr(&sbad, 1u);
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[(int64_t)blockIdx.x * E + e] = total[e];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int it = 0; it < kMultiItems; ++it) {
+    const int f = begin + w * kMultiItems * kWave + it * kWave + lane;
+    if (f >= n) continue;
+    slot[f] = ex[it] >= 0 ? cnt[w * E + ex[it]] + lr[it] : -1;
+  }
+  if (threadIdx.x == 0) bstat[blockIdx.x] = sbad;
+}
+
+// Multi-block pass 2 (one workgroup): per-expert prefix over chunks, the scan
+// over experts, counts/offsets/statistics/status.  hist[b*E + e] becomes the
+// first receive row of chunk b's pairs with expert e.
+__global__ __launch_bounds__(kThreads) void layout_scan_kernel(int nblocks, int E, int *__restrict__ hist,
+                                                               const uint32_t *__restrict__ bstat,
+                                                               int64_t *__restrict__ recv_count,
+                                                               int *__restrict__ cum,
+                                                               int *__restrict__ offsets,
+                                                               uint32_t *__restrict__ status) {
+  __shared__ int wsum[kWaves];
+  __shared__ int nrows;
+  __shared__ uint32_t sbad;
+  if (threadIdx.x == 0) sbad = 0;
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E) {
+    for (int b = 0; b < nblocks; ++b) {
+      const int h = hist[(int64_t)b * E + e];
+      hist[(int64_t)b * E + e] = c;
+      c += h;
+    }
+  }
+  uint32_t bad = 0;
+  for (int b = threadIdx.x; b < nblocks; b += kThreads) bad |= bstat[b];
+  __syncthreads();
+  if (bad) atomicOr(&sbad, bad);
+  const int pre = block_exclusive_scan(c, wsum, &nrows);
+  if (e < E) {
+    recv_count[e] = c;
+    offsets[e] = pre;
+    if (cum) cum[e] += c;
+    for (int b = 0; b < nblocks; ++b) hist[(int64_t)b * E + e] += pre;
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = nrows;
+    *status = sbad;
+  }
+}
+
+// Multi-block pass 3: final rows, row_src, and -1 for rows past R.
+template <typename IdxT>
+__global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
+    const IdxT *__restrict__ idx, int n, int E, int max_rows, const int *__restrict__ hist,
+    const int *__restrict__ offsets, int *__restrict__ slot, int *__restrict__ row_src) {
+  const int i = blockIdx.x * kFinalizeThreads + threadIdx.x;
+  if (i < n) {
+    bool bad = false;
+    const int e = expert_of(idx, i, n, E, bad);
+    if (e >= 0) {
+      const int r = hist[(int64_t)(i / kMultiChunk) * E + e] + slot[i];
+      slot[i] = r;
+      row_src[r] = i;
+    }
+  }
+  const int R = offsets[E];
+  if (i >= R && i < max_rows) row_src[i] = -1;
+}
+
+template <typename IdxT>
+hipError_t launch_typed(const IdxT *idx, int n, int32_t E, int max_rows, int64_t *recv_count, int32_t *cum,
+                        char *ws, const WsLayout &wl, hipStream_t s) {
+  int *offsets = (int *)(ws + wl.offsets);
+  int *slot = (int *)(ws + wl.slot);
+  int *row_src = (int *)(ws + wl.row_src);
+  uint32_t *status = (uint32_t *)(ws + wl.status);
+  if (n <= kSingleMaxPairs && max_rows <= kSingleMaxRows) {
+    hipLaunchKernelGGL(layout_single_kernel<IdxT>, dim3(1), dim3(kThreads), 0, s, idx, n, E, max_rows,
+                       recv_count, cum, offsets, slot, row_src, status);
+    return hipGetLastError();
+  }
+  int *hist = (int *)(ws + wl.hist);
+  uint32_t *bstat = (uint32_t *)(ws + wl.bstat);
+  const int nb = (n + kMultiChunk - 1) / kMultiChunk;
+  if (nb > 0) {
+    hipLaunchKernelGGL(layout_rank_kernel<IdxT>, dim3(nb), dim3(kThreads), 0, s, idx, n, E, hist, bstat, slot);
+  }
+  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kThreads), 0, s, nb, E, hist, bstat, recv_count, cum,
+                     offsets, status);
+  const int span = max_rows > n ? max_rows : n;
+  const int grid = (span + kFinalizeThreads - 1) / kFinalizeThreads;
+  if (grid > 0) {
+    hipLaunchKernelGGL(layout_finalize_kernel<IdxT>, dim3(grid), dim3(kFinalizeThreads), 0, s, idx, n, E,
+                       max_rows, hist, offsets, slot, row_src);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+WsLayout workspace_layout(int64_t max_tokens, int32_t k, int32_t E) {
+  WsLayout wl{};
+  const int64_t pairs = max_tokens * k;
+  const int64_t nb = (pairs + kMultiChunk - 1) / kMultiChunk;
+  size_t off = 0;
+  wl.offsets = off; off = align_up(off + sizeof(int32_t) * (size_t)(E + 1), kWsAlign);
+  wl.slot = off;    off = align_up(off + sizeof(int32_t) * (size_t)pairs, kWsAlign);
+  wl.row_src = off; off = align_up(off + sizeof(int32_t) * (size_t)pairs, kWsAlign);
+  wl.status = off;  off = align_up(off + sizeof(uint32_t), kWsAlign);
+  wl.hist = off;    off = align_up(off + sizeof(int32_t) * (size_t)(nb * E), kWsAlign);
+  wl.bstat = off;   off = align_up(off + sizeof(uint32_t) * (size_t)nb, kWsAlign);
+  wl.total = off;
+  wl.nblocks = nb;
+  return wl;
+}
+
+hipError_t launch_layout(const void *idx, int idx64, int64_t T, int32_t k, int32_t E, int64_t max_rows,
+                         int64_t *recv_count, int32_t *cum, char *ws, const WsLayout &wl, hipStream_t s) {
+  const int n = (int)(T * k);
+  if (idx64) return launch_typed((const int64_t *)idx, n, E, (int)max_rows, recv_count, cum, ws, wl, s);
+  return launch_typed((const int32_t *)idx, n, E, (int)max_rows, recv_count, cum, ws, wl, s);
+}
+
+}  // namespace ep

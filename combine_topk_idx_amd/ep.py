@@ -1,0 +1,276 @@
+"""ctypes binding of libep.so (argument marshalling only).
+
+The functions ``ep_workspace_bytes``, ``ep_buffer_bytes``, ``ep_layout``,
+``ep_dispatch``, ``ep_combine``, ``ep_read_status``, ``ep_last_error`` and
+``ep_abi_version`` have the names and arguments of the C ABI in
+``include/ep.h``; torch tensors stand in for device pointers and torch's
+current stream is used unless one is passed.  Every computation runs in the
+library's HIP kernels.  Importing this module loads the library and raises
+``ImportError`` if it is missing: there is no fallback.
+
+``low_latency_dispatch`` / ``low_latency_combine`` follow the argument lists of
+the "Low-Latency Mode API" page: they allocate the outputs with torch and call
+the same entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m combine_topk_idx_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_BUFFER_TOO_SMALL, EP_ERR_HIP = range(5)
+EP_IDX_INT32, EP_IDX_INT64 = 0, 1
+QUANT = {"none": 0, "int8_token": 1, "fp8_b128": 2, "mxfp8": 3, "mxfp4": 4}
+EP_STATUS_ID_OUT_OF_RANGE = 1
+
+SYMBOLS = ("ep_workspace_bytes", "ep_buffer_bytes", "ep_layout", "ep_dispatch", "ep_combine",
+           "ep_read_status", "ep_last_error", "ep_abi_version")
+
+
+class ep_handle_t(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("num_max_tokens", ctypes.c_int64),
+        ("max_rows", ctypes.c_int64),
+        ("num_topk", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("offsets", ctypes.c_void_p),
+        ("slot", ctypes.c_void_p),
+        ("row_src", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_lib.ep_workspace_bytes.argtypes = [_i64, _i32, _i32]
+_lib.ep_workspace_bytes.restype = _sz
+_lib.ep_buffer_bytes.argtypes = [_i64, _i32, ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+_lib.ep_buffer_bytes.restype = ctypes.c_int
+_lib.ep_layout.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _sz,
+                           ctypes.POINTER(ep_handle_t), _vp]
+_lib.ep_layout.restype = ctypes.c_int
+_lib.ep_dispatch.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp, _vp]
+_lib.ep_dispatch.restype = ctypes.c_int
+_lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int, _i32, _vp, _vp, _vp]
+_lib.ep_combine.restype = ctypes.c_int
+_lib.ep_read_status.argtypes = [ctypes.POINTER(ep_handle_t), ctypes.POINTER(ctypes.c_uint32), _vp]
+_lib.ep_read_status.restype = ctypes.c_int
+_lib.ep_last_error.argtypes = []
+_lib.ep_last_error.restype = ctypes.c_char_p
+_lib.ep_abi_version.argtypes = []
+_lib.ep_abi_version.restype = _i32
+
+
+class EpError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def _check(code: int) -> None:
+    if code != EP_OK:
+        raise EpError(code, ep_last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _quant(q) -> int:
+    return QUANT[q] if isinstance(q, str) else int(q)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+# ---------------------------------------------------------------------------
+# C ABI, one function each
+# ---------------------------------------------------------------------------
+
+
+def ep_abi_version() -> int:
+    return _lib.ep_abi_version()
+
+
+def ep_last_error() -> str:
+    return (_lib.ep_last_error() or b"").decode()
+
+
+def ep_workspace_bytes(num_max_dispatch_tokens: int, num_topk: int, num_experts: int) -> int:
+    return _lib.ep_workspace_bytes(num_max_dispatch_tokens, num_topk, num_experts)
+
+
+def ep_buffer_bytes(rows: int, hidden: int, quant) -> tuple[int, int]:
+    """(total bytes, scale-region offset)."""
+    total, off = _sz(0), _sz(0)
+    _check(_lib.ep_buffer_bytes(rows, hidden, _quant(quant), ctypes.byref(total), ctypes.byref(off)))
+    return total.value, off.value
+
+
+def ep_layout(topk_idx, num_experts: int, num_max_dispatch_tokens: int, recv_count, workspace,
+              cumulative_recv_stats=None, *, num_tokens=None, num_topk=None, idx_dtype=None,
+              stream=None) -> ep_handle_t:
+    """topk_idx: device tensor [T, k] int32/int64 (or a raw pointer with
+    num_tokens / num_topk / idx_dtype given).  Returns the handle."""
+    if isinstance(topk_idx, torch.Tensor):
+        if topk_idx.dim() != 2 or not topk_idx.is_contiguous():
+            raise EpError(EP_ERR_INVALID_ARG, "topk_idx must be a contiguous [num_tokens, num_topk] tensor")
+        if topk_idx.dtype not in (torch.int32, torch.int64):
+            raise EpError(EP_ERR_INVALID_ARG, "topk_idx dtype must be int32 or int64")
+        num_tokens, num_topk = topk_idx.shape
+        idx_dtype = EP_IDX_INT64 if topk_idx.dtype == torch.int64 else EP_IDX_INT32
+    h = ep_handle_t()
+    _check(_lib.ep_layout(_ptr(topk_idx), idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
+                          num_experts, _ptr(recv_count), _ptr(cumulative_recv_stats), _ptr(workspace),
+                          _nbytes(workspace) if isinstance(workspace, torch.Tensor) else 0,
+                          ctypes.byref(h), _stream(stream)))
+    return h
+
+
+def ep_dispatch(handle: ep_handle_t, x, hidden: int, quant, recv_buf, topk_weights=None,
+                recv_weights=None, *, recv_buf_bytes=None, stream=None) -> None:
+    nbytes = _nbytes(recv_buf) if recv_buf_bytes is None else recv_buf_bytes
+    _check(_lib.ep_dispatch(ctypes.byref(handle), _ptr(x), hidden, _ptr(topk_weights), _quant(quant),
+                            _ptr(recv_buf), nbytes, _ptr(recv_weights), _stream(stream)))
+
+
+def ep_combine(handle: ep_handle_t, expert_out, in_quant, hidden: int, topk_weights, out, *,
+               expert_out_bytes=None, stream=None) -> None:
+    nbytes = _nbytes(expert_out) if expert_out_bytes is None else expert_out_bytes
+    _check(_lib.ep_combine(ctypes.byref(handle), _ptr(expert_out), nbytes, _quant(in_quant), hidden,
+                           _ptr(topk_weights), _ptr(out), _stream(stream)))
+
+
+def ep_read_status(handle: ep_handle_t, stream=None) -> int:
+    flags = ctypes.c_uint32(0)
+    _check(_lib.ep_read_status(ctypes.byref(handle), ctypes.byref(flags), _stream(stream)))
+    return flags.value
+
+
+# ---------------------------------------------------------------------------
+# "Low-Latency Mode API"-shaped wrappers
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class Handle:
+    """What low_latency_dispatch hands to low_latency_combine: the C handle
+    plus the tensors its pointers live in (kept alive here)."""
+    c: ep_handle_t
+    workspace: torch.Tensor
+    hidden: int
+    quant: str
+    topk_idx_shape: tuple
+    topk_idx_dtype: torch.dtype
+
+
+def quant_mode(use_fp8=True, use_ue8m0=False, use_mxfp4=False, quant=None) -> str:
+    """Flag mapping of the "Low-Latency Mode API" page: no use_fp8 -> bf16;
+    use_fp8 -> int8 per token; + use_ue8m0 -> MXFP8; + use_mxfp4 -> MXFP4.
+    ``quant="fp8_b128"`` selects e4m3 with per-128-channel scales."""
+    if quant is not None:
+        if quant not in QUANT:
+            raise EpError(EP_ERR_INVALID_ARG, f"unknown quant {quant!r}")
+        return quant
+    if (use_ue8m0 or use_mxfp4) and not use_fp8:
+        raise EpError(EP_ERR_INVALID_ARG, "use_ue8m0 / use_mxfp4 require use_fp8")
+    if use_ue8m0 and use_mxfp4:
+        raise EpError(EP_ERR_INVALID_ARG, "use_ue8m0 and use_mxfp4 are exclusive")
+    if not use_fp8:
+        return "none"
+    return "mxfp4" if use_mxfp4 else ("mxfp8" if use_ue8m0 else "int8_token")
+
+
+def split_recv(buf: torch.Tensor, rows: int, hidden: int, quant: str):
+    """Views of a receive buffer in the shapes of the page's Return Values."""
+    total, off = ep_buffer_bytes(rows, hidden, quant)
+    q = quant
+    if q == "none":
+        return buf[: rows * hidden * 2].view(torch.bfloat16).view(rows, hidden)
+    if q == "int8_token":
+        return (buf[: rows * hidden].view(torch.int8).view(rows, hidden),
+                buf[off: off + rows * 4].view(torch.float32))
+    if q == "fp8_b128":
+        return (buf[: rows * hidden].view(torch.float8_e4m3fn).view(rows, hidden),
+                buf[off: off + rows * (hidden // 128) * 4].view(torch.float32).view(rows, hidden // 128))
+    if q == "mxfp8":
+        return (buf[: rows * hidden].view(torch.float8_e4m3fn).view(rows, hidden),
+                buf[off: off + rows * (hidden // 32)].view(torch.float8_e8m0fnu))
+    return (buf[: rows * hidden // 2].view(torch.float4_e2m1fn_x2).view(rows, hidden // 2),
+            buf[off: off + rows * (hidden // 32)].view(torch.float8_e8m0fnu))
+
+
+def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispatch_tokens_per_rank: int,
+                         num_experts: int, cumulative_local_expert_recv_stats=None, use_fp8: bool = True,
+                         round_scale: bool = False, use_ue8m0: bool = False, use_mxfp4: bool = False,
+                         async_finish: bool = False, return_recv_hook: bool = False, topk_weights=None,
+                         quant: Optional[str] = None):
+    """Returns (recv_x, recv_count, handle, event, hook) with event and hook
+    None (there is no transport to overlap or to wait for)."""
+    if round_scale or return_recv_hook:
+        raise EpError(EP_ERR_UNSUPPORTED, "round_scale / return_recv_hook are not supported")
+    q = quant_mode(use_fp8, use_ue8m0, use_mxfp4, quant)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise EpError(EP_ERR_INVALID_ARG, "x must be a contiguous bf16 [num_tokens, hidden] tensor")
+    T, H = x.shape
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != T:
+        raise EpError(EP_ERR_INVALID_ARG, "topk_idx must be [num_tokens, num_topk]")
+    k = topk_idx.shape[1]
+    dev = x.device
+    ws = torch.empty(max(ep_workspace_bytes(num_max_dispatch_tokens_per_rank, k, num_experts), 1),
+                     dtype=torch.uint8, device=dev)
+    recv_count = torch.empty(num_experts, dtype=torch.int64, device=dev)
+    h = ep_layout(topk_idx, num_experts, num_max_dispatch_tokens_per_rank, recv_count, ws,
+                  cumulative_local_expert_recv_stats)
+    rows = h.max_rows
+    total, _ = ep_buffer_bytes(rows, H, q)
+    buf = torch.empty(max(total, 16), dtype=torch.uint8, device=dev)
+    recv_w = None
+    if topk_weights is not None:
+        recv_w = torch.empty(max(rows, 1), dtype=torch.float32, device=dev)
+    ep_dispatch(h, x, H, q, buf, topk_weights, recv_w)
+    handle = Handle(h, ws, H, q, tuple(topk_idx.shape), topk_idx.dtype)
+    recv_x = split_recv(buf, rows, H, q)
+    if recv_w is not None:
+        handle.recv_weights = recv_w
+    return recv_x, recv_count, handle, None, None
+
+
+def low_latency_combine(x, topk_idx: torch.Tensor, topk_weights: torch.Tensor, handle: Handle,
+                        zero_copy: bool = False, async_finish: bool = False, return_recv_hook: bool = False,
+                        out: Optional[torch.Tensor] = None, in_quant: str = "none"):
+    """x: bf16 [max_rows, hidden] expert outputs (or a raw uint8 receive-format
+    buffer with ``in_quant``).  Returns (combined_x, event, hook)."""
+    if zero_copy or return_recv_hook:
+        raise EpError(EP_ERR_UNSUPPORTED, "zero_copy / return_recv_hook are not supported")
+    if tuple(topk_idx.shape) != handle.topk_idx_shape or topk_idx.dtype != handle.topk_idx_dtype:
+        raise EpError(EP_ERR_INVALID_ARG, "topk_idx does not match the one given to dispatch")
+    T, H = handle.topk_idx_shape[0], handle.hidden
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=topk_weights.device)
+    ep_combine(handle.c, x, in_quant, H, topk_weights, out)
+    return out, None, None

@@ -150,13 +150,21 @@ def make_inputs(w: Workload) -> dict:
 
 def make_expert_out(w: Workload, rows: int | None = None, chunk: int = 4096) -> np.ndarray:
     """bf16 N(0,1) expert-output rows (uint16 [rows, H]); rows defaults to
-    the workload's max_rows."""
+    the workload's max_rows.  Each block of ``chunk`` rows has its own PCG64
+    stream (seeded from the workload seed and the block number), so the
+    result does not depend on how many threads draw it."""
+    from concurrent.futures import ThreadPoolExecutor
     rows = w.max_rows if rows is None else rows
-    _, _, _, ry = _streams(w.seed)
     y = np.empty((rows, w.H), np.uint16)
-    for r0 in range(0, rows, chunk):
-        r1 = min(rows, r0 + chunk)
-        y[r0:r1] = bf16_from_f32(ry.standard_normal((r1 - r0, w.H), dtype=np.float32))
+
+    def block(b):
+        r0, r1 = b * chunk, min(rows, (b + 1) * chunk)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 4, b])))
+        y[r0:r1] = bf16_from_f32(g.standard_normal((r1 - r0, w.H), dtype=np.float32))
+
+    nblocks = (rows + chunk - 1) // chunk
+    with ThreadPoolExecutor(max_workers=min(8, max(1, nblocks))) as ex:
+        list(ex.map(block, range(nblocks)))
     return y
 
 

@@ -1,0 +1,179 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE token dispatch / combine library
+ * (libep.so).
+ *
+ * The operation is the one the "Low-Latency Mode API" page (DeepEP-Ascend,
+ * sections `low_latency_dispatch` and `low_latency_combine`) states for many
+ * devices, done on one GPU that holds every expert:
+ *
+ *   ep_layout    routing layout from topk_idx: per-expert receive counts, the
+ *                exclusive scan of those counts and a stable token-order row
+ *                for every (token, j) pair.
+ *   ep_dispatch  quantises each bf16 token row once and writes it to the
+ *                receive row of every expert it is routed to.
+ *   ep_combine   gathers each token's expert-output rows, dequantises them and
+ *                reduces them in float32, weighted by topk_weights, in
+ *                ascending j, rounding once to bf16.
+ *
+ * Conventions for every function below:
+ *   - Array arguments are DEVICE pointers unless marked "host".  The caller
+ *     owns every buffer; the library never allocates and never frees.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call is asynchronous on that stream, except ep_read_status, which
+ *     waits for it.
+ *   - All arguments are checked on the host before anything is launched.  On
+ *     failure a call returns a non-zero ep_status_t, launches nothing, and
+ *     ep_last_error() describes the failing check (the "Runtime Validation"
+ *     rule of the "DeepEP topk_idx_t Custom Dtype Requirements" page).
+ *   - Arrays are dense and row-major; "[T, k]" means T rows of k elements.
+ *
+ * Receive buffer format (ep_dispatch output and ep_combine input).  One
+ * caller buffer holds a data region followed by a scale region ("EP dispatch
+ * with unfused MXFP8 quantization", Changes: data and block scales share one
+ * buffer sliced into data then scales):
+ *   data region   rows x Dq bytes, row r at byte r*Dq
+ *   scale region  starts at align_up(rows*Dq, 256); rows x Sq bytes
+ * with rows = handle.max_rows and, for hidden size H:
+ *   EP_QUANT_NONE        Dq = 2H (bf16)             Sq = 0
+ *   EP_QUANT_INT8_TOKEN  Dq = H  (int8)             Sq = 4   (one float32)
+ *   EP_QUANT_FP8_B128    Dq = H  (e4m3fn)           Sq = H/32 (H/128 float32)
+ *   EP_QUANT_MXFP8       Dq = H  (e4m3fn)           Sq = H/32 (e8m0 bytes)
+ *   EP_QUANT_MXFP4       Dq = H/2 (e2m1, element 2i in the low nibble)
+ *                                                   Sq = H/32 (e8m0 bytes)
+ * Expert e owns rows [offsets[e], offsets[e] + recv_count[e]); rows of one
+ * expert are in ascending (token, j) order.  Rows at or past R = offsets[E]
+ * and the padding between the regions are left unspecified.
+ */
+#ifndef EP_H_
+#define EP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_ABI_VERSION 1
+
+typedef enum {
+  EP_OK = 0,
+  EP_ERR_INVALID_ARG = 1,      /* a shape, enum, pointer or alignment check failed */
+  EP_ERR_UNSUPPORTED = 2,      /* a valid request this library does not implement */
+  EP_ERR_BUFFER_TOO_SMALL = 3, /* a caller buffer is smaller than required        */
+  EP_ERR_HIP = 4               /* the HIP runtime reported an error                */
+} ep_status_t;
+
+/* Index dtype of topk_idx ("DeepEP topk_idx_t Custom Dtype Requirements":
+ * int32 or int64; here chosen per call instead of at build time). */
+typedef enum { EP_IDX_INT32 = 0, EP_IDX_INT64 = 1 } ep_idx_dtype_t;
+
+/* Quantisation of a receive row ("Low-Latency Mode API", Parameters use_fp8,
+ * use_ue8m0, use_mxfp4; "DeepEP FP8 Dispatch and Combine Operations", The
+ * Dispatch Stage, for the per-128-channel e4m3 mode). */
+typedef enum {
+  EP_QUANT_NONE = 0,       /* bf16 copy                                          */
+  EP_QUANT_INT8_TOKEN = 1, /* int8, scale amax/127 per token                      */
+  EP_QUANT_FP8_B128 = 2,   /* e4m3fn, scale amax/448 per 128 channels             */
+  EP_QUANT_MXFP8 = 3,      /* e4m3fn, e8m0 power-of-two scale per 32 elements     */
+  EP_QUANT_MXFP4 = 4       /* e2m1 x2 per byte, e8m0 scale per 32 elements        */
+} ep_quant_t;
+
+/* Layout handle ("Low-Latency Mode API": the handle returned by dispatch is
+ * passed unchanged to combine).  Plain data filled in by ep_layout; its
+ * pointers point into the caller's workspace and stay valid while that
+ * workspace lives and is not reused by another ep_layout call. */
+typedef struct {
+  int64_t num_tokens;     /* T                                               */
+  int64_t num_max_tokens; /* capacity num_max_dispatch_tokens (>= T)         */
+  int64_t max_rows;       /* num_max_tokens * num_topk: receive rows         */
+  int32_t num_topk;       /* k                                               */
+  int32_t num_experts;    /* E                                               */
+  int32_t *offsets;       /* device [E+1]: exclusive scan, offsets[E] = R    */
+  int32_t *slot;          /* device [T*k]: receive row of (t, j), or -1      */
+  int32_t *row_src;       /* device [max_rows]: t*k + j of each row, -1 >= R */
+  uint32_t *status;       /* device [1]: bit 0 = some id outside [-1, E)     */
+} ep_handle_t;
+
+/* Status bits written by ep_layout into *handle.status. */
+#define EP_STATUS_ID_OUT_OF_RANGE 1u
+
+/* Bytes of workspace ep_layout needs for the given capacity; 0 if the
+ * arguments are out of range.  Host-only; no device work. */
+size_t ep_workspace_bytes(int64_t num_max_dispatch_tokens, int32_t num_topk, int32_t num_experts);
+
+/* Size of a receive buffer of `rows` rows (format above): writes the total
+ * byte count and the scale-region offset to the host pointers (either may be
+ * NULL).  Host-only. */
+ep_status_t ep_buffer_bytes(int64_t rows, int32_t hidden, ep_quant_t quant, size_t *total_bytes,
+                            size_t *scale_offset);
+
+/* Routing layout ("Low-Latency Mode API", Parameters topk_idx,
+ * num_max_dispatch_tokens_per_rank, num_experts,
+ * cumulative_local_expert_recv_stats; Return Values recv_count).
+ *   topk_idx         device [T, k] of idx_dtype; -1 = no expert.  Ids outside
+ *                    [-1, E) are dropped like -1 and set status bit 0.
+ *                    May be NULL when num_tokens == 0.
+ *   num_tokens       T, 0 <= T <= num_max_dispatch_tokens
+ *   num_topk         k, 0 < k <= 16
+ *   num_max_dispatch_tokens  capacity; max_rows = capacity * k <= 2^31 - 1
+ *   num_experts      E, 0 < E <= 512
+ *   recv_count       device int64 [E], written: rows received per expert
+ *   cumulative_recv_stats  device int32 [E] or NULL: += recv_count
+ *   workspace        device, 256-byte aligned, >= ep_workspace_bytes(...)
+ *   handle           host, written on success
+ * The receive-row order is deterministic: ascending (t, j) within an
+ * expert, independent of timing. */
+ep_status_t ep_layout(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                      int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts,
+                      int64_t *recv_count, int32_t *cumulative_recv_stats, void *workspace,
+                      size_t workspace_bytes, ep_handle_t *handle, void *stream);
+
+/* Dispatch ("Low-Latency Mode API", low_latency_dispatch; "DeepEP FP8
+ * Dispatch and Combine Operations", The Dispatch Stage).
+ *   handle         host, from ep_layout on the same stream (or ordered after it)
+ *   x              device bf16 [T, H], 16-byte aligned.  Only bf16 input is
+ *                  accepted: pre-quantised input is not a valid x.
+ *   hidden         H > 0, H % 32 == 0 (H % 128 == 0 for EP_QUANT_FP8_B128)
+ *   topk_weights   device float32 [T, k] or NULL
+ *   recv_buf       device, 16-byte aligned, >= ep_buffer_bytes(max_rows, H, quant)
+ *   recv_weights   device float32 [max_rows] or NULL; if given (and
+ *                  topk_weights too) row slot[t, j] receives topk_weights[t, j]
+ * Each token row is read once and quantised once; its packed row and scales
+ * are written to every routed row. */
+ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden,
+                        const float *topk_weights, ep_quant_t quant, void *recv_buf,
+                        size_t recv_buf_bytes, float *recv_weights, void *stream);
+
+/* Combine ("Low-Latency Mode API", low_latency_combine; "DeepEP FP8 Dispatch
+ * and Combine Operations", The FP8 Combine Operation).
+ *   handle          host, from the ep_layout of the matching dispatch
+ *   expert_out      device receive-format buffer (format above, rows =
+ *                   max_rows) of in_quant, 16-byte aligned
+ *   topk_weights    device float32 [T, k], required
+ *   out             device bf16 [T, H], 16-byte aligned, written
+ * out[t] = bf16_rne( sum over j = 0..k-1 with slot[t, j] >= 0 of
+ *                    fl32(w[t, j] * dequant(row slot[t, j])) ), accumulated in
+ * float32 in ascending j with one rounding per multiply and per add; a token
+ * with no routed pair gets +0.  Dequantisation: int8 and e4m3-per-128 codes
+ * times their float32 scale (one rounding); MX codes times 2^(byte-127)
+ * (exact unless the product leaves float32's range); e8m0 byte 0xFF is NaN.
+ * The routing comes from the handle (the topk_idx that produced it). */
+ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t expert_out_bytes,
+                       ep_quant_t in_quant, int32_t hidden, const float *topk_weights, void *out,
+                       void *stream);
+
+/* Waits for `stream` and copies the status word of `handle` to host *flags. */
+ep_status_t ep_read_status(const ep_handle_t *handle, uint32_t *flags, void *stream);
+
+/* Text of the last failed check or runtime error on the calling thread. */
+const char *ep_last_error(void);
+
+/* EP_ABI_VERSION of the built library. */
+int32_t ep_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H_ */

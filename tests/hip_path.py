@@ -1,0 +1,140 @@
+"""Test helpers: run the HIP library and the CPU oracle on the same seeded
+inputs and read the HIP results back for comparison.
+
+The HIP side goes only through the C ABI (``combine_topk_idx_amd.ep``); the
+oracle side only through ``oracle``.  The two never exchange data: each one
+builds its own combine input from its own dispatch output when the workload
+feeds dispatched rows back into combine.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from combine_topk_idx_amd import workloads as W
+
+NAN_BF16 = 0x7FC0
+DEV = "cuda"
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@dataclass
+class HipRun:
+    handle: object
+    workspace: torch.Tensor
+    recv_count: np.ndarray
+    offsets: np.ndarray
+    slot: np.ndarray
+    row_src: np.ndarray
+    status: int
+    recv: torch.Tensor            # uint8 receive buffer
+    recv_weights: torch.Tensor | None
+    out: np.ndarray | None        # uint16 [T, H]
+
+
+def ws_view(ws: torch.Tensor, ptr: int, n: int, dtype) -> torch.Tensor:
+    off = ptr - ws.data_ptr()
+    item = torch.empty((), dtype=dtype).element_size()
+    return ws[off: off + n * item].view(dtype)
+
+
+def canary_buffer(total: int) -> torch.Tensor:
+    """uint8 buffer whose every bf16 lane is a NaN canary (0x7FC0)."""
+    b = torch.empty(max(total, 16) // 2 * 2 + 16, dtype=torch.uint8, device=DEV)
+    b.view(torch.int16).fill_(NAN_BF16)
+    return b
+
+
+def run_layout(ep, w: W.Workload, idx: np.ndarray, cum=None):
+    ws = torch.empty(max(ep.ep_workspace_bytes(w.t_max, w.k, w.E), 256), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)                                   # garbage: nothing may rely on zeroed workspace
+    recv_count = torch.full((w.E,), -7, dtype=torch.int64, device=DEV)
+    h = ep.ep_layout(to_dev(idx), w.E, w.t_max, recv_count, ws, cum)
+    return h, ws, recv_count
+
+
+def read_layout(ep, h, ws, recv_count, w):
+    torch.cuda.synchronize()
+    return dict(
+        recv_count=recv_count.cpu().numpy(),
+        offsets=ws_view(ws, h.offsets, w.E + 1, torch.int32).cpu().numpy(),
+        slot=ws_view(ws, h.slot, w.T * w.k, torch.int32).cpu().numpy().reshape(w.T, w.k),
+        row_src=ws_view(ws, h.row_src, w.max_rows, torch.int32).cpu().numpy(),
+        status=ep.ep_read_status(h),
+    )
+
+
+def run_path(ep, w: W.Workload, inp: dict, *, expert_out: np.ndarray | None = None,
+             with_recv_weights=True, do_combine=True) -> HipRun:
+    """layout -> dispatch -> (expert step) -> combine on the GPU."""
+    h, ws, recv_count = run_layout(ep, w, inp["topk_idx"])
+    x = to_dev(inp["x"])
+    wts = to_dev(inp["topk_weights"])
+    total, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    recv = canary_buffer(total)
+    recv_w = torch.full((max(w.max_rows, 1),), float("nan"), device=DEV) if with_recv_weights else None
+    ep.ep_dispatch(h, x, w.H, w.mode, recv, wts if with_recv_weights else None, recv_w)
+    lay = read_layout(ep, h, ws, recv_count, w)
+    out = None
+    if do_combine:
+        if w.combine_input == "identity":
+            src, q = recv, w.mode
+        elif w.combine_input == "scaled_dispatch":
+            assert w.mode == "none"
+            rows = recv[: w.max_rows * w.H * 2].view(torch.bfloat16)
+            src = canary_buffer(total)
+            src[: w.max_rows * w.H * 2].view(torch.bfloat16).copy_((rows.float() * 1.5).to(torch.bfloat16))
+            q = "none"
+        else:
+            assert expert_out is not None
+            y = expert_out.copy()
+            y[int(lay["offsets"][-1]):] = NAN_BF16
+            src, q = to_dev(y).view(torch.uint8).reshape(-1), "none"
+        o = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
+        ep.ep_combine(h, src, q, w.H, wts, o)
+        torch.cuda.synchronize()
+        out = bf16_bits(o)
+    return HipRun(h, ws, lay["recv_count"], lay["offsets"], lay["slot"], lay["row_src"], lay["status"],
+                  recv, recv_w, out)
+
+
+def recv_rows(ep, run: HipRun, w: W.Workload, rows=None):
+    """(data [n, Dq], scales [n, Sq]) of the HIP receive buffer (numpy)."""
+    from oracle import quant as Q   # row sizes only
+    dq, sq = Q.row_bytes(w.mode, w.H)
+    _, off = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    buf = run.recv
+    data = buf[: w.max_rows * dq].view(w.max_rows, dq)
+    scales = buf[off: off + w.max_rows * sq].view(w.max_rows, sq) if sq else buf[:0].view(0, 0)
+    if rows is not None:
+        idx = torch.as_tensor(np.asarray(rows, np.int64), device=DEV)
+        data = data.index_select(0, idx)
+        scales = scales.index_select(0, idx) if sq else scales
+    return data.cpu().numpy(), scales.cpu().numpy()
+
+
+def sample_tokens(w: W.Workload, idx: np.ndarray, n: int = 48, seed: int = 0) -> np.ndarray:
+    """First and last tokens, random ones, and some routed to the busiest expert."""
+    rng = np.random.default_rng(seed)
+    T = w.T
+    picks = set(range(min(8, T))) | set(range(max(0, T - 8), T))
+    picks |= set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    flat = idx.reshape(-1)
+    valid = flat[(flat >= 0) & (flat < w.E)]
+    if valid.size:
+        hot = np.bincount(valid, minlength=w.E).argmax()
+        hot_tok = np.nonzero((idx == hot).any(axis=1))[0]
+        picks |= set(hot_tok[:8].tolist()) | set(hot_tok[-8:].tolist())
+    return np.array(sorted(picks), np.int64)
