@@ -122,7 +122,7 @@ template <int Q, int NT, int VPT>
 hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out, hipStream_t s) {
   size_t dq, sq;
   row_bytes(Q, hidden, &dq, &sq);
-  const size_t scale_off = align_up((size_t)h.max_rows * dq, kScaleAlign);
+  const size_t scale_off = scale_offset(h.max_rows, dq, sq);
   const int nvec = hidden / 8;
   const int chunks = (nvec + NT * VPT - 1) / (NT * VPT);
   const int64_t blocks = h.num_tokens * chunks;

@@ -33,6 +33,12 @@ __host__ __device__ inline void row_bytes(int quant, int hidden, size_t *dq, siz
   }
 }
 
+// Byte offset of the scale region in a receive buffer of `rows` rows (no
+// padding when there is no scale region).
+__host__ __device__ inline size_t scale_offset(int64_t rows, size_t dq, size_t sq) {
+  return sq ? align_up((size_t)rows * dq, kScaleAlign) : (size_t)rows * dq;
+}
+
 // DPP lane exchanges (wave64, no LDS traffic).  Controls: quad_perm
 // [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E; row_ror:n = 0x120 + n (rotate within a
 // row of 16 lanes).

@@ -273,7 +273,7 @@ hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const fl
                        float *recv_w, hipStream_t s) {
   size_t dq, sq;
   row_bytes(Q, hidden, &dq, &sq);
-  const size_t scale_off = align_up((size_t)h.max_rows * dq, kScaleAlign);
+  const size_t scale_off = scale_offset(h.max_rows, dq, sq);
   const int nvec = hidden / 8;
   if constexpr (Q == EP_QUANT_INT8_TOKEN) {
     // the whole row must sit in one workgroup (its amax is a row reduction)

@@ -60,7 +60,7 @@ ep_status_t check_handle(const ep_handle_t *h, const char *fn) {
 size_t buffer_bytes(int64_t rows, int32_t hidden, int quant, size_t *scale_off) {
   size_t dq, sq;
   ep::row_bytes(quant, hidden, &dq, &sq);
-  const size_t off = ep::align_up((size_t)rows * dq, ep::kScaleAlign);
+  const size_t off = ep::scale_offset(rows, dq, sq);
   if (scale_off) *scale_off = off;
   return off + (size_t)rows * sq;
 }
@@ -156,7 +156,7 @@ ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden
   const size_t need = buffer_bytes(handle->max_rows, hidden, quant, nullptr);
   if (recv_buf_bytes < need)
     return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: recv_buf has %zu bytes, needs %zu", fn, recv_buf_bytes, need);
-  if (recv_weights && !topk_weights)
+  if (recv_weights && !topk_weights && handle->num_tokens > 0)
     return fail(EP_ERR_INVALID_ARG, "%s: recv_weights given without topk_weights", fn);
   if ((topk_weights && !aligned(topk_weights, 4)) || (recv_weights && !aligned(recv_weights, 4)))
     return fail(EP_ERR_INVALID_ARG, "%s: weights are misaligned", fn);

@@ -33,6 +33,7 @@
  * buffer sliced into data then scales):
  *   data region   rows x Dq bytes, row r at byte r*Dq
  *   scale region  starts at align_up(rows*Dq, 256); rows x Sq bytes
+ *                 (EP_QUANT_NONE has no scale region and no padding)
  * with rows = handle.max_rows and, for hidden size H:
  *   EP_QUANT_NONE        Dq = 2H (bf16)             Sq = 0
  *   EP_QUANT_INT8_TOKEN  Dq = H  (int8)             Sq = 4   (one float32)

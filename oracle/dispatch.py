@@ -11,7 +11,7 @@ sliced into a data region followed by a scale region):
 
 * data region: ``max_rows`` rows of ``Dq`` bytes, row-major;
 * scale region: starts at ``align_up(max_rows * Dq, 256)``; ``max_rows`` rows
-  of ``Sq`` bytes.
+  of ``Sq`` bytes.  bf16 rows have no scale region and no padding.
 
 ``Dq``/``Sq`` per mode are in ``quant.row_bytes``.  Rows at or past R and the
 padding between the regions are unspecified and never compared.
@@ -42,7 +42,7 @@ def align_up(n: int, a: int) -> int:
 def buffer_bytes(rows: int, hidden: int, mode: str) -> tuple[int, int]:
     """(total bytes, scale-region offset) of a receive buffer of ``rows``."""
     dq, sq = quant.row_bytes(mode, hidden)
-    off = align_up(rows * dq, SCALE_REGION_ALIGN)
+    off = align_up(rows * dq, SCALE_REGION_ALIGN) if sq else rows * dq
     return off + rows * sq, off
 
 

@@ -117,11 +117,16 @@ def recv_rows(ep, run: HipRun, w: W.Workload, rows=None):
     _, off = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
     buf = run.recv
     data = buf[: w.max_rows * dq].view(w.max_rows, dq)
-    scales = buf[off: off + w.max_rows * sq].view(w.max_rows, sq) if sq else buf[:0].view(0, 0)
+    n = w.max_rows
     if rows is not None:
         idx = torch.as_tensor(np.asarray(rows, np.int64), device=DEV)
         data = data.index_select(0, idx)
-        scales = scales.index_select(0, idx) if sq else scales
+        n = len(rows)
+    if not sq:
+        return data.cpu().numpy(), np.zeros((n, 0), np.uint8)
+    scales = buf[off: off + w.max_rows * sq].view(w.max_rows, sq)
+    if rows is not None:
+        scales = scales.index_select(0, idx)
     return data.cpu().numpy(), scales.cpu().numpy()
 
 

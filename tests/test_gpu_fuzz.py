@@ -159,7 +159,8 @@ def test_low_latency_wrappers(ep):
     """The page-shaped Python wrappers return the page's shapes and the same
     bytes as the oracle."""
     _announce("low_latency_dispatch / low_latency_combine wrappers")
-    w = W.Workload("ll", 24, 256, 8, 4, "int64", "mxfp4", "uniform", neg_frac=0.1, seed=31)
+    w = W.Workload("ll", 24, 256, 8, 4, "int64", "mxfp4", "uniform", neg_frac=0.1, seed=31,
+                   combine_input="identity")
     inp = W.make_inputs(w)
     x = to_dev(inp["x"])
     idx = to_dev(inp["topk_idx"])
