@@ -17,6 +17,7 @@
 // run in ascending j.
 #include "common.hpp"
 #include "formats.hpp"
+#include "tuning.hpp"
 
 namespace ep {
 
@@ -31,7 +32,9 @@ template <> struct Raw<EP_QUANT_MXFP4> { using T = uint32_t; };
 
 template <int Q> constexpr int kBytesPerVec = sizeof(typename Raw<Q>::T);
 
-// dequantised 8 elements of one row vector
+// dequantised 8 elements of one row vector; `scale` is the row's float32
+// scale (int8), the block's float32 scale (e4m3 per 128) or the block's
+// power of two 2^(byte-127) (MX)
 template <int Q>
 __device__ __forceinline__ void dequant8(const typename Raw<Q>::T &r, float scale, float (&y)[8]) {
   if constexpr (Q == EP_QUANT_NONE) {
@@ -46,17 +49,19 @@ __device__ __forceinline__ void dequant8(const typename Raw<Q>::T &r, float scal
       const int q = (int)(int8_t)((r[i >> 2] >> (8 * (i & 3))) & 0xffu);
       y[i] = (float)q * scale;
     }
-  } else if constexpr (Q == EP_QUANT_FP8_B128 || Q == EP_QUANT_MXFP8) {
+  } else if constexpr (Q == EP_QUANT_FP8_B128) {
+    e4m3x8_decode(r, y);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = e4m3_decode((r[i >> 2] >> (8 * (i & 3))) & 0xffu) * scale;
+    for (int i = 0; i < 8; ++i) y[i] = y[i] * scale;
+  } else if constexpr (Q == EP_QUANT_MXFP8) {
+    e4m3x8_decode_scaled(r, scale, y);
   } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = e2m1_decode((r >> (4 * i)) & 0xfu) * scale;
+    e2m1x8_decode_scaled(r, scale, y);
   }
 }
 
 template <int Q, int NT, int VPT>
-__global__ __launch_bounds__(NT) void combine_kernel(const char *__restrict__ data, const char *__restrict__ scales,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void combine_kernel(const char *__restrict__ data, const char *__restrict__ scales,
                                                      int64_t dq, int64_t sq, int nvec, int k, int chunks,
                                                      const int *__restrict__ slot, const float *__restrict__ w,
                                                      u32x4 *__restrict__ out) {
@@ -84,37 +89,50 @@ __global__ __launch_bounds__(NT) void combine_kernel(const char *__restrict__ da
   for (int i = 0; i < VPT; ++i) {
     const int v = v0 + i * NT;
     if (v >= nvec) continue;
+    // phase 1: issue every row load (data and scale) of this vector
     RawT raw[kMaxTopk];
-    float sc[kMaxTopk];
+    uint32_t sraw[kMaxTopk];
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) {
+      raw[j] = RawT{};
+      sraw[j] = 0;
       if (s[j] < 0) continue;
-      raw[j] = *(const RawT *)(data + s[j] * dq + (int64_t)v * kBytesPerVec<Q>);
-      if constexpr (Q == EP_QUANT_NONE) {
-        sc[j] = 1.0f;
-      } else if constexpr (Q == EP_QUANT_INT8_TOKEN) {
-        sc[j] = rs[j];
-      } else if constexpr (Q == EP_QUANT_FP8_B128) {
-        sc[j] = *(const float *)(scales + s[j] * sq + (int64_t)(v >> 4) * 4);
-      } else {
-        sc[j] = e8m0_decode(*(const uint8_t *)(scales + s[j] * sq + (int64_t)(v >> 2)));
+      const RawT *src = (const RawT *)(data + s[j] * dq + (int64_t)v * kBytesPerVec<Q>);
+#if EP_COMBINE_NT_LOAD
+      raw[j] = __builtin_nontemporal_load(src);
+#else
+      raw[j] = *src;
+#endif
+      if constexpr (Q == EP_QUANT_FP8_B128) {
+        sraw[j] = *(const uint32_t *)(scales + s[j] * sq + (int64_t)(v >> 4) * 4);
+      } else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) {
+        sraw[j] = *(const uint8_t *)(scales + s[j] * sq + (int64_t)(v >> 2));
       }
     }
+    // phase 2: dequantise and accumulate in ascending j
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) {
       if (s[j] < 0) continue;
+      float sc = 1.0f;
+      if constexpr (Q == EP_QUANT_INT8_TOKEN) sc = rs[j];
+      else if constexpr (Q == EP_QUANT_FP8_B128) sc = __uint_as_float(sraw[j]);
+      else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) sc = e8m0_decode(sraw[j]);
       float y[8];
-      dequant8<Q>(raw[j], sc[j], y);
+      dequant8<Q>(raw[j], sc, y);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = acc[e] + wt[j] * y[e];
     }
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+#if EP_COMBINE_NT_STORE
+    __builtin_nontemporal_store(o, out + (int64_t)t * nvec + v);
+#else
     out[(int64_t)t * nvec + v] = o;
+#endif
   }
 }
 
@@ -136,12 +154,13 @@ hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const floa
 
 hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const float *w, void *out,
                           hipStream_t s) {
+  constexpr int NT = EP_COMBINE_THREADS, VPT = EP_COMBINE_VPT;
   switch (quant) {
-    case EP_QUANT_NONE: return launch_q<EP_QUANT_NONE, 128, 1>(h, in, hidden, w, out, s);
-    case EP_QUANT_INT8_TOKEN: return launch_q<EP_QUANT_INT8_TOKEN, 128, 1>(h, in, hidden, w, out, s);
-    case EP_QUANT_FP8_B128: return launch_q<EP_QUANT_FP8_B128, 128, 1>(h, in, hidden, w, out, s);
-    case EP_QUANT_MXFP8: return launch_q<EP_QUANT_MXFP8, 128, 1>(h, in, hidden, w, out, s);
-    default: return launch_q<EP_QUANT_MXFP4, 128, 1>(h, in, hidden, w, out, s);
+    case EP_QUANT_NONE: return launch_q<EP_QUANT_NONE, NT, VPT>(h, in, hidden, w, out, s);
+    case EP_QUANT_INT8_TOKEN: return launch_q<EP_QUANT_INT8_TOKEN, NT, VPT>(h, in, hidden, w, out, s);
+    case EP_QUANT_FP8_B128: return launch_q<EP_QUANT_FP8_B128, NT, VPT>(h, in, hidden, w, out, s);
+    case EP_QUANT_MXFP8: return launch_q<EP_QUANT_MXFP8, NT, VPT>(h, in, hidden, w, out, s);
+    default: return launch_q<EP_QUANT_MXFP4, NT, VPT>(h, in, hidden, w, out, s);
   }
 }
 

@@ -18,25 +18,29 @@
 // adjacent lanes and a 128-channel block 16 adjacent lanes, so block maxima
 // are DPP exchanges inside a quad or a 16-lane row; the int8 row maximum is a
 // workgroup reduction.  Routed rows and weights are read once per workgroup
-// (scalar loads).  Stores are non-temporal: the receive buffer is written
-// once and not read back by this kernel.
+// (scalar loads).  Stores go through the cache hierarchy (which merges the
+// 4-8 byte lane stores into full lines); a non-temporal variant is a build
+// option in tuning.hpp.
+#include <type_traits>
+
 #include "common.hpp"
 #include "formats.hpp"
+#include "tuning.hpp"
 
 namespace ep {
 
 namespace {
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
 // largest |x| of the 8 bf16 elements of a vector, as the bits of a
-// non-negative bf16 (unsigned order == float order for these)
+// non-negative bf16 (unsigned order == float order for these); packed
+// 16-bit max over the four words, then the two halves
 __device__ __forceinline__ uint32_t vec_absmax_bits(const u32x4 &r) {
-  uint32_t m = 0;
+  u16x2 m = __builtin_bit_cast(u16x2, r[0] & 0x7fff7fffu);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = max(m, r[i] & 0x7fffu);
-    m = max(m, (r[i] >> 16) & 0x7fffu);
-  }
-  return m;
+  for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, r[i] & 0x7fff7fffu));
+  return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 __device__ __forceinline__ void unpack8(const u32x4 &r, float (&f)[8]) {
@@ -73,54 +77,54 @@ __device__ __forceinline__ u32x2 codes_int8(const float (&f)[8], const ScaledBlo
   return u32x2{w[0], w[1]};
 }
 
+// e4m3 codes of fl(x*m) clamped to +-448; a zero block stores +0 codes
 __device__ __forceinline__ u32x2 codes_e4m3_scaled(const float (&f)[8], const ScaledBlock &b) {
-  uint32_t w[2] = {0, 0};
+  float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float v = fminf(fmaxf(f[i] * b.m, -448.0f), 448.0f);
-    const uint32_t c = b.zero ? 0u : e4m3_encode(v);
-    w[i >> 2] |= c << (8 * (i & 3));
+    v[i] = fminf(fmaxf(f[i] * b.m, -448.0f), 448.0f);
+    v[i] = b.zero ? 0.0f : v[i];
   }
-  return u32x2{w[0], w[1]};
+  return e4m3x8_encode(v);
 }
 
-// MX shared exponent of a block from its amax bits (bf16 pattern); returns the
-// e8m0 byte and the float32 multiplier 2^-exp.
-__device__ __forceinline__ uint32_t mx_scale(uint32_t amax_bits, int emax, float &mult) {
+// MX shared exponent of a block from its amax bits (bf16 pattern): returns
+// the e8m0 byte, 2^-exp in `mult` and 2^exp in `scale` (both exact float32;
+// exp = -127 makes `scale` the subnormal 2^-127).
+__device__ __forceinline__ uint32_t mx_scale(uint32_t amax_bits, int emax, float &mult, float &scale) {
   int se = -127;
   if (amax_bits != 0) {
     se = floor_log2_bits(amax_bits << 16) - emax;
     se = se < -127 ? -127 : (se > 127 ? 127 : se);
   }
-  // 2^-se with se in [-127, 126] is a normal float32 (se = 127 cannot occur
-  // for finite bf16 input because floor(log2) <= 127 and emax >= 2)
+  // se <= 127 - emax for finite bf16 input, so 2^-se is a normal float32
   mult = __uint_as_float((uint32_t)(127 - se) << 23);
+  scale = se == -127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(se + 127) << 23);
   return (uint32_t)(se + 127);
 }
 
 __device__ __forceinline__ u32x2 codes_mxfp8(const float (&f)[8], float mult) {
-  uint32_t w[2] = {0, 0};
+  float v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float v = fminf(fmaxf(f[i] * mult, -448.0f), 448.0f);
-    w[i >> 2] |= e4m3_encode(v) << (8 * (i & 3));
-  }
-  return u32x2{w[0], w[1]};
+  for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(f[i] * mult, -448.0f), 448.0f);
+  return e4m3x8_encode(v);
 }
 
-__device__ __forceinline__ uint32_t codes_mxfp4(const float (&f)[8], float mult) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float v = fminf(fmaxf(f[i] * mult, -6.0f), 6.0f);
-    w |= e2m1_encode(v) << (4 * i);
-  }
-  return w;
+// Keeps a computed value in registers as is: without it the compiler re-derives
+// the codes inside every per-row store branch instead of once per vector.
+template <typename T>
+__device__ __forceinline__ T pin(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 template <typename T>
-__device__ __forceinline__ void st_nt(char *p, const T &v) {
+__device__ __forceinline__ void st_row(char *p, const T &v) {
+#if EP_DISPATCH_NT_STORE
   __builtin_nontemporal_store(v, (T *)p);
+#else
+  *(T *)p = v;
+#endif
 }
 
 // Workgroup max of one unsigned per thread (NT threads).
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
       if (v >= nvec) continue;
 #pragma unroll
       for (int j = 0; j < kMaxTopk; ++j)
-        if (s[j] >= 0) st_nt(data + s[j] * dq + (int64_t)v * 16, raw[i]);
+        if (s[j] >= 0) st_row(data + s[j] * dq + (int64_t)v * 16, raw[i]);
     }
   } else if constexpr (Q == EP_QUANT_INT8_TOKEN) {
     __shared__ uint32_t red[NT / kWave];
@@ -190,38 +194,38 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
       if (v >= nvec) continue;
       float f[8];
       unpack8(raw[i], f);
-      const u32x2 q = codes_int8(f, b);
+      const u32x2 q = pin(codes_int8(f, b));
 #pragma unroll
       for (int j = 0; j < kMaxTopk; ++j)
-        if (s[j] >= 0) st_nt(data + s[j] * dq + (int64_t)v * 8, q);
+        if (s[j] >= 0) st_row(data + s[j] * dq + (int64_t)v * 8, q);
     }
     if (threadIdx.x == 0) {
 #pragma unroll
       for (int j = 0; j < kMaxTopk; ++j)
-        if (s[j] >= 0) st_nt(scales + s[j] * sq, b.scale);
+        if (s[j] >= 0) st_row(scales + s[j] * sq, b.scale);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int v = v0 + i * NT;
-      float f[8];
-      unpack8(raw[i], f);
       const uint32_t am = vec_absmax_bits(raw[i]);
       if constexpr (Q == EP_QUANT_FP8_B128) {
+        float f[8];
+        unpack8(raw[i], f);
         const ScaledBlock b = scaled_block(row16_max(am), 448.0f);   // all 16 lanes
         if (v >= nvec) continue;
-        const u32x2 q = codes_e4m3_scaled(f, b);
+        const u32x2 q = pin(codes_e4m3_scaled(f, b));
         const bool lead = (v & 15) == 0;
 #pragma unroll
         for (int j = 0; j < kMaxTopk; ++j) {
           if (s[j] < 0) continue;
-          st_nt(data + s[j] * dq + (int64_t)v * 8, q);
-          if (lead) st_nt(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
+          st_row(data + s[j] * dq + (int64_t)v * 8, q);
+          if (lead) st_row(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
         }
       } else {
         constexpr int emax = Q == EP_QUANT_MXFP8 ? 8 : 2;
-        float mult;
-        const uint32_t sbyte = mx_scale(quad_max(am), emax, mult);
+        float mult, scale;
+        const uint32_t sbyte = mx_scale(quad_max(am), emax, mult, scale);
         uint32_t sword = sbyte;
         if constexpr (PACK) {
           // gather the scale bytes of 4 consecutive blocks (lanes 0, 4, 8, 12
@@ -237,19 +241,24 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
         }
         if (v >= nvec) continue;
         const bool lead = PACK ? (v & 15) == 0 : (v & 3) == 0;
+        constexpr int kBytes = Q == EP_QUANT_MXFP8 ? 8 : 4;
+        using Codes = typename std::conditional<Q == EP_QUANT_MXFP8, u32x2, uint32_t>::type;
+        Codes q;
+        if constexpr (Q == EP_QUANT_MXFP8) {
+          float f[8];
+          unpack8(raw[i], f);
+          q = pin(codes_mxfp8(f, mult));
+        } else {
+          q = pin(e2m1x8_encode_bf16(raw[i], scale));
+        }
 #pragma unroll
         for (int j = 0; j < kMaxTopk; ++j) {
           if (s[j] < 0) continue;
-          char *drow = data + s[j] * dq;
-          if constexpr (Q == EP_QUANT_MXFP8) {
-            st_nt(drow + (int64_t)v * 8, codes_mxfp8(f, mult));
-          } else {
-            st_nt(drow + (int64_t)v * 4, codes_mxfp4(f, mult));
-          }
+          st_row(data + s[j] * dq + (int64_t)v * kBytes, q);
           if (lead) {
             char *sp = scales + s[j] * sq + (int64_t)(v >> 2);
-            if constexpr (PACK) st_nt(sp, sword);
-            else st_nt(sp, (uint8_t)sbyte);
+            if constexpr (PACK) st_row(sp, sword);
+            else st_row(sp, (uint8_t)sbyte);
           }
         }
       }
@@ -283,10 +292,11 @@ hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const fl
     if (nvec <= 2048) return launch_q<Q, 256, 8>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
     return launch_q<Q, 1024, 8>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
   } else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) {
-    if (hidden % 128 == 0) return launch_q<Q, 128, 1, true>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    return launch_q<Q, 128, 1, false>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    constexpr int NT = EP_DISPATCH_THREADS, VPT = EP_DISPATCH_VPT;
+    if (hidden % 128 == 0) return launch_q<Q, NT, VPT, true>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    return launch_q<Q, NT, VPT, false>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
   } else {
-    return launch_q<Q, 128, 1>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    return launch_q<Q, EP_DISPATCH_THREADS, EP_DISPATCH_VPT>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
   }
 }
 

@@ -1,98 +1,43 @@
 // Device-side element codecs for gfx950: bf16, e4m3fn, e2m1, e8m0.
 //
-// Written from the public OCP definitions of the formats the "Low-Latency
-// Mode API" page names for its receive buffers (float8_e4m3fn data,
-// float4_e2m1fn_x2 data, float8_e8m0fnu scales) and from IEEE bf16.  All
-// roundings are round-to-nearest, ties to even.  Encoders take float32 input
-// already clamped to the format's largest finite value.
+// The formats are the OCP ones the "Low-Latency Mode API" page names for its
+// receive buffers (float8_e4m3fn data, float4_e2m1fn_x2 data, float8_e8m0fnu
+// scales) and IEEE bf16.  All roundings are round-to-nearest, ties to even.
+// The conversions use gfx950's hardware convert instructions; each wrapper
+// states the input range for which it was checked bit-exact, over every input
+// of that range, against a software implementation of the format definition.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace ep {
 
 // bf16 <-> f32 ---------------------------------------------------------------
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Round-to-nearest-even on the 16 dropped bits; NaN becomes a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// Two float32 -> two bf16 (round to nearest even), element `lo` in bits 0-15.
+// gfx950 converts in hardware (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-}
-
-// e4m3fn: bias 7, 3 mantissa bits, largest finite 448 ---------------------------
-
-// |v| <= 448.  Below 2^-6 the format is subnormal with step 2^-9: scale by
-// 2^9 (exact) and round to an integer.  Otherwise round the float32 mantissa
-// to 3 bits with the usual add-half-minus-one-plus-lsb trick on the bit
-// pattern (a carry propagates into the exponent) and rebias 127 -> 7.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  uint32_t mag;
-  if (a < 0x3c800000u) {
-    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  } else {
-    mag = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  }
-  return sign | mag;
-}
-
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const uint32_t sign = (c & 0x80u) << 24;
-  float mag;
-  if (e == 0) {
-    mag = (float)m * 0.001953125f;                               // m * 2^-9, exact
-  } else if (e == 15 && m == 7) {
-    mag = __uint_as_float(0x7fc00000u);
-  } else {
-    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  }
-  return __uint_as_float(__float_as_uint(mag) | sign);
-}
-
-// e2m1: bias 1, 1 mantissa bit, values 0 .5 1 1.5 2 3 4 6 ------------------------
-
-// |v| <= 6.  Below 1 the step is 0.5 (subnormal); otherwise round the mantissa
-// to one bit and rebias 127 -> 1.  Returns the 4-bit code, sign in bit 3.
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 28) & 0x8u;
-  const uint32_t a = u & 0x7fffffffu;
-  uint32_t mag;
-  if (a < 0x3f800000u) {
-    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
-  } else {
-    mag = ((a + 0x1fffffu + ((a >> 22) & 1u)) >> 22) - (126u << 1);
-  }
-  return sign | mag;
-}
-
-__device__ __forceinline__ float e2m1_decode(uint32_t c) {
-  // magnitudes x2: 0 1 2 3 4 6 8 12, halved exactly
-  const uint32_t twice = (0xC8643210u >> ((c & 7u) * 4u)) & 0xFu;
-  const float mag = (float)twice * 0.5f;
-  return (c & 8u) ? -mag : mag;
+  const bf16x2 p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
 }
 
 // e8m0 -----------------------------------------------------------------------
 
 // 2^(b-127) as float32; b = 0 gives the subnormal 2^-127; 0xFF is NaN.
 __device__ __forceinline__ float e8m0_decode(uint32_t b) {
-  if (b == 0xffu) return __uint_as_float(0x7fc00000u);
-  if (b == 0u) return __uint_as_float(0x00400000u);
-  return __uint_as_float(b << 23);
+  uint32_t bits = b ? b << 23 : 0x00400000u;
+  bits = b == 0xffu ? 0x7fc00000u : bits;
+  return __uint_as_float(bits);
 }
 
 // floor(log2(a)) of a positive finite float32 given by its bits (subnormals
@@ -100,6 +45,72 @@ __device__ __forceinline__ float e8m0_decode(uint32_t b) {
 __device__ __forceinline__ int floor_log2_bits(uint32_t a) {
   const int ef = (int)(a >> 23);
   return ef ? ef - 127 : (31 - __builtin_clz(a)) - 149;
+}
+
+// e4m3fn (bias 7, 3 mantissa bits, largest finite 448, no infinity) -----------
+//
+// gfx950's fp8 conversions use this OCP format.  The encoder below is exact
+// round-to-nearest-even for every float32 input already clamped to +-448
+// (the instruction itself would turn larger values into NaN instead of
+// saturating, hence the clamp in the callers); the decoders are exact.
+// Byte i of a word holds element i.
+
+// 8 float32 (clamped to +-448) -> 8 codes, elements 0-3 in word 0.
+__device__ __forceinline__ u32x2 e4m3x8_encode(const float (&v)[8]) {
+  uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
+  uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
+  return u32x2{w0, w1};
+}
+
+// 8 codes -> exact float32 values.
+__device__ __forceinline__ void e4m3x8_decode(const u32x2 &w, float (&y)[8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+    y[4 * i] = a.x; y[4 * i + 1] = a.y; y[4 * i + 2] = b.x; y[4 * i + 3] = b.y;
+  }
+}
+
+// 8 codes times the power of two `scale` (exact unless the product leaves
+// float32's range).
+__device__ __forceinline__ void e4m3x8_decode_scaled(const u32x2 &w, float scale, float (&y)[8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], scale, false);
+    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], scale, true);
+    y[4 * i] = a.x; y[4 * i + 1] = a.y; y[4 * i + 2] = b.x; y[4 * i + 3] = b.y;
+  }
+}
+
+// e2m1 (bias 1, 1 mantissa bit: 0 .5 1 1.5 2 3 4 6) --------------------------
+//
+// Nibble 2i of a word (low nibble of byte i) holds element 2i.
+
+// 8 bf16 (4 words, element 2i in the low half of word i) divided by the power
+// of two `scale` and rounded to e2m1, nearest even, saturating at +-6, sign
+// kept.  One instruction per pair; exact for every bf16 input and every
+// scale 2^-127 .. 2^126.
+__device__ __forceinline__ uint32_t e2m1x8_encode_bf16(const u32x4 &r, float scale) {
+  // copy the words to scalars first: bit-casting a vector element in place
+  // makes this compiler pass element 0 to every call
+  const uint32_t w0 = r.x, w1 = r.y, w2 = r.z, w3 = r.w;
+  uint32_t q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, w0), scale, 0);
+  q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, __builtin_bit_cast(bf16x2, w1), scale, 1);
+  q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, __builtin_bit_cast(bf16x2, w2), scale, 2);
+  q = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(q, __builtin_bit_cast(bf16x2, w3), scale, 3);
+  return q;
+}
+
+// 8 nibbles times the power of two `scale`.
+__device__ __forceinline__ void e2m1x8_decode_scaled(uint32_t w, float scale, float (&y)[8]) {
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1);
+  const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
+  y[0] = a.x; y[1] = a.y; y[2] = b.x; y[3] = b.y; y[4] = c.x; y[5] = c.y; y[6] = d.x; y[7] = d.y;
 }
 
 }  // namespace ep

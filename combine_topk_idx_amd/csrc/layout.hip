@@ -18,8 +18,9 @@
 // order in which atomics or waves happen to run: the result is deterministic.
 //
 // Small problems (pairs <= 16384) run in one workgroup that also does the
-// scan over experts and writes every output: one launch.  Larger ones run
-// rank -> scan -> finalize over 4096-pair chunks.
+// scan over experts and writes every output: one launch.  Larger ones run in
+// two launches over 4096-pair chunks: rank (per-chunk counts and ranks), then
+// finalize (each workgroup redoes the small scan over chunk counts itself).
 #include "common.hpp"
 
 namespace ep {
@@ -33,7 +34,6 @@ constexpr int kMultiItems = 4;                     // 4096-pair chunks
 constexpr int kMultiChunk = kMultiItems * kThreads;
 constexpr int64_t kSingleMaxPairs = (int64_t)kSingleItems * kThreads;
 constexpr int64_t kSingleMaxRows = 65536;          // single workgroup also clears row_src tail
-constexpr int kFinalizeThreads = 256;
 
 // Expert of pair f, or -1 for -1 / out-of-range ids / f past the end.
 template <typename IdxT>
@@ -45,21 +45,27 @@ __device__ __forceinline__ int expert_of(const IdxT *__restrict__ idx, int f, in
   return -1;
 }
 
-// Stable rank of each of this thread's ITEMS pairs among the equal-expert
-// pairs of its wave's sub-range [begin + w*ITEMS*64, ...).  On return,
+// Stable rank of each of this thread's pairs among the equal-expert pairs
+// of its wave's sub-range.  Wave w owns pairs [begin + w*steps*64, begin +
+// (w+1)*steps*64) (steps <= ITEMS, uniform), walked 64 at a time.  On return
 // cnt[w*E + e] is the number of wave-w pairs with expert e; ex[i] is the
-// expert (or -1) and lr[i] the rank within the wave.
+// expert (or -1) and lr[i] the rank within the wave.  All ids are loaded
+// before the matching starts, so a wave has its ITEMS loads in flight at once.
 template <typename IdxT, int ITEMS>
 __device__ __forceinline__ void wave_rank(const IdxT *__restrict__ idx, int begin, int n, int E, int nbits,
-                                          int *cnt, int (&ex)[ITEMS], int (&lr)[ITEMS], bool &bad) {
+                                          int steps, int *cnt, int (&ex)[ITEMS], int (&lr)[ITEMS],
+                                          bool &bad) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   int *my = cnt + w * E;
   const uint64_t below = (1ull << lane) - 1ull;
-  const int wbegin = begin + w * ITEMS * kWave;
+  const int wbegin = begin + w * steps * kWave;
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) ex[it] = expert_of(idx, it < steps ? wbegin + it * kWave + lane : n, n, E, bad);
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
-    const int f = wbegin + it * kWave + lane;
-    const int e = expert_of(idx, f, n, E, bad);
+    lr[it] = 0;
+    if (it >= steps) continue;                       // uniform
+    const int e = ex[it];
     const int key = e < 0 ? E : e;
     uint64_t same = ~0ull;
     for (int b = 0; b < nbits; ++b) {
@@ -72,7 +78,6 @@ __device__ __forceinline__ void wave_rank(const IdxT *__restrict__ idx, int begi
     int r = 0;
     if (e >= 0) r = my[e] + rank;
     if (e >= 0 && rank == 0) my[e] = r + tot;
-    ex[it] = e;
     lr[it] = r;
   }
 }
@@ -131,9 +136,10 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
   __syncthreads();
 
   const int nbits = 32 - __builtin_clz((unsigned)E);   // keys 0..E
+  const int steps = (n + kThreads - 1) / kThreads;     // 64-pair steps per wave, <= kSingleItems
   int ex[kSingleItems], lr[kSingleItems];
   bool bad = false;
-  wave_rank<IdxT, kSingleItems>(idx, 0, n, E, nbits, cnt, ex, lr, bad);
+  wave_rank<IdxT, kSingleItems>(idx, 0, n, E, nbits, steps, cnt, ex, lr, bad);
   __syncthreads();
   wave_bases(cnt, total, E);
   __syncthreads();
@@ -153,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
 #pragma unroll
   for (int it = 0; it < kSingleItems; ++it) {
-    const int f = w * kSingleItems * kWave + it * kWave + lane;
-    if (f >= n) continue;
+    const int f = w * steps * kWave + it * kWave + lane;
+    if (it >= steps || f >= n) continue;
     const int e = ex[it];
     if (e >= 0) {
       const int r = excl[e] + cnt[w * E + e] + lr[it];
@@ -168,7 +174,9 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
   if (threadIdx.x == 0) *status = sbad;
 }
 
-// Multi-block pass 1: per-chunk counts and chunk-local ranks (kept in slot[]).
+// Multi-block pass 1: per-chunk counts hist[b*E + e] and, in slot[f], the
+// pair's expert and chunk-local rank packed as (e << 16) | rank (-1 if not
+// routed); bstat[b] = out-of-range flag of the chunk.
 template <typename IdxT>
 __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__restrict__ idx, int n, int E,
                                                                int *__restrict__ hist,
@@ -185,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
   const int begin = blockIdx.x * kMultiChunk;
   int ex[kMultiItems], lr[kMultiItems];
   bool bad = false;
-  wave_rank<IdxT, kMultiItems>(idx, begin, n, E, nbits, cnt, ex, lr, bad);
+  wave_rank<IdxT, kMultiItems>(idx, begin, n, E, nbits, kMultiItems, cnt, ex, lr, bad);
   __syncthreads();
   wave_bases(cnt, total, E);
   if (bad) atomicOr(&sbad, 1u);
@@ -197,67 +205,75 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
   for (int it = 0; it < kMultiItems; ++it) {
     const int f = begin + w * kMultiItems * kWave + it * kWave + lane;
     if (f >= n) continue;
-    slot[f] = ex[it] >= 0 ? cnt[w * E + ex[it]] + lr[it] : -1;
+    const int e = ex[it];
+    slot[f] = e >= 0 ? (e << 16) | (cnt[w * E + e] + lr[it]) : -1;
   }
   if (threadIdx.x == 0) bstat[blockIdx.x] = sbad;
 }
 
-// Multi-block pass 2 (one workgroup): per-expert prefix over chunks, the scan
-// over experts, counts/offsets/statistics/status.  hist[b*E + e] becomes the
-// first receive row of chunk b's pairs with expert e.
-__global__ __launch_bounds__(kThreads) void layout_scan_kernel(int nblocks, int E, int *__restrict__ hist,
-                                                               const uint32_t *__restrict__ bstat,
-                                                               int64_t *__restrict__ recv_count,
-                                                               int *__restrict__ cum,
-                                                               int *__restrict__ offsets,
-                                                               uint32_t *__restrict__ status) {
+// Multi-block pass 2.  Every workgroup re-derives from hist (read through
+// LDS in tiles, a few tens of KB from L2) the per-expert totals, the
+// exclusive scan over experts and its own chunk's per-expert base, so no
+// workgroup waits for another.  Workgroup b < nblocks finalises the slots of
+// chunk b; workgroup 0 also writes counts, offsets, statistics and status;
+// all of them clear row_src past R.
+__global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
+    int n, int E, int max_rows, int nblocks, const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
+    int64_t *__restrict__ recv_count, int *__restrict__ cum, int *__restrict__ offsets, int *__restrict__ slot,
+    int *__restrict__ row_src, uint32_t *__restrict__ status) {
+  constexpr int kTileRows = 16;
+  __shared__ int tile[kTileRows * kMaxExperts];
+  __shared__ int base[kMaxExperts];
   __shared__ int wsum[kWaves];
   __shared__ int nrows;
   __shared__ uint32_t sbad;
-  if (threadIdx.x == 0) sbad = 0;
+  const int b = blockIdx.x;
   const int e = threadIdx.x;
-  int c = 0;
-  if (e < E) {
-    for (int b = 0; b < nblocks; ++b) {
-      const int h = hist[(int64_t)b * E + e];
-      hist[(int64_t)b * E + e] = c;
-      c += h;
+  if (threadIdx.x == 0) sbad = 0;
+  int tot = 0, pre = 0;
+  for (int b0 = 0; b0 < nblocks; b0 += kTileRows) {
+    const int rows = min(kTileRows, nblocks - b0);
+    for (int i = threadIdx.x; i < rows * E; i += kThreads) tile[i] = hist[(int64_t)b0 * E + i];
+    __syncthreads();
+    if (e < E) {
+      for (int r = 0; r < rows; ++r) {
+        const int v = tile[r * E + e];
+        tot += v;
+        if (b0 + r < b) pre += v;
+      }
     }
+    __syncthreads();
   }
-  uint32_t bad = 0;
-  for (int b = threadIdx.x; b < nblocks; b += kThreads) bad |= bstat[b];
+  const int p = block_exclusive_scan(e < E ? tot : 0, wsum, &nrows);
+  if (e < E) base[e] = p + pre;
+  if (b == 0) {
+    if (e < E) {
+      recv_count[e] = tot;
+      offsets[e] = p;
+      if (cum) cum[e] += tot;
+    }
+    uint32_t bad = 0;
+    for (int i = threadIdx.x; i < nblocks; i += kThreads) bad |= bstat[i];
+    if (bad) atomicOr(&sbad, bad);
+  }
   __syncthreads();
-  if (bad) atomicOr(&sbad, bad);
-  const int pre = block_exclusive_scan(c, wsum, &nrows);
-  if (e < E) {
-    recv_count[e] = c;
-    offsets[e] = pre;
-    if (cum) cum[e] += c;
-    for (int b = 0; b < nblocks; ++b) hist[(int64_t)b * E + e] += pre;
-  }
-  if (threadIdx.x == 0) {
+  if (b == 0 && threadIdx.x == 0) {
     offsets[E] = nrows;
     *status = sbad;
   }
-}
-
-// Multi-block pass 3: final rows, row_src, and -1 for rows past R.
-template <typename IdxT>
-__global__ __launch_bounds__(kFinalizeThreads) void layout_finalize_kernel(
-    const IdxT *__restrict__ idx, int n, int E, int max_rows, const int *__restrict__ hist,
-    const int *__restrict__ offsets, int *__restrict__ slot, int *__restrict__ row_src) {
-  const int i = blockIdx.x * kFinalizeThreads + threadIdx.x;
-  if (i < n) {
-    bool bad = false;
-    const int e = expert_of(idx, i, n, E, bad);
-    if (e >= 0) {
-      const int r = hist[(int64_t)(i / kMultiChunk) * E + e] + slot[i];
-      slot[i] = r;
-      row_src[r] = i;
+  if (b < nblocks) {
+#pragma unroll
+    for (int it = 0; it < kMultiItems; ++it) {
+      const int f = b * kMultiChunk + it * kThreads + threadIdx.x;
+      if (f >= n) continue;
+      const int v = slot[f];
+      if (v < 0) continue;
+      const int r = base[v >> 16] + (v & 0xffff);
+      slot[f] = r;
+      row_src[r] = f;
     }
   }
-  const int R = offsets[E];
-  if (i >= R && i < max_rows) row_src[i] = -1;
+  for (int r = nrows + b * kThreads + threadIdx.x; r < max_rows; r += gridDim.x * kThreads) row_src[r] = -1;
 }
 
 template <typename IdxT>
@@ -278,14 +294,11 @@ hipError_t launch_typed(const IdxT *idx, int n, int32_t E, int max_rows, int64_t
   if (nb > 0) {
     hipLaunchKernelGGL(layout_rank_kernel<IdxT>, dim3(nb), dim3(kThreads), 0, s, idx, n, E, hist, bstat, slot);
   }
-  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kThreads), 0, s, nb, E, hist, bstat, recv_count, cum,
-                     offsets, status);
-  const int span = max_rows > n ? max_rows : n;
-  const int grid = (span + kFinalizeThreads - 1) / kFinalizeThreads;
-  if (grid > 0) {
-    hipLaunchKernelGGL(layout_finalize_kernel<IdxT>, dim3(grid), dim3(kFinalizeThreads), 0, s, idx, n, E,
-                       max_rows, hist, offsets, slot, row_src);
-  }
+  // enough workgroups for the slots of every chunk and for clearing row_src past R
+  const int fill_blocks = (int)((max_rows + kMultiChunk - 1) / kMultiChunk);
+  const int grid = nb > fill_blocks ? nb : (fill_blocks > 0 ? fill_blocks : 1);
+  hipLaunchKernelGGL(layout_finalize_kernel, dim3(grid), dim3(kThreads), 0, s, n, E, max_rows, nb, hist, bstat,
+                     recv_count, cum, offsets, slot, row_src, status);
   return hipGetLastError();
 }
 
