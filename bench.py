@@ -141,6 +141,9 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0: enough to exceed 1 GB)")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: workload default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a known-size kernel "
+                         "for calibrating rocprofv3 byte counters)")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
@@ -187,6 +190,13 @@ def main() -> int:
         sets.append(s)
     del y_host
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(s):
         h = ep.ep_layout(s["idx"], w.E, w.t_max, s["rc"], s["ws"], stream=stream)

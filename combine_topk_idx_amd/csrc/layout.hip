@@ -46,7 +46,7 @@ __device__ __forceinline__ int expert_of(const IdxT *__restrict__ idx, int f, in
 }
 
 // Stable rank of each of this thread's pairs among the equal-expert pairs
-// of its wave's sub-range.  Wave w owns pairs [begin + w*steps*64, begin +
+// of its wave's sub-range (the wave clears its own counters first).  Wave w owns pairs [begin + w*steps*64, begin +
 // (w+1)*steps*64) (steps <= ITEMS, uniform), walked 64 at a time.  On return
 // cnt[w*E + e] is the number of wave-w pairs with expert e; ex[i] is the
 // expert (or -1) and lr[i] the rank within the wave.  All ids are loaded
@@ -61,6 +61,9 @@ __device__ __forceinline__ void wave_rank(const IdxT *__restrict__ idx, int begi
   const int wbegin = begin + w * steps * kWave;
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) ex[it] = expert_of(idx, it < steps ? wbegin + it * kWave + lane : n, n, E, bad);
+  // this wave's counters; only this wave touches them until the caller's
+  // barrier, and a wave's LDS accesses complete in program order
+  for (int e = lane; e < E; e += kWave) my[e] = 0;
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     lr[it] = 0;
@@ -83,21 +86,27 @@ __device__ __forceinline__ void wave_rank(const IdxT *__restrict__ idx, int begi
 }
 
 // cnt[w*E + e] (counts) -> per-wave exclusive bases; total[e] = block count.
+// All 16 counts of an expert are read before any is written, so the reads
+// are in flight together.
 __device__ __forceinline__ void wave_bases(int *cnt, int *total, int E) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) c[w] = cnt[w * E + e];
     int run = 0;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const int c = cnt[w * E + e];
       cnt[w * E + e] = run;
-      run += c;
+      run += c[w];
     }
     total[e] = run;
   }
 }
 
-// Exclusive scan of one int per thread over a 1024-thread block.  Returns the
-// exclusive prefix; *sum (LDS) receives the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int *sum) {
+// Exclusive scan of one int per thread over a 1024-thread block: a wave
+// scan, then every thread adds the totals of the waves before its own (16
+// broadcast LDS reads).  Returns the exclusive prefix and the block total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int &total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   int x = v;
 #pragma unroll
@@ -107,17 +116,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int *sum) 
   }
   if (lane == kWave - 1) wsum[w] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < kWaves; ++i) {
-      const int c = wsum[i];
-      wsum[i] = run;
-      run += c;
-    }
-    *sum = run;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int c = wsum[i];
+    all += c;
+    before += i < w ? c : 0;
   }
-  __syncthreads();
-  return wsum[w] + x - v;
+  total = all;
+  return before + x - v;
 }
 
 template <typename IdxT>
@@ -129,11 +136,8 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
   __shared__ int total[kMaxExperts];
   __shared__ int excl[kMaxExperts];
   __shared__ int wsum[kWaves];
-  __shared__ int nrows;
   __shared__ uint32_t sbad;
-  for (int i = threadIdx.x; i < kWaves * E; i += kThreads) cnt[i] = 0;
   if (threadIdx.x == 0) sbad = 0;
-  __syncthreads();
 
   const int nbits = 32 - __builtin_clz((unsigned)E);   // keys 0..E
   const int steps = (n + kThreads - 1) / kThreads;     // 64-pair steps per wave, <= kSingleItems
@@ -145,7 +149,8 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
   __syncthreads();
 
   const int c = threadIdx.x < E ? total[threadIdx.x] : 0;
-  const int pre = block_exclusive_scan(c, wsum, &nrows);
+  int nrows;
+  const int pre = block_exclusive_scan(c, wsum, nrows);
   if (threadIdx.x < E) {
     excl[threadIdx.x] = pre;
     recv_count[threadIdx.x] = c;
@@ -185,9 +190,7 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
   __shared__ int cnt[kWaves * kMaxExperts];
   __shared__ int total[kMaxExperts];
   __shared__ uint32_t sbad;
-  for (int i = threadIdx.x; i < kWaves * E; i += kThreads) cnt[i] = 0;
   if (threadIdx.x == 0) sbad = 0;
-  __syncthreads();
 
   const int nbits = 32 - __builtin_clz((unsigned)E);
   const int begin = blockIdx.x * kMultiChunk;
@@ -212,39 +215,59 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
 }
 
 // Multi-block pass 2.  Every workgroup re-derives from hist (read through
-// LDS in tiles, a few tens of KB from L2) the per-expert totals, the
-// exclusive scan over experts and its own chunk's per-expert base, so no
-// workgroup waits for another.  Workgroup b < nblocks finalises the slots of
-// chunk b; workgroup 0 also writes counts, offsets, statistics and status;
-// all of them clear row_src past R.
+// LDS, a few tens of KB from L2) the per-expert totals, the exclusive scan
+// over experts and its own chunk's per-expert base, so no workgroup waits for
+// another.  Workgroup b < nblocks finalises the slots of chunk b (loaded
+// first, so that load overlaps the scan); workgroup 0 also writes counts,
+// offsets, statistics and status; all of them clear row_src past R.
 __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
     int n, int E, int max_rows, int nblocks, const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
     int64_t *__restrict__ recv_count, int *__restrict__ cum, int *__restrict__ offsets, int *__restrict__ slot,
     int *__restrict__ row_src, uint32_t *__restrict__ status) {
-  constexpr int kTileRows = 16;
-  __shared__ int tile[kTileRows * kMaxExperts];
+  constexpr int kTileInts = 8192;
+  __shared__ int tile[kTileInts];
   __shared__ int base[kMaxExperts];
   __shared__ int wsum[kWaves];
-  __shared__ int nrows;
   __shared__ uint32_t sbad;
   const int b = blockIdx.x;
   const int e = threadIdx.x;
   if (threadIdx.x == 0) sbad = 0;
+
+  int v[kMultiItems];
+#pragma unroll
+  for (int it = 0; it < kMultiItems; ++it) {
+    const int f = b * kMultiChunk + it * kThreads + threadIdx.x;
+    v[it] = (b < nblocks && f < n) ? slot[f] : -1;
+  }
+  uint32_t bad = 0;
+  if (b == 0)
+    for (int i = threadIdx.x; i < nblocks; i += kThreads) bad |= bstat[i];
+
+  const int tile_rows = kTileInts / E;
   int tot = 0, pre = 0;
-  for (int b0 = 0; b0 < nblocks; b0 += kTileRows) {
-    const int rows = min(kTileRows, nblocks - b0);
+  for (int b0 = 0; b0 < nblocks; b0 += tile_rows) {
+    const int rows = min(tile_rows, nblocks - b0);
     for (int i = threadIdx.x; i < rows * E; i += kThreads) tile[i] = hist[(int64_t)b0 * E + i];
     __syncthreads();
     if (e < E) {
-      for (int r = 0; r < rows; ++r) {
-        const int v = tile[r * E + e];
-        tot += v;
-        if (b0 + r < b) pre += v;
+      const int mine = min(max(b - b0, 0), rows);   // rows of this tile before chunk b
+      int r = 0;
+      for (; r + 4 <= rows; r += 4) {
+        const int c0 = tile[r * E + e], c1 = tile[(r + 1) * E + e];
+        const int c2 = tile[(r + 2) * E + e], c3 = tile[(r + 3) * E + e];
+        tot += c0 + c1 + c2 + c3;
+        pre += (r < mine ? c0 : 0) + (r + 1 < mine ? c1 : 0) + (r + 2 < mine ? c2 : 0) + (r + 3 < mine ? c3 : 0);
+      }
+      for (; r < rows; ++r) {
+        const int c0 = tile[r * E + e];
+        tot += c0;
+        pre += r < mine ? c0 : 0;
       }
     }
     __syncthreads();
   }
-  const int p = block_exclusive_scan(e < E ? tot : 0, wsum, &nrows);
+  int nrows;
+  const int p = block_exclusive_scan(e < E ? tot : 0, wsum, nrows);
   if (e < E) base[e] = p + pre;
   if (b == 0) {
     if (e < E) {
@@ -252,8 +275,6 @@ __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
       offsets[e] = p;
       if (cum) cum[e] += tot;
     }
-    uint32_t bad = 0;
-    for (int i = threadIdx.x; i < nblocks; i += kThreads) bad |= bstat[i];
     if (bad) atomicOr(&sbad, bad);
   }
   __syncthreads();
@@ -261,17 +282,13 @@ __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
     offsets[E] = nrows;
     *status = sbad;
   }
-  if (b < nblocks) {
 #pragma unroll
-    for (int it = 0; it < kMultiItems; ++it) {
-      const int f = b * kMultiChunk + it * kThreads + threadIdx.x;
-      if (f >= n) continue;
-      const int v = slot[f];
-      if (v < 0) continue;
-      const int r = base[v >> 16] + (v & 0xffff);
-      slot[f] = r;
-      row_src[r] = f;
-    }
+  for (int it = 0; it < kMultiItems; ++it) {
+    if (v[it] < 0) continue;
+    const int f = b * kMultiChunk + it * kThreads + threadIdx.x;
+    const int r = base[v[it] >> 16] + (v[it] & 0xffff);
+    slot[f] = r;
+    row_src[r] = f;
   }
   for (int r = nrows + b * kThreads + threadIdx.x; r < max_rows; r += gridDim.x * kThreads) row_src[r] = -1;
 }
