@@ -60,107 +60,135 @@ __device__ __forceinline__ void dequant8(const typename Raw<Q>::T &r, float scal
   }
 }
 
-template <int Q, int NT, int VPT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void combine_kernel(const char *__restrict__ data, const char *__restrict__ scales,
-                                                     int64_t dq, int64_t sq, int nvec, int k, int chunks,
-                                                     const int *__restrict__ slot, const float *__restrict__ w,
-                                                     u32x4 *__restrict__ out) {
+template <int Q, int NT, int KMAX, int CV, bool EXACT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void combine_kernel(
+    const char *__restrict__ data, const char *__restrict__ scales, int64_t dq, int64_t sq, int nvec, int k,
+    int chunks, const int *__restrict__ slot, const float *__restrict__ w, u32x4 *__restrict__ out) {
   using RawT = typename Raw<Q>::T;
   const int t = blockIdx.x / chunks;
   const int c = blockIdx.x - t * chunks;
   const int64_t pair0 = (int64_t)t * k;
 
-  int s[kMaxTopk];
-  float wt[kMaxTopk];
+  // routed rows and weights: loads from valid addresses first, then masking,
+  // so the loads are in flight together (with k == KMAX they are contiguous
+  // and become one wide scalar load each)
+  int s[KMAX];
+  float wt[KMAX];
 #pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j) {
-    s[j] = j < k ? slot[pair0 + j] : -1;
-    wt[j] = j < k ? w[pair0 + j] : 0.0f;
+  for (int j = 0; j < KMAX; ++j) {
+    const int jj = EXACT ? j : min(j, k - 1);
+    s[j] = slot[pair0 + jj];
+    wt[j] = w[pair0 + jj];
   }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) s[j] = j < k ? s[j] : -1;
   // per-row int8 scales are workgroup-uniform
-  float rs[kMaxTopk];
+  float rs[KMAX];
   if constexpr (Q == EP_QUANT_INT8_TOKEN) {
 #pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j) rs[j] = s[j] >= 0 ? *(const float *)(scales + s[j] * sq) : 0.0f;
+    for (int j = 0; j < KMAX; ++j) rs[j] = *(const float *)(scales + max(s[j], 0) * sq);
   }
 
-  const int v0 = c * NT * VPT + threadIdx.x;
+  // this lane's CV consecutive 8-element vectors
+  const int v0 = (c * NT + threadIdx.x) * CV;
+  if (v0 >= nvec) return;
+
+  // phase 1: issue every row load (data and scale)
+  RawT raw[KMAX][CV];
+  uint32_t sraw[KMAX][CV];
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int v = v0 + i * NT;
-    if (v >= nvec) continue;
-    // phase 1: issue every row load (data and scale) of this vector
-    RawT raw[kMaxTopk];
-    uint32_t sraw[kMaxTopk];
+  for (int j = 0; j < KMAX; ++j) {
 #pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j) {
-      raw[j] = RawT{};
-      sraw[j] = 0;
-      if (s[j] < 0) continue;
+    for (int h = 0; h < CV; ++h) {
+      raw[j][h] = RawT{};
+      sraw[j][h] = 0;
+    }
+    if (s[j] < 0) continue;
+#pragma unroll
+    for (int h = 0; h < CV; ++h) {
+      const int v = v0 + h;
       const RawT *src = (const RawT *)(data + s[j] * dq + (int64_t)v * kBytesPerVec<Q>);
 #if EP_COMBINE_NT_LOAD
-      raw[j] = __builtin_nontemporal_load(src);
+      raw[j][h] = __builtin_nontemporal_load(src);
 #else
-      raw[j] = *src;
+      raw[j][h] = *src;
 #endif
       if constexpr (Q == EP_QUANT_FP8_B128) {
-        sraw[j] = *(const uint32_t *)(scales + s[j] * sq + (int64_t)(v >> 4) * 4);
+        sraw[j][h] = *(const uint32_t *)(scales + s[j] * sq + (int64_t)(v >> 4) * 4);
       } else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) {
-        sraw[j] = *(const uint8_t *)(scales + s[j] * sq + (int64_t)(v >> 2));
+        sraw[j][h] = *(const uint8_t *)(scales + s[j] * sq + (int64_t)(v >> 2));
       }
     }
-    // phase 2: dequantise and accumulate in ascending j
-    float acc[8];
+  }
+  // phase 2: dequantise and accumulate in ascending j
+  float acc[CV][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int h = 0; h < CV; ++h)
 #pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j) {
-      if (s[j] < 0) continue;
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (s[j] < 0) continue;
+#pragma unroll
+    for (int h = 0; h < CV; ++h) {
       float sc = 1.0f;
       if constexpr (Q == EP_QUANT_INT8_TOKEN) sc = rs[j];
-      else if constexpr (Q == EP_QUANT_FP8_B128) sc = __uint_as_float(sraw[j]);
-      else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) sc = e8m0_decode(sraw[j]);
+      else if constexpr (Q == EP_QUANT_FP8_B128) sc = __uint_as_float(sraw[j][h]);
+      else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) sc = e8m0_decode(sraw[j][h]);
       float y[8];
-      dequant8<Q>(raw[j], sc, y);
+      dequant8<Q>(raw[j][h], sc, y);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + wt[j] * y[e];
+      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] + wt[j] * y[e];
     }
+  }
+#pragma unroll
+  for (int h = 0; h < CV; ++h) {
     u32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[h][2 * e], acc[h][2 * e + 1]);
 #if EP_COMBINE_NT_STORE
-    __builtin_nontemporal_store(o, out + (int64_t)t * nvec + v);
+    __builtin_nontemporal_store(pin(o), out + (int64_t)t * nvec + v0 + h);
 #else
-    out[(int64_t)t * nvec + v] = o;
+    out[(int64_t)t * nvec + v0 + h] = o;
 #endif
   }
 }
 
-template <int Q, int NT, int VPT>
+template <int Q, int NT, int KMAX, int CV, bool EXACT>
 hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out, hipStream_t s) {
   size_t dq, sq;
   row_bytes(Q, hidden, &dq, &sq);
   const size_t scale_off = scale_offset(h.max_rows, dq, sq);
-  const int nvec = hidden / 8;
-  const int chunks = (nvec + NT * VPT - 1) / (NT * VPT);
+  const int nvec = hidden / 8;                      // a multiple of 4 (hidden % 32 == 0)
+  const int per_block = NT * CV;
+  const int chunks = (nvec + per_block - 1) / per_block;
   const int64_t blocks = h.num_tokens * chunks;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((combine_kernel<Q, NT, VPT>), dim3((unsigned)blocks), dim3(NT), 0, s, in, in + scale_off,
-                     (int64_t)dq, (int64_t)sq, nvec, h.num_topk, chunks, h.slot, w, (u32x4 *)out);
+  hipLaunchKernelGGL((combine_kernel<Q, NT, KMAX, CV, EXACT>), dim3((unsigned)blocks), dim3(NT), EP_COMBINE_LDS_CAP, s, in,
+                     in + scale_off, (int64_t)dq, (int64_t)sq, nvec, h.num_topk, chunks, h.slot, w, (u32x4 *)out);
   return hipGetLastError();
+}
+
+template <int Q>
+hipError_t launch_mode(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out,
+                       hipStream_t s) {
+  constexpr int NT = EP_COMBINE_THREADS, CV = EP_COMBINE_CV;
+  if (EP_COMBINE_KMAX_MIN <= 8 && h.num_topk == 8) return launch_q<Q, NT, 8, CV, true>(h, in, hidden, w, out, s);
+  if (EP_COMBINE_KMAX_MIN <= 8 && h.num_topk < 8) return launch_q<Q, NT, 8, CV, false>(h, in, hidden, w, out, s);
+  if (h.num_topk == kMaxTopk) return launch_q<Q, NT, kMaxTopk, CV, true>(h, in, hidden, w, out, s);
+  return launch_q<Q, NT, kMaxTopk, CV, false>(h, in, hidden, w, out, s);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const float *w, void *out,
                           hipStream_t s) {
-  constexpr int NT = EP_COMBINE_THREADS, VPT = EP_COMBINE_VPT;
   switch (quant) {
-    case EP_QUANT_NONE: return launch_q<EP_QUANT_NONE, NT, VPT>(h, in, hidden, w, out, s);
-    case EP_QUANT_INT8_TOKEN: return launch_q<EP_QUANT_INT8_TOKEN, NT, VPT>(h, in, hidden, w, out, s);
-    case EP_QUANT_FP8_B128: return launch_q<EP_QUANT_FP8_B128, NT, VPT>(h, in, hidden, w, out, s);
-    case EP_QUANT_MXFP8: return launch_q<EP_QUANT_MXFP8, NT, VPT>(h, in, hidden, w, out, s);
-    default: return launch_q<EP_QUANT_MXFP4, NT, VPT>(h, in, hidden, w, out, s);
+    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE>(h, in, hidden, w, out, s);
+    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN>(h, in, hidden, w, out, s);
+    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128>(h, in, hidden, w, out, s);
+    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8>(h, in, hidden, w, out, s);
+    default: return launch_mode<EP_QUANT_MXFP4>(h, in, hidden, w, out, s);
   }
 }
 

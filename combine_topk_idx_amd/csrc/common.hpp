@@ -39,6 +39,17 @@ __host__ __device__ inline size_t scale_offset(int64_t rows, size_t dq, size_t s
   return sq ? align_up((size_t)rows * dq, kScaleAlign) : (size_t)rows * dq;
 }
 
+// Makes a value opaque to the optimizer at this point (an empty asm that
+// claims to modify it).  Used (a) so that codes computed once are not
+// re-derived inside every per-row store branch and (b) so that a store built
+// from bit-cast conversion results keeps its non-temporal hint (without it the
+// optimizer rewrites such a store and drops the hint).
+template <typename T>
+__device__ __forceinline__ T pin(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // DPP lane exchanges (wave64, no LDS traffic).  Controls: quad_perm
 // [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E; row_ror:n = 0x120 + n (rotate within a
 // row of 16 lanes).

@@ -110,14 +110,6 @@ __device__ __forceinline__ u32x2 codes_mxfp8(const float (&f)[8], float mult) {
   return e4m3x8_encode(v);
 }
 
-// Keeps a computed value in registers as is: without it the compiler re-derives
-// the codes inside every per-row store branch instead of once per vector.
-template <typename T>
-__device__ __forceinline__ T pin(T v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
 template <typename T>
 __device__ __forceinline__ void st_row(char *p, const T &v) {
 #if EP_DISPATCH_NT_STORE
@@ -141,7 +133,7 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red) {
   return m;
 }
 
-template <int Q, int NT, int VPT, bool PACK>
+template <int Q, int NT, int VPT, int KMAX, bool EXACT, bool PACK>
 __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ x, int nvec, int k, int chunks,
                                                       const int *__restrict__ slot,
                                                       const float *__restrict__ w, float *__restrict__ recv_w,
@@ -151,11 +143,15 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
   const int c = blockIdx.x - t * chunks;
   const int64_t pair0 = (int64_t)t * k;
 
-  int s[kMaxTopk];
+  // routed rows: loads from valid addresses first, then masking, so the loads
+  // are in flight together (with k == KMAX they are one wide scalar load)
+  int s[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) s[j] = slot[pair0 + (EXACT ? j : min(j, k - 1))];
   bool any = false;
 #pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j) {
-    s[j] = j < k ? slot[pair0 + j] : -1;
+  for (int j = 0; j < KMAX; ++j) {
+    s[j] = j < k ? s[j] : -1;
     any |= s[j] >= 0;
   }
   if (!any) return;   // uniform: the token is routed nowhere
@@ -179,7 +175,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
       const int v = v0 + i * NT;
       if (v >= nvec) continue;
 #pragma unroll
-      for (int j = 0; j < kMaxTopk; ++j)
+      for (int j = 0; j < KMAX; ++j)
         if (s[j] >= 0) st_row(data + s[j] * dq + (int64_t)v * 16, raw[i]);
     }
   } else if constexpr (Q == EP_QUANT_INT8_TOKEN) {
@@ -196,12 +192,12 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
       unpack8(raw[i], f);
       const u32x2 q = pin(codes_int8(f, b));
 #pragma unroll
-      for (int j = 0; j < kMaxTopk; ++j)
+      for (int j = 0; j < KMAX; ++j)
         if (s[j] >= 0) st_row(data + s[j] * dq + (int64_t)v * 8, q);
     }
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int j = 0; j < kMaxTopk; ++j)
+      for (int j = 0; j < KMAX; ++j)
         if (s[j] >= 0) st_row(scales + s[j] * sq, b.scale);
     }
   } else {
@@ -217,7 +213,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
         const u32x2 q = pin(codes_e4m3_scaled(f, b));
         const bool lead = (v & 15) == 0;
 #pragma unroll
-        for (int j = 0; j < kMaxTopk; ++j) {
+        for (int j = 0; j < KMAX; ++j) {
           if (s[j] < 0) continue;
           st_row(data + s[j] * dq + (int64_t)v * 8, q);
           if (lead) st_row(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
@@ -252,7 +248,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
           q = pin(e2m1x8_encode_bf16(raw[i], scale));
         }
 #pragma unroll
-        for (int j = 0; j < kMaxTopk; ++j) {
+        for (int j = 0; j < KMAX; ++j) {
           if (s[j] < 0) continue;
           st_row(data + s[j] * dq + (int64_t)v * kBytes, q);
           if (lead) {
@@ -272,8 +268,15 @@ hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *
   const int chunks = (nvec + NT * VPT - 1) / (NT * VPT);
   const int64_t blocks = h.num_tokens * chunks;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((dispatch_kernel<Q, NT, VPT, PACK>), dim3((unsigned)blocks), dim3(NT), 0, s, (const u32x4 *)x,
-                     nvec, h.num_topk, chunks, h.slot, w, recv_w, recv, recv + scale_off, dq, sq);
+#define EP_LAUNCH_DISPATCH(KMAX, EXACT)                                                                     \
+  hipLaunchKernelGGL((dispatch_kernel<Q, NT, VPT, KMAX, EXACT, PACK>), dim3((unsigned)blocks), dim3(NT),          \
+                     EP_DISPATCH_LDS_CAP, s, (const u32x4 *)x, nvec, h.num_topk, chunks, h.slot, w, recv_w, recv, \
+                     recv + scale_off, dq, sq)
+  if (h.num_topk == 8) EP_LAUNCH_DISPATCH(8, true);
+  else if (h.num_topk < 8) EP_LAUNCH_DISPATCH(8, false);
+  else if (h.num_topk == kMaxTopk) EP_LAUNCH_DISPATCH(kMaxTopk, true);
+  else EP_LAUNCH_DISPATCH(kMaxTopk, false);
+#undef EP_LAUNCH_DISPATCH
   return hipGetLastError();
 }
 

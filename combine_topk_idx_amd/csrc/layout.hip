@@ -17,11 +17,14 @@
 // into per-wave bases by a prefix over the 16 waves.  Nothing depends on the
 // order in which atomics or waves happen to run: the result is deterministic.
 //
-// Small problems (pairs <= 16384) run in one workgroup that also does the
-// scan over experts and writes every output: one launch.  Larger ones run in
-// two launches over 4096-pair chunks: rank (per-chunk counts and ranks), then
+// Small problems (pairs <= 4096) run in one workgroup that also does the scan
+// over experts and writes every output: one launch.  (All of its waves share
+// one CU, so its cost grows by about a microsecond per 64-pair step of a
+// wave; past 4096 pairs two launches are faster.)  Larger ones run in two
+// launches over 2048-pair chunks: rank (per-chunk counts and ranks), then
 // finalize (each workgroup redoes the small scan over chunk counts itself).
 #include "common.hpp"
+#include "tuning.hpp"
 
 namespace ep {
 
@@ -29,19 +32,18 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kSingleItems = 16;                   // 16 * 1024 pairs in one workgroup
-constexpr int kMultiItems = 4;                     // 4096-pair chunks
+constexpr int kSingleItems = 4;                    // up to 4 * 1024 pairs in one workgroup
+constexpr int kMultiItems = EP_LAYOUT_ITEMS;       // pairs per thread in a multi-block chunk
 constexpr int kMultiChunk = kMultiItems * kThreads;
 constexpr int64_t kSingleMaxPairs = (int64_t)kSingleItems * kThreads;
 constexpr int64_t kSingleMaxRows = 65536;          // single workgroup also clears row_src tail
 
-// Expert of pair f, or -1 for -1 / out-of-range ids / f past the end.
+// Expert of an id, or -1 for -1 / ids outside [-1, E) (which set `bad`).
 template <typename IdxT>
-__device__ __forceinline__ int expert_of(const IdxT *__restrict__ idx, int f, int n, int E, bool &bad) {
-  if (f >= n) return -1;
-  const int64_t v = (int64_t)idx[f];
+__device__ __forceinline__ int expert_of(IdxT raw, int E, bool &bad) {
+  const int64_t v = (int64_t)raw;
   if (v >= 0 && v < (int64_t)E) return (int)v;
-  if (v != -1) bad = true;
+  bad |= v != -1;
   return -1;
 }
 
@@ -59,8 +61,18 @@ __device__ __forceinline__ void wave_rank(const IdxT *__restrict__ idx, int begi
   int *my = cnt + w * E;
   const uint64_t below = (1ull << lane) - 1ull;
   const int wbegin = begin + w * steps * kWave;
+  // all loads first (clamped to a valid pair, so none sits in a branch and
+  // they are in flight together), then the classification
+  IdxT raw[ITEMS];
+  if (n > 0) {
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) ex[it] = expert_of(idx, it < steps ? wbegin + it * kWave + lane : n, n, E, bad);
+    for (int it = 0; it < ITEMS; ++it) raw[it] = idx[min(wbegin + it * kWave + lane, n - 1)];
+  }
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int f = wbegin + it * kWave + lane;
+    ex[it] = (it < steps && f < n) ? expert_of(raw[it], E, bad) : -1;
+  }
   // this wave's counters; only this wave touches them until the caller's
   // barrier, and a wave's LDS accesses complete in program order
   for (int e = lane; e < E; e += kWave) my[e] = 0;
@@ -179,30 +191,26 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
   if (threadIdx.x == 0) *status = sbad;
 }
 
-// Multi-block pass 1: per-chunk counts hist[b*E + e] and, in slot[f], the
-// pair's expert and chunk-local rank packed as (e << 16) | rank (-1 if not
-// routed); bstat[b] = out-of-range flag of the chunk.
+// Multi-block pass 1 (chunk b): per-chunk counts hist[b*E + e] and, in
+// slot[f], the pair's expert and chunk-local rank packed as (e << 16) | rank
+// (-1 if not routed); bstat[b] = out-of-range flag of the chunk.  `cnt` is
+// LDS of kWaves * E ints, `total` of E ints.
 template <typename IdxT>
-__global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__restrict__ idx, int n, int E,
-                                                               int *__restrict__ hist,
-                                                               uint32_t *__restrict__ bstat,
-                                                               int *__restrict__ slot) {
-  __shared__ int cnt[kWaves * kMaxExperts];
-  __shared__ int total[kMaxExperts];
-  __shared__ uint32_t sbad;
-  if (threadIdx.x == 0) sbad = 0;
-
+__device__ __forceinline__ void rank_chunk(const IdxT *__restrict__ idx, int n, int E, int b, int *__restrict__ hist,
+                                           uint32_t *__restrict__ bstat, int *__restrict__ slot, int *cnt,
+                                           int *total, uint32_t *sbad) {
+  if (threadIdx.x == 0) *sbad = 0;
   const int nbits = 32 - __builtin_clz((unsigned)E);
-  const int begin = blockIdx.x * kMultiChunk;
+  const int begin = b * kMultiChunk;
   int ex[kMultiItems], lr[kMultiItems];
   bool bad = false;
   wave_rank<IdxT, kMultiItems>(idx, begin, n, E, nbits, kMultiItems, cnt, ex, lr, bad);
   __syncthreads();
   wave_bases(cnt, total, E);
-  if (bad) atomicOr(&sbad, 1u);
+  if (bad) atomicOr(sbad, 1u);
   __syncthreads();
 
-  for (int e = threadIdx.x; e < E; e += kThreads) hist[(int64_t)blockIdx.x * E + e] = total[e];
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[(int64_t)b * E + e] = total[e];
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
 #pragma unroll
   for (int it = 0; it < kMultiItems; ++it) {
@@ -211,7 +219,18 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
     const int e = ex[it];
     slot[f] = e >= 0 ? (e << 16) | (cnt[w * E + e] + lr[it]) : -1;
   }
-  if (threadIdx.x == 0) bstat[blockIdx.x] = sbad;
+  if (threadIdx.x == 0) bstat[b] = *sbad;
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__restrict__ idx, int n, int E,
+                                                               int *__restrict__ hist,
+                                                               uint32_t *__restrict__ bstat,
+                                                               int *__restrict__ slot) {
+  __shared__ int cnt[kWaves * kMaxExperts];
+  __shared__ int total[kMaxExperts];
+  __shared__ uint32_t sbad;
+  rank_chunk(idx, n, E, blockIdx.x, hist, bstat, slot, cnt, total, &sbad);
 }
 
 // Multi-block pass 2.  Every workgroup re-derives from hist (read through
@@ -219,25 +238,28 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
 // over experts and its own chunk's per-expert base, so no workgroup waits for
 // another.  Workgroup b < nblocks finalises the slots of chunk b (loaded
 // first, so that load overlaps the scan); workgroup 0 also writes counts,
-// offsets, statistics and status; all of them clear row_src past R.
-__global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
-    int n, int E, int max_rows, int nblocks, const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
-    int64_t *__restrict__ recv_count, int *__restrict__ cum, int *__restrict__ offsets, int *__restrict__ slot,
-    int *__restrict__ row_src, uint32_t *__restrict__ status) {
-  constexpr int kTileInts = 8192;
-  __shared__ int tile[kTileInts];
-  __shared__ int base[kMaxExperts];
-  __shared__ int wsum[kWaves];
-  __shared__ uint32_t sbad;
-  const int b = blockIdx.x;
+// offsets, statistics and status; all of them clear row_src past R.  `tile`
+// is LDS of kTileInts ints, `base` of E ints.
+constexpr int kTileInts = 8192;
+
+__device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int nblocks, int b,
+                                               const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
+                                               int64_t *__restrict__ recv_count, int *__restrict__ cum,
+                                               int *__restrict__ offsets, int *__restrict__ slot,
+                                               int *__restrict__ row_src, uint32_t *__restrict__ status, int *tile,
+                                               int *base, int *wsum, uint32_t *sbad) {
   const int e = threadIdx.x;
-  if (threadIdx.x == 0) sbad = 0;
+  if (threadIdx.x == 0) *sbad = 0;
 
   int v[kMultiItems];
+  if (n > 0) {
+#pragma unroll
+    for (int it = 0; it < kMultiItems; ++it) v[it] = slot[min(b * kMultiChunk + it * kThreads + (int)threadIdx.x, n - 1)];
+  }
 #pragma unroll
   for (int it = 0; it < kMultiItems; ++it) {
     const int f = b * kMultiChunk + it * kThreads + threadIdx.x;
-    v[it] = (b < nblocks && f < n) ? slot[f] : -1;
+    v[it] = (b < nblocks && f < n) ? v[it] : -1;
   }
   uint32_t bad = 0;
   if (b == 0)
@@ -275,12 +297,12 @@ __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
       offsets[e] = p;
       if (cum) cum[e] += tot;
     }
-    if (bad) atomicOr(&sbad, bad);
+    if (bad) atomicOr(sbad, bad);
   }
   __syncthreads();
   if (b == 0 && threadIdx.x == 0) {
     offsets[E] = nrows;
-    *status = sbad;
+    *status = *sbad;
   }
 #pragma unroll
   for (int it = 0; it < kMultiItems; ++it) {
@@ -291,6 +313,18 @@ __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
     row_src[r] = f;
   }
   for (int r = nrows + b * kThreads + threadIdx.x; r < max_rows; r += gridDim.x * kThreads) row_src[r] = -1;
+}
+
+__global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
+    int n, int E, int max_rows, int nblocks, const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
+    int64_t *__restrict__ recv_count, int *__restrict__ cum, int *__restrict__ offsets, int *__restrict__ slot,
+    int *__restrict__ row_src, uint32_t *__restrict__ status) {
+  __shared__ int tile[kTileInts];
+  __shared__ int base[kMaxExperts];
+  __shared__ int wsum[kWaves];
+  __shared__ uint32_t sbad;
+  finalize_chunk(n, E, max_rows, nblocks, blockIdx.x, hist, bstat, recv_count, cum, offsets, slot, row_src, status,
+                 tile, base, wsum, &sbad);
 }
 
 template <typename IdxT>
@@ -308,12 +342,12 @@ hipError_t launch_typed(const IdxT *idx, int n, int32_t E, int max_rows, int64_t
   int *hist = (int *)(ws + wl.hist);
   uint32_t *bstat = (uint32_t *)(ws + wl.bstat);
   const int nb = (n + kMultiChunk - 1) / kMultiChunk;
-  if (nb > 0) {
-    hipLaunchKernelGGL(layout_rank_kernel<IdxT>, dim3(nb), dim3(kThreads), 0, s, idx, n, E, hist, bstat, slot);
-  }
   // enough workgroups for the slots of every chunk and for clearing row_src past R
   const int fill_blocks = (int)((max_rows + kMultiChunk - 1) / kMultiChunk);
   const int grid = nb > fill_blocks ? nb : (fill_blocks > 0 ? fill_blocks : 1);
+  if (nb > 0) {
+    hipLaunchKernelGGL(layout_rank_kernel<IdxT>, dim3(nb), dim3(kThreads), 0, s, idx, n, E, hist, bstat, slot);
+  }
   hipLaunchKernelGGL(layout_finalize_kernel, dim3(grid), dim3(kThreads), 0, s, n, E, max_rows, nb, hist, bstat,
                      recv_count, cum, offsets, slot, row_src, status);
   return hipGetLastError();

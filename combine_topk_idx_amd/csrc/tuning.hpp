@@ -15,12 +15,24 @@
 #ifndef EP_COMBINE_THREADS
 #define EP_COMBINE_THREADS 128
 #endif
-#ifndef EP_COMBINE_VPT
-#define EP_COMBINE_VPT 1          // 8-element output vectors per thread
+#ifndef EP_COMBINE_CV
+#define EP_COMBINE_CV 1           // consecutive 8-element output vectors per thread (1 or 2)
 #endif
 #ifndef EP_COMBINE_NT_LOAD
 #define EP_COMBINE_NT_LOAD 1      // non-temporal loads of expert rows
 #endif
 #ifndef EP_COMBINE_NT_STORE
 #define EP_COMBINE_NT_STORE 1     // non-temporal stores of the output
+#endif
+#ifndef EP_COMBINE_LDS_CAP
+#define EP_COMBINE_LDS_CAP 0      // LDS bytes reserved per combine workgroup (caps resident workgroups per CU)
+#endif
+#ifndef EP_DISPATCH_LDS_CAP
+#define EP_DISPATCH_LDS_CAP 0     // same for dispatch
+#endif
+#ifndef EP_COMBINE_KMAX_MIN
+#define EP_COMBINE_KMAX_MIN 8     // smallest compile-time top-k bound used by combine (8 or 16)
+#endif
+#ifndef EP_LAYOUT_ITEMS
+#define EP_LAYOUT_ITEMS 2         // pairs per thread of a multi-block layout chunk (chunk = 1024 * this)
 #endif

@@ -91,8 +91,16 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+try:
+    _raw_stream = torch._C._cuda_getCurrentRawStream   # int handle, no Stream object
+except AttributeError:  # pragma: no cover
+    _raw_stream = None
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device())
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream
