@@ -38,7 +38,7 @@ KERNEL_SOURCES = ["combine_topk_idx_amd/csrc/combine.hip", "combine_topk_idx_amd
 
 
 def algorithmic_bytes(w, R: int) -> dict:
-    """Bytes the method has to move, per phase (Measurement).
+    """Bytes the method has to move, per phase.
 
     layout:   read ids, write counts/offsets, slot map and row sources
     dispatch: read x once and the slot map, write every routed packed row
@@ -132,6 +132,74 @@ def cpu_baseline(name: str, tokens: int) -> dict:
 # ---------------------------------------------------------------------------
 
 
+def backward_main(args) -> int:
+    """layout + ep_combine_backward on one workload's routing; one JSON line."""
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+    from combine_topk_idx_amd import ep, workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    q = args.combine_backward
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = W.make_inputs(w)
+    grad = W.make_expert_out(w, rows=w.T)
+    total, _ = ep.ep_buffer_bytes(w.max_rows, w.H, q)
+    nsets = args.sets or max(2, -(-(1 << 30) // max(4 * w.T * w.H + total, 1)))
+    sets = [dict(idx=torch.from_numpy(inp["topk_idx"]).to(dev), w=torch.from_numpy(inp["topk_weights"]).to(dev),
+                 g=torch.from_numpy(grad.view(np.int16)).to(dev).view(torch.bfloat16),
+                 ws=torch.empty(ep.ep_workspace_bytes(w.t_max, w.k, w.E), dtype=torch.uint8, device=dev),
+                 rc=torch.empty(w.E, dtype=torch.int64, device=dev),
+                 buf=torch.empty(total, dtype=torch.uint8, device=dev)) for _ in range(min(nsets, 64))]
+    stream = torch.cuda.current_stream()
+
+    def lay(s):
+        s["h"] = ep.ep_layout(s["idx"], w.E, w.t_max, s["rc"], s["ws"])
+
+    def bwd(s):
+        ep.ep_combine_backward(s["h"], s["g"], w.H, q, s["buf"], s["w"])
+
+    for i in range(max(args.warmup, len(sets))):
+        lay(sets[i % len(sets)])
+        bwd(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    R = int(sets[0]["rc"].sum().item())
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        ev[i][0].record(stream)
+        lay(s)
+        ev[i][1].record(stream)
+        bwd(s)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    dq, sqb = _row_bytes(q, w.H)
+    b_idx = 4 if w.idx_dtype == "int32" else 8
+    b_lay = w.T * w.k * b_idx + w.E * 8 + (w.E + 1) * 4 + w.T * w.k * 4 + R * 4
+    b_bwd = 2 * w.T * w.H + w.T * w.k * 8 + R * (dq + sqb)
+    gbps = (b_lay + b_bwd) / (ms * 1e-3) / 1e9
+    bwd_gbps = b_bwd / (bwd_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "combine-backward reverse dispatch tokens/s and achieved HBM GB/s (% of peak), H=7168 k=8",
+        "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name} routing: T={w.T} H={w.H} E={w.E} k={w.k}, weighted gradient rows "
+                               f"quantised to {q}", "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R},
+        "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "phase_ms": {"layout": round(ms - bwd_ms, 5), "combine_backward": round(bwd_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": "combine_backward", "achieved": round(bwd_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "alg_bytes_per_launch": b_bwd, "avg_launch_ms": round(bwd_ms, 5)},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,12 +212,17 @@ def main() -> int:
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a known-size kernel "
                          "for calibrating rocprofv3 byte counters)")
+    ap.add_argument("--combine-backward", default=None, metavar="QUANT",
+                    help="time layout + ep_combine_backward (weighted reverse dispatch of a bf16 gradient "
+                         "to the expert rows, quantised to QUANT, e.g. mxfp8) instead of the forward path")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     if args.cpu_baseline_child:
         cpu_baseline_child(args.cpu_baseline_child, args.cpu_tokens)
         return 0
+    if args.combine_backward:
+        return backward_main(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path has no "
               f"multi-GPU exchange)", file=sys.stderr)

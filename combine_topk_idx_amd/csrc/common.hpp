@@ -98,4 +98,7 @@ hipError_t launch_dispatch(const ep_handle_t &h, const void *x, int hidden, cons
 hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const float *w,
                           void *out, hipStream_t s);
 
+hipError_t launch_combine_backward(const ep_handle_t &h, const void *grad, int hidden, const float *w, int quant,
+                                   char *buf, hipStream_t s);
+
 }  // namespace ep

@@ -125,6 +125,7 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d));
   const int w = threadIdx.x / kWave;
+  __syncthreads();   // `red` may still be read by a previous call
   if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
   __syncthreads();
   uint32_t m = 0;
@@ -133,42 +134,23 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *red) {
   return m;
 }
 
-template <int Q, int NT, int VPT, int KMAX, bool EXACT, bool PACK>
-__global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ x, int nvec, int k, int chunks,
-                                                      const int *__restrict__ slot,
-                                                      const float *__restrict__ w, float *__restrict__ recv_w,
-                                                      char *__restrict__ data, char *__restrict__ scales,
-                                                      int64_t dq, int64_t sq) {
-  const int t = blockIdx.x / chunks;
-  const int c = blockIdx.x - t * chunks;
-  const int64_t pair0 = (int64_t)t * k;
-
-  // routed rows: loads from valid addresses first, then masking, so the loads
-  // are in flight together (with k == KMAX they are one wide scalar load)
-  int s[KMAX];
+// bf16(fl32(w * x)) of the 8 bf16 elements of a vector (round to nearest even)
+__device__ __forceinline__ u32x4 scale_bf16x8(const u32x4 &r, float w) {
+  u32x4 o;
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) s[j] = slot[pair0 + (EXACT ? j : min(j, k - 1))];
-  bool any = false;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    s[j] = j < k ? s[j] : -1;
-    any |= s[j] >= 0;
-  }
-  if (!any) return;   // uniform: the token is routed nowhere
-  if (recv_w != nullptr && c == 0 && threadIdx.x < k) {
-    const int r = slot[pair0 + threadIdx.x];
-    if (r >= 0) recv_w[r] = w[pair0 + threadIdx.x];
-  }
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(w * bf16_lo(r[i]), w * bf16_hi(r[i]));
+  return o;
+}
 
-  const u32x4 *xr = x + (int64_t)t * nvec;
-  const int v0 = c * NT * VPT + threadIdx.x;
-  u32x4 raw[VPT];
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int v = v0 + i * NT;
-    raw[i] = v < nvec ? xr[v] : u32x4{0u, 0u, 0u, 0u};
-  }
-
+// Quantises this thread's VPT row vectors (vector v0 + i*NT of one token row)
+// and stores the packed codes and scales to every receive row s[j] >= 0 with
+// j0 <= j < j1.  Every thread of the workgroup calls it (the int8 row maximum
+// is a workgroup reduction through `red`).
+template <int Q, int NT, int VPT, int KMAX, bool PACK>
+__device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, int nvec, const int (&s)[KMAX],
+                                               int j0, int j1, char *__restrict__ data, char *__restrict__ scales,
+                                               int64_t dq, int64_t sq, uint32_t *red) {
+  auto routed = [&](int j) { return j >= j0 && j < j1 && s[j] >= 0; };
   if constexpr (Q == EP_QUANT_NONE) {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -176,10 +158,9 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
       if (v >= nvec) continue;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (s[j] >= 0) st_row(data + s[j] * dq + (int64_t)v * 16, raw[i]);
+        if (routed(j)) st_row(data + s[j] * dq + (int64_t)v * 16, raw[i]);
     }
   } else if constexpr (Q == EP_QUANT_INT8_TOKEN) {
-    __shared__ uint32_t red[NT / kWave];
     uint32_t am = 0;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) am = max(am, vec_absmax_bits(raw[i]));
@@ -193,12 +174,12 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
       const u32x2 q = pin(codes_int8(f, b));
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (s[j] >= 0) st_row(data + s[j] * dq + (int64_t)v * 8, q);
+        if (routed(j)) st_row(data + s[j] * dq + (int64_t)v * 8, q);
     }
     if (threadIdx.x == 0) {
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (s[j] >= 0) st_row(scales + s[j] * sq, b.scale);
+        if (routed(j)) st_row(scales + s[j] * sq, b.scale);
     }
   } else {
 #pragma unroll
@@ -214,7 +195,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
         const bool lead = (v & 15) == 0;
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
-          if (s[j] < 0) continue;
+          if (!routed(j)) continue;
           st_row(data + s[j] * dq + (int64_t)v * 8, q);
           if (lead) st_row(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
         }
@@ -249,7 +230,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
         }
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
-          if (s[j] < 0) continue;
+          if (!routed(j)) continue;
           st_row(data + s[j] * dq + (int64_t)v * kBytes, q);
           if (lead) {
             char *sp = scales + s[j] * sq + (int64_t)(v >> 2);
@@ -262,14 +243,75 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
   }
 }
 
-template <int Q, int NT, int VPT, bool PACK = false>
+// One workgroup per (token, span of its row).  WEIGHTED = false: dispatch --
+// the token row is quantised once and stored to every routed row (and, if
+// recv_w is given, row slot[t, j] receives w[t, j]).  WEIGHTED = true: the
+// reverse dispatch of combine's gradient -- row slot[t, j] receives the
+// quantised bf16(w[t, j] * x[t]), one quantisation per routed pair.
+template <int Q, int NT, int VPT, int KMAX, bool EXACT, bool PACK, bool WEIGHTED>
+__global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ x, int nvec, int k, int chunks,
+                                                      const int *__restrict__ slot,
+                                                      const float *__restrict__ w, float *__restrict__ recv_w,
+                                                      char *__restrict__ data, char *__restrict__ scales,
+                                                      int64_t dq, int64_t sq) {
+  __shared__ uint32_t red[NT / kWave];
+  const int t = blockIdx.x / chunks;
+  const int c = blockIdx.x - t * chunks;
+  const int64_t pair0 = (int64_t)t * k;
+
+  // routed rows: loads from valid addresses first, then masking, so the loads
+  // are in flight together (with k == KMAX they are one wide scalar load)
+  int s[KMAX];
+  float wj[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int jj = EXACT ? j : min(j, k - 1);
+    s[j] = slot[pair0 + jj];
+    if constexpr (WEIGHTED) wj[j] = w[pair0 + jj];
+  }
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    s[j] = j < k ? s[j] : -1;
+    any |= s[j] >= 0;
+  }
+  if (!any) return;   // uniform: the token is routed nowhere
+  if (!WEIGHTED && recv_w != nullptr && c == 0 && threadIdx.x < k) {
+    const int r = slot[pair0 + threadIdx.x];
+    if (r >= 0) recv_w[r] = w[pair0 + threadIdx.x];
+  }
+
+  const u32x4 *xr = x + (int64_t)t * nvec;
+  const int v0 = c * NT * VPT + threadIdx.x;
+  u32x4 raw[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = v0 + i * NT;
+    raw[i] = v < nvec ? xr[v] : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  if constexpr (!WEIGHTED) {
+    quantize_store<Q, NT, VPT, KMAX, PACK>(raw, v0, nvec, s, 0, KMAX, data, scales, dq, sq, red);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (s[j] < 0) continue;   // uniform
+      u32x4 sr[VPT];
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) sr[i] = scale_bf16x8(raw[i], wj[j]);
+      quantize_store<Q, NT, VPT, KMAX, PACK>(sr, v0, nvec, s, j, j + 1, data, scales, dq, sq, red);
+    }
+  }
+}
+
+template <int Q, int NT, int VPT, bool PACK, bool WEIGHTED>
 hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *w, char *recv, float *recv_w,
                     int64_t dq, int64_t sq, size_t scale_off, hipStream_t s) {
   const int chunks = (nvec + NT * VPT - 1) / (NT * VPT);
   const int64_t blocks = h.num_tokens * chunks;
   if (blocks == 0) return hipSuccess;
 #define EP_LAUNCH_DISPATCH(KMAX, EXACT)                                                                     \
-  hipLaunchKernelGGL((dispatch_kernel<Q, NT, VPT, KMAX, EXACT, PACK>), dim3((unsigned)blocks), dim3(NT),          \
+  hipLaunchKernelGGL((dispatch_kernel<Q, NT, VPT, KMAX, EXACT, PACK, WEIGHTED>), dim3((unsigned)blocks), dim3(NT), \
                      EP_DISPATCH_LDS_CAP, s, (const u32x4 *)x, nvec, h.num_topk, chunks, h.slot, w, recv_w, recv, \
                      recv + scale_off, dq, sq)
   if (h.num_topk == 8) EP_LAUNCH_DISPATCH(8, true);
@@ -280,7 +322,7 @@ hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *
   return hipGetLastError();
 }
 
-template <int Q>
+template <int Q, bool WEIGHTED>
 hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const float *w, char *recv,
                        float *recv_w, hipStream_t s) {
   size_t dq, sq;
@@ -289,17 +331,31 @@ hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const fl
   const int nvec = hidden / 8;
   if constexpr (Q == EP_QUANT_INT8_TOKEN) {
     // the whole row must sit in one workgroup (its amax is a row reduction)
-    if (nvec <= 256) return launch_q<Q, 256, 1>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    if (nvec <= 512) return launch_q<Q, 256, 2>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    if (nvec <= 1024) return launch_q<Q, 256, 4>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    if (nvec <= 2048) return launch_q<Q, 256, 8>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    return launch_q<Q, 1024, 8>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (nvec <= 256) return launch_q<Q, 256, 1, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (nvec <= 512) return launch_q<Q, 256, 2, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (nvec <= 1024) return launch_q<Q, 256, 4, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (nvec <= 2048) return launch_q<Q, 256, 8, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    return launch_q<Q, 1024, 8, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
   } else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) {
     constexpr int NT = EP_DISPATCH_THREADS, VPT = EP_DISPATCH_VPT;
-    if (hidden % 128 == 0) return launch_q<Q, NT, VPT, true>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    return launch_q<Q, NT, VPT, false>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (hidden % 128 == 0)
+      return launch_q<Q, NT, VPT, true, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    return launch_q<Q, NT, VPT, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
   } else {
-    return launch_q<Q, EP_DISPATCH_THREADS, EP_DISPATCH_VPT>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    return launch_q<Q, EP_DISPATCH_THREADS, EP_DISPATCH_VPT, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq,
+                                                                          scale_off, s);
+  }
+}
+
+template <bool WEIGHTED>
+hipError_t launch_any(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant, char *recv,
+                      float *recv_w, hipStream_t s) {
+  switch (quant) {
+    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
+    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
+    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
+    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
+    default: return launch_mode<EP_QUANT_MXFP4, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
   }
 }
 
@@ -307,13 +363,13 @@ hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const fl
 
 hipError_t launch_dispatch(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant,
                            char *recv, float *recv_w, hipStream_t s) {
-  switch (quant) {
-    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE>(h, x, hidden, w, recv, recv_w, s);
-    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN>(h, x, hidden, w, recv, recv_w, s);
-    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128>(h, x, hidden, w, recv, recv_w, s);
-    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8>(h, x, hidden, w, recv, recv_w, s);
-    default: return launch_mode<EP_QUANT_MXFP4>(h, x, hidden, w, recv, recv_w, s);
-  }
+  return launch_any<false>(h, x, hidden, w, quant, recv, recv_w, s);
+}
+
+hipError_t launch_combine_backward(const ep_handle_t &h, const void *grad, int hidden, const float *w, int quant,
+                                   char *buf, hipStream_t s) {
+  if (w == nullptr) return launch_any<false>(h, grad, hidden, nullptr, quant, buf, nullptr, s);
+  return launch_any<true>(h, grad, hidden, w, quant, buf, nullptr, s);
 }
 
 }  // namespace ep

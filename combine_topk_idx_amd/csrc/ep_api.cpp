@@ -188,6 +188,30 @@ ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t
   return EP_OK;
 }
 
+ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out, int32_t hidden,
+                                const float *topk_weights, ep_quant_t quant, void *grad_buf, size_t grad_buf_bytes,
+                                void *stream) {
+  const char *fn = "ep_combine_backward";
+  ep_status_t st = check_handle(handle, fn);
+  if (st != EP_OK) return st;
+  st = check_hidden(hidden, quant, fn);
+  if (st != EP_OK) return st;
+  if (handle->num_tokens > 0 && !grad_out) return fail(EP_ERR_INVALID_ARG, "%s: grad_out is NULL", fn);
+  if (grad_out && !aligned(grad_out, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: grad_out is not 16-byte aligned", fn);
+  if (!grad_buf || !aligned(grad_buf, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: grad_buf is NULL or not 16-byte aligned", fn);
+  const size_t need = buffer_bytes(handle->max_rows, hidden, quant, nullptr);
+  if (grad_buf_bytes < need)
+    return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: grad_buf has %zu bytes, needs %zu", fn, grad_buf_bytes, need);
+  if (topk_weights && !aligned(topk_weights, 4))
+    return fail(EP_ERR_INVALID_ARG, "%s: topk_weights is misaligned", fn);
+  const hipError_t e = ep::launch_combine_backward(*handle, grad_out, hidden, topk_weights, quant, (char *)grad_buf,
+                                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return EP_OK;
+}
+
 ep_status_t ep_read_status(const ep_handle_t *handle, uint32_t *flags, void *stream) {
   const char *fn = "ep_read_status";
   if (!handle || !handle->status) return fail(EP_ERR_INVALID_ARG, "%s: handle is NULL", fn);

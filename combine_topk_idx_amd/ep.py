@@ -35,7 +35,7 @@ QUANT = {"none": 0, "int8_token": 1, "fp8_b128": 2, "mxfp8": 3, "mxfp4": 4}
 EP_STATUS_ID_OUT_OF_RANGE = 1
 
 SYMBOLS = ("ep_workspace_bytes", "ep_buffer_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-           "ep_read_status", "ep_last_error", "ep_abi_version")
+           "ep_combine_backward", "ep_read_status", "ep_last_error", "ep_abi_version")
 
 
 class ep_handle_t(ctypes.Structure):
@@ -64,6 +64,8 @@ _lib.ep_dispatch.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes
 _lib.ep_dispatch.restype = ctypes.c_int
 _lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int, _i32, _vp, _vp, _vp]
 _lib.ep_combine.restype = ctypes.c_int
+_lib.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp]
+_lib.ep_combine_backward.restype = ctypes.c_int
 _lib.ep_read_status.argtypes = [ctypes.POINTER(ep_handle_t), ctypes.POINTER(ctypes.c_uint32), _vp]
 _lib.ep_read_status.restype = ctypes.c_int
 _lib.ep_last_error.argtypes = []
@@ -171,6 +173,13 @@ def ep_combine(handle: ep_handle_t, expert_out, in_quant, hidden: int, topk_weig
     nbytes = _nbytes(expert_out) if expert_out_bytes is None else expert_out_bytes
     _check(_lib.ep_combine(ctypes.byref(handle), _ptr(expert_out), nbytes, _quant(in_quant), hidden,
                            _ptr(topk_weights), _ptr(out), _stream(stream)))
+
+
+def ep_combine_backward(handle: ep_handle_t, grad_out, hidden: int, quant, grad_buf, topk_weights=None, *,
+                        grad_buf_bytes=None, stream=None) -> None:
+    nbytes = _nbytes(grad_buf) if grad_buf_bytes is None else grad_buf_bytes
+    _check(_lib.ep_combine_backward(ctypes.byref(handle), _ptr(grad_out), hidden, _ptr(topk_weights),
+                                    _quant(quant), _ptr(grad_buf), nbytes, _stream(stream)))
 
 
 def ep_read_status(handle: ep_handle_t, stream=None) -> int:

@@ -164,6 +164,26 @@ ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t
                        ep_quant_t in_quant, int32_t hidden, const float *topk_weights, void *out,
                        void *stream);
 
+/* Backward of combine with respect to the expert outputs, as a reverse
+ * dispatch ("EP dispatch with unfused MXFP8 quantization", Description and
+ * Changes: the result gradient is scattered back to the expert rows through
+ * the same dispatch operation, quantised).
+ *   handle         host, from the ep_layout of the forward pass
+ *   grad_out       device bf16 [T, H] (gradient of combine's output), 16-byte aligned
+ *   hidden         H, as for ep_dispatch
+ *   topk_weights   device float32 [T, k] or NULL
+ *   quant          format of the gradient rows (any ep_quant_t)
+ *   grad_buf       device receive-format buffer (rows = max_rows), 16-byte
+ *                  aligned, >= ep_buffer_bytes(max_rows, H, quant)
+ * With topk_weights, row slot[t, j] receives the quantised
+ * bf16_rne(fl32(topk_weights[t, j] * grad_out[t])) -- the gradient of the
+ * weighted sum with respect to expert row j -- quantised once per routed
+ * pair.  Without, it receives the quantised grad_out[t] (exactly
+ * ep_dispatch of grad_out).  Rows at or past R are left unspecified. */
+ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out, int32_t hidden,
+                                const float *topk_weights, ep_quant_t quant, void *grad_buf,
+                                size_t grad_buf_bytes, void *stream);
+
 /* Waits for `stream` and copies the status word of `handle` to host *flags. */
 ep_status_t ep_read_status(const ep_handle_t *handle, uint32_t *flags, void *stream);
 

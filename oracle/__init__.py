@@ -17,12 +17,12 @@ the source pages it follows.  The pages are:
 * "[feat] A5 deep fused moe" (sgl-kernel-npu pull request 661), section
   Testing (the fused-counts table).
 * "EP dispatch with unfused MXFP8 quantization" (TransformerEngine pull
-  request 3270), section Changes.
+  request 3270), sections Description and Changes.
 * "DeepEP topk_idx_t Custom Dtype Requirements", sections "Tensor
   Requirements and Constraints" and "Runtime Validation".
 
-Where the pages are silent or garbled the oracle takes the readings listed
-in DESIGN.md under "Readings of the pages".
+Where the pages are silent or garbled, each module states the reading it
+takes.
 
 Modules:
 
@@ -31,12 +31,14 @@ Modules:
 * ``layout``   -- expert histogram, exclusive scan, stable slot assignment.
 * ``dispatch`` -- quantise each token once and copy it to each routed row.
 * ``combine``  -- gather, dequantise, fp32 weighted sum in top-k order.
+* ``backward`` -- combine's gradient with respect to the expert rows, as a
+  reverse dispatch.
 * ``validate`` -- the argument rules the C ABI enforces before any launch.
 
 Parity status of every function is listed in each module's header.
 """
 
-from . import codecs, quant, layout, dispatch, combine, validate  # noqa: F401
+from . import codecs, quant, layout, dispatch, combine, backward, validate  # noqa: F401
 from .layout import Layout  # noqa: F401
 
 QUANT_MODES = ("none", "int8_token", "fp8_b128", "mxfp8", "mxfp4")

@@ -163,7 +163,7 @@ def e2m1_encode(v: np.ndarray) -> np.ndarray:
 def pack_e2m1_pairs(codes: np.ndarray) -> np.ndarray:
     """Two e2m1 codes per byte along the last axis: element 2i in the low
     nibble, element 2i+1 in the high nibble (the pages do not fix the order;
-    this is the reading the design doc records)."""
+    this is the reading taken)."""
     c = np.asarray(codes, dtype=np.uint8)
     if c.shape[-1] % 2:
         raise ValueError("odd number of e2m1 codes")

@@ -13,8 +13,10 @@ by the stored inverse scale through float32 and accumulated):
     out[t] = bf16 round-half-even of acc
 
 One multiply then one add per term, float32, no fused multiply-add and no
-reordering (reading S17).  A token with no routed pair gives +0 (reading
-S15).
+reordering (one page describes the accumulation as bf16 in one place and as
+going through float32 in another; float32 accumulation, rounded once, is the
+reading taken).  A token with no
+routed pair gives +0 (the pages are silent on this case).
 
 Parity: pinned by the closed form for unit weights and bf16 rows (the sum
 of k_eff equal terms is exact in float32, so out == bf16(k_eff * x)), and for

@@ -5,9 +5,10 @@ Each token row is quantised once ("Low-Latency Mode API", Parameters
 Operations", "The Dispatch Stage") and copied to the receive row
 ``slot[t, j]`` of every routed pair.
 
-Receive buffer (reading S9 and S11; "EP dispatch with unfused MXFP8
-quantization", Changes: data and block scales share one caller buffer,
-sliced into a data region followed by a scale region):
+Receive buffer ("EP dispatch with unfused MXFP8 quantization", Changes: data
+and block scales share one caller buffer, sliced into a data region followed
+by a scale region; the pages do not fix the exact layout, so this is the
+reading taken -- compact expert-major rows, row-major scales):
 
 * data region: ``max_rows`` rows of ``Dq`` bytes, row-major;
 * scale region: starts at ``align_up(max_rows * Dq, 256)``; ``max_rows`` rows
@@ -17,7 +18,8 @@ sliced into a data region followed by a scale region):
 padding between the regions are unspecified and never compared.
 
 If ``topk_weights`` is given, ``recv_weights[slot[t, j]] = topk_weights[t, j]``
-(reading S16).
+(the pages list the argument without saying what dispatch does with it;
+this is the reading taken).
 
 Parity: the ``none`` mode is pinned by ``recv[slot[t, j]] == x[t]`` bit for
 bit; the quantised modes inherit the pins of ``quant``.

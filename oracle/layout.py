@@ -5,17 +5,20 @@ Return Values ``recv_count``; the expert histogram, exclusive scan and
 stable token-order slot assignment of the hot path):
 
 * ``count[e]``  -- how many (token, j) pairs chose expert ``e``; ``-1`` means
-  no expert.  Duplicates within one token count once each (reading S8).
+  no expert.  Duplicates within one token count once each (the pages are silent;
+  each pair gets its own row).
 * ``offsets``   -- exclusive prefix sum of ``count``; ``offsets[E]`` is the
   number of routed rows R.  Expert ``e`` owns rows
   ``[offsets[e], offsets[e] + count[e])`` of the compact receive buffer
-  (reading S9).
+  (the pages show both a flat and a per-expert padded form; compact
+  expert-major rows are the reading taken).
 * ``slot[t, j]`` -- the receive row of pair (t, j), or -1.  Rows of one
-  expert are in ascending (t, j) order (reading S7).
+  expert are in ascending (t, j) order (stable token order, ties within a
+  token by j).
 * ``row_src[r]`` -- ``t * k + j`` of the pair stored in row r, -1 for
   ``r >= R``.
 * ``status``    -- bit 0 set when some id lies outside [-1, E); such pairs
-  are dropped as if they were -1 (reading S14).
+  are dropped as if they were -1 (the pages are silent on such ids).
 * ``cum_stats`` -- ``cumulative_local_expert_recv_stats`` plus ``count``
   ("Low-Latency Mode API", Parameters).
 

@@ -13,20 +13,22 @@ modes and the passages they follow:
   hidden dimension is cut into 128-element blocks, each with its own amax
   and scale; "The FP8 Combine Operation": the stored inverse scale multiplies
   the codes back).  The page prints the multiplier as 127/amax; for e4m3 the
-  largest code is 448, so the oracle uses 448 (reading S1).
+  largest code is 448, so the oracle uses 448.
 * ``mxfp8``      -- e4m3 codes plus one e8m0 scale per 32-element block
   ("Low-Latency Mode API", ``use_ue8m0``).
 * ``mxfp4``      -- e2m1 codes, two per byte, plus one e8m0 scale per
   32-element block ("Low-Latency Mode API", ``use_mxfp4``).
 
-Arithmetic for the scaled modes (reading S2): with ``qmax`` the largest code
+Arithmetic for the scaled modes (the pages give the scale, not the order of
+operations; this is the reading taken): with ``qmax`` the largest code
 (127 or 448), the multiplier ``m = fl32(qmax / amax)`` scales the elements
 and the stored scale is ``s = fl32(amax / qmax)`` -- two separate float32
 divisions, each rounded once.  Each element is ``fl32(x * m)``, clamped to
 +-qmax and rounded to the code.  If ``amax`` is zero or ``m`` is not finite
-the block stores scale 0 and all codes 0 (reading S3).
+the block stores scale 0 and all codes 0 (the pages are silent on this case).
 
-MX scale rule (reading S6): with ``e = floor(log2(amax))`` and ``emax`` the
+MX scale rule (the pages give only the block size, 32 elements, and the scale
+format; this is the OCP MX rule): with ``e = floor(log2(amax))`` and ``emax`` the
 exponent of the element format's largest value (8 for e4m3, whose largest is
 1.75 * 2**8; 2 for e2m1, whose largest is 1.5 * 2**2), the shared exponent is
 ``clamp(e - emax, -127, 127)`` (-127 when amax is zero) and the stored byte
@@ -38,7 +40,7 @@ element mapping to +-qmax and the per-element error bound; the MX scale byte
 pinned by recomputation with ``math.frexp``; all element rounding is in
 ``codecs`` (pinned there).  The MX rule itself is pinned only by the OCP MX
 specification, which is not among the pages: that part is "parity unpinned"
-with respect to the pages and is stated so in the design doc.
+with respect to the pages.
 """
 
 from __future__ import annotations
@@ -77,7 +79,7 @@ def _amax(x_f32: np.ndarray) -> np.float32:
 
 def _scaled_block(x_f32: np.ndarray, qmax: np.float32):
     """Multiplier, stored scale and the scaled, clamped elements of one block
-    (see the module header: reading S2 and S3)."""
+    (see the module header)."""
     amax = _amax(x_f32)
     with np.errstate(divide="ignore", over="ignore"):
         m = np.float32(qmax / amax) if amax != 0 else np.float32(np.inf)

@@ -7,7 +7,8 @@ Constraints": exact index dtype, two dimensions [num_tokens, num_topk],
 contiguous).  The numeric limits follow "Low-Latency Mode API",
 Constraints: num_topk in (0, 16], num_experts in (0, 512], hidden a positive
 multiple of 32, and the token count bounded by num_max_dispatch_tokens_per_rank
-(reading S13: "at most", not "less than").  The per-128 FP8 mode also needs
+(read as "at most": the page gives a strict and a non-strict bound in two
+places).  The per-128 FP8 mode also needs
 hidden % 128 == 0 (its blocks are 128 wide).
 
 ``check_*`` raise ``ValueError`` exactly where the ABI returns

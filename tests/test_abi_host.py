@@ -140,6 +140,22 @@ def test_combine_rejects(ep, kw, code):
     assert ep.ep_last_error().startswith("ep_combine")
 
 
+BACKWARD_BAD = [
+    (dict(hidden=48), 1), (dict(quant=9), 1), (dict(grad=None), 1), (dict(grad=FAKE + 8), 1),
+    (dict(buf=None), 1), (dict(buf=FAKE + 4), 1), (dict(buf_bytes=3), 3), (dict(w=FAKE + 1), 1),
+    (dict(hidden=160, quant=2), 1),
+]
+
+
+@pytest.mark.parametrize("kw,code", BACKWARD_BAD)
+def test_combine_backward_rejects(ep, kw, code):
+    h = _handle(ep)
+    rc = ep._lib.ep_combine_backward(ctypes.byref(h), kw.get("grad", FAKE), kw.get("hidden", 256), kw.get("w", None),
+                                     kw.get("quant", 3), kw.get("buf", FAKE), kw.get("buf_bytes", 1 << 30), None)
+    assert rc == code, ep.ep_last_error()
+    assert ep.ep_last_error().startswith("ep_combine_backward")
+
+
 @pytest.mark.parametrize("hidden,mode", [(32, "none"), (7168, "int8_token"), (7168, "fp8_b128"),
                                          (96, "mxfp8"), (7168, "mxfp4"), (1024, "mxfp4")])
 @pytest.mark.parametrize("rows", [0, 1, 37, 131072])
