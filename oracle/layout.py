@@ -25,6 +25,21 @@ stable token-order slot assignment of the hot path):
 The loop below is the definition itself: walk the pairs in (t, j) order and
 hand each routed pair the next free row of its expert.
 
+Two receive-row arrangements besides the compact one:
+
+* ``row_align = A > 1`` -- every expert's block of rows starts at a multiple
+  of A: ``offsets`` is the exclusive prefix sum of ``align_up(count[e], A)``
+  (the per-expert alignment a grouped GEMM wants; "EP dispatch with unfused
+  MXFP8 quantization", Tests: the grouped path pins a per-expert alignment).
+* ``expert_capacity = C > 0`` -- expert e owns rows [e*C, (e+1)*C): the padded
+  per-expert form of the combine input in "Low-Latency Mode API"
+  (``low_latency_combine`` Parameters, ``x``).  Pairs past the C-th of an
+  expert are dropped (slot -1) and set status bit 1; ``count`` reports the
+  rows actually received (at most C) while ``cum_stats`` adds the full demand.
+
+Rows not holding a pair (alignment or capacity padding, and rows past the
+last used one) have ``row_src`` -1.
+
 Parity: pinned by brute force against ``np.argsort(kind="stable")`` and
 ``np.bincount`` (library routines), by the invariants sum(count) == number
 of valid ids and "slot is a bijection onto [0, R)", and by the worked
@@ -54,27 +69,47 @@ class Layout:
 
     @property
     def num_rows(self) -> int:
+        """Rows up to the end of the last expert's block (compact: R)."""
         return int(self.offsets[-1])
+
+    def valid_rows(self) -> np.ndarray:
+        """Indices of the rows that hold a pair."""
+        return np.nonzero(self.row_src >= 0)[0]
 
 
 def layout(topk_idx: np.ndarray, num_experts: int, num_max_dispatch_tokens: int,
-           cum_stats: np.ndarray | None = None) -> Layout:
+           cum_stats: np.ndarray | None = None, row_align: int = 1, expert_capacity: int = 0) -> Layout:
     idx = np.asarray(topk_idx).astype(np.int64)
     if idx.ndim != 2:
         raise ValueError("topk_idx must be [num_tokens, num_topk]")
+    if row_align < 1 or expert_capacity < 0:
+        raise ValueError("row_align >= 1 and expert_capacity >= 0")
+    if expert_capacity > 0 and row_align > 1:
+        raise ValueError("expert_capacity and row_align > 1 are exclusive")
     T, k = idx.shape
     E = int(num_experts)
-    max_rows = int(num_max_dispatch_tokens) * k
+    if expert_capacity > 0:
+        max_rows = E * int(expert_capacity)
+    else:
+        max_rows = int(num_max_dispatch_tokens) * k + E * (row_align - 1)
     flat = idx.reshape(-1)
     valid = (flat >= 0) & (flat < E)
     status = 1 if np.any((flat != -1) & ~valid) else 0
 
-    count = np.zeros(E, dtype=np.int64)
+    demand = np.zeros(E, dtype=np.int64)
     for e in flat[valid]:
-        count[e] += 1
+        demand[e] += 1
+    if expert_capacity > 0:
+        count = np.minimum(demand, expert_capacity)
+        block = np.full(E, expert_capacity, dtype=np.int64)
+        if np.any(demand > expert_capacity):
+            status |= 2
+    else:
+        count = demand.copy()
+        block = (count + row_align - 1) // row_align * row_align
     offsets = np.zeros(E + 1, dtype=np.int64)
     for e in range(E):
-        offsets[e + 1] = offsets[e] + count[e]
+        offsets[e + 1] = offsets[e] + block[e]
 
     slot = np.full(T * k, -1, dtype=np.int32)
     row_src = np.full(max_rows, -1, dtype=np.int32)
@@ -83,11 +118,14 @@ def layout(topk_idx: np.ndarray, num_experts: int, num_max_dispatch_tokens: int,
         if not valid[f]:
             continue
         e = flat[f]
-        r = offsets[e] + fill[e]
+        rank = fill[e]
         fill[e] += 1
+        if expert_capacity > 0 and rank >= expert_capacity:
+            continue
+        r = offsets[e] + rank
         slot[f] = r
         row_src[r] = f
 
     if cum_stats is not None:
-        cum_stats += count.astype(cum_stats.dtype)
+        cum_stats += demand.astype(cum_stats.dtype)
     return Layout(T, k, E, max_rows, count, offsets, slot.reshape(T, k), row_src, status)

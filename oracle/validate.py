@@ -38,6 +38,28 @@ def check_layout(num_tokens: int, num_topk: int, num_max_dispatch_tokens: int, n
         raise ValueError("num_max_dispatch_tokens * num_topk exceeds int32")
 
 
+MAX_ROW_ALIGN = 1024
+
+
+def check_padding(num_topk: int, num_max_dispatch_tokens: int, num_experts: int, row_align: int,
+                  expert_capacity: int) -> int:
+    """Rules of the aligned / capacity-padded receive arrangements (limits
+    chosen here: the pages fix none).  Returns the receive rows."""
+    if not (1 <= row_align <= MAX_ROW_ALIGN):
+        raise ValueError("row_align must be in [1, 1024]")
+    if expert_capacity < 0:
+        raise ValueError("negative expert_capacity")
+    if expert_capacity > 0 and row_align > 1:
+        raise ValueError("expert_capacity and row_align > 1 are exclusive")
+    if expert_capacity > 0:
+        rows = num_experts * expert_capacity
+    else:
+        rows = num_max_dispatch_tokens * num_topk + num_experts * (row_align - 1)
+    if rows > 2 ** 31 - 1:
+        raise ValueError("receive rows exceed int32")
+    return rows
+
+
 def check_hidden(hidden: int, mode: str) -> None:
     if mode not in QUANT_MODES:
         raise ValueError(f"unknown quant mode {mode!r}")

@@ -100,3 +100,125 @@ def test_layout_cumulative_stats():
     cum = np.array([5, 0, 2], np.int32)
     L.layout(idx, 3, 2, cum_stats=cum)
     assert cum.tolist() == [6, 3, 2]
+
+
+# ---------------------------------------------------------------------------
+# aligned and capacity-padded per-expert arrangements
+# ---------------------------------------------------------------------------
+
+
+def _brute_padded(idx, E, tmax, align=1, cap=0):
+    """Expected (count, offsets, row_src, slot, status) from the stable
+    argsort: expert e's pairs in (t, j) order, placed at the start of its
+    block (blocks of align_up(count, align) rows, or of cap rows)."""
+    T, k = idx.shape
+    demand, order = _brute(idx, E)
+    starts_compact = np.concatenate([[0], np.cumsum(demand)])
+    if cap:
+        blocks = np.full(E, cap)
+        max_rows = E * cap
+    else:
+        blocks = -(-demand // align) * align
+        max_rows = tmax * k + E * (align - 1)
+    offsets = np.concatenate([[0], np.cumsum(blocks)])
+    row_src = np.full(max_rows, -1)
+    slot = np.full(T * k, -1)
+    for e in range(E):
+        mine = order[starts_compact[e]:starts_compact[e + 1]]
+        if cap:
+            mine = mine[:cap]
+        rows = offsets[e] + np.arange(mine.size)
+        row_src[rows] = mine
+        slot[mine] = rows
+    flat = idx.reshape(-1)
+    status = int(np.any((flat != -1) & ((flat < 0) | (flat >= E))))
+    if cap and np.any(demand > cap):
+        status |= 2
+    count = np.minimum(demand, cap) if cap else demand
+    return count, offsets, row_src, slot.reshape(T, k), status, demand
+
+
+@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("align", [1, 2, 8, 128])
+def test_aligned_layout_matches_brute(seed, align):
+    rng = np.random.default_rng(500 + seed)
+    T = int(rng.integers(0, 50))
+    k = int(rng.integers(1, 17))
+    E = int(rng.integers(1, 30))
+    idx = rng.integers(-1, E, size=(T, k))
+    if seed % 4 == 1 and T:
+        idx[0, 0] = E + 1
+    stats = np.zeros(E, np.int64)
+    lay = L.layout(idx, E, T + 3, cum_stats=stats, row_align=align)
+    count, offsets, row_src, slot, status, demand = _brute_padded(idx, E, T + 3, align=align)
+    assert lay.max_rows == row_src.size
+    assert np.array_equal(lay.count, count)
+    assert np.array_equal(lay.offsets, offsets)
+    assert np.all(lay.offsets % align == 0)
+    assert np.array_equal(lay.row_src, row_src)
+    assert np.array_equal(lay.slot, slot)
+    assert lay.status == status
+    assert np.array_equal(stats, demand)
+    assert lay.num_rows <= lay.max_rows
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_capacity_layout_matches_brute(seed):
+    rng = np.random.default_rng(700 + seed)
+    T = int(rng.integers(1, 50))
+    k = int(rng.integers(1, 9))
+    E = int(rng.integers(1, 20))
+    idx = rng.integers(-1, E, size=(T, k))
+    demand = np.bincount(idx[idx >= 0], minlength=E)
+    cap = int(rng.integers(1, demand.max() + 3)) if demand.max() > 0 else 1
+    stats = np.zeros(E, np.int64)
+    lay = L.layout(idx, E, T, cum_stats=stats, expert_capacity=cap)
+    count, offsets, row_src, slot, status, dem = _brute_padded(idx, E, T, cap=cap)
+    assert lay.max_rows == E * cap
+    assert np.array_equal(lay.count, count)
+    assert np.array_equal(lay.offsets, offsets)
+    assert np.array_equal(lay.row_src, row_src)
+    assert np.array_equal(lay.slot, slot)
+    assert lay.status == status
+    assert np.array_equal(stats, dem)          # statistics count the whole demand
+
+
+def test_align_one_and_large_capacity_reduce_to_compact():
+    rng = np.random.default_rng(9)
+    idx = rng.integers(-1, 12, size=(40, 6))
+    base = L.layout(idx, 12, 40)
+    same = L.layout(idx, 12, 40, row_align=1)
+    assert np.array_equal(base.slot, same.slot) and np.array_equal(base.row_src, same.row_src)
+    # capacity >= every demand: the slot of a pair is e*C + (its compact row - offsets[e])
+    C = int(base.count.max())
+    padded = L.layout(idx, 12, 40, expert_capacity=C)
+    assert padded.status == 0
+    flat, s0, s1 = idx.reshape(-1), base.slot.reshape(-1), padded.slot.reshape(-1)
+    ok = flat >= 0
+    assert np.array_equal(s1[ok], flat[ok] * C + (s0[ok] - base.offsets[flat[ok]]))
+    assert np.all(s1[~ok] == -1)
+
+
+def test_padded_layouts_worked_example():
+    # two tokens, top-3, four experts: expert 1 gets pairs (0,2), (1,0);
+    # expert 3 gets (0,0), (0,1), (1,2), in that order
+    idx = np.array([[3, 3, 1], [1, -1, 3]])
+    a = L.layout(idx, 4, 2, row_align=4)
+    assert a.offsets.tolist() == [0, 0, 4, 4, 8]
+    assert a.slot.tolist() == [[4, 5, 0], [1, -1, 6]]
+    assert a.row_src.tolist()[:8] == [2, 3, -1, -1, 0, 1, 5, -1]
+    assert a.max_rows == 2 * 3 + 4 * 3
+    c = L.layout(idx, 4, 2, expert_capacity=2)
+    assert c.offsets.tolist() == [0, 2, 4, 6, 8]
+    assert c.slot.tolist() == [[6, 7, 2], [3, -1, -1]]
+    assert c.row_src.tolist() == [-1, -1, 2, 3, -1, -1, 0, 1]
+    assert c.count.tolist() == [0, 2, 0, 2]
+    assert c.status == 2
+
+
+def test_padded_layout_rejects_bad_arguments():
+    idx = np.zeros((2, 2), np.int64)
+    with pytest.raises(ValueError):
+        L.layout(idx, 4, 2, row_align=0)
+    with pytest.raises(ValueError):
+        L.layout(idx, 4, 2, expert_capacity=-1)
