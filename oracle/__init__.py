@@ -27,7 +27,7 @@ takes.
 Modules:
 
 * ``codecs``   -- bf16, int8, OCP e4m3fn, OCP e2m1 and e8m0 element codecs.
-* ``quant``    -- the five per-row quantisation modes.
+* ``quant``    -- the seven per-row quantisation modes.
 * ``layout``   -- expert histogram, exclusive scan, stable slot assignment.
 * ``dispatch`` -- quantise each token once and copy it to each routed row.
 * ``combine``  -- gather, dequantise, fp32 weighted sum in top-k order.
@@ -41,4 +41,4 @@ Parity status of every function is listed in each module's header.
 from . import codecs, quant, layout, dispatch, combine, backward, validate  # noqa: F401
 from .layout import Layout  # noqa: F401
 
-QUANT_MODES = ("none", "int8_token", "fp8_b128", "mxfp8", "mxfp4")
+QUANT_MODES = ("none", "int8_token", "fp8_b128", "mxfp8", "mxfp4", "fp8_b128_pow2", "fp8_b128_ue8m0")

@@ -1,6 +1,6 @@
 """Per-row quantisation of the oracle (test infrastructure only).
 
-Every token row is quantised once, then copied to each routed row.  The five
+Every token row is quantised once, then copied to each routed row.  The seven
 modes and the passages they follow:
 
 * ``none``       -- bf16 passes through ("Low-Latency Mode API", Return
@@ -14,6 +14,16 @@ modes and the passages they follow:
   and scale; "The FP8 Combine Operation": the stored inverse scale multiplies
   the codes back).  The page prints the multiplier as 127/amax; for e4m3 the
   largest code is 448, so the oracle uses 448.
+* ``fp8_b128_pow2`` -- as ``fp8_b128`` with every scale rounded to a power
+  of two ("DeepEP FP8 Dispatch and Combine Operations", Advanced
+  Configuration Options: ``round_scale``; "Low-Latency Mode API",
+  Parameters: ``round_scale``).  The page says "nearest"; rounding a scale
+  down would push the block's largest element past 448, so the reading
+  taken is: round the computed scale UP to the next power of two.
+* ``fp8_b128_ue8m0`` -- the same codes and power-of-two scales, each scale
+  stored as one e8m0 byte instead of a float32 (same page and section:
+  ``use_ue8m0`` packs the scales into 8 bits); byte g of a row's scales is
+  128-channel block g, so four consecutive blocks share one int32.
 * ``mxfp8``      -- e4m3 codes plus one e8m0 scale per 32-element block
   ("Low-Latency Mode API", ``use_ue8m0``).
 * ``mxfp4``      -- e2m1 codes, two per byte, plus one e8m0 scale per
@@ -27,6 +37,15 @@ divisions, each rounded once.  Each element is ``fl32(x * m)``, clamped to
 +-qmax and rounded to the code.  If ``amax`` is zero or ``m`` is not finite
 the block stores scale 0 and all codes 0 (the pages are silent on this case).
 
+Power-of-two scale (``fp8_b128_pow2`` / ``fp8_b128_ue8m0``): with
+``s0 = fl32(amax / 448)`` (the ``fp8_b128`` scale) and ``e = ceil(log2 s0)``
+read off the float32 bits of s0, the scale is ``2**e`` and the multiplier
+``2**-e``; both are exact, so each element is ``fl32(x * 2**-e)`` (exact
+unless it falls below float32's normal range), clamped to +-448 and rounded
+to e4m3.  A block with amax zero, or with ``e < -127`` (its multiplier would
+overflow float32, the same condition under which ``fp8_b128`` zeroes a
+block), stores scale 0 (byte 0) and zero codes.  The e8m0 byte is ``e + 127``.
+
 MX scale rule (the pages give only the block size, 32 elements, and the scale
 format; this is the OCP MX rule): with ``e = floor(log2(amax))`` and ``emax`` the
 exponent of the element format's largest value (8 for e4m3, whose largest is
@@ -35,7 +54,10 @@ exponent of the element format's largest value (8 for e4m3, whose largest is
 is that plus 127.  Elements are ``fl32(x * 2**-exp)``, clamped to the
 element format's largest value, then rounded.
 
-Parity: ``int8``/``fp8_b128`` pinned by the properties |q| <= qmax, the amax
+Parity: ``fp8_b128_pow2``/``ue8m0`` pinned by the properties "scale is the
+smallest power of two >= s0", |code value| <= 448, the per-element error
+bound, reduction to ``fp8_b128`` when s0 is itself a power of two, and a hand
+example.  ``int8``/``fp8_b128`` pinned by the properties |q| <= qmax, the amax
 element mapping to +-qmax and the per-element error bound; the MX scale byte
 pinned by recomputation with ``math.frexp``; all element rounding is in
 ``codecs`` (pinned there).  The MX rule itself is pinned only by the OCP MX
@@ -63,8 +85,10 @@ def row_bytes(mode: str, hidden: int) -> tuple[int, int]:
         return 2 * hidden, 0
     if mode == "int8_token":
         return hidden, 4
-    if mode == "fp8_b128":
+    if mode in ("fp8_b128", "fp8_b128_pow2"):
         return hidden, 4 * (hidden // 128)
+    if mode == "fp8_b128_ue8m0":
+        return hidden, hidden // 128
     if mode == "mxfp8":
         return hidden, hidden // 32
     if mode == "mxfp4":
@@ -114,6 +138,44 @@ def quant_fp8_b128(x_bits: np.ndarray):
         scales[g] = s
         codes[g * 128:(g + 1) * 128] = 0 if zero else codecs.e4m3_encode(v)
     return codes, scales
+
+
+def ceil_log2(s: np.float32) -> int:
+    """ceil(log2 s) of a positive finite float32, from its bit pattern: the
+    exponent of the leading one, plus one unless s is a power of two."""
+    b = int(np.float32(s).view(np.uint32)) & 0x7FFFFFFF
+    if b == 0 or b >= 0x7F800000:
+        raise ValueError("ceil_log2 needs a positive finite value")
+    ef, mant = b >> 23, b & 0x7FFFFF
+    if ef == 0:                            # subnormal: s = mant * 2**-149
+        lead = mant.bit_length() - 1
+        return lead - 149 + (0 if mant == 1 << lead else 1)
+    return ef - 127 + (0 if mant == 0 else 1)
+
+
+def quant_fp8_b128_pow2(x_bits: np.ndarray):
+    """One bf16 row -> (e4m3 codes [H] uint8, exponents e [H/128] (int, the
+    scale is 2**e), zero flags [H/128])."""
+    x = codecs.bf16_bits_to_f32(x_bits)
+    H = x.shape[0]
+    codes = np.zeros(H, np.uint8)
+    exps = np.zeros(H // 128, np.int64)
+    zero = np.zeros(H // 128, bool)
+    for g in range(H // 128):
+        blk = x[g * 128:(g + 1) * 128]
+        amax = _amax(blk)
+        if amax == 0:
+            zero[g] = True
+            continue
+        e = ceil_log2(np.float32(amax / E4M3_QMAX))
+        if e < -127:
+            zero[g] = True
+            continue
+        exps[g] = e
+        v = (blk.astype(np.float64) * 2.0 ** -e).astype(np.float32)    # one rounding
+        v = np.clip(v, -E4M3_QMAX, E4M3_QMAX).astype(np.float32)
+        codes[g * 128:(g + 1) * 128] = codecs.e4m3_encode(v)
+    return codes, exps, zero
 
 
 def mx_shared_exponent(amax: np.float32, emax: int) -> int:
@@ -171,6 +233,12 @@ def quantize_row(mode: str, x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]
     if mode == "fp8_b128":
         q, s = quant_fp8_b128(x_bits)
         return q, s.astype("<f4").view(np.uint8)
+    if mode in ("fp8_b128_pow2", "fp8_b128_ue8m0"):
+        q, e, zero = quant_fp8_b128_pow2(x_bits)
+        if mode == "fp8_b128_ue8m0":
+            return q, np.where(zero, 0, e + 127).astype(np.uint8)
+        s = np.where(zero, 0.0, np.exp2(e.astype(np.float64))).astype("<f4")   # exact powers of two
+        return q, s.view(np.uint8)
     if mode == "mxfp8":
         return quant_mxfp8(x_bits)
     if mode == "mxfp4":
@@ -183,7 +251,8 @@ def dequantize_row(mode: str, data: np.ndarray, scales: np.ndarray, hidden: int)
 
     ``none``: the bf16 value.  ``int8_token`` and ``fp8_b128``: fl32(code *
     scale) ("DeepEP FP8 Dispatch and Combine Operations", "The FP8 Combine
-    Operation": codes times the stored inverse scale, through float32).  MX:
+    Operation": codes times the stored inverse scale, through float32);
+    ``fp8_b128_pow2`` likewise.  ``fp8_b128_ue8m0`` and MX:
     code value times 2**(b-127), formed exactly in float64 and rounded once to
     float32 (the same number a float32 multiply by the exact power of two
     gives).
@@ -195,10 +264,14 @@ def dequantize_row(mode: str, data: np.ndarray, scales: np.ndarray, hidden: int)
     if mode == "int8_token":
         s = scales.view(np.float32)[0]
         return (data.view(np.int8).astype(np.float32) * s).astype(np.float32)
-    if mode == "fp8_b128":
+    if mode in ("fp8_b128", "fp8_b128_pow2"):
         s = np.repeat(scales.view("<f4").astype(np.float32), 128)
         val = codecs.e4m3_decode(data).astype(np.float32)     # exact
         return (val * s).astype(np.float32)
+    if mode == "fp8_b128_ue8m0":
+        sc = np.repeat(codecs.e8m0_decode(scales), 128)
+        with np.errstate(over="ignore", invalid="ignore"):
+            return (codecs.e4m3_decode(data) * sc).astype(np.float32)
     if mode in ("mxfp8", "mxfp4"):
         if mode == "mxfp8":
             val = codecs.e4m3_decode(data)

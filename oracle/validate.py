@@ -22,7 +22,7 @@ from __future__ import annotations
 
 MAX_TOPK = 16
 MAX_EXPERTS = 512
-QUANT_MODES = ("none", "int8_token", "fp8_b128", "mxfp8", "mxfp4")
+QUANT_MODES = ("none", "int8_token", "fp8_b128", "mxfp8", "mxfp4", "fp8_b128_pow2", "fp8_b128_ue8m0")
 
 
 def check_layout(num_tokens: int, num_topk: int, num_max_dispatch_tokens: int, num_experts: int) -> None:
@@ -65,16 +65,20 @@ def check_hidden(hidden: int, mode: str) -> None:
         raise ValueError(f"unknown quant mode {mode!r}")
     if hidden <= 0 or hidden % 32:
         raise ValueError("hidden must be a positive multiple of 32")
-    if mode == "fp8_b128" and hidden % 128:
-        raise ValueError("fp8_b128 needs hidden % 128 == 0")
+    if mode.startswith("fp8_b128") and hidden % 128:
+        raise ValueError("the per-128 e4m3 modes need hidden % 128 == 0")
 
 
 def check_flags(use_fp8: bool, use_ue8m0: bool, use_mxfp4: bool, round_scale: bool,
                 return_recv_hook: bool) -> str:
     """Map the low_latency_dispatch flags to a mode ("Low-Latency Mode API",
-    Parameters: use_ue8m0 and use_mxfp4 both require use_fp8)."""
-    if round_scale or return_recv_hook:
-        raise NotImplementedError("round_scale / return_recv_hook are not supported")
+    Parameters: use_ue8m0 and use_mxfp4 both require use_fp8; round_scale
+    goes with use_ue8m0, whose e8m0 scales are powers of two already, so it
+    changes nothing there and is refused without it)."""
+    if return_recv_hook:
+        raise NotImplementedError("return_recv_hook is not supported")
+    if round_scale and not use_ue8m0:
+        raise ValueError("round_scale is used together with use_ue8m0")
     if (use_ue8m0 or use_mxfp4) and not use_fp8:
         raise ValueError("use_ue8m0 / use_mxfp4 require use_fp8")
     if use_ue8m0 and use_mxfp4:

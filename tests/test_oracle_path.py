@@ -83,7 +83,8 @@ def test_combine_general_weights_within_one_ulp(seed):
 
 
 @pytest.mark.parametrize("mode,rel", [("int8_token", 0.02), ("fp8_b128", 0.04),
-                                      ("mxfp8", 0.05), ("mxfp4", 0.2)])
+                                      ("mxfp8", 0.05), ("mxfp4", 0.2),
+                                      ("fp8_b128_pow2", 0.05), ("fp8_b128_ue8m0", 0.05)])
 def test_dispatch_combine_quantised_roundtrip(mode, rel):
     w, inp = _case(5, T=24, H=256, E=8, k=3, neg=0.0, mode=mode)
     lay = L.layout(inp["topk_idx"], w.E, w.T)
@@ -99,6 +100,18 @@ def test_buffer_bytes_layout():
     assert off == D.align_up(10 * 3584, 256) and total == off + 10 * 224
     total, off = D.buffer_bytes(3, 32, "int8_token")
     assert off == 256 and total == 256 + 12
+
+
+def test_ue8m0_and_pow2_buffers_decode_alike():
+    """The two power-of-two scale stores hold the same codes and the same
+    scale values, so combine gives the same bits from either."""
+    w, inp = _case(11, T=16, H=256, E=4, k=2, mode="fp8_b128_pow2")
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    a = D.dispatch(inp["x"], lay, "fp8_b128_pow2")
+    b = D.dispatch(inp["x"], lay, "fp8_b128_ue8m0")
+    assert np.array_equal(a.data, b.data)
+    assert a.scales.shape[1] == 4 * b.scales.shape[1]
+    assert np.array_equal(C.combine(a, lay, inp["topk_weights"]), C.combine(b, lay, inp["topk_weights"]))
 
 
 def test_recv_buffer_bytes_roundtrip():
