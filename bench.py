@@ -1,6 +1,7 @@
 """Benchmark of MoE dispatch + combine on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--row-align A | --expert-capacity C]
 
 One step is one pass of the whole path over one batch: ep_layout (routing
 layout), ep_dispatch (quantise + scatter) and ep_combine (gather + dequantise
@@ -8,7 +9,8 @@ layout), ep_dispatch (quantise + scatter) and ep_combine (gather + dequantise
 Buffer sets rotate between steps so that no step finds its inputs in the
 256 MB last-level cache.  The default workload is "large": 16384 tokens,
 hidden 7168, top-8 of 256 experts with 5% of the pairs unrouted, MXFP4
-dispatch and a bf16 combine.
+dispatch and a bf16 combine.  --row-align / --expert-capacity time the same
+workload on aligned or capacity-padded expert blocks (ep_layout_ex).
 
 Prints one JSON line: tokens/s over the timed steps, the algorithmic bytes
 and GB/s of the whole step, the roofline entry of the dominant kernel
@@ -57,6 +59,7 @@ def algorithmic_bytes(w, R: int) -> dict:
 
 def _row_bytes(mode: str, H: int):
     return {"none": (2 * H, 0), "int8_token": (H, 4), "fp8_b128": (H, 4 * (H // 128)),
+            "fp8_b128_pow2": (H, 4 * (H // 128)), "fp8_b128_ue8m0": (H, H // 128),
             "mxfp8": (H, H // 32), "mxfp4": (H // 2, H // 32)}[mode]
 
 
@@ -215,6 +218,12 @@ def main() -> int:
     ap.add_argument("--combine-backward", default=None, metavar="QUANT",
                     help="time layout + ep_combine_backward (weighted reverse dispatch of a bf16 gradient "
                          "to the expert rows, quantised to QUANT, e.g. mxfp8) instead of the forward path")
+    ap.add_argument("--row-align", type=int, default=1,
+                    help="expert blocks start at multiples of this many rows (ep_layout_ex)")
+    ap.add_argument("--expert-capacity", type=int, default=0,
+                    help="every expert block has this many rows; later pairs are dropped (ep_layout_ex)")
+    ap.add_argument("--quant", default=None,
+                    help="dispatch quantisation in place of the workload's own (e.g. fp8_b128_ue8m0)")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
@@ -232,15 +241,26 @@ def main() -> int:
     import torch
     from combine_topk_idx_amd import ep, workloads as W
 
+    from dataclasses import replace
     w = W.WORKLOADS[args.workload]
+    padded = args.row_align > 1 or args.expert_capacity > 0
+    if padded:
+        w = replace(w, row_align=args.row_align, expert_capacity=args.expert_capacity)
+    variant = padded or (args.quant is not None and args.quant != w.mode)
+    if args.quant is not None:
+        w = replace(w, mode=args.quant)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    print(f"[bench] generating {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} {w.mode}", file=sys.stderr, flush=True)
+    print(f"[bench] generating {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} {w.mode} rows={w.max_rows}",
+          file=sys.stderr, flush=True)
     inp = W.make_inputs(w)
-    y_host = W.make_expert_out(w) if w.combine_input == "normal" else None
+    # padded blocks can hold far more rows than pairs: their bf16 N(0,1) expert
+    # rows are drawn on the device (timing data only; parity is tested apart)
+    y_host = W.make_expert_out(w) if w.combine_input == "normal" and not padded else None
+    y_dev = w.combine_input == "normal" and padded
 
     total_recv, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
-    per_set = (w.T * w.H * 2 * 2 + total_recv + (w.max_rows * w.H * 2 if y_host is not None else 0))
+    per_set = (w.T * w.H * 2 * 2 + total_recv + (w.max_rows * w.H * 2 if w.combine_input == "normal" else 0))
     nsets = args.sets or max(2, -(-(1 << 30) // max(per_set, 1)))
     nsets = min(nsets, 64)
 
@@ -253,13 +273,24 @@ def main() -> int:
             "x": dev_bf16(inp["x"]),
             "idx": torch.from_numpy(inp["topk_idx"]).to(dev),
             "w": torch.from_numpy(inp["topk_weights"]).to(dev),
-            "ws": torch.empty(ep.ep_workspace_bytes(w.t_max, w.k, w.E), dtype=torch.uint8, device=dev),
+            "ws": torch.empty(ep.ep_workspace_bytes_ex(w.t_max, w.k, w.E, w.row_align, w.expert_capacity),
+                              dtype=torch.uint8, device=dev),
             "rc": torch.empty(w.E, dtype=torch.int64, device=dev),
             "recv": torch.empty(total_recv, dtype=torch.uint8, device=dev),
             "out": torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev),
         }
         if y_host is not None:
             s["y"] = dev_bf16(y_host).view(torch.uint8).reshape(-1) if i == 0 else sets[0]["y"].clone()
+        elif y_dev and i == 0:
+            g = torch.Generator(device=dev)
+            g.manual_seed(w.seed)
+            y = torch.empty((w.max_rows, w.H), dtype=torch.bfloat16, device=dev)
+            for r0 in range(0, w.max_rows, 16384):
+                n = min(16384, w.max_rows - r0)
+                y[r0:r0 + n] = torch.randn((n, w.H), generator=g, device=dev).to(torch.bfloat16)
+            s["y"] = y.view(torch.uint8).reshape(-1)
+        elif y_dev:
+            s["y"] = sets[0]["y"].clone()
         sets.append(s)
     del y_host
     stream = torch.cuda.current_stream()
@@ -274,7 +305,10 @@ def main() -> int:
     def phases(s):
         """The three calls of one step on buffer set s, on torch's current stream."""
         def lay():
-            s["h"] = ep.ep_layout(s["idx"], w.E, w.t_max, s["rc"], s["ws"])
+            if padded:
+                s["h"] = ep.ep_layout_ex(s["idx"], w.E, w.t_max, w.row_align, w.expert_capacity, s["rc"], s["ws"])
+            else:
+                s["h"] = ep.ep_layout(s["idx"], w.E, w.t_max, s["rc"], s["ws"])
 
         def disp():
             ep.ep_dispatch(s["h"], s["x"], w.H, w.mode, s["recv"])
@@ -322,13 +356,13 @@ def main() -> int:
     b = algorithmic_bytes(w, R)
     gbps = b["total"] / (ms_per_step * 1e-3) / 1e9
     comb_gbps = b["combine"] / (comb_ms * 1e-3) / 1e9
-    traffic = _traffic(w.name)
+    traffic = None if variant else _traffic(w.name)
     roof = {"bound": "hbm", "kernel": "combine", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(comb_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
             "alg_bytes_per_launch": b["combine"], "avg_launch_ms": round(comb_ms, 5)}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not variant:
         tokens = args.cpu_tokens or {"large": 1536, "prefill": 1024}.get(w.name, w.T)
         print(f"[bench] cpu oracle on {tokens} tokens", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w.name, tokens)
@@ -341,7 +375,9 @@ def main() -> int:
         "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E} k={w.k} ids={w.idx_dtype} "
                                f"dispatch={w.mode} routing={w.routing} unrouted={w.neg_frac} "
                                f"combine_input={w.combine_input}",
-                   "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R, "buffer_sets": nsets},
+                   "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R, "buffer_sets": nsets,
+                   "row_align": w.row_align, "expert_capacity": w.expert_capacity,
+                   "receive_rows": w.max_rows},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "alg_bytes_per_step": b["total"],
         "phase_ms": {"layout": round(lay_ms, 5), "dispatch": round(disp_ms, 5), "combine": round(comb_ms, 5)},

@@ -29,12 +29,14 @@ template <> struct Raw<EP_QUANT_INT8_TOKEN> { using T = u32x2; };
 template <> struct Raw<EP_QUANT_FP8_B128> { using T = u32x2; };
 template <> struct Raw<EP_QUANT_MXFP8> { using T = u32x2; };
 template <> struct Raw<EP_QUANT_MXFP4> { using T = uint32_t; };
+template <> struct Raw<EP_QUANT_FP8_B128_POW2> { using T = u32x2; };
+template <> struct Raw<EP_QUANT_FP8_B128_UE8M0> { using T = u32x2; };
 
 template <int Q> constexpr int kBytesPerVec = sizeof(typename Raw<Q>::T);
 
 // dequantised 8 elements of one row vector; `scale` is the row's float32
-// scale (int8), the block's float32 scale (e4m3 per 128) or the block's
-// power of two 2^(byte-127) (MX)
+// scale (int8), the block's float32 scale (e4m3 per 128, also when it is a
+// power of two) or the block's power of two 2^(byte-127) (MX, per-128 e8m0)
 template <int Q>
 __device__ __forceinline__ void dequant8(const typename Raw<Q>::T &r, float scale, float (&y)[8]) {
   if constexpr (Q == EP_QUANT_NONE) {
@@ -49,11 +51,11 @@ __device__ __forceinline__ void dequant8(const typename Raw<Q>::T &r, float scal
       const int q = (int)(int8_t)((r[i >> 2] >> (8 * (i & 3))) & 0xffu);
       y[i] = (float)q * scale;
     }
-  } else if constexpr (Q == EP_QUANT_FP8_B128) {
+  } else if constexpr (Q == EP_QUANT_FP8_B128 || Q == EP_QUANT_FP8_B128_POW2) {
     e4m3x8_decode(r, y);
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = y[i] * scale;
-  } else if constexpr (Q == EP_QUANT_MXFP8) {
+  } else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_FP8_B128_UE8M0) {
     e4m3x8_decode_scaled(r, scale, y);
   } else {
     e2m1x8_decode_scaled(r, scale, y);
@@ -113,8 +115,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void co
 #else
       raw[j][h] = *src;
 #endif
-      if constexpr (Q == EP_QUANT_FP8_B128) {
+      if constexpr (Q == EP_QUANT_FP8_B128 || Q == EP_QUANT_FP8_B128_POW2) {
         sraw[j][h] = *(const uint32_t *)(scales + s[j] * sq + (int64_t)(v >> 4) * 4);
+      } else if constexpr (Q == EP_QUANT_FP8_B128_UE8M0) {
+        sraw[j][h] = *(const uint8_t *)(scales + s[j] * sq + (int64_t)(v >> 4));
       } else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) {
         sraw[j][h] = *(const uint8_t *)(scales + s[j] * sq + (int64_t)(v >> 2));
       }
@@ -133,8 +137,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void co
     for (int h = 0; h < CV; ++h) {
       float sc = 1.0f;
       if constexpr (Q == EP_QUANT_INT8_TOKEN) sc = rs[j];
-      else if constexpr (Q == EP_QUANT_FP8_B128) sc = __uint_as_float(sraw[j][h]);
-      else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) sc = e8m0_decode(sraw[j][h]);
+      else if constexpr (Q == EP_QUANT_FP8_B128 || Q == EP_QUANT_FP8_B128_POW2) sc = __uint_as_float(sraw[j][h]);
+      else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4 || Q == EP_QUANT_FP8_B128_UE8M0)
+        sc = e8m0_decode(sraw[j][h]);
       float y[8];
       dequant8<Q>(raw[j][h], sc, y);
 #pragma unroll
@@ -188,6 +193,8 @@ hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int h
     case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN>(h, in, hidden, w, out, s);
     case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128>(h, in, hidden, w, out, s);
     case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8>(h, in, hidden, w, out, s);
+    case EP_QUANT_FP8_B128_POW2: return launch_mode<EP_QUANT_FP8_B128_POW2>(h, in, hidden, w, out, s);
+    case EP_QUANT_FP8_B128_UE8M0: return launch_mode<EP_QUANT_FP8_B128_UE8M0>(h, in, hidden, w, out, s);
     default: return launch_mode<EP_QUANT_MXFP4>(h, in, hidden, w, out, s);
   }
 }

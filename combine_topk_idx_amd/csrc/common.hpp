@@ -16,6 +16,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kMaxTopk = 16;
 constexpr int kMaxExperts = 512;
+
+// the three e4m3 modes with one scale per 128 channels
+__host__ __device__ constexpr bool is_b128(int q) {
+  return q == EP_QUANT_FP8_B128 || q == EP_QUANT_FP8_B128_POW2 || q == EP_QUANT_FP8_B128_UE8M0;
+}
 constexpr size_t kScaleAlign = 256;   // scale region alignment inside a receive buffer
 constexpr size_t kWsAlign = 256;      // alignment of each workspace sub-array
 
@@ -27,7 +32,9 @@ __host__ __device__ inline void row_bytes(int quant, int hidden, size_t *dq, siz
   switch (quant) {
     case EP_QUANT_NONE: *dq = 2 * H; *sq = 0; break;
     case EP_QUANT_INT8_TOKEN: *dq = H; *sq = 4; break;
-    case EP_QUANT_FP8_B128: *dq = H; *sq = 4 * (H / 128); break;
+    case EP_QUANT_FP8_B128:
+    case EP_QUANT_FP8_B128_POW2: *dq = H; *sq = 4 * (H / 128); break;
+    case EP_QUANT_FP8_B128_UE8M0: *dq = H; *sq = H / 128; break;
     case EP_QUANT_MXFP8: *dq = H; *sq = H / 32; break;
     default: *dq = H / 2; *sq = H / 32; break;   // EP_QUANT_MXFP4
   }
@@ -86,10 +93,22 @@ struct WsLayout {      // byte offsets of the workspace sub-arrays
   int64_t nblocks;     // blocks of the multi-block layout path (0 = single block)
 };
 
-WsLayout workspace_layout(int64_t max_tokens, int32_t k, int32_t E);
+// Receive rows of a layout: num_max_tokens * k (+ E * (align - 1) when
+// blocks are aligned), or E * cap when every block has cap rows; -1 when
+// the arguments are out of range (align outside [1, kMaxRowAlign], cap < 0,
+// both set, or more than 2^31 - 1 rows).
+constexpr int32_t kMaxRowAlign = 1024;
+__host__ inline int64_t layout_rows(int64_t max_tokens, int32_t k, int32_t E, int32_t align, int32_t cap) {
+  if (max_tokens < 0 || k <= 0 || E <= 0 || align < 1 || align > kMaxRowAlign || cap < 0 || (cap > 0 && align > 1))
+    return -1;
+  const int64_t rows = cap > 0 ? (int64_t)E * cap : max_tokens * k + (int64_t)E * (align - 1);
+  return rows > INT32_MAX ? -1 : rows;
+}
 
-hipError_t launch_layout(const void *idx, int idx64, int64_t T, int32_t k, int32_t E, int64_t max_rows,
-                         int64_t *recv_count, int32_t *cum, char *ws, const WsLayout &wl,
+WsLayout workspace_layout(int64_t max_tokens, int32_t k, int32_t E, int64_t max_rows);
+
+hipError_t launch_layout(const void *idx, int idx64, int64_t T, int32_t k, int32_t E, int64_t max_rows, int32_t align,
+                         int32_t cap, int64_t *recv_count, int32_t *cum, char *ws, const WsLayout &wl,
                          hipStream_t s);
 
 hipError_t launch_dispatch(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant,

@@ -7,6 +7,10 @@
 //   INT8_TOKEN  amax over the row;  m = 127/amax, scale = amax/127,
 //               code = clamp(rint(x*m), +-127)
 //   FP8_B128    the same per 128 channels with 448, code = e4m3(clamp(x*m))
+//   FP8_B128_POW2 / _UE8M0  per 128 channels: s0 = amax/448, scale 2^e with
+//               e = ceil(log2 s0) (bits of s0), code = e4m3(clamp(x*2^-e));
+//               the scale is stored as float32 or as the byte e+127; e < -127
+//               counts as a zero block
 //   MXFP8/MXFP4 per 32 elements: shared exponent clamp(floor(log2 amax) -
 //               emax, +-127) (emax 8 for e4m3, 2 for e2m1), byte = exp+127,
 //               code = enc(clamp(x * 2^-exp, +-max))
@@ -63,6 +67,22 @@ __device__ __forceinline__ ScaledBlock scaled_block(uint32_t amax_bits, float qm
   b.scale = amax / qmax;
   b.zero = (amax_bits == 0) || __builtin_isinf(b.m);
   if (b.zero) b.scale = 0.0f;
+  return b;
+}
+
+// Per-128 power-of-two block: s0 = fl(amax/448) rounded up to 2^e.  m = 2^-e
+// and scale = 2^e are exact float32 (e >= -127 keeps 2^-e finite; e <= 120
+// for finite bf16 input); `byte` receives the e8m0 code e + 127.
+__device__ __forceinline__ ScaledBlock pow2_block(uint32_t amax_bits, uint32_t &byte) {
+  const float amax = __uint_as_float(amax_bits << 16);
+  const uint32_t s0 = __float_as_uint(amax / 448.0f);
+  const int e = s0 ? ceil_log2_bits(s0) : 0;
+  ScaledBlock b;
+  b.zero = amax_bits == 0 || e < -127;
+  const int ec = b.zero ? 0 : e;
+  b.m = __uint_as_float((uint32_t)(127 - ec) << 23);
+  b.scale = b.zero ? 0.0f : (ec == -127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(ec + 127) << 23));
+  byte = b.zero ? 0u : (uint32_t)(ec + 127);
   return b;
 }
 
@@ -186,10 +206,14 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
     for (int i = 0; i < VPT; ++i) {
       const int v = v0 + i * NT;
       const uint32_t am = vec_absmax_bits(raw[i]);
-      if constexpr (Q == EP_QUANT_FP8_B128) {
+      if constexpr (is_b128(Q)) {
         float f[8];
         unpack8(raw[i], f);
-        const ScaledBlock b = scaled_block(row16_max(am), 448.0f);   // all 16 lanes
+        const uint32_t bmax = row16_max(am);                          // all 16 lanes
+        uint32_t sbyte = 0;
+        ScaledBlock b;
+        if constexpr (Q == EP_QUANT_FP8_B128) b = scaled_block(bmax, 448.0f);
+        else b = pow2_block(bmax, sbyte);
         if (v >= nvec) continue;
         const u32x2 q = pin(codes_e4m3_scaled(f, b));
         const bool lead = (v & 15) == 0;
@@ -197,7 +221,10 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
         for (int j = 0; j < KMAX; ++j) {
           if (!routed(j)) continue;
           st_row(data + s[j] * dq + (int64_t)v * 8, q);
-          if (lead) st_row(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
+          if (lead) {
+            if constexpr (Q == EP_QUANT_FP8_B128_UE8M0) st_row(scales + s[j] * sq + (int64_t)(v >> 4), (uint8_t)sbyte);
+            else st_row(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
+          }
         }
       } else {
         constexpr int emax = Q == EP_QUANT_MXFP8 ? 8 : 2;
@@ -355,6 +382,10 @@ hipError_t launch_any(const ep_handle_t &h, const void *x, int hidden, const flo
     case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
     case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
     case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
+    case EP_QUANT_FP8_B128_POW2:
+      return launch_mode<EP_QUANT_FP8_B128_POW2, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
+    case EP_QUANT_FP8_B128_UE8M0:
+      return launch_mode<EP_QUANT_FP8_B128_UE8M0, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
     default: return launch_mode<EP_QUANT_MXFP4, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
   }
 }

@@ -32,7 +32,7 @@ ep_status_t hip_fail(hipError_t e, const char *where) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool valid_quant(int q) { return q >= EP_QUANT_NONE && q <= EP_QUANT_MXFP4; }
+bool valid_quant(int q) { return q >= EP_QUANT_NONE && q <= EP_QUANT_FP8_B128_UE8M0; }
 
 constexpr int32_t kMaxHidden = 65536;
 
@@ -41,7 +41,7 @@ ep_status_t check_hidden(int32_t hidden, int quant, const char *fn) {
   if (hidden <= 0 || hidden % 32 != 0)
     return fail(EP_ERR_INVALID_ARG, "%s: hidden must be a positive multiple of 32 (got %d)", fn, hidden);
   if (hidden > kMaxHidden) return fail(EP_ERR_UNSUPPORTED, "%s: hidden %d exceeds %d", fn, hidden, kMaxHidden);
-  if (quant == EP_QUANT_FP8_B128 && hidden % 128 != 0)
+  if (ep::is_b128(quant) && hidden % 128 != 0)
     return fail(EP_ERR_INVALID_ARG, "%s: per-128 e4m3 needs hidden %% 128 == 0 (got %d)", fn, hidden);
   return EP_OK;
 }
@@ -50,7 +50,9 @@ ep_status_t check_handle(const ep_handle_t *h, const char *fn) {
   if (!h) return fail(EP_ERR_INVALID_ARG, "%s: handle is NULL", fn);
   if (h->num_topk <= 0 || h->num_topk > ep::kMaxTopk || h->num_experts <= 0 ||
       h->num_experts > ep::kMaxExperts || h->num_tokens < 0 || h->num_tokens > h->num_max_tokens ||
-      h->max_rows != h->num_max_tokens * h->num_topk || h->max_rows > INT32_MAX)
+      h->max_rows < 0 ||
+      h->max_rows != ep::layout_rows(h->num_max_tokens, h->num_topk, h->num_experts, h->row_align,
+                                     h->expert_capacity))
     return fail(EP_ERR_INVALID_ARG, "%s: handle fields are inconsistent (not made by ep_layout?)", fn);
   if (!h->offsets || !h->slot || !h->row_src || !h->status)
     return fail(EP_ERR_INVALID_ARG, "%s: handle holds NULL pointers", fn);
@@ -77,7 +79,23 @@ size_t ep_workspace_bytes(int64_t num_max_dispatch_tokens, int32_t num_topk, int
   if (num_max_dispatch_tokens < 0 || num_topk <= 0 || num_topk > ep::kMaxTopk || num_experts <= 0 ||
       num_experts > ep::kMaxExperts || num_max_dispatch_tokens * num_topk > INT32_MAX)
     return 0;
-  return ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts).total;
+  return ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts,
+                              num_max_dispatch_tokens * num_topk).total;
+}
+
+int64_t ep_layout_rows(int64_t num_max_dispatch_tokens, int32_t num_topk, int32_t num_experts, int32_t row_align,
+                       int32_t expert_capacity) {
+  if (num_max_dispatch_tokens < 0 || num_topk <= 0 || num_topk > ep::kMaxTopk || num_experts <= 0 ||
+      num_experts > ep::kMaxExperts || num_max_dispatch_tokens * num_topk > INT32_MAX)
+    return -1;
+  return ep::layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity);
+}
+
+size_t ep_workspace_bytes_ex(int64_t num_max_dispatch_tokens, int32_t num_topk, int32_t num_experts,
+                             int32_t row_align, int32_t expert_capacity) {
+  const int64_t rows = ep_layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity);
+  if (rows < 0) return 0;
+  return ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts, rows).total;
 }
 
 ep_status_t ep_buffer_bytes(int64_t rows, int32_t hidden, ep_quant_t quant, size_t *total_bytes,
@@ -90,11 +108,14 @@ ep_status_t ep_buffer_bytes(int64_t rows, int32_t hidden, ep_quant_t quant, size
   return EP_OK;
 }
 
-ep_status_t ep_layout(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens, int32_t num_topk,
-                      int64_t num_max_dispatch_tokens, int32_t num_experts, int64_t *recv_count,
-                      int32_t *cumulative_recv_stats, void *workspace, size_t workspace_bytes,
-                      ep_handle_t *handle, void *stream) {
-  const char *fn = "ep_layout";
+}  // extern "C"
+
+namespace {
+
+ep_status_t layout_impl(const char *fn, const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                        int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts, int32_t row_align,
+                        int32_t expert_capacity, int64_t *recv_count, int32_t *cumulative_recv_stats,
+                        void *workspace, size_t workspace_bytes, ep_handle_t *handle, void *stream) {
   if (idx_dtype != EP_IDX_INT32 && idx_dtype != EP_IDX_INT64)
     return fail(EP_ERR_INVALID_ARG, "%s: topk_idx dtype must be int32 or int64", fn);
   if (num_topk <= 0 || num_topk > ep::kMaxTopk)
@@ -108,6 +129,14 @@ ep_status_t ep_layout(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t nu
                 (long long)num_tokens, (long long)num_max_dispatch_tokens);
   if (num_max_dispatch_tokens > INT32_MAX / num_topk)
     return fail(EP_ERR_INVALID_ARG, "%s: num_max_dispatch_tokens * num_topk exceeds 2^31-1", fn);
+  if (row_align < 1 || row_align > ep::kMaxRowAlign)
+    return fail(EP_ERR_INVALID_ARG, "%s: row_align must be in [1, %d] (got %d)", fn, ep::kMaxRowAlign, row_align);
+  if (expert_capacity < 0) return fail(EP_ERR_INVALID_ARG, "%s: negative expert_capacity", fn);
+  if (expert_capacity > 0 && row_align > 1)
+    return fail(EP_ERR_INVALID_ARG, "%s: expert_capacity and row_align > 1 are exclusive", fn);
+  const int64_t max_rows = ep::layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align,
+                                           expert_capacity);
+  if (max_rows < 0) return fail(EP_ERR_INVALID_ARG, "%s: receive rows exceed 2^31-1", fn);
   if (num_tokens > 0 && !topk_idx) return fail(EP_ERR_INVALID_ARG, "%s: topk_idx is NULL", fn);
   if (topk_idx && !aligned(topk_idx, idx_dtype == EP_IDX_INT64 ? 8 : 4))
     return fail(EP_ERR_INVALID_ARG, "%s: topk_idx is not aligned to its dtype", fn);
@@ -118,7 +147,7 @@ ep_status_t ep_layout(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t nu
   if (!workspace || !aligned(workspace, ep::kWsAlign))
     return fail(EP_ERR_INVALID_ARG, "%s: workspace is NULL or not 256-byte aligned", fn);
   if (!handle) return fail(EP_ERR_INVALID_ARG, "%s: handle is NULL", fn);
-  const ep::WsLayout wl = ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts);
+  const ep::WsLayout wl = ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts, max_rows);
   if (workspace_bytes < wl.total)
     return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, wl.total);
 
@@ -126,19 +155,42 @@ ep_status_t ep_layout(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t nu
   ep_handle_t h;
   h.num_tokens = num_tokens;
   h.num_max_tokens = num_max_dispatch_tokens;
-  h.max_rows = num_max_dispatch_tokens * num_topk;
+  h.max_rows = max_rows;
   h.num_topk = num_topk;
   h.num_experts = num_experts;
+  h.row_align = row_align;
+  h.expert_capacity = expert_capacity;
   h.offsets = (int32_t *)(ws + wl.offsets);
   h.slot = (int32_t *)(ws + wl.slot);
   h.row_src = (int32_t *)(ws + wl.row_src);
   h.status = (uint32_t *)(ws + wl.status);
   const hipError_t e = ep::launch_layout(topk_idx, idx_dtype == EP_IDX_INT64, num_tokens, num_topk, num_experts,
-                                         h.max_rows, recv_count, cumulative_recv_stats, ws, wl,
-                                         (hipStream_t)stream);
+                                         h.max_rows, row_align, expert_capacity, recv_count, cumulative_recv_stats,
+                                         ws, wl, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   *handle = h;
   return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ep_status_t ep_layout_ex(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens, int32_t num_topk,
+                         int64_t num_max_dispatch_tokens, int32_t num_experts, int32_t row_align,
+                         int32_t expert_capacity, int64_t *recv_count, int32_t *cumulative_recv_stats,
+                         void *workspace, size_t workspace_bytes, ep_handle_t *handle, void *stream) {
+  return layout_impl("ep_layout_ex", topk_idx, idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
+                     num_experts, row_align, expert_capacity, recv_count, cumulative_recv_stats, workspace,
+                     workspace_bytes, handle, stream);
+}
+
+ep_status_t ep_layout(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens, int32_t num_topk,
+                      int64_t num_max_dispatch_tokens, int32_t num_experts, int64_t *recv_count,
+                      int32_t *cumulative_recv_stats, void *workspace, size_t workspace_bytes,
+                      ep_handle_t *handle, void *stream) {
+  return layout_impl("ep_layout", topk_idx, idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens, num_experts,
+                     1, 0, recv_count, cumulative_recv_stats, workspace, workspace_bytes, handle, stream);
 }
 
 ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden, const float *topk_weights,

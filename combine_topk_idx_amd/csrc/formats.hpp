@@ -47,6 +47,15 @@ __device__ __forceinline__ int floor_log2_bits(uint32_t a) {
   return ef ? ef - 127 : (31 - __builtin_clz(a)) - 149;
 }
 
+// ceil(log2 v) of a positive finite float32 from its bits `a`: floor, plus
+// one unless v is a power of two (a normal with zero mantissa, or a
+// subnormal with a single bit set)
+__device__ __forceinline__ int ceil_log2_bits(uint32_t a) {
+  const uint32_t mant = a & 0x7fffffu;
+  const bool pow2 = (a >> 23) ? mant == 0 : (mant & (mant - 1)) == 0;
+  return floor_log2_bits(a) + (pow2 ? 0 : 1);
+}
+
 // e4m3fn (bias 7, 3 mantissa bits, largest finite 448, no infinity) -----------
 //
 // gfx950's fp8 conversions use this OCP format.  The encoder below is exact

@@ -17,6 +17,12 @@
 // into per-wave bases by a prefix over the 16 waves.  Nothing depends on the
 // order in which atomics or waves happen to run: the result is deterministic.
 //
+// Receive rows are arranged in one of three ways: compact (expert e's block
+// is exactly its count), aligned (every block is rounded up to a multiple of
+// `align` rows) or capacity-padded (every block is `cap` rows; pairs past the
+// cap-th of an expert are dropped and set a status bit).  Rows that hold no
+// pair get row_src -1.
+//
 // Small problems (pairs <= 4096) run in one workgroup that also does the scan
 // over experts and writes every output: one launch.  (All of its waves share
 // one CU, so its cost grows by about a microsecond per 64-pair step of a
@@ -37,6 +43,7 @@ constexpr int kMultiItems = EP_LAYOUT_ITEMS;       // pairs per thread in a mult
 constexpr int kMultiChunk = kMultiItems * kThreads;
 constexpr int64_t kSingleMaxPairs = (int64_t)kSingleItems * kThreads;
 constexpr int64_t kSingleMaxRows = 65536;          // single workgroup also clears row_src tail
+constexpr int kMaxFillBlocks = 512;                // finalize workgroups beyond the chunk count
 
 // Expert of an id, or -1 for -1 / ids outside [-1, E) (which set `bad`).
 template <typename IdxT>
@@ -45,6 +52,39 @@ __device__ __forceinline__ int expert_of(IdxT raw, int E, bool &bad) {
   if (v >= 0 && v < (int64_t)E) return (int)v;
   bad |= v != -1;
   return -1;
+}
+
+// Rows of expert block with `c` pairs: c rounded up to `align`, or `cap`.
+__device__ __forceinline__ int block_rows(int c, int align, int cap) {
+  return cap > 0 ? cap : (c + align - 1) / align * align;
+}
+
+// -1 into row_src for every row that holds no pair.  This thread is number
+// `first` of `step` (both multiples of the wave size apart).  offs[e] (block
+// start) and kept[e] (pairs the block holds) are in LDS.
+//   capacity C: row r is in block r / C; it is free past the kept pairs;
+//   aligned:    rows at or past nrows, and fewer than `align` rows after the
+//               pairs of each block (one wave per block);
+//   compact:    only rows at or past nrows.
+__device__ __forceinline__ void clear_free_rows(int *__restrict__ row_src, int first, int step, int max_rows,
+                                                int nrows, int E, int align, int cap, const int *offs,
+                                                const int *kept) {
+  if (cap > 0) {
+    for (int r = first; r < max_rows; r += step) {
+      const int e = (int)((unsigned)r / (unsigned)cap);
+      if (r - e * cap >= kept[e]) row_src[r] = -1;
+    }
+    return;
+  }
+  for (int r = nrows + first; r < max_rows; r += step) row_src[r] = -1;
+  if (align > 1) {
+    const int lane = first & (kWave - 1);
+    for (int e = first / kWave; e < E; e += step / kWave) {
+      const int lo = offs[e] + kept[e];
+      const int hi = offs[e] + block_rows(kept[e], align, 0);
+      for (int r = lo + lane; r < hi; r += kWave) row_src[r] = -1;
+    }
+  }
 }
 
 // Stable rank of each of this thread's pairs among the equal-expert pairs
@@ -141,12 +181,13 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int &total
 
 template <typename IdxT>
 __global__ __launch_bounds__(kThreads) void layout_single_kernel(
-    const IdxT *__restrict__ idx, int n, int E, int max_rows, int64_t *__restrict__ recv_count,
-    int *__restrict__ cum, int *__restrict__ offsets, int *__restrict__ slot, int *__restrict__ row_src,
-    uint32_t *__restrict__ status) {
+    const IdxT *__restrict__ idx, int n, int E, int max_rows, int align, int cap,
+    int64_t *__restrict__ recv_count, int *__restrict__ cum, int *__restrict__ offsets, int *__restrict__ slot,
+    int *__restrict__ row_src, uint32_t *__restrict__ status) {
   __shared__ int cnt[kWaves * kMaxExperts];
   __shared__ int total[kMaxExperts];
   __shared__ int excl[kMaxExperts];
+  __shared__ int kept[kMaxExperts];
   __shared__ int wsum[kWaves];
   __shared__ uint32_t sbad;
   if (threadIdx.x == 0) sbad = 0;
@@ -162,15 +203,18 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
 
   const int c = threadIdx.x < E ? total[threadIdx.x] : 0;
   int nrows;
-  const int pre = block_exclusive_scan(c, wsum, nrows);
+  const int pre = block_exclusive_scan(threadIdx.x < E ? block_rows(c, align, cap) : 0, wsum, nrows);
+  const int k_e = cap > 0 ? min(c, cap) : c;
   if (threadIdx.x < E) {
     excl[threadIdx.x] = pre;
-    recv_count[threadIdx.x] = c;
+    kept[threadIdx.x] = k_e;
+    recv_count[threadIdx.x] = k_e;
     offsets[threadIdx.x] = pre;
     if (cum) cum[threadIdx.x] += c;
   }
   if (threadIdx.x == 0) offsets[E] = nrows;
-  if (bad) atomicOr(&sbad, 1u);
+  if (bad) atomicOr(&sbad, EP_STATUS_ID_OUT_OF_RANGE);
+  if (k_e < c) atomicOr(&sbad, EP_STATUS_CAPACITY_OVERFLOW);
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -179,15 +223,16 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
     const int f = w * steps * kWave + it * kWave + lane;
     if (it >= steps || f >= n) continue;
     const int e = ex[it];
-    if (e >= 0) {
-      const int r = excl[e] + cnt[w * E + e] + lr[it];
+    const int local = e >= 0 ? cnt[w * E + e] + lr[it] : 0;
+    if (e >= 0 && (cap <= 0 || local < cap)) {
+      const int r = excl[e] + local;
       slot[f] = r;
       row_src[r] = f;
     } else {
       slot[f] = -1;
     }
   }
-  for (int r = nrows + threadIdx.x; r < max_rows; r += kThreads) row_src[r] = -1;
+  clear_free_rows(row_src, threadIdx.x, kThreads, max_rows, nrows, E, align, cap, excl, kept);
   if (threadIdx.x == 0) *status = sbad;
 }
 
@@ -242,12 +287,12 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
 // is LDS of kTileInts ints, `base` of E ints.
 constexpr int kTileInts = 8192;
 
-__device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int nblocks, int b,
+__device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int align, int cap, int nblocks, int b,
                                                const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
                                                int64_t *__restrict__ recv_count, int *__restrict__ cum,
                                                int *__restrict__ offsets, int *__restrict__ slot,
                                                int *__restrict__ row_src, uint32_t *__restrict__ status, int *tile,
-                                               int *base, int *wsum, uint32_t *sbad) {
+                                               int *base, int *offs, int *kept, int *wsum, uint32_t *sbad) {
   const int e = threadIdx.x;
   if (threadIdx.x == 0) *sbad = 0;
 
@@ -289,14 +334,20 @@ __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int n
     __syncthreads();
   }
   int nrows;
-  const int p = block_exclusive_scan(e < E ? tot : 0, wsum, nrows);
-  if (e < E) base[e] = p + pre;
+  const int p = block_exclusive_scan(e < E ? block_rows(tot, align, cap) : 0, wsum, nrows);
+  const int k_e = cap > 0 ? min(tot, cap) : tot;
+  if (e < E) {
+    base[e] = pre;
+    offs[e] = p;
+    kept[e] = k_e;
+  }
   if (b == 0) {
     if (e < E) {
-      recv_count[e] = tot;
+      recv_count[e] = k_e;
       offsets[e] = p;
       if (cum) cum[e] += tot;
     }
+    if (k_e < tot) bad |= EP_STATUS_CAPACITY_OVERFLOW;
     if (bad) atomicOr(sbad, bad);
   }
   __syncthreads();
@@ -308,61 +359,73 @@ __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int n
   for (int it = 0; it < kMultiItems; ++it) {
     if (v[it] < 0) continue;
     const int f = b * kMultiChunk + it * kThreads + threadIdx.x;
-    const int r = base[v[it] >> 16] + (v[it] & 0xffff);
+    const int e = v[it] >> 16;
+    const int local = base[e] + (v[it] & 0xffff);
+    if (cap > 0 && local >= cap) {
+      slot[f] = -1;
+      continue;
+    }
+    const int r = offs[e] + local;
     slot[f] = r;
     row_src[r] = f;
   }
-  for (int r = nrows + b * kThreads + threadIdx.x; r < max_rows; r += gridDim.x * kThreads) row_src[r] = -1;
+  clear_free_rows(row_src, b * kThreads + threadIdx.x, gridDim.x * kThreads, max_rows, nrows, E, align, cap,
+                  offs, kept);
 }
 
 __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
-    int n, int E, int max_rows, int nblocks, const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
-    int64_t *__restrict__ recv_count, int *__restrict__ cum, int *__restrict__ offsets, int *__restrict__ slot,
-    int *__restrict__ row_src, uint32_t *__restrict__ status) {
+    int n, int E, int max_rows, int align, int cap, int nblocks, const int *__restrict__ hist,
+    const uint32_t *__restrict__ bstat, int64_t *__restrict__ recv_count, int *__restrict__ cum,
+    int *__restrict__ offsets, int *__restrict__ slot, int *__restrict__ row_src, uint32_t *__restrict__ status) {
   __shared__ int tile[kTileInts];
   __shared__ int base[kMaxExperts];
+  __shared__ int offs[kMaxExperts];
+  __shared__ int kept[kMaxExperts];
   __shared__ int wsum[kWaves];
   __shared__ uint32_t sbad;
-  finalize_chunk(n, E, max_rows, nblocks, blockIdx.x, hist, bstat, recv_count, cum, offsets, slot, row_src, status,
-                 tile, base, wsum, &sbad);
+  finalize_chunk(n, E, max_rows, align, cap, nblocks, blockIdx.x, hist, bstat, recv_count, cum, offsets, slot,
+                 row_src, status, tile, base, offs, kept, wsum, &sbad);
 }
 
 template <typename IdxT>
-hipError_t launch_typed(const IdxT *idx, int n, int32_t E, int max_rows, int64_t *recv_count, int32_t *cum,
-                        char *ws, const WsLayout &wl, hipStream_t s) {
+hipError_t launch_typed(const IdxT *idx, int n, int32_t E, int max_rows, int align, int cap, int64_t *recv_count,
+                        int32_t *cum, char *ws, const WsLayout &wl, hipStream_t s) {
   int *offsets = (int *)(ws + wl.offsets);
   int *slot = (int *)(ws + wl.slot);
   int *row_src = (int *)(ws + wl.row_src);
   uint32_t *status = (uint32_t *)(ws + wl.status);
   if (n <= kSingleMaxPairs && max_rows <= kSingleMaxRows) {
-    hipLaunchKernelGGL(layout_single_kernel<IdxT>, dim3(1), dim3(kThreads), 0, s, idx, n, E, max_rows,
+    hipLaunchKernelGGL(layout_single_kernel<IdxT>, dim3(1), dim3(kThreads), 0, s, idx, n, E, max_rows, align, cap,
                        recv_count, cum, offsets, slot, row_src, status);
     return hipGetLastError();
   }
   int *hist = (int *)(ws + wl.hist);
   uint32_t *bstat = (uint32_t *)(ws + wl.bstat);
   const int nb = (n + kMultiChunk - 1) / kMultiChunk;
-  // enough workgroups for the slots of every chunk and for clearing row_src past R
-  const int fill_blocks = (int)((max_rows + kMultiChunk - 1) / kMultiChunk);
+  // enough workgroups for the slots of every chunk and for clearing free rows
+  // (capped: every workgroup re-reads the chunk counts, and a grid-stride
+  // loop covers any number of rows)
+  const int64_t want = (max_rows + kMultiChunk - 1) / kMultiChunk;
+  const int fill_blocks = (int)(want < kMaxFillBlocks ? want : kMaxFillBlocks);
   const int grid = nb > fill_blocks ? nb : (fill_blocks > 0 ? fill_blocks : 1);
   if (nb > 0) {
     hipLaunchKernelGGL(layout_rank_kernel<IdxT>, dim3(nb), dim3(kThreads), 0, s, idx, n, E, hist, bstat, slot);
   }
-  hipLaunchKernelGGL(layout_finalize_kernel, dim3(grid), dim3(kThreads), 0, s, n, E, max_rows, nb, hist, bstat,
-                     recv_count, cum, offsets, slot, row_src, status);
+  hipLaunchKernelGGL(layout_finalize_kernel, dim3(grid), dim3(kThreads), 0, s, n, E, max_rows, align, cap, nb, hist,
+                     bstat, recv_count, cum, offsets, slot, row_src, status);
   return hipGetLastError();
 }
 
 }  // namespace
 
-WsLayout workspace_layout(int64_t max_tokens, int32_t k, int32_t E) {
+WsLayout workspace_layout(int64_t max_tokens, int32_t k, int32_t E, int64_t max_rows) {
   WsLayout wl{};
   const int64_t pairs = max_tokens * k;
   const int64_t nb = (pairs + kMultiChunk - 1) / kMultiChunk;
   size_t off = 0;
   wl.offsets = off; off = align_up(off + sizeof(int32_t) * (size_t)(E + 1), kWsAlign);
   wl.slot = off;    off = align_up(off + sizeof(int32_t) * (size_t)pairs, kWsAlign);
-  wl.row_src = off; off = align_up(off + sizeof(int32_t) * (size_t)pairs, kWsAlign);
+  wl.row_src = off; off = align_up(off + sizeof(int32_t) * (size_t)max_rows, kWsAlign);
   wl.status = off;  off = align_up(off + sizeof(uint32_t), kWsAlign);
   wl.hist = off;    off = align_up(off + sizeof(int32_t) * (size_t)(nb * E), kWsAlign);
   wl.bstat = off;   off = align_up(off + sizeof(uint32_t) * (size_t)nb, kWsAlign);
@@ -371,11 +434,12 @@ WsLayout workspace_layout(int64_t max_tokens, int32_t k, int32_t E) {
   return wl;
 }
 
-hipError_t launch_layout(const void *idx, int idx64, int64_t T, int32_t k, int32_t E, int64_t max_rows,
-                         int64_t *recv_count, int32_t *cum, char *ws, const WsLayout &wl, hipStream_t s) {
+hipError_t launch_layout(const void *idx, int idx64, int64_t T, int32_t k, int32_t E, int64_t max_rows, int32_t align,
+                         int32_t cap, int64_t *recv_count, int32_t *cum, char *ws, const WsLayout &wl,
+                         hipStream_t s) {
   const int n = (int)(T * k);
-  if (idx64) return launch_typed((const int64_t *)idx, n, E, (int)max_rows, recv_count, cum, ws, wl, s);
-  return launch_typed((const int32_t *)idx, n, E, (int)max_rows, recv_count, cum, ws, wl, s);
+  if (idx64) return launch_typed((const int64_t *)idx, n, E, (int)max_rows, align, cap, recv_count, cum, ws, wl, s);
+  return launch_typed((const int32_t *)idx, n, E, (int)max_rows, align, cap, recv_count, cum, ws, wl, s);
 }
 
 }  // namespace ep

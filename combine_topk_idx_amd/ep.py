@@ -1,8 +1,9 @@
 """ctypes binding of libep.so (argument marshalling only).
 
-The functions ``ep_workspace_bytes``, ``ep_buffer_bytes``, ``ep_layout``,
-``ep_dispatch``, ``ep_combine``, ``ep_read_status``, ``ep_last_error`` and
-``ep_abi_version`` have the names and arguments of the C ABI in
+The functions ``ep_workspace_bytes``, ``ep_workspace_bytes_ex``,
+``ep_layout_rows``, ``ep_buffer_bytes``, ``ep_layout``, ``ep_layout_ex``,
+``ep_dispatch``, ``ep_combine``, ``ep_combine_backward``, ``ep_read_status``,
+``ep_last_error`` and ``ep_abi_version`` have the names and arguments of the C ABI in
 ``include/ep.h``; torch tensors stand in for device pointers and torch's
 current stream is used unless one is passed.  Every computation runs in the
 library's HIP kernels.  Importing this module loads the library and raises
@@ -31,11 +32,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_BUFFER_TOO_SMALL, EP_ERR_HIP = range(5)
 EP_IDX_INT32, EP_IDX_INT64 = 0, 1
-QUANT = {"none": 0, "int8_token": 1, "fp8_b128": 2, "mxfp8": 3, "mxfp4": 4}
+QUANT = {"none": 0, "int8_token": 1, "fp8_b128": 2, "mxfp8": 3, "mxfp4": 4, "fp8_b128_pow2": 5,
+         "fp8_b128_ue8m0": 6}
 EP_STATUS_ID_OUT_OF_RANGE = 1
+EP_STATUS_CAPACITY_OVERFLOW = 2
 
-SYMBOLS = ("ep_workspace_bytes", "ep_buffer_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-           "ep_combine_backward", "ep_read_status", "ep_last_error", "ep_abi_version")
+SYMBOLS = ("ep_workspace_bytes", "ep_workspace_bytes_ex", "ep_layout_rows", "ep_buffer_bytes", "ep_layout",
+           "ep_layout_ex", "ep_dispatch", "ep_combine", "ep_combine_backward", "ep_read_status", "ep_last_error",
+           "ep_abi_version")
 
 
 class ep_handle_t(ctypes.Structure):
@@ -45,6 +49,8 @@ class ep_handle_t(ctypes.Structure):
         ("max_rows", ctypes.c_int64),
         ("num_topk", ctypes.c_int32),
         ("num_experts", ctypes.c_int32),
+        ("row_align", ctypes.c_int32),
+        ("expert_capacity", ctypes.c_int32),
         ("offsets", ctypes.c_void_p),
         ("slot", ctypes.c_void_p),
         ("row_src", ctypes.c_void_p),
@@ -55,11 +61,18 @@ class ep_handle_t(ctypes.Structure):
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _lib.ep_workspace_bytes.argtypes = [_i64, _i32, _i32]
 _lib.ep_workspace_bytes.restype = _sz
+_lib.ep_workspace_bytes_ex.argtypes = [_i64, _i32, _i32, _i32, _i32]
+_lib.ep_workspace_bytes_ex.restype = _sz
+_lib.ep_layout_rows.argtypes = [_i64, _i32, _i32, _i32, _i32]
+_lib.ep_layout_rows.restype = _i64
 _lib.ep_buffer_bytes.argtypes = [_i64, _i32, ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
 _lib.ep_buffer_bytes.restype = ctypes.c_int
 _lib.ep_layout.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i64, _i32, _vp, _vp, _vp, _sz,
                            ctypes.POINTER(ep_handle_t), _vp]
 _lib.ep_layout.restype = ctypes.c_int
+_lib.ep_layout_ex.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
+                              ctypes.POINTER(ep_handle_t), _vp]
+_lib.ep_layout_ex.restype = ctypes.c_int
 _lib.ep_dispatch.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp, _vp]
 _lib.ep_dispatch.restype = ctypes.c_int
 _lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int, _i32, _vp, _vp, _vp]
@@ -134,6 +147,16 @@ def ep_workspace_bytes(num_max_dispatch_tokens: int, num_topk: int, num_experts:
     return _lib.ep_workspace_bytes(num_max_dispatch_tokens, num_topk, num_experts)
 
 
+def ep_workspace_bytes_ex(num_max_dispatch_tokens: int, num_topk: int, num_experts: int, row_align: int = 1,
+                          expert_capacity: int = 0) -> int:
+    return _lib.ep_workspace_bytes_ex(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity)
+
+
+def ep_layout_rows(num_max_dispatch_tokens: int, num_topk: int, num_experts: int, row_align: int = 1,
+                   expert_capacity: int = 0) -> int:
+    return _lib.ep_layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity)
+
+
 def ep_buffer_bytes(rows: int, hidden: int, quant) -> tuple[int, int]:
     """(total bytes, scale-region offset)."""
     total, off = _sz(0), _sz(0)
@@ -141,11 +164,7 @@ def ep_buffer_bytes(rows: int, hidden: int, quant) -> tuple[int, int]:
     return total.value, off.value
 
 
-def ep_layout(topk_idx, num_experts: int, num_max_dispatch_tokens: int, recv_count, workspace,
-              cumulative_recv_stats=None, *, num_tokens=None, num_topk=None, idx_dtype=None,
-              stream=None) -> ep_handle_t:
-    """topk_idx: device tensor [T, k] int32/int64 (or a raw pointer with
-    num_tokens / num_topk / idx_dtype given).  Returns the handle."""
+def _idx_args(topk_idx, num_tokens, num_topk, idx_dtype):
     if isinstance(topk_idx, torch.Tensor):
         if topk_idx.dim() != 2 or not topk_idx.is_contiguous():
             raise EpError(EP_ERR_INVALID_ARG, "topk_idx must be a contiguous [num_tokens, num_topk] tensor")
@@ -153,11 +172,35 @@ def ep_layout(topk_idx, num_experts: int, num_max_dispatch_tokens: int, recv_cou
             raise EpError(EP_ERR_INVALID_ARG, "topk_idx dtype must be int32 or int64")
         num_tokens, num_topk = topk_idx.shape
         idx_dtype = EP_IDX_INT64 if topk_idx.dtype == torch.int64 else EP_IDX_INT32
+    return num_tokens, num_topk, idx_dtype
+
+
+def ep_layout(topk_idx, num_experts: int, num_max_dispatch_tokens: int, recv_count, workspace,
+              cumulative_recv_stats=None, *, num_tokens=None, num_topk=None, idx_dtype=None,
+              stream=None) -> ep_handle_t:
+    """topk_idx: device tensor [T, k] int32/int64 (or a raw pointer with
+    num_tokens / num_topk / idx_dtype given).  Returns the handle."""
+    num_tokens, num_topk, idx_dtype = _idx_args(topk_idx, num_tokens, num_topk, idx_dtype)
     h = ep_handle_t()
     _check(_lib.ep_layout(_ptr(topk_idx), idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
                           num_experts, _ptr(recv_count), _ptr(cumulative_recv_stats), _ptr(workspace),
                           _nbytes(workspace) if isinstance(workspace, torch.Tensor) else 0,
                           ctypes.byref(h), _stream(stream)))
+    return h
+
+
+def ep_layout_ex(topk_idx, num_experts: int, num_max_dispatch_tokens: int, row_align: int, expert_capacity: int,
+                 recv_count, workspace, cumulative_recv_stats=None, *, num_tokens=None, num_topk=None,
+                 idx_dtype=None, stream=None) -> ep_handle_t:
+    """As ep_layout, with aligned (row_align) or capacity-padded
+    (expert_capacity) expert blocks."""
+    num_tokens, num_topk, idx_dtype = _idx_args(topk_idx, num_tokens, num_topk, idx_dtype)
+    h = ep_handle_t()
+    _check(_lib.ep_layout_ex(_ptr(topk_idx), idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
+                             num_experts, row_align, expert_capacity, _ptr(recv_count),
+                             _ptr(cumulative_recv_stats), _ptr(workspace),
+                             _nbytes(workspace) if isinstance(workspace, torch.Tensor) else 0,
+                             ctypes.byref(h), _stream(stream)))
     return h
 
 
@@ -205,14 +248,19 @@ class Handle:
     topk_idx_dtype: torch.dtype
 
 
-def quant_mode(use_fp8=True, use_ue8m0=False, use_mxfp4=False, quant=None) -> str:
+def quant_mode(use_fp8=True, use_ue8m0=False, use_mxfp4=False, quant=None, round_scale=False) -> str:
     """Flag mapping of the "Low-Latency Mode API" page: no use_fp8 -> bf16;
-    use_fp8 -> int8 per token; + use_ue8m0 -> MXFP8; + use_mxfp4 -> MXFP4.
-    ``quant="fp8_b128"`` selects e4m3 with per-128-channel scales."""
+    use_fp8 -> int8 per token; + use_ue8m0 -> MXFP8; + use_mxfp4 -> MXFP4;
+    round_scale goes with use_ue8m0 (whose scales are powers of two
+    already).  ``quant=`` names a mode directly, e.g. "fp8_b128" (e4m3 with
+    per-128-channel scales) or its power-of-two variants "fp8_b128_pow2" /
+    "fp8_b128_ue8m0"."""
     if quant is not None:
         if quant not in QUANT:
             raise EpError(EP_ERR_INVALID_ARG, f"unknown quant {quant!r}")
         return quant
+    if round_scale and not use_ue8m0:
+        raise EpError(EP_ERR_INVALID_ARG, "round_scale is used together with use_ue8m0")
     if (use_ue8m0 or use_mxfp4) and not use_fp8:
         raise EpError(EP_ERR_INVALID_ARG, "use_ue8m0 / use_mxfp4 require use_fp8")
     if use_ue8m0 and use_mxfp4:
@@ -231,9 +279,12 @@ def split_recv(buf: torch.Tensor, rows: int, hidden: int, quant: str):
     if q == "int8_token":
         return (buf[: rows * hidden].view(torch.int8).view(rows, hidden),
                 buf[off: off + rows * 4].view(torch.float32))
-    if q == "fp8_b128":
+    if q in ("fp8_b128", "fp8_b128_pow2"):
         return (buf[: rows * hidden].view(torch.float8_e4m3fn).view(rows, hidden),
                 buf[off: off + rows * (hidden // 128) * 4].view(torch.float32).view(rows, hidden // 128))
+    if q == "fp8_b128_ue8m0":
+        return (buf[: rows * hidden].view(torch.float8_e4m3fn).view(rows, hidden),
+                buf[off: off + rows * (hidden // 128)].view(torch.float8_e8m0fnu).view(rows, hidden // 128))
     if q == "mxfp8":
         return (buf[: rows * hidden].view(torch.float8_e4m3fn).view(rows, hidden),
                 buf[off: off + rows * (hidden // 32)].view(torch.float8_e8m0fnu))
@@ -245,12 +296,14 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispat
                          num_experts: int, cumulative_local_expert_recv_stats=None, use_fp8: bool = True,
                          round_scale: bool = False, use_ue8m0: bool = False, use_mxfp4: bool = False,
                          async_finish: bool = False, return_recv_hook: bool = False, topk_weights=None,
-                         quant: Optional[str] = None):
+                         quant: Optional[str] = None, row_align: int = 1, expert_capacity: int = 0):
     """Returns (recv_x, recv_count, handle, event, hook) with event and hook
-    None (there is no transport to overlap or to wait for)."""
-    if round_scale or return_recv_hook:
-        raise EpError(EP_ERR_UNSUPPORTED, "round_scale / return_recv_hook are not supported")
-    q = quant_mode(use_fp8, use_ue8m0, use_mxfp4, quant)
+    None (there is no transport to overlap or to wait for).  ``row_align`` /
+    ``expert_capacity`` select aligned or capacity-padded expert blocks; with
+    a capacity C the data views are shaped [num_experts, C, ...]."""
+    if return_recv_hook:
+        raise EpError(EP_ERR_UNSUPPORTED, "return_recv_hook is not supported")
+    q = quant_mode(use_fp8, use_ue8m0, use_mxfp4, quant, round_scale)
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise EpError(EP_ERR_INVALID_ARG, "x must be a contiguous bf16 [num_tokens, hidden] tensor")
     T, H = x.shape
@@ -258,11 +311,11 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispat
         raise EpError(EP_ERR_INVALID_ARG, "topk_idx must be [num_tokens, num_topk]")
     k = topk_idx.shape[1]
     dev = x.device
-    ws = torch.empty(max(ep_workspace_bytes(num_max_dispatch_tokens_per_rank, k, num_experts), 1),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ep_workspace_bytes_ex(num_max_dispatch_tokens_per_rank, k, num_experts, row_align,
+                                               expert_capacity), 1), dtype=torch.uint8, device=dev)
     recv_count = torch.empty(num_experts, dtype=torch.int64, device=dev)
-    h = ep_layout(topk_idx, num_experts, num_max_dispatch_tokens_per_rank, recv_count, ws,
-                  cumulative_local_expert_recv_stats)
+    h = ep_layout_ex(topk_idx, num_experts, num_max_dispatch_tokens_per_rank, row_align, expert_capacity,
+                     recv_count, ws, cumulative_local_expert_recv_stats)
     rows = h.max_rows
     total, _ = ep_buffer_bytes(rows, H, q)
     buf = torch.empty(max(total, 16), dtype=torch.uint8, device=dev)
@@ -272,6 +325,11 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispat
     ep_dispatch(h, x, H, q, buf, topk_weights, recv_w)
     handle = Handle(h, ws, H, q, tuple(topk_idx.shape), topk_idx.dtype)
     recv_x = split_recv(buf, rows, H, q)
+    if expert_capacity > 0:
+        if isinstance(recv_x, tuple):
+            recv_x = (recv_x[0].view(num_experts, expert_capacity, -1),) + recv_x[1:]
+        else:
+            recv_x = recv_x.view(num_experts, expert_capacity, H)
     if recv_w is not None:
         handle.recv_weights = recv_w
     return recv_x, recv_count, handle, None, None
@@ -280,8 +338,9 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispat
 def low_latency_combine(x, topk_idx: torch.Tensor, topk_weights: torch.Tensor, handle: Handle,
                         zero_copy: bool = False, async_finish: bool = False, return_recv_hook: bool = False,
                         out: Optional[torch.Tensor] = None, in_quant: str = "none"):
-    """x: bf16 [max_rows, hidden] expert outputs (or a raw uint8 receive-format
-    buffer with ``in_quant``).  Returns (combined_x, event, hook)."""
+    """x: bf16 [max_rows, hidden] expert outputs ([num_experts, C, hidden]
+    for a capacity-padded layout), or a raw uint8 receive-format buffer with
+    ``in_quant``.  Returns (combined_x, event, hook)."""
     if zero_copy or return_recv_hook:
         raise EpError(EP_ERR_UNSUPPORTED, "zero_copy / return_recv_hook are not supported")
     if tuple(topk_idx.shape) != handle.topk_idx_shape or topk_idx.dtype != handle.topk_idx_dtype:

@@ -55,6 +55,8 @@ class Workload:
     combine_input: str = "normal"   # "scaled_dispatch" | "identity" | "normal"
     seed: int = 0
     num_max_tokens: int = 0         # 0 -> T
+    row_align: int = 1              # > 1: expert blocks start at multiples of it
+    expert_capacity: int = 0        # > 0: every expert block has this many rows
 
     @property
     def t_max(self) -> int:
@@ -62,7 +64,9 @@ class Workload:
 
     @property
     def max_rows(self) -> int:
-        return self.t_max * self.k
+        if self.expert_capacity:
+            return self.E * self.expert_capacity
+        return self.t_max * self.k + self.E * (self.row_align - 1)
 
 
 WORKLOADS = {

@@ -34,16 +34,20 @@
  *   data region   rows x Dq bytes, row r at byte r*Dq
  *   scale region  starts at align_up(rows*Dq, 256); rows x Sq bytes
  *                 (EP_QUANT_NONE has no scale region and no padding)
- * with rows = handle.max_rows and, for hidden size H:
+ * with rows = handle.max_rows (num_max_tokens * k for the compact layout of
+ * ep_layout; see ep_layout_rows for the others) and, for hidden size H:
  *   EP_QUANT_NONE        Dq = 2H (bf16)             Sq = 0
  *   EP_QUANT_INT8_TOKEN  Dq = H  (int8)             Sq = 4   (one float32)
  *   EP_QUANT_FP8_B128    Dq = H  (e4m3fn)           Sq = H/32 (H/128 float32)
  *   EP_QUANT_MXFP8       Dq = H  (e4m3fn)           Sq = H/32 (e8m0 bytes)
+ *   EP_QUANT_FP8_B128_POW2  Dq = H (e4m3fn)         Sq = H/32 (H/128 float32)
+ *   EP_QUANT_FP8_B128_UE8M0 Dq = H (e4m3fn)         Sq = H/128 (e8m0 bytes)
  *   EP_QUANT_MXFP4       Dq = H/2 (e2m1, element 2i in the low nibble)
  *                                                   Sq = H/32 (e8m0 bytes)
  * Expert e owns rows [offsets[e], offsets[e] + recv_count[e]); rows of one
- * expert are in ascending (token, j) order.  Rows at or past R = offsets[E]
- * and the padding between the regions are left unspecified.
+ * expert are in ascending (token, j) order.  Rows that hold no pair (rows at
+ * or past offsets[E], the padding of aligned or capacity-padded blocks) and
+ * the padding between the regions are left unspecified.
  */
 #ifndef EP_H_
 #define EP_H_
@@ -55,7 +59,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 1
+#define EP_ABI_VERSION 2
 
 typedef enum {
   EP_OK = 0,
@@ -71,13 +75,20 @@ typedef enum { EP_IDX_INT32 = 0, EP_IDX_INT64 = 1 } ep_idx_dtype_t;
 
 /* Quantisation of a receive row ("Low-Latency Mode API", Parameters use_fp8,
  * use_ue8m0, use_mxfp4; "DeepEP FP8 Dispatch and Combine Operations", The
- * Dispatch Stage, for the per-128-channel e4m3 mode). */
+ * Dispatch Stage, for the per-128-channel e4m3 mode, and Advanced
+ * Configuration Options, for its round_scale and use_ue8m0 variants).
+ * Per-128 power-of-two scale: s0 = amax/448 rounded UP to a power of two 2^e
+ * (e read off the float32 bits of s0), codes e4m3(clamp(x * 2^-e, +-448));
+ * a block with amax 0 or e < -127 stores scale 0 (byte 0) and zero codes;
+ * the e8m0 byte is e + 127, four consecutive blocks per int32. */
 typedef enum {
   EP_QUANT_NONE = 0,       /* bf16 copy                                          */
   EP_QUANT_INT8_TOKEN = 1, /* int8, scale amax/127 per token                      */
   EP_QUANT_FP8_B128 = 2,   /* e4m3fn, scale amax/448 per 128 channels             */
   EP_QUANT_MXFP8 = 3,      /* e4m3fn, e8m0 power-of-two scale per 32 elements     */
-  EP_QUANT_MXFP4 = 4       /* e2m1 x2 per byte, e8m0 scale per 32 elements        */
+  EP_QUANT_MXFP4 = 4,      /* e2m1 x2 per byte, e8m0 scale per 32 elements        */
+  EP_QUANT_FP8_B128_POW2 = 5,  /* e4m3fn, power-of-two float32 scale per 128     */
+  EP_QUANT_FP8_B128_UE8M0 = 6  /* e4m3fn, power-of-two e8m0 scale per 128        */
 } ep_quant_t;
 
 /* Layout handle ("Low-Latency Mode API": the handle returned by dispatch is
@@ -87,21 +98,41 @@ typedef enum {
 typedef struct {
   int64_t num_tokens;     /* T                                               */
   int64_t num_max_tokens; /* capacity num_max_dispatch_tokens (>= T)         */
-  int64_t max_rows;       /* num_max_tokens * num_topk: receive rows         */
+  int64_t max_rows;       /* receive rows: ep_layout_rows(num_max_tokens, k, */
+                          /* E, row_align, expert_capacity)                  */
   int32_t num_topk;       /* k                                               */
   int32_t num_experts;    /* E                                               */
-  int32_t *offsets;       /* device [E+1]: exclusive scan, offsets[E] = R    */
+  int32_t row_align;      /* 1, or the alignment of every expert block       */
+  int32_t expert_capacity;/* 0, or the rows of every expert block            */
+  int32_t *offsets;       /* device [E+1]: block starts; offsets[E] = rows   */
+                          /* up to the end of the last block                 */
   int32_t *slot;          /* device [T*k]: receive row of (t, j), or -1      */
-  int32_t *row_src;       /* device [max_rows]: t*k + j of each row, -1 >= R */
-  uint32_t *status;       /* device [1]: bit 0 = some id outside [-1, E)     */
+  int32_t *row_src;       /* device [max_rows]: t*k + j of the pair in each  */
+                          /* row, -1 for a row that holds none               */
+  uint32_t *status;       /* device [1]: EP_STATUS_* bits                    */
 } ep_handle_t;
 
-/* Status bits written by ep_layout into *handle.status. */
-#define EP_STATUS_ID_OUT_OF_RANGE 1u
+/* Status bits written by the layout calls into *handle.status. */
+#define EP_STATUS_ID_OUT_OF_RANGE 1u   /* some id outside [-1, E), dropped     */
+#define EP_STATUS_CAPACITY_OVERFLOW 2u /* some expert got more pairs than its  */
+                                       /* capacity; the later ones dropped     */
 
 /* Bytes of workspace ep_layout needs for the given capacity; 0 if the
  * arguments are out of range.  Host-only; no device work. */
 size_t ep_workspace_bytes(int64_t num_max_dispatch_tokens, int32_t num_topk, int32_t num_experts);
+
+/* Receive rows (handle.max_rows) of a layout made by ep_layout_ex:
+ *   expert_capacity == 0: num_max_dispatch_tokens * num_topk
+ *                         + num_experts * (row_align - 1)
+ *   expert_capacity  > 0: num_experts * expert_capacity
+ * -1 if the arguments are out of range (see ep_layout_ex).  Host-only. */
+int64_t ep_layout_rows(int64_t num_max_dispatch_tokens, int32_t num_topk, int32_t num_experts,
+                       int32_t row_align, int32_t expert_capacity);
+
+/* Workspace bytes of ep_layout_ex; 0 if the arguments are out of range.
+ * Host-only. */
+size_t ep_workspace_bytes_ex(int64_t num_max_dispatch_tokens, int32_t num_topk, int32_t num_experts,
+                             int32_t row_align, int32_t expert_capacity);
 
 /* Size of a receive buffer of `rows` rows (format above): writes the total
  * byte count and the scale-region offset to the host pointers (either may be
@@ -130,12 +161,34 @@ ep_status_t ep_layout(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t nu
                       int64_t *recv_count, int32_t *cumulative_recv_stats, void *workspace,
                       size_t workspace_bytes, ep_handle_t *handle, void *stream);
 
+/* Routing layout with per-expert blocks that are aligned or padded to a fixed
+ * capacity -- the receive forms a grouped GEMM reads ("EP dispatch with
+ * unfused MXFP8 quantization", Tests: the grouped path fixes one per-expert
+ * alignment; "Low-Latency Mode API", low_latency_combine Parameters: x is
+ * [num_local_experts, capacity, hidden]).  Arguments as ep_layout, plus:
+ *   row_align        1 <= row_align <= 1024: every expert block starts at a
+ *                    multiple of row_align rows; block e has
+ *                    align_up(recv_count[e], row_align) rows.
+ *   expert_capacity  0, or C > 0: block e is rows [e*C, (e+1)*C) (row_align
+ *                    must then be 1).  Pairs past the C-th of an expert (in
+ *                    (token, j) order) get slot -1 and set
+ *                    EP_STATUS_CAPACITY_OVERFLOW; recv_count reports the rows
+ *                    kept (<= C), cumulative_recv_stats adds the full demand.
+ *   workspace        >= ep_workspace_bytes_ex(...)
+ * ep_layout is ep_layout_ex with row_align 1 and expert_capacity 0.  The
+ * other calls read only the handle, so they take any of these layouts. */
+ep_status_t ep_layout_ex(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                         int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts,
+                         int32_t row_align, int32_t expert_capacity, int64_t *recv_count,
+                         int32_t *cumulative_recv_stats, void *workspace, size_t workspace_bytes,
+                         ep_handle_t *handle, void *stream);
+
 /* Dispatch ("Low-Latency Mode API", low_latency_dispatch; "DeepEP FP8
  * Dispatch and Combine Operations", The Dispatch Stage).
  *   handle         host, from ep_layout on the same stream (or ordered after it)
  *   x              device bf16 [T, H], 16-byte aligned.  Only bf16 input is
  *                  accepted: pre-quantised input is not a valid x.
- *   hidden         H > 0, H % 32 == 0 (H % 128 == 0 for EP_QUANT_FP8_B128)
+ *   hidden         H > 0, H % 32 == 0 (H % 128 == 0 for the three per-128 modes)
  *   topk_weights   device float32 [T, k] or NULL
  *   recv_buf       device, 16-byte aligned, >= ep_buffer_bytes(max_rows, H, quant)
  *   recv_weights   device float32 [max_rows] or NULL; if given (and
@@ -157,8 +210,9 @@ ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden
  *                    fl32(w[t, j] * dequant(row slot[t, j])) ), accumulated in
  * float32 in ascending j with one rounding per multiply and per add; a token
  * with no routed pair gets +0.  Dequantisation: int8 and e4m3-per-128 codes
- * times their float32 scale (one rounding); MX codes times 2^(byte-127)
- * (exact unless the product leaves float32's range); e8m0 byte 0xFF is NaN.
+ * times their float32 scale (one rounding); MX and per-128 e8m0 codes times
+ * 2^(byte-127) (exact unless the product leaves float32's range); e8m0 byte
+ * 0xFF is NaN.
  * The routing comes from the handle (the topk_idx that produced it). */
 ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t expert_out_bytes,
                        ep_quant_t in_quant, int32_t hidden, const float *topk_weights, void *out,
@@ -179,7 +233,7 @@ ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t
  * bf16_rne(fl32(topk_weights[t, j] * grad_out[t])) -- the gradient of the
  * weighted sum with respect to expert row j -- quantised once per routed
  * pair.  Without, it receives the quantised grad_out[t] (exactly
- * ep_dispatch of grad_out).  Rows at or past R are left unspecified. */
+ * ep_dispatch of grad_out).  Rows that hold no pair are left unspecified. */
 ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out, int32_t hidden,
                                 const float *topk_weights, ep_quant_t quant, void *grad_buf,
                                 size_t grad_buf_bytes, void *stream);

@@ -58,10 +58,19 @@ def canary_buffer(total: int) -> torch.Tensor:
 
 
 def run_layout(ep, w: W.Workload, idx: np.ndarray, cum=None):
-    ws = torch.empty(max(ep.ep_workspace_bytes(w.t_max, w.k, w.E), 256), dtype=torch.uint8, device=DEV)
+    padded = w.row_align > 1 or w.expert_capacity > 0
+    if padded:
+        nbytes = ep.ep_workspace_bytes_ex(w.t_max, w.k, w.E, w.row_align, w.expert_capacity)
+    else:
+        nbytes = ep.ep_workspace_bytes(w.t_max, w.k, w.E)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
     ws.fill_(0xA5)                                   # garbage: nothing may rely on zeroed workspace
     recv_count = torch.full((w.E,), -7, dtype=torch.int64, device=DEV)
-    h = ep.ep_layout(to_dev(idx), w.E, w.t_max, recv_count, ws, cum)
+    if padded:
+        h = ep.ep_layout_ex(to_dev(idx), w.E, w.t_max, w.row_align, w.expert_capacity, recv_count, ws, cum)
+    else:
+        h = ep.ep_layout(to_dev(idx), w.E, w.t_max, recv_count, ws, cum)
+    assert h.max_rows == w.max_rows
     return h, ws, recv_count
 
 
@@ -100,7 +109,7 @@ def run_path(ep, w: W.Workload, inp: dict, *, expert_out: np.ndarray | None = No
         else:
             assert expert_out is not None
             y = expert_out.copy()
-            y[int(lay["offsets"][-1]):] = NAN_BF16
+            y[lay["row_src"] < 0] = NAN_BF16             # rows holding no pair: canaries
             src, q = to_dev(y).view(torch.uint8).reshape(-1), "none"
         o = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
         ep.ep_combine(h, src, q, w.H, wts, o)

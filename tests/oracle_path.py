@@ -10,7 +10,7 @@ from oracle import combine as C, dispatch as D, layout as L, quant as Q
 
 
 def oracle_run(w: W.Workload, inp: dict, expert_out: np.ndarray | None = None, tokens=None):
-    lay = L.layout(inp["topk_idx"], w.E, w.t_max)
+    lay = L.layout(inp["topk_idx"], w.E, w.t_max, row_align=w.row_align, expert_capacity=w.expert_capacity)
     dq, sq = Q.row_bytes(w.mode, w.H)
     if tokens is None:
         rb = D.dispatch(inp["x"], lay, w.mode, inp["topk_weights"])

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(ep):
 
 
 def test_abi_version(ep):
-    assert ep.ep_abi_version() == 1
+    assert ep.ep_abi_version() == 2
 
 
 FAKE = 1 << 40          # 256-byte aligned, never dereferenced on the host
@@ -89,10 +89,60 @@ def test_oracle_validate_accepts_defaults():
         OV.check_hidden(7168, m)
 
 
+def _layout_ex(ep, align=1, cap=0, tmax=8, k=2, E=8, wsb=1 << 30):
+    h = ep.ep_handle_t()
+    return ep._lib.ep_layout_ex(FAKE, 1, 4, k, tmax, E, align, cap, FAKE, None, FAKE, wsb, ctypes.byref(h), None)
+
+
+LAYOUT_EX_BAD = [
+    (dict(align=0), 1), (dict(align=1025), 1), (dict(cap=-1), 1), (dict(align=2, cap=4), 1),
+    (dict(cap=1 << 23, E=512), 1), (dict(tmax=(1 << 30) - 1, align=1024), 1), (dict(align=64, wsb=64), 3),
+]
+
+
+@pytest.mark.parametrize("kw,code", LAYOUT_EX_BAD)
+def test_layout_ex_rejects(ep, kw, code):
+    assert _layout_ex(ep, **kw) == code
+    assert ep.ep_last_error().startswith("ep_layout_ex")
+
+
+@pytest.mark.parametrize("kw,code", LAYOUT_EX_BAD)
+def test_oracle_validate_agrees_on_padding_limits(kw, code):
+    if "wsb" in kw:
+        pytest.skip("buffer-size check has no oracle counterpart")
+    a = dict(align=1, cap=0, tmax=8, k=2, E=8)
+    a.update(kw)
+    with pytest.raises(ValueError):
+        OV.check_padding(a["k"], a["tmax"], a["E"], a["align"], a["cap"])
+
+
+@pytest.mark.parametrize("tmax,k,E,align,cap", [(8, 2, 8, 1, 0), (100, 8, 256, 128, 0), (100, 8, 256, 1, 100),
+                                                (0, 1, 1, 7, 0), (16384, 8, 256, 1, 16384), (3, 16, 512, 1024, 0)])
+def test_layout_rows_matches_oracle(ep, tmax, k, E, align, cap):
+    from oracle import layout as OL
+    import numpy as np
+    rows = ep.ep_layout_rows(tmax, k, E, align, cap)
+    assert rows == OV.check_padding(k, tmax, E, align, cap)
+    if tmax * k <= 4096:
+        lay = OL.layout(np.zeros((0, k), np.int64), E, tmax, row_align=align, expert_capacity=cap)
+        assert lay.max_rows == rows
+    assert ep.ep_workspace_bytes_ex(tmax, k, E, align, cap) >= 4 * rows
+    if align == 1 and cap == 0:
+        assert ep.ep_workspace_bytes_ex(tmax, k, E, 1, 0) == ep.ep_workspace_bytes(tmax, k, E)
+
+
+def test_layout_rows_rejects(ep):
+    assert ep.ep_layout_rows(8, 2, 8, 0, 0) == -1
+    assert ep.ep_layout_rows(8, 2, 8, 2, 3) == -1
+    assert ep.ep_layout_rows(8, 0, 8, 1, 0) == -1
+    assert ep.ep_workspace_bytes_ex(8, 2, 8, 1, -2) == 0
+
+
 def _handle(ep, T=4, k=2, tmax=8, E=8):
     h = ep.ep_handle_t()
     h.num_tokens, h.num_max_tokens, h.max_rows = T, tmax, tmax * k
     h.num_topk, h.num_experts = k, E
+    h.row_align, h.expert_capacity = 1, 0
     h.offsets = h.slot = h.row_src = h.status = FAKE
     return h
 
@@ -102,6 +152,7 @@ DISPATCH_BAD = [
     (dict(hidden=65568), 2), (dict(x=None), 1), (dict(x=FAKE + 8), 1), (dict(recv=None), 1),
     (dict(recv=FAKE + 8), 1), (dict(recv_bytes=10), 3), (dict(rw=FAKE, w=None), 1), (dict(w=FAKE + 2), 1),
     (dict(h_bad="k"), 1), (dict(h_bad="rows"), 1), (dict(h_bad="ptr"), 1), (dict(h_none=True), 1),
+    (dict(h_bad="align"), 1),
 ]
 
 
@@ -114,6 +165,8 @@ def test_dispatch_rejects(ep, kw, code):
         h.max_rows = 3
     elif kw.get("h_bad") == "ptr":
         h.slot = None
+    elif kw.get("h_bad") == "align":
+        h.row_align = 4             # max_rows no longer matches the arrangement
     hp = None if kw.get("h_none") else ctypes.byref(h)
     hidden = kw.get("hidden", 256)
     quant = kw.get("quant", 3)
@@ -126,7 +179,8 @@ def test_dispatch_rejects(ep, kw, code):
 COMBINE_BAD = [
     (dict(hidden=40), 1), (dict(quant=-1), 1), (dict(inp=None), 1), (dict(inp=FAKE + 4), 1),
     (dict(in_bytes=5), 3), (dict(w=None), 1), (dict(out=None), 1), (dict(out=FAKE + 2), 1),
-    (dict(hidden=128 + 32, quant=2), 1),
+    (dict(hidden=128 + 32, quant=2), 1), (dict(hidden=128 + 64, quant=5), 1), (dict(hidden=96, quant=6), 1),
+    (dict(quant=7), 1),
 ]
 
 
@@ -157,7 +211,9 @@ def test_combine_backward_rejects(ep, kw, code):
 
 
 @pytest.mark.parametrize("hidden,mode", [(32, "none"), (7168, "int8_token"), (7168, "fp8_b128"),
-                                         (96, "mxfp8"), (7168, "mxfp4"), (1024, "mxfp4")])
+                                         (96, "mxfp8"), (7168, "mxfp4"), (1024, "mxfp4"),
+                                         (7168, "fp8_b128_pow2"), (7168, "fp8_b128_ue8m0"),
+                                         (384, "fp8_b128_ue8m0")])
 @pytest.mark.parametrize("rows", [0, 1, 37, 131072])
 def test_buffer_bytes_matches_oracle(ep, hidden, mode, rows):
     assert ep.ep_buffer_bytes(rows, hidden, mode) == OD.buffer_bytes(rows, hidden, mode)
@@ -171,6 +227,11 @@ def test_buffer_bytes_rejects(ep):
         ep.ep_buffer_bytes(-1, 128, "none")
     with pytest.raises(ep.EpError):
         ep.ep_buffer_bytes(1, 96, "fp8_b128")
+    for q in ("fp8_b128_pow2", "fp8_b128_ue8m0"):
+        with pytest.raises(ep.EpError):
+            ep.ep_buffer_bytes(1, 160, q)
+        with pytest.raises(ValueError):
+            OV.check_hidden(160, q)
 
 
 def test_workspace_bytes(ep):
@@ -189,6 +250,12 @@ def test_flag_mapping(ep):
     assert ep.quant_mode(use_fp8=True, use_mxfp4=True) == "mxfp4"
     with pytest.raises(ep.EpError):
         ep.quant_mode(use_fp8=False, use_ue8m0=True)
+    assert ep.quant_mode(use_fp8=True, use_ue8m0=True, round_scale=True) == "mxfp8"
+    assert OV.check_flags(True, True, False, True, False) == "mxfp8"
+    with pytest.raises(ep.EpError):
+        ep.quant_mode(use_fp8=True, round_scale=True)
+    with pytest.raises(ValueError):
+        OV.check_flags(True, False, False, True, False)
     for flags in [dict(use_fp8=False), dict(use_fp8=True), dict(use_fp8=True, use_ue8m0=True),
                   dict(use_fp8=True, use_mxfp4=True)]:
         assert ep.quant_mode(**flags) == OV.check_flags(flags.get("use_fp8"), flags.get("use_ue8m0", False),

@@ -41,6 +41,8 @@ CASES = [
     ("b5", 64, 128, 32, 16, "none", 0.1),
     ("b6", 9, 7168, 256, 8, "mxfp8", 0.0),
     ("b7", 0, 256, 8, 4, "mxfp8", 0.0),
+    ("b8", 30, 512, 16, 8, "fp8_b128_ue8m0", 0.1),
+    ("b9", 30, 384, 16, 4, "fp8_b128_pow2", 0.0),
 ]
 
 

@@ -5,7 +5,9 @@ pair, duplicate experts in a row, out-of-range ids (status bit), k = 1 and
 k = 16, E = 1 and E = 512, hidden sizes that are and are not multiples of 128
 (MX scale packing), ragged tails of the row tiling, int32 and int64 ids, the
 multi-workgroup layout path (more than 16384 pairs), every bf16 bit pattern
-through every quantiser, blocks of zeros, subnormals and huge values.
+through every quantiser, blocks of zeros, subnormals and huge values (for the
+power-of-two per-128 scales this includes the last kept exponent, -127, and
+the zeroed blocks below it).
 """
 
 import sys
@@ -22,7 +24,7 @@ from tests.test_gpu_parity import check_combine, check_layout
 
 pytestmark = pytest.mark.gpu
 
-MODES = ["none", "int8_token", "fp8_b128", "mxfp8", "mxfp4"]
+MODES = ["none", "int8_token", "fp8_b128", "mxfp8", "mxfp4", "fp8_b128_pow2", "fp8_b128_ue8m0"]
 
 
 @pytest.fixture(scope="module")
@@ -64,6 +66,10 @@ CASES = [
     (10, 2500, 64, 512, 16, "int8_token", "int32", 0.0, 2600, "identity"),
     (11, 12, 16384, 16, 4, "int8_token", "int64", 0.0, 12, "identity"),  # largest int8 tile
     (12, 6, 8192, 4, 2, "mxfp4", "int32", 0.0, 6000, "normal"),           # capacity >> T
+    (13, 50, 640, 16, 4, "fp8_b128_pow2", "int64", 0.1, 60, "identity"),
+    (14, 3000, 512, 64, 8, "fp8_b128_ue8m0", "int32", 0.05, 3000, "identity"),  # multi-block layout
+    (15, 7, 384, 8, 2, "fp8_b128_ue8m0", "int64", 0.0, 7, "identity"),     # 3 scale bytes per row
+    (16, 128, 7168, 256, 8, "fp8_b128_pow2", "int64", 0.1, 128, "identity"),
 ]
 
 

@@ -55,13 +55,18 @@ def _ulp_bf16(v):
 def check_combine(w, got_bits, want_bits):
     got = codecs.bf16_bits_to_f32(got_bits).astype(np.float64)
     want = codecs.bf16_bits_to_f32(want_bits).astype(np.float64)
-    assert not np.isnan(got).any(), "NaN in combine output (stray read of an unused row?)"
+    assert not (np.isnan(got) & ~np.isnan(want)).any(), "NaN in combine output (stray read of an unused row?)"
+    # a dequantised value past float32's range is +-inf on both sides (IEEE);
+    # those elements must match exactly, the tolerances apply to the rest
+    fin = np.isfinite(want)
+    assert np.array_equal(got_bits[~fin], want_bits[~fin])
     if w.combine_input == "identity" and w.mode != "none":
-        num = np.linalg.norm(got - want, axis=1)
-        den = np.maximum(np.linalg.norm(want, axis=1), 1e-30)
+        rows = fin.all(axis=1)
+        num = np.linalg.norm(got[rows] - want[rows], axis=1)
+        den = np.maximum(np.linalg.norm(want[rows], axis=1), 1e-30)
         assert np.all(num / den <= 2e-2)
     else:
-        assert np.all(np.abs(got - want) <= _ulp_bf16(want))
+        assert np.all(np.abs(got[fin] - want[fin]) <= _ulp_bf16(want[fin]))
     # same float32 operations in the same order: expect identical bits
     assert np.array_equal(got_bits, want_bits)
 
