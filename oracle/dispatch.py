@@ -14,8 +14,14 @@ reading taken -- compact expert-major rows, row-major scales):
 * scale region: starts at ``align_up(max_rows * Dq, 256)``; ``max_rows`` rows
   of ``Sq`` bytes.  bf16 rows have no scale region and no padding.
 
-``Dq``/``Sq`` per mode are in ``quant.row_bytes``.  Rows at or past R and the
-padding between the regions are unspecified and never compared.
+``Dq``/``Sq`` per mode are in ``quant.row_bytes``.  Rows that hold no pair and
+the padding between the regions are unspecified and never compared.
+
+Interleaved form ("DeepEP FP8 Dispatch and Combine Operations", Message
+Transmission via IBGDA: each token's message is its FP8 payload followed by
+its scales): row r starts at ``r * stride`` with ``stride = align_up(Dq + Sq,
+16)``; its Dq data bytes come first, then its Sq scale bytes, then zero
+padding.  (16 bytes keeps every row start aligned for 16-byte accesses.)
 
 If ``topk_weights`` is given, ``recv_weights[slot[t, j]] = topk_weights[t, j]``
 (the pages list the argument without saying what dispatch does with it;
@@ -41,9 +47,21 @@ def align_up(n: int, a: int) -> int:
     return (n + a - 1) // a * a
 
 
-def buffer_bytes(rows: int, hidden: int, mode: str) -> tuple[int, int]:
-    """(total bytes, scale-region offset) of a receive buffer of ``rows``."""
+INTERLEAVED_ROW_ALIGN = 16
+
+
+def interleaved_stride(hidden: int, mode: str) -> int:
     dq, sq = quant.row_bytes(mode, hidden)
+    return align_up(dq + sq, INTERLEAVED_ROW_ALIGN)
+
+
+def buffer_bytes(rows: int, hidden: int, mode: str, interleaved: bool = False) -> tuple[int, int]:
+    """(total bytes, scale offset) of a receive buffer of ``rows``: the
+    scale-region offset, or for the interleaved form the offset of the
+    scales inside a row."""
+    dq, sq = quant.row_bytes(mode, hidden)
+    if interleaved:
+        return rows * interleaved_stride(hidden, mode), dq
     off = align_up(rows * dq, SCALE_REGION_ALIGN) if sq else rows * dq
     return off + rows * sq, off
 
@@ -57,22 +75,36 @@ class RecvBuffer:
     scales: np.ndarray           # uint8 [max_rows, Sq]
     weights: np.ndarray | None   # float32 [max_rows] or None
 
-    def to_bytes(self) -> np.ndarray:
-        """The flat buffer: data region, zero padding, scale region."""
-        rows = self.data.shape[0]
-        total, off = buffer_bytes(rows, self.hidden, self.mode)
+    def to_bytes(self, interleaved: bool = False) -> np.ndarray:
+        """The flat buffer: data region, zero padding, scale region; or, in
+        the interleaved form, one row after another, each data then scales
+        then zero padding."""
+        rows, dq = self.data.shape
+        sq = self.scales.shape[1]
+        total, off = buffer_bytes(rows, self.hidden, self.mode, interleaved)
         buf = np.zeros(total, np.uint8)
+        if interleaved:
+            stride = interleaved_stride(self.hidden, self.mode)
+            for r in range(rows):
+                buf[r * stride:r * stride + dq] = self.data[r]
+                buf[r * stride + dq:r * stride + dq + sq] = self.scales[r]
+            return buf
         buf[:self.data.size] = self.data.reshape(-1)
         buf[off:off + self.scales.size] = self.scales.reshape(-1)
         return buf
 
     @staticmethod
-    def from_bytes(buf: np.ndarray, rows: int, hidden: int, mode: str, num_rows: int) -> "RecvBuffer":
+    def from_bytes(buf: np.ndarray, rows: int, hidden: int, mode: str, num_rows: int,
+                   interleaved: bool = False) -> "RecvBuffer":
         dq, sq = quant.row_bytes(mode, hidden)
-        total, off = buffer_bytes(rows, hidden, mode)
+        total, off = buffer_bytes(rows, hidden, mode, interleaved)
         buf = np.asarray(buf, np.uint8).reshape(-1)
         if buf.size < total:
             raise ValueError("buffer too small")
+        if interleaved:
+            stride = interleaved_stride(hidden, mode)
+            rowsv = buf[:rows * stride].reshape(rows, stride)
+            return RecvBuffer(mode, hidden, num_rows, rowsv[:, :dq].copy(), rowsv[:, dq:dq + sq].copy(), None)
         data = buf[:rows * dq].reshape(rows, dq)
         scales = buf[off:off + rows * sq].reshape(rows, sq)
         return RecvBuffer(mode, hidden, num_rows, data, scales, None)

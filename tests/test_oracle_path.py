@@ -114,6 +114,35 @@ def test_ue8m0_and_pow2_buffers_decode_alike():
     assert np.array_equal(C.combine(a, lay, inp["topk_weights"]), C.combine(b, lay, inp["topk_weights"]))
 
 
+def test_interleaved_buffer_worked_example():
+    # 2 rows, H = 32, mxfp8: 32 data bytes + 1 scale byte -> rows 48 bytes apart
+    data = np.arange(64, dtype=np.uint8).reshape(2, 32)
+    scales = np.array([[200], [201]], np.uint8)
+    rb = D.RecvBuffer("mxfp8", 32, 2, data, scales, None)
+    buf = rb.to_bytes(interleaved=True)
+    assert buf.size == 96 and D.buffer_bytes(2, 32, "mxfp8", True) == (96, 32)
+    assert buf[:32].tolist() == list(range(32)) and buf[32] == 200 and not buf[33:48].any()
+    assert buf[48:80].tolist() == list(range(32, 64)) and buf[80] == 201 and not buf[81:].any()
+    # int8 per token at H = 64: 64 + 4 -> 80; the float32 scale sits right after the codes
+    assert D.interleaved_stride(64, "int8_token") == 80
+    assert D.interleaved_stride(7168, "fp8_b128") == 7168 + 224
+    assert D.interleaved_stride(7168, "mxfp4") == 3584 + 224
+    assert D.interleaved_stride(256, "none") == 512
+
+
+@pytest.mark.parametrize("mode", ["int8_token", "fp8_b128", "mxfp8", "mxfp4", "fp8_b128_ue8m0", "none"])
+def test_interleaved_roundtrip(mode):
+    w, inp = _case(12, T=9, H=384, E=4, k=2, mode=mode)
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    rb = D.dispatch(inp["x"], lay, mode)
+    buf = rb.to_bytes(interleaved=True)
+    rb2 = D.RecvBuffer.from_bytes(buf, w.max_rows, w.H, mode, rb.num_rows, interleaved=True)
+    assert np.array_equal(rb.data, rb2.data) and np.array_equal(rb.scales, rb2.scales)
+    # the same rows, region form
+    rb3 = D.RecvBuffer.from_bytes(rb.to_bytes(), w.max_rows, w.H, mode, rb.num_rows)
+    assert np.array_equal(rb3.data, rb2.data) and np.array_equal(rb3.scales, rb2.scales)
+
+
 def test_recv_buffer_bytes_roundtrip():
     w, inp = _case(9, T=10, H=64, E=4, k=2, mode="mxfp8")
     lay = L.layout(inp["topk_idx"], w.E, w.T)
