@@ -115,18 +115,19 @@ def test_ue8m0_and_pow2_buffers_decode_alike():
 
 
 def test_interleaved_buffer_worked_example():
-    # 2 rows, H = 32, mxfp8: 32 data bytes + 1 scale byte -> rows 48 bytes apart
+    # 2 rows, H = 32, mxfp8: 32 data bytes + 1 scale byte -> one 128-byte line per row
     data = np.arange(64, dtype=np.uint8).reshape(2, 32)
     scales = np.array([[200], [201]], np.uint8)
     rb = D.RecvBuffer("mxfp8", 32, 2, data, scales, None)
     buf = rb.to_bytes(interleaved=True)
-    assert buf.size == 96 and D.buffer_bytes(2, 32, "mxfp8", True) == (96, 32)
-    assert buf[:32].tolist() == list(range(32)) and buf[32] == 200 and not buf[33:48].any()
-    assert buf[48:80].tolist() == list(range(32, 64)) and buf[80] == 201 and not buf[81:].any()
-    # int8 per token at H = 64: 64 + 4 -> 80; the float32 scale sits right after the codes
-    assert D.interleaved_stride(64, "int8_token") == 80
-    assert D.interleaved_stride(7168, "fp8_b128") == 7168 + 224
-    assert D.interleaved_stride(7168, "mxfp4") == 3584 + 224
+    assert buf.size == 256 and D.buffer_bytes(2, 32, "mxfp8", True) == (256, 32)
+    assert buf[:32].tolist() == list(range(32)) and buf[32] == 200 and not buf[33:128].any()
+    assert buf[128:160].tolist() == list(range(32, 64)) and buf[160] == 201 and not buf[161:].any()
+    # int8 per token at H = 64: 64 + 4 bytes -> 128; the float32 scale sits right after the codes
+    assert D.interleaved_stride(64, "int8_token") == 128
+    assert D.interleaved_stride(7168, "fp8_b128") == 7424          # 7168 + 224 = 7392 -> 58 lines
+    assert D.interleaved_stride(7168, "mxfp4") == 3840             # 3584 + 224 = 3808 -> 30 lines
+    assert D.interleaved_stride(7168, "fp8_b128_ue8m0") == 7296    # 7168 + 56 -> 57 lines
     assert D.interleaved_stride(256, "none") == 512
 
 
