@@ -222,6 +222,8 @@ def main() -> int:
                     help="expert blocks start at multiples of this many rows (ep_layout_ex)")
     ap.add_argument("--expert-capacity", type=int, default=0,
                     help="every expert block has this many rows; later pairs are dropped (ep_layout_ex)")
+    ap.add_argument("--interleaved", action="store_true",
+                    help="receive rows hold their data then their scales (EP_RECV_INTERLEAVED)")
     ap.add_argument("--quant", default=None,
                     help="dispatch quantisation in place of the workload's own (e.g. fp8_b128_ue8m0)")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
@@ -246,9 +248,11 @@ def main() -> int:
     padded = args.row_align > 1 or args.expert_capacity > 0
     if padded:
         w = replace(w, row_align=args.row_align, expert_capacity=args.expert_capacity)
-    variant = padded or (args.quant is not None and args.quant != w.mode)
+    variant = padded or args.interleaved or (args.quant is not None and args.quant != w.mode)
     if args.quant is not None:
         w = replace(w, mode=args.quant)
+    if args.interleaved:
+        w = replace(w, interleaved=True)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     print(f"[bench] generating {w.name}: T={w.T} H={w.H} E={w.E} k={w.k} {w.mode} rows={w.max_rows}",
@@ -259,7 +263,7 @@ def main() -> int:
     y_host = W.make_expert_out(w) if w.combine_input == "normal" and not padded else None
     y_dev = w.combine_input == "normal" and padded
 
-    total_recv, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    total_recv, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode, w.interleaved)
     per_set = (w.T * w.H * 2 * 2 + total_recv + (w.max_rows * w.H * 2 if w.combine_input == "normal" else 0))
     nsets = args.sets or max(2, -(-(1 << 30) // max(per_set, 1)))
     nsets = min(nsets, 64)
@@ -311,11 +315,11 @@ def main() -> int:
                 s["h"] = ep.ep_layout(s["idx"], w.E, w.t_max, s["rc"], s["ws"])
 
         def disp():
-            ep.ep_dispatch(s["h"], s["x"], w.H, w.mode, s["recv"])
+            ep.ep_dispatch(s["h"], s["x"], w.H, w.mode, s["recv"], interleaved=w.interleaved)
 
         def comb():
             if w.combine_input == "identity":
-                ep.ep_combine(s["h"], s["recv"], w.mode, w.H, s["w"], s["out"])
+                ep.ep_combine(s["h"], s["recv"], w.mode, w.H, s["w"], s["out"], interleaved=w.interleaved)
             elif w.combine_input == "scaled_dispatch":
                 # the x1.5 expert step is not part of the path: combine reads
                 # the dispatched bf16 rows (same bytes, same work)
@@ -376,7 +380,7 @@ def main() -> int:
                                f"dispatch={w.mode} routing={w.routing} unrouted={w.neg_frac} "
                                f"combine_input={w.combine_input}",
                    "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R, "buffer_sets": nsets,
-                   "row_align": w.row_align, "expert_capacity": w.expert_capacity,
+                   "row_align": w.row_align, "expert_capacity": w.expert_capacity, "interleaved": w.interleaved,
                    "receive_rows": w.max_rows},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "alg_bytes_per_step": b["total"],

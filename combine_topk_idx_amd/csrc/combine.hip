@@ -159,11 +159,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void co
   }
 }
 
+// `quant` is Q possibly OR-ed with EP_RECV_INTERLEAVED; the kernel takes the
+// row strides of data and scales (equal for interleaved rows) and the scale base.
 template <int Q, int NT, int KMAX, int CV, bool EXACT>
-hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out, hipStream_t s) {
-  size_t dq, sq;
-  row_bytes(Q, hidden, &dq, &sq);
-  const size_t scale_off = scale_offset(h.max_rows, dq, sq);
+hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out, int quant,
+                    hipStream_t s) {
+  const RecvGeom g = recv_geom(h.max_rows, hidden, quant);
+  const int64_t dq = g.data_stride, sq = g.scale_stride;
+  const size_t scale_off = g.scale_off;
   const int nvec = hidden / 8;                      // a multiple of 4 (hidden % 32 == 0)
   const int per_block = NT * CV;
   const int chunks = (nvec + per_block - 1) / per_block;
@@ -175,27 +178,29 @@ hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const floa
 }
 
 template <int Q>
-hipError_t launch_mode(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out,
+hipError_t launch_mode(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out, int quant,
                        hipStream_t s) {
   constexpr int NT = EP_COMBINE_THREADS, CV = EP_COMBINE_CV;
-  if (EP_COMBINE_KMAX_MIN <= 8 && h.num_topk == 8) return launch_q<Q, NT, 8, CV, true>(h, in, hidden, w, out, s);
-  if (EP_COMBINE_KMAX_MIN <= 8 && h.num_topk < 8) return launch_q<Q, NT, 8, CV, false>(h, in, hidden, w, out, s);
-  if (h.num_topk == kMaxTopk) return launch_q<Q, NT, kMaxTopk, CV, true>(h, in, hidden, w, out, s);
-  return launch_q<Q, NT, kMaxTopk, CV, false>(h, in, hidden, w, out, s);
+  if (EP_COMBINE_KMAX_MIN <= 8 && h.num_topk == 8)
+    return launch_q<Q, NT, 8, CV, true>(h, in, hidden, w, out, quant, s);
+  if (EP_COMBINE_KMAX_MIN <= 8 && h.num_topk < 8)
+    return launch_q<Q, NT, 8, CV, false>(h, in, hidden, w, out, quant, s);
+  if (h.num_topk == kMaxTopk) return launch_q<Q, NT, kMaxTopk, CV, true>(h, in, hidden, w, out, quant, s);
+  return launch_q<Q, NT, kMaxTopk, CV, false>(h, in, hidden, w, out, quant, s);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const float *w, void *out,
                           hipStream_t s) {
-  switch (quant) {
-    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE>(h, in, hidden, w, out, s);
-    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN>(h, in, hidden, w, out, s);
-    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128>(h, in, hidden, w, out, s);
-    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8>(h, in, hidden, w, out, s);
-    case EP_QUANT_FP8_B128_POW2: return launch_mode<EP_QUANT_FP8_B128_POW2>(h, in, hidden, w, out, s);
-    case EP_QUANT_FP8_B128_UE8M0: return launch_mode<EP_QUANT_FP8_B128_UE8M0>(h, in, hidden, w, out, s);
-    default: return launch_mode<EP_QUANT_MXFP4>(h, in, hidden, w, out, s);
+  switch (quant & kQuantMask) {
+    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE>(h, in, hidden, w, out, quant, s);
+    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN>(h, in, hidden, w, out, quant, s);
+    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128>(h, in, hidden, w, out, quant, s);
+    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8>(h, in, hidden, w, out, quant, s);
+    case EP_QUANT_FP8_B128_POW2: return launch_mode<EP_QUANT_FP8_B128_POW2>(h, in, hidden, w, out, quant, s);
+    case EP_QUANT_FP8_B128_UE8M0: return launch_mode<EP_QUANT_FP8_B128_UE8M0>(h, in, hidden, w, out, quant, s);
+    default: return launch_mode<EP_QUANT_MXFP4>(h, in, hidden, w, out, quant, s);
   }
 }
 

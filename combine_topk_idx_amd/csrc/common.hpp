@@ -46,6 +46,36 @@ __host__ __device__ inline size_t scale_offset(int64_t rows, size_t dq, size_t s
   return sq ? align_up((size_t)rows * dq, kScaleAlign) : (size_t)rows * dq;
 }
 
+// A quant argument is the mode in the low byte, possibly OR-ed with
+// EP_RECV_INTERLEAVED.
+constexpr int kQuantMask = 0xff;
+constexpr size_t kInterleavedRowAlign = 128;   // interleaved rows start on cache lines
+
+// Geometry of a receive buffer: byte strides of data rows and of scale rows,
+// where the scales start (the scale region, or inside each interleaved row),
+// and the total size.
+struct RecvGeom {
+  int64_t data_stride, scale_stride;
+  size_t scale_off, total;
+};
+__host__ inline RecvGeom recv_geom(int64_t rows, int hidden, int quant) {
+  size_t dq, sq;
+  row_bytes(quant & kQuantMask, hidden, &dq, &sq);
+  RecvGeom g;
+  if (quant & EP_RECV_INTERLEAVED) {
+    const size_t stride = align_up(dq + sq, kInterleavedRowAlign);
+    g.data_stride = g.scale_stride = (int64_t)stride;
+    g.scale_off = dq;
+    g.total = (size_t)rows * stride;
+  } else {
+    g.data_stride = (int64_t)dq;
+    g.scale_stride = (int64_t)sq;
+    g.scale_off = scale_offset(rows, dq, sq);
+    g.total = g.scale_off + (size_t)rows * sq;
+  }
+  return g;
+}
+
 // Makes a value opaque to the optimizer at this point (an empty asm that
 // claims to modify it).  Used (a) so that codes computed once are not
 // re-derived inside every per-row store branch and (b) so that a store built

@@ -349,12 +349,14 @@ hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *
   return hipGetLastError();
 }
 
+// `quant` is Q possibly OR-ed with EP_RECV_INTERLEAVED; the kernels take the
+// row strides of data and scales (equal for interleaved rows) and the scale base.
 template <int Q, bool WEIGHTED>
 hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const float *w, char *recv,
-                       float *recv_w, hipStream_t s) {
-  size_t dq, sq;
-  row_bytes(Q, hidden, &dq, &sq);
-  const size_t scale_off = scale_offset(h.max_rows, dq, sq);
+                       float *recv_w, int quant, hipStream_t s) {
+  const RecvGeom g = recv_geom(h.max_rows, hidden, quant);
+  const int64_t dq = g.data_stride, sq = g.scale_stride;
+  const size_t scale_off = g.scale_off;
   const int nvec = hidden / 8;
   if constexpr (Q == EP_QUANT_INT8_TOKEN) {
     // the whole row must sit in one workgroup (its amax is a row reduction)
@@ -377,17 +379,17 @@ hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const fl
 template <bool WEIGHTED>
 hipError_t launch_any(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant, char *recv,
                       float *recv_w, hipStream_t s) {
-  switch (quant) {
-    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
-    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
-    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
-    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
-    case EP_QUANT_FP8_B128_POW2:
-      return launch_mode<EP_QUANT_FP8_B128_POW2, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
-    case EP_QUANT_FP8_B128_UE8M0:
-      return launch_mode<EP_QUANT_FP8_B128_UE8M0, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
-    default: return launch_mode<EP_QUANT_MXFP4, WEIGHTED>(h, x, hidden, w, recv, recv_w, s);
+#define EP_MODE(QQ) launch_mode<QQ, WEIGHTED>(h, x, hidden, w, recv, recv_w, quant, s)
+  switch (quant & kQuantMask) {
+    case EP_QUANT_NONE: return EP_MODE(EP_QUANT_NONE);
+    case EP_QUANT_INT8_TOKEN: return EP_MODE(EP_QUANT_INT8_TOKEN);
+    case EP_QUANT_FP8_B128: return EP_MODE(EP_QUANT_FP8_B128);
+    case EP_QUANT_MXFP8: return EP_MODE(EP_QUANT_MXFP8);
+    case EP_QUANT_FP8_B128_POW2: return EP_MODE(EP_QUANT_FP8_B128_POW2);
+    case EP_QUANT_FP8_B128_UE8M0: return EP_MODE(EP_QUANT_FP8_B128_UE8M0);
+    default: return EP_MODE(EP_QUANT_MXFP4);
   }
+#undef EP_MODE
 }
 
 }  // namespace

@@ -32,7 +32,11 @@ ep_status_t hip_fail(hipError_t e, const char *where) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool valid_quant(int q) { return q >= EP_QUANT_NONE && q <= EP_QUANT_FP8_B128_UE8M0; }
+bool valid_quant(int q) {
+  const int mode = q & ep::kQuantMask;
+  return (q & ~(ep::kQuantMask | EP_RECV_INTERLEAVED)) == 0 && mode >= EP_QUANT_NONE &&
+         mode <= EP_QUANT_FP8_B128_UE8M0;
+}
 
 constexpr int32_t kMaxHidden = 65536;
 
@@ -41,7 +45,7 @@ ep_status_t check_hidden(int32_t hidden, int quant, const char *fn) {
   if (hidden <= 0 || hidden % 32 != 0)
     return fail(EP_ERR_INVALID_ARG, "%s: hidden must be a positive multiple of 32 (got %d)", fn, hidden);
   if (hidden > kMaxHidden) return fail(EP_ERR_UNSUPPORTED, "%s: hidden %d exceeds %d", fn, hidden, kMaxHidden);
-  if (ep::is_b128(quant) && hidden % 128 != 0)
+  if (ep::is_b128(quant & ep::kQuantMask) && hidden % 128 != 0)
     return fail(EP_ERR_INVALID_ARG, "%s: per-128 e4m3 needs hidden %% 128 == 0 (got %d)", fn, hidden);
   return EP_OK;
 }
@@ -60,11 +64,9 @@ ep_status_t check_handle(const ep_handle_t *h, const char *fn) {
 }
 
 size_t buffer_bytes(int64_t rows, int32_t hidden, int quant, size_t *scale_off) {
-  size_t dq, sq;
-  ep::row_bytes(quant, hidden, &dq, &sq);
-  const size_t off = ep::scale_offset(rows, dq, sq);
-  if (scale_off) *scale_off = off;
-  return off + (size_t)rows * sq;
+  const ep::RecvGeom g = ep::recv_geom(rows, hidden, quant);
+  if (scale_off) *scale_off = g.scale_off;
+  return g.total;
 }
 
 }  // namespace

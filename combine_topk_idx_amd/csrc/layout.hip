@@ -24,7 +24,8 @@
 // pair get row_src -1.
 //
 // Small problems (pairs <= 4096) run in one workgroup that also does the scan
-// over experts and writes every output: one launch.  (All of its waves share
+// over experts and writes every output: one launch (padded arrangements with
+// many rows add workgroups that only clear free rows).  (All of its waves share
 // one CU, so its cost grows by about a microsecond per 64-pair step of a
 // wave; past 4096 pairs two launches are faster.)  Larger ones run in two
 // launches over 2048-pair chunks: rank (per-chunk counts and ranks), then
@@ -44,6 +45,7 @@ constexpr int kMultiChunk = kMultiItems * kThreads;
 constexpr int64_t kSingleMaxPairs = (int64_t)kSingleItems * kThreads;
 constexpr int64_t kSingleMaxRows = 65536;          // single workgroup also clears row_src tail
 constexpr int kMaxFillBlocks = 512;                // finalize workgroups beyond the chunk count
+constexpr int kHelperRows = 2048;                  // rows per clearing helper of the single-workgroup path
 
 // Expert of an id, or -1 for -1 / ids outside [-1, E) (which set `bad`).
 template <typename IdxT>
@@ -61,29 +63,24 @@ __device__ __forceinline__ int block_rows(int c, int align, int cap) {
 
 // -1 into row_src for every row that holds no pair.  This thread is number
 // `first` of `step` (both multiples of the wave size apart).  offs[e] (block
-// start) and kept[e] (pairs the block holds) are in LDS.
-//   capacity C: row r is in block r / C; it is free past the kept pairs;
-//   aligned:    rows at or past nrows, and fewer than `align` rows after the
-//               pairs of each block (one wave per block);
-//   compact:    only rows at or past nrows.
+// start) and kept[e] (pairs the block holds) are in LDS.  Free rows are the
+// rows at or past nrows (compact and aligned arrangements) and the end of
+// every padded block, [offs[e] + kept[e], block end): each such tail is
+// walked by a wave (by S waves together when there are S times more waves
+// than experts), so no row has to search for its block.
 __device__ __forceinline__ void clear_free_rows(int *__restrict__ row_src, int first, int step, int max_rows,
                                                 int nrows, int E, int align, int cap, const int *offs,
                                                 const int *kept) {
-  if (cap > 0) {
-    for (int r = first; r < max_rows; r += step) {
-      const int e = (int)((unsigned)r / (unsigned)cap);
-      if (r - e * cap >= kept[e]) row_src[r] = -1;
-    }
-    return;
-  }
   for (int r = nrows + first; r < max_rows; r += step) row_src[r] = -1;
-  if (align > 1) {
-    const int lane = first & (kWave - 1);
-    for (int e = first / kWave; e < E; e += step / kWave) {
-      const int lo = offs[e] + kept[e];
-      const int hi = offs[e] + block_rows(kept[e], align, 0);
-      for (int r = lo + lane; r < hi; r += kWave) row_src[r] = -1;
-    }
+  if (align <= 1 && cap <= 0) return;
+  const int lane = first & (kWave - 1);
+  const int nw = step / kWave, gw = first / kWave;
+  const int S = nw > E ? nw / E : 1;
+  for (int u = gw; u < E * S; u += nw) {
+    const int e = u / S, part = u - e * S;
+    const int lo = offs[e] + kept[e];
+    const int hi = offs[e] + (cap > 0 ? cap : block_rows(kept[e], align, 0));
+    for (int r = lo + part * kWave + lane; r < hi; r += S * kWave) row_src[r] = -1;
   }
 }
 
@@ -190,6 +187,31 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
   __shared__ int kept[kMaxExperts];
   __shared__ int wsum[kWaves];
   __shared__ uint32_t sbad;
+  if (blockIdx.x > 0) {
+    // helper workgroups (padded arrangements with many rows): recount the
+    // experts with LDS atomics (order-free, so the same counts as workgroup
+    // 0), redo the scan over blocks and clear a share of the free rows --
+    // one workgroup alone is limited by the stores it can keep in flight
+    for (int e = threadIdx.x; e < E; e += kThreads) total[e] = 0;
+    __syncthreads();
+    bool ignored = false;
+    for (int f = threadIdx.x; f < n; f += kThreads) {
+      const int e = expert_of(idx[f], E, ignored);
+      if (e >= 0) atomicAdd(&total[e], 1);
+    }
+    __syncthreads();
+    const int c = threadIdx.x < E ? total[threadIdx.x] : 0;
+    int nrows;
+    const int pre = block_exclusive_scan(threadIdx.x < E ? block_rows(c, align, cap) : 0, wsum, nrows);
+    if (threadIdx.x < E) {
+      excl[threadIdx.x] = pre;
+      kept[threadIdx.x] = cap > 0 ? min(c, cap) : c;
+    }
+    __syncthreads();
+    clear_free_rows(row_src, (blockIdx.x - 1) * kThreads + threadIdx.x, (gridDim.x - 1) * kThreads, max_rows,
+                    nrows, E, align, cap, excl, kept);
+    return;
+  }
   if (threadIdx.x == 0) sbad = 0;
 
   const int nbits = 32 - __builtin_clz((unsigned)E);   // keys 0..E
@@ -232,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void layout_single_kernel(
       slot[f] = -1;
     }
   }
-  clear_free_rows(row_src, threadIdx.x, kThreads, max_rows, nrows, E, align, cap, excl, kept);
+  if (gridDim.x == 1) clear_free_rows(row_src, threadIdx.x, kThreads, max_rows, nrows, E, align, cap, excl, kept);
   if (threadIdx.x == 0) *status = sbad;
 }
 
@@ -395,8 +417,12 @@ hipError_t launch_typed(const IdxT *idx, int n, int32_t E, int max_rows, int ali
   int *row_src = (int *)(ws + wl.row_src);
   uint32_t *status = (uint32_t *)(ws + wl.status);
   if (n <= kSingleMaxPairs && max_rows <= kSingleMaxRows) {
-    hipLaunchKernelGGL(layout_single_kernel<IdxT>, dim3(1), dim3(kThreads), 0, s, idx, n, E, max_rows, align, cap,
-                       recv_count, cum, offsets, slot, row_src, status);
+    // padded arrangements with many rows add helper workgroups that clear
+    // the free rows (about kHelperRows rows each)
+    const bool padded = align > 1 || cap > 0;
+    const int helpers = padded && max_rows > kHelperRows ? (max_rows + kHelperRows - 1) / kHelperRows : 0;
+    hipLaunchKernelGGL(layout_single_kernel<IdxT>, dim3(1 + helpers), dim3(kThreads), 0, s, idx, n, E, max_rows,
+                       align, cap, recv_count, cum, offsets, slot, row_src, status);
     return hipGetLastError();
   }
   int *hist = (int *)(ws + wl.hist);

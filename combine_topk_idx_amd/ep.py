@@ -34,6 +34,7 @@ EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_BUFFER_TOO_SMALL, EP_ERR_H
 EP_IDX_INT32, EP_IDX_INT64 = 0, 1
 QUANT = {"none": 0, "int8_token": 1, "fp8_b128": 2, "mxfp8": 3, "mxfp4": 4, "fp8_b128_pow2": 5,
          "fp8_b128_ue8m0": 6}
+EP_RECV_INTERLEAVED = 0x100
 EP_STATUS_ID_OUT_OF_RANGE = 1
 EP_STATUS_CAPACITY_OVERFLOW = 2
 
@@ -122,8 +123,9 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _quant(q) -> int:
-    return QUANT[q] if isinstance(q, str) else int(q)
+def _quant(q, interleaved: bool = False) -> int:
+    v = QUANT[q] if isinstance(q, str) else int(q)
+    return v | EP_RECV_INTERLEAVED if interleaved else v
 
 
 def _nbytes(t) -> int:
@@ -157,10 +159,11 @@ def ep_layout_rows(num_max_dispatch_tokens: int, num_topk: int, num_experts: int
     return _lib.ep_layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity)
 
 
-def ep_buffer_bytes(rows: int, hidden: int, quant) -> tuple[int, int]:
-    """(total bytes, scale-region offset)."""
+def ep_buffer_bytes(rows: int, hidden: int, quant, interleaved: bool = False) -> tuple[int, int]:
+    """(total bytes, scale offset): the scale region's start, or for
+    interleaved rows the scales' offset inside a row."""
     total, off = _sz(0), _sz(0)
-    _check(_lib.ep_buffer_bytes(rows, hidden, _quant(quant), ctypes.byref(total), ctypes.byref(off)))
+    _check(_lib.ep_buffer_bytes(rows, hidden, _quant(quant, interleaved), ctypes.byref(total), ctypes.byref(off)))
     return total.value, off.value
 
 
@@ -205,24 +208,24 @@ def ep_layout_ex(topk_idx, num_experts: int, num_max_dispatch_tokens: int, row_a
 
 
 def ep_dispatch(handle: ep_handle_t, x, hidden: int, quant, recv_buf, topk_weights=None,
-                recv_weights=None, *, recv_buf_bytes=None, stream=None) -> None:
+                recv_weights=None, *, recv_buf_bytes=None, interleaved=False, stream=None) -> None:
     nbytes = _nbytes(recv_buf) if recv_buf_bytes is None else recv_buf_bytes
-    _check(_lib.ep_dispatch(ctypes.byref(handle), _ptr(x), hidden, _ptr(topk_weights), _quant(quant),
+    _check(_lib.ep_dispatch(ctypes.byref(handle), _ptr(x), hidden, _ptr(topk_weights), _quant(quant, interleaved),
                             _ptr(recv_buf), nbytes, _ptr(recv_weights), _stream(stream)))
 
 
 def ep_combine(handle: ep_handle_t, expert_out, in_quant, hidden: int, topk_weights, out, *,
-               expert_out_bytes=None, stream=None) -> None:
+               expert_out_bytes=None, interleaved=False, stream=None) -> None:
     nbytes = _nbytes(expert_out) if expert_out_bytes is None else expert_out_bytes
-    _check(_lib.ep_combine(ctypes.byref(handle), _ptr(expert_out), nbytes, _quant(in_quant), hidden,
+    _check(_lib.ep_combine(ctypes.byref(handle), _ptr(expert_out), nbytes, _quant(in_quant, interleaved), hidden,
                            _ptr(topk_weights), _ptr(out), _stream(stream)))
 
 
 def ep_combine_backward(handle: ep_handle_t, grad_out, hidden: int, quant, grad_buf, topk_weights=None, *,
-                        grad_buf_bytes=None, stream=None) -> None:
+                        grad_buf_bytes=None, interleaved=False, stream=None) -> None:
     nbytes = _nbytes(grad_buf) if grad_buf_bytes is None else grad_buf_bytes
     _check(_lib.ep_combine_backward(ctypes.byref(handle), _ptr(grad_out), hidden, _ptr(topk_weights),
-                                    _quant(quant), _ptr(grad_buf), nbytes, _stream(stream)))
+                                    _quant(quant, interleaved), _ptr(grad_buf), nbytes, _stream(stream)))
 
 
 def ep_read_status(handle: ep_handle_t, stream=None) -> int:

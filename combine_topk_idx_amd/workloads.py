@@ -57,6 +57,7 @@ class Workload:
     num_max_tokens: int = 0         # 0 -> T
     row_align: int = 1              # > 1: expert blocks start at multiples of it
     expert_capacity: int = 0        # > 0: every expert block has this many rows
+    interleaved: bool = False       # receive rows hold data then scales
 
     @property
     def t_max(self) -> int:

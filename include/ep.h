@@ -44,6 +44,11 @@
  *   EP_QUANT_FP8_B128_UE8M0 Dq = H (e4m3fn)         Sq = H/128 (e8m0 bytes)
  *   EP_QUANT_MXFP4       Dq = H/2 (e2m1, element 2i in the low nibble)
  *                                                   Sq = H/32 (e8m0 bytes)
+ * Interleaved form (quant OR-ed with EP_RECV_INTERLEAVED): row r starts at
+ * byte r * align_up(Dq + Sq, 128) (rows on 128-byte cache lines) and holds its
+ * Dq data bytes, then its Sq scale bytes, then padding -- the per-token message of "DeepEP FP8 Dispatch
+ * and Combine Operations", Message Transmission via IBGDA (the payload
+ * followed by its scales).
  * Expert e owns rows [offsets[e], offsets[e] + recv_count[e]); rows of one
  * expert are in ascending (token, j) order.  Rows that hold no pair (rows at
  * or past offsets[E], the padding of aligned or capacity-padded blocks) and
@@ -91,6 +96,12 @@ typedef enum {
   EP_QUANT_FP8_B128_UE8M0 = 6  /* e4m3fn, power-of-two e8m0 scale per 128        */
 } ep_quant_t;
 
+/* Receive-format flag OR-ed into the quant argument of ep_buffer_bytes,
+ * ep_dispatch, ep_combine and ep_combine_backward (C++ callers cast the
+ * result back to ep_quant_t): rows in the interleaved form above.  No other
+ * bits above the low byte are accepted. */
+#define EP_RECV_INTERLEAVED 0x100
+
 /* Layout handle ("Low-Latency Mode API": the handle returned by dispatch is
  * passed unchanged to combine).  Plain data filled in by ep_layout; its
  * pointers point into the caller's workspace and stay valid while that
@@ -135,8 +146,9 @@ size_t ep_workspace_bytes_ex(int64_t num_max_dispatch_tokens, int32_t num_topk, 
                              int32_t row_align, int32_t expert_capacity);
 
 /* Size of a receive buffer of `rows` rows (format above): writes the total
- * byte count and the scale-region offset to the host pointers (either may be
- * NULL).  Host-only. */
+ * byte count and the scale offset to the host pointers (either may be NULL):
+ * the start of the scale region, or for the interleaved form the offset of
+ * the scales inside each row (Dq).  Host-only. */
 ep_status_t ep_buffer_bytes(int64_t rows, int32_t hidden, ep_quant_t quant, size_t *total_bytes,
                             size_t *scale_offset);
 

@@ -91,15 +91,16 @@ def run_path(ep, w: W.Workload, inp: dict, *, expert_out: np.ndarray | None = No
     h, ws, recv_count = run_layout(ep, w, inp["topk_idx"])
     x = to_dev(inp["x"])
     wts = to_dev(inp["topk_weights"])
-    total, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    total, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode, w.interleaved)
     recv = canary_buffer(total)
     recv_w = torch.full((max(w.max_rows, 1),), float("nan"), device=DEV) if with_recv_weights else None
-    ep.ep_dispatch(h, x, w.H, w.mode, recv, wts if with_recv_weights else None, recv_w)
+    ep.ep_dispatch(h, x, w.H, w.mode, recv, wts if with_recv_weights else None, recv_w, interleaved=w.interleaved)
     lay = read_layout(ep, h, ws, recv_count, w)
     out = None
     if do_combine:
+        il = False
         if w.combine_input == "identity":
-            src, q = recv, w.mode
+            src, q, il = recv, w.mode, w.interleaved
         elif w.combine_input == "scaled_dispatch":
             assert w.mode == "none"
             rows = recv[: w.max_rows * w.H * 2].view(torch.bfloat16)
@@ -112,7 +113,7 @@ def run_path(ep, w: W.Workload, inp: dict, *, expert_out: np.ndarray | None = No
             y[lay["row_src"] < 0] = NAN_BF16             # rows holding no pair: canaries
             src, q = to_dev(y).view(torch.uint8).reshape(-1), "none"
         o = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
-        ep.ep_combine(h, src, q, w.H, wts, o)
+        ep.ep_combine(h, src, q, w.H, wts, o, interleaved=il)
         torch.cuda.synchronize()
         out = bf16_bits(o)
     return HipRun(h, ws, lay["recv_count"], lay["offsets"], lay["slot"], lay["row_src"], lay["status"],
@@ -123,10 +124,18 @@ def recv_rows(ep, run: HipRun, w: W.Workload, rows=None):
     """(data [n, Dq], scales [n, Sq]) of the HIP receive buffer (numpy)."""
     from oracle import quant as Q   # row sizes only
     dq, sq = Q.row_bytes(w.mode, w.H)
-    _, off = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    total, off = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode, w.interleaved)
     buf = run.recv
-    data = buf[: w.max_rows * dq].view(w.max_rows, dq)
     n = w.max_rows
+    if w.interleaved:
+        stride = total // max(w.max_rows, 1)
+        rowsv = buf[: w.max_rows * stride].view(w.max_rows, stride)
+        if rows is not None:
+            rowsv = rowsv.index_select(0, torch.as_tensor(np.asarray(rows, np.int64), device=DEV))
+            n = len(rows)
+        r = rowsv.cpu().numpy()
+        return r[:, :dq].copy(), r[:, off:off + sq].copy()
+    data = buf[: w.max_rows * dq].view(w.max_rows, dq)
     if rows is not None:
         idx = torch.as_tensor(np.asarray(rows, np.int64), device=DEV)
         data = data.index_select(0, idx)

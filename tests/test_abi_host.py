@@ -219,6 +219,21 @@ def test_buffer_bytes_matches_oracle(ep, hidden, mode, rows):
     assert ep.ep_buffer_bytes(rows, hidden, mode) == OD.buffer_bytes(rows, hidden, mode)
 
 
+@pytest.mark.parametrize("hidden,mode", [(32, "none"), (7168, "int8_token"), (64, "int8_token"),
+                                         (7168, "fp8_b128"), (96, "mxfp8"), (7168, "mxfp4"),
+                                         (384, "fp8_b128_ue8m0"), (7168, "fp8_b128_pow2")])
+@pytest.mark.parametrize("rows", [0, 1, 37, 131072])
+def test_interleaved_buffer_bytes_matches_oracle(ep, hidden, mode, rows):
+    assert ep.ep_buffer_bytes(rows, hidden, mode, interleaved=True) == OD.buffer_bytes(rows, hidden, mode, True)
+
+
+def test_quant_flag_bits_rejected(ep):
+    for bad in (0x200, 0x101 | 0x400, 0x107):
+        with pytest.raises(ep.EpError) as e:
+            ep.ep_buffer_bytes(4, 256, bad)
+        assert e.value.code == 1
+
+
 def test_buffer_bytes_rejects(ep):
     with pytest.raises(ep.EpError) as e:
         ep.ep_buffer_bytes(10, 100, "none")
