@@ -196,3 +196,72 @@ def with_duplicates(idx: np.ndarray, seed: int, frac: float = 0.2) -> np.ndarray
 
 def scaled(w: Workload, **kw) -> Workload:
     return replace(w, **kw)
+
+
+# ---------------------------------------------------------------------------
+# expert MLP (fused MoE) workloads: one GPU's share of an expert-parallel group
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class MoeWorkload:
+    """T tokens routed top-k over E_total experts, of which this GPU owns the
+    first E_local; pairs routed elsewhere are -1 in the local ids.  Expert
+    MLP: hidden H, intermediate I (W1 [E_local, 2I, H], W2 [E_local, H, I],
+    MXFP8)."""
+    name: str
+    T: int
+    H: int
+    I: int
+    E_total: int
+    E_local: int
+    k: int
+    seed: int
+    idx_dtype: str = "int64"
+
+    @property
+    def max_rows(self) -> int:
+        return self.T * self.k
+
+
+MOE_WORKLOADS = {
+    # the 128-tokens-per-device point of the fused-MoE benchmark: 8 ranks x 128
+    # tokens, 6 experts per device (48 in all), top-6, hidden 7168, inter 3072
+    "moe_share": MoeWorkload("moe_share", 1024, 7168, 3072, 48, 6, 6, seed=1021),
+    "moe_small": MoeWorkload("moe_small", 96, 512, 256, 12, 4, 3, seed=1022),
+}
+
+
+def make_mx_weights(seed: int, E: int, N: int, K: int):
+    """Synthetic MXFP8 weights drawn directly as codes and scale bytes:
+    codes [E, N, K] uint8 (random sign, e4m3 exponent field 4..8 weighted
+    towards 6, uniform mantissa: magnitudes 0.125 .. 3.75, never NaN) and e8m0 scale bytes
+    [E, N, K/32] around 2**-round(log2(K)/2) (+-1), so a dot product over K
+    stays of order one."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77, E, N, K])))
+    # one random byte per code: bit 7 the sign, bits 0-2 the mantissa; a
+    # second byte picks the exponent field 4..8 with weights 26/51/90/64/25 of 256
+    lut = np.repeat(np.arange(4, 9, dtype=np.uint8), [26, 51, 90, 64, 25])
+    b = g.integers(0, 256, size=(E, N, K), dtype=np.uint8)
+    e = lut[g.integers(0, 256, size=(E, N, K), dtype=np.uint8)]
+    codes = (b & np.uint8(0x87)) | (e << np.uint8(3))
+    base = 127 - int(round(np.log2(K) / 2))
+    scales = (base - 1 + g.integers(0, 3, size=(E, N, K // 32))).astype(np.uint8)
+    return codes, scales
+
+
+def make_moe_inputs(w: MoeWorkload) -> dict:
+    """x (bf16 patterns [T, H]), global ids [T, k] (uniform k-subsets of
+    E_total), local ids (the global id if it is one of this GPU's experts,
+    else -1), topk_weights (float32 softmax over k), and W1 / W2 codes and
+    scale bytes."""
+    rx, ri, rw, _ = _streams(w.seed)
+    x = _draw_x(rx, w.T, w.H, 0.0)
+    gid = np.argsort(ri.random((w.T, w.E_total)), axis=1)[:, :w.k].astype(np.int64)
+    lid = np.where(gid < w.E_local, gid, -1)
+    dt = np.int32 if w.idx_dtype == "int32" else np.int64
+    w1c, w1s = make_mx_weights(w.seed, w.E_local, 2 * w.I, w.H)
+    w2c, w2s = make_mx_weights(w.seed + 1, w.E_local, w.H, w.I)
+    return {"x": x, "global_idx": gid.astype(dt), "topk_idx": lid.astype(dt),
+            "topk_weights": _draw_weights(rw, w.T, w.k),
+            "w1_codes": w1c, "w1_scales": w1s, "w2_codes": w2c, "w2_scales": w2s}

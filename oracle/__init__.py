@@ -33,12 +33,14 @@ Modules:
 * ``combine``  -- gather, dequantise, fp32 weighted sum in top-k order.
 * ``backward`` -- combine's gradient with respect to the expert rows, as a
   reverse dispatch.
+* ``moe``      -- the expert MLP between dispatch and combine (GMM1, SwiGLU,
+  MXFP8 requant, GMM2).
 * ``validate`` -- the argument rules the C ABI enforces before any launch.
 
 Parity status of every function is listed in each module's header.
 """
 
-from . import codecs, quant, layout, dispatch, combine, backward, validate  # noqa: F401
+from . import codecs, quant, layout, dispatch, combine, backward, validate, moe  # noqa: F401
 from .layout import Layout  # noqa: F401
 
 QUANT_MODES = ("none", "int8_token", "fp8_b128", "mxfp8", "mxfp4", "fp8_b128_pow2", "fp8_b128_ue8m0")

@@ -195,7 +195,12 @@ def mx_shared_exponent(amax: np.float32, emax: int) -> int:
 
 
 def _quant_mx(x_bits: np.ndarray, emax: int, vmax: float, encode):
-    x = codecs.bf16_bits_to_f32(x_bits)
+    return _quant_mx_values(codecs.bf16_bits_to_f32(x_bits), emax, vmax, encode)
+
+
+def _quant_mx_values(x: np.ndarray, emax: int, vmax: float, encode):
+    """The MX rule on a float32 row (length a multiple of 32)."""
+    x = np.asarray(x, dtype=np.float32)
     H = x.shape[0]
     codes = np.empty(H, np.uint8)
     scale_bytes = np.empty(H // 32, np.uint8)
@@ -213,6 +218,15 @@ def _quant_mx(x_bits: np.ndarray, emax: int, vmax: float, encode):
 def quant_mxfp8(x_bits: np.ndarray):
     """One bf16 row -> (e4m3 codes [H] uint8, e8m0 scale bytes [H/32])."""
     return _quant_mx(x_bits, 8, codecs.E4M3_MAX, codecs.e4m3_encode)
+
+
+def quant_mxfp8_f32(x_f32: np.ndarray):
+    """One float32 row -> (e4m3 codes uint8, e8m0 scale bytes per 32): the
+    MXFP8 rule of ``quant_mxfp8`` applied to float32 values (the requant of
+    an activation that is not bf16)."""
+    if not np.all(np.isfinite(np.asarray(x_f32, np.float32))):
+        raise ValueError("MX quantisation needs finite input")
+    return _quant_mx_values(x_f32, 8, codecs.E4M3_MAX, codecs.e4m3_encode)
 
 
 def quant_mxfp4(x_bits: np.ndarray):
