@@ -23,7 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libep.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "ep_api.cpp"]
+SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "moe.hip", "ep_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -150,4 +150,10 @@ hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int h
 hipError_t launch_combine_backward(const ep_handle_t &h, const void *grad, int hidden, const float *w, int quant,
                                    char *buf, hipStream_t s);
 
+hipError_t launch_moe_gmm1(const ep_handle_t &h, const int64_t *recv_count, const char *x_buf, int hidden, int inter,
+                           const void *w1, const void *w1_scales, int out_quant, char *out_buf, hipStream_t s);
+
+hipError_t launch_moe_gmm2(const ep_handle_t &h, const int64_t *recv_count, const char *a_buf, int inter, int hidden,
+                           const void *w2, const void *w2_scales, char *out_buf, hipStream_t s);
+
 }  // namespace ep

@@ -266,6 +266,60 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
   return EP_OK;
 }
 
+ep_status_t ep_moe_gmm1(const ep_handle_t *handle, const int64_t *recv_count, const void *x_buf, size_t x_buf_bytes,
+                        int32_t hidden, int32_t inter, const void *w1, const void *w1_scales, ep_quant_t out_quant,
+                        void *out_buf, size_t out_buf_bytes, void *stream) {
+  const char *fn = "ep_moe_gmm1";
+  ep_status_t st = check_handle(handle, fn);
+  if (st != EP_OK) return st;
+  if (hidden <= 0 || hidden % 64 != 0 || inter <= 0 || inter % 64 != 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: hidden and inter must be positive multiples of 64 (got %d, %d)", fn, hidden,
+                inter);
+  if (hidden > kMaxHidden || inter > kMaxHidden)
+    return fail(EP_ERR_UNSUPPORTED, "%s: hidden / inter above %d", fn, kMaxHidden);
+  if (out_quant != EP_QUANT_MXFP8 && out_quant != EP_QUANT_NONE)
+    return fail(EP_ERR_INVALID_ARG, "%s: out_quant must be EP_QUANT_MXFP8 or EP_QUANT_NONE", fn);
+  if (!x_buf || !aligned(x_buf, 16) || !out_buf || !aligned(out_buf, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: x_buf / out_buf NULL or not 16-byte aligned", fn);
+  if (!w1 || !w1_scales || !aligned(w1, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: w1 NULL or not 16-byte aligned, or w1_scales NULL", fn);
+  if (recv_count && !aligned(recv_count, 8)) return fail(EP_ERR_INVALID_ARG, "%s: recv_count misaligned", fn);
+  const size_t need_x = buffer_bytes(handle->max_rows, hidden, EP_QUANT_MXFP8, nullptr);
+  const size_t need_o = buffer_bytes(handle->max_rows, inter, out_quant, nullptr);
+  if (x_buf_bytes < need_x || out_buf_bytes < need_o)
+    return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: x_buf needs %zu bytes, out_buf %zu", fn, need_x, need_o);
+  const hipError_t e = ep::launch_moe_gmm1(*handle, recv_count, (const char *)x_buf, hidden, inter, w1, w1_scales,
+                                           out_quant, (char *)out_buf, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return EP_OK;
+}
+
+ep_status_t ep_moe_gmm2(const ep_handle_t *handle, const int64_t *recv_count, const void *a_buf, size_t a_buf_bytes,
+                        int32_t inter, int32_t hidden, const void *w2, const void *w2_scales, void *out_buf,
+                        size_t out_buf_bytes, void *stream) {
+  const char *fn = "ep_moe_gmm2";
+  ep_status_t st = check_handle(handle, fn);
+  if (st != EP_OK) return st;
+  if (inter <= 0 || inter % 64 != 0 || hidden <= 0 || hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: inter must be a positive multiple of 64 and hidden of 128 (got %d, %d)", fn,
+                inter, hidden);
+  if (hidden > kMaxHidden || inter > kMaxHidden)
+    return fail(EP_ERR_UNSUPPORTED, "%s: hidden / inter above %d", fn, kMaxHidden);
+  if (!a_buf || !aligned(a_buf, 16) || !out_buf || !aligned(out_buf, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: a_buf / out_buf NULL or not 16-byte aligned", fn);
+  if (!w2 || !w2_scales || !aligned(w2, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: w2 NULL or not 16-byte aligned, or w2_scales NULL", fn);
+  if (recv_count && !aligned(recv_count, 8)) return fail(EP_ERR_INVALID_ARG, "%s: recv_count misaligned", fn);
+  const size_t need_a = buffer_bytes(handle->max_rows, inter, EP_QUANT_MXFP8, nullptr);
+  const size_t need_o = buffer_bytes(handle->max_rows, hidden, EP_QUANT_NONE, nullptr);
+  if (a_buf_bytes < need_a || out_buf_bytes < need_o)
+    return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: a_buf needs %zu bytes, out_buf %zu", fn, need_a, need_o);
+  const hipError_t e = ep::launch_moe_gmm2(*handle, recv_count, (const char *)a_buf, inter, hidden, w2, w2_scales,
+                                           (char *)out_buf, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return EP_OK;
+}
+
 ep_status_t ep_read_status(const ep_handle_t *handle, uint32_t *flags, void *stream) {
   const char *fn = "ep_read_status";
   if (!handle || !handle->status) return fail(EP_ERR_INVALID_ARG, "%s: handle is NULL", fn);

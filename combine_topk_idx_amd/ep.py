@@ -2,7 +2,8 @@
 
 The functions ``ep_workspace_bytes``, ``ep_workspace_bytes_ex``,
 ``ep_layout_rows``, ``ep_buffer_bytes``, ``ep_layout``, ``ep_layout_ex``,
-``ep_dispatch``, ``ep_combine``, ``ep_combine_backward``, ``ep_read_status``,
+``ep_dispatch``, ``ep_combine``, ``ep_combine_backward``, ``ep_moe_gmm1``,
+``ep_moe_gmm2``, ``ep_read_status``,
 ``ep_last_error`` and ``ep_abi_version`` have the names and arguments of the C ABI in
 ``include/ep.h``; torch tensors stand in for device pointers and torch's
 current stream is used unless one is passed.  Every computation runs in the
@@ -39,8 +40,8 @@ EP_STATUS_ID_OUT_OF_RANGE = 1
 EP_STATUS_CAPACITY_OVERFLOW = 2
 
 SYMBOLS = ("ep_workspace_bytes", "ep_workspace_bytes_ex", "ep_layout_rows", "ep_buffer_bytes", "ep_layout",
-           "ep_layout_ex", "ep_dispatch", "ep_combine", "ep_combine_backward", "ep_read_status", "ep_last_error",
-           "ep_abi_version")
+           "ep_layout_ex", "ep_dispatch", "ep_combine", "ep_combine_backward", "ep_moe_gmm1", "ep_moe_gmm2",
+           "ep_read_status", "ep_last_error", "ep_abi_version")
 
 
 class ep_handle_t(ctypes.Structure):
@@ -80,6 +81,11 @@ _lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int,
 _lib.ep_combine.restype = ctypes.c_int
 _lib.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp]
 _lib.ep_combine_backward.restype = ctypes.c_int
+_lib.ep_moe_gmm1.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _vp, _sz, _i32, _i32, _vp, _vp, ctypes.c_int, _vp,
+                             _sz, _vp]
+_lib.ep_moe_gmm1.restype = ctypes.c_int
+_lib.ep_moe_gmm2.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _vp, _sz, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.ep_moe_gmm2.restype = ctypes.c_int
 _lib.ep_read_status.argtypes = [ctypes.POINTER(ep_handle_t), ctypes.POINTER(ctypes.c_uint32), _vp]
 _lib.ep_read_status.restype = ctypes.c_int
 _lib.ep_last_error.argtypes = []
@@ -226,6 +232,22 @@ def ep_combine_backward(handle: ep_handle_t, grad_out, hidden: int, quant, grad_
     nbytes = _nbytes(grad_buf) if grad_buf_bytes is None else grad_buf_bytes
     _check(_lib.ep_combine_backward(ctypes.byref(handle), _ptr(grad_out), hidden, _ptr(topk_weights),
                                     _quant(quant, interleaved), _ptr(grad_buf), nbytes, _stream(stream)))
+
+
+def ep_moe_gmm1(handle: ep_handle_t, x_buf, hidden: int, inter: int, w1, w1_scales, out_quant, out_buf, *,
+                recv_count=None, x_buf_bytes=None, out_buf_bytes=None, stream=None) -> None:
+    _check(_lib.ep_moe_gmm1(ctypes.byref(handle), _ptr(recv_count), _ptr(x_buf),
+                            _nbytes(x_buf) if x_buf_bytes is None else x_buf_bytes, hidden, inter, _ptr(w1),
+                            _ptr(w1_scales), _quant(out_quant), _ptr(out_buf),
+                            _nbytes(out_buf) if out_buf_bytes is None else out_buf_bytes, _stream(stream)))
+
+
+def ep_moe_gmm2(handle: ep_handle_t, a_buf, inter: int, hidden: int, w2, w2_scales, out_buf, *,
+                recv_count=None, a_buf_bytes=None, out_buf_bytes=None, stream=None) -> None:
+    _check(_lib.ep_moe_gmm2(ctypes.byref(handle), _ptr(recv_count), _ptr(a_buf),
+                            _nbytes(a_buf) if a_buf_bytes is None else a_buf_bytes, inter, hidden, _ptr(w2),
+                            _ptr(w2_scales), _ptr(out_buf), _nbytes(out_buf) if out_buf_bytes is None else out_buf_bytes,
+                            _stream(stream)))
 
 
 def ep_read_status(handle: ep_handle_t, stream=None) -> int:

@@ -250,6 +250,42 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
                                 const float *topk_weights, ep_quant_t quant, void *grad_buf,
                                 size_t grad_buf_bytes, void *stream);
 
+/* Expert MLP between dispatch and combine ("[feat] A5 deep fused moe": the
+ * fused operator runs dispatch, GMM1, SwiGLU, requant, GMM2 and combine; its
+ * GMM1 A operand is e4m3 with one e8m0 scale per 32 elements).  Each expert e
+ * multiplies the receive rows of its block (the first recv_count[e] rows, or
+ * the whole block when recv_count is NULL) by its own weights.  Weights are
+ * MXFP8, dense and row-major: codes [E, N, K] (e4m3), scale bytes
+ * [E, N, K/32] (e8m0, one per 32 consecutive codes of a row).  Products are
+ * summed by the MX-scaled matrix cores in float32 accumulators; the
+ * instruction adds each 64-product block with less than float32 precision
+ * (about 3e-4 of the block's sum of |products|).
+ *
+ * ep_moe_gmm1: GMM1 + SwiGLU.
+ *   x_buf      MXFP8 receive buffer of ep_dispatch (region form), rows = max_rows
+ *   hidden     H (K of GMM1), H % 64 == 0
+ *   inter      I, I % 64 == 0
+ *   w1         codes [E, 2I, H]: rows 0..I-1 are the gate rows, I..2I-1 the up rows;
+ *   w1_scales  [E, 2I, H/32]
+ *   out_quant  EP_QUANT_MXFP8: row r of out_buf (an MXFP8 receive buffer of
+ *              width I, region form) gets MXFP8(a) with the MX rule of
+ *              dispatch; EP_QUANT_NONE: bf16(a) [max_rows, I]
+ *   where a_n = silu(g_n) * u_n in float32, g = gate rows . x, u = up rows . x,
+ *   silu(z) = z / (1 + exp(-z)).  Rows holding no pair are not written.
+ * ep_moe_gmm2: GMM2.
+ *   a_buf      MXFP8 receive buffer of width I (ep_moe_gmm1's output)
+ *   w2         codes [E, H, I], w2_scales [E, H, I/32]; H % 128 == 0
+ *   out_buf    bf16 [max_rows, H]: row r gets bf16(W2[e] . a_r), the
+ *              expert-output rows ep_combine reads (in_quant EP_QUANT_NONE)
+ */
+ep_status_t ep_moe_gmm1(const ep_handle_t *handle, const int64_t *recv_count, const void *x_buf,
+                        size_t x_buf_bytes, int32_t hidden, int32_t inter, const void *w1,
+                        const void *w1_scales, ep_quant_t out_quant, void *out_buf, size_t out_buf_bytes,
+                        void *stream);
+ep_status_t ep_moe_gmm2(const ep_handle_t *handle, const int64_t *recv_count, const void *a_buf,
+                        size_t a_buf_bytes, int32_t inter, int32_t hidden, const void *w2,
+                        const void *w2_scales, void *out_buf, size_t out_buf_bytes, void *stream);
+
 /* Waits for `stream` and copies the status word of `handle` to host *flags. */
 ep_status_t ep_read_status(const ep_handle_t *handle, uint32_t *flags, void *stream);
 
