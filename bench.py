@@ -203,6 +203,125 @@ def backward_main(args) -> int:
     return 0
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 / MXFP8 matrix-core peak
+
+
+def moe_algorithmic(w, R: int) -> dict:
+    """Bytes and flops of the expert-MLP path for R routed rows.
+
+    dispatch: read the x rows of routed tokens (at most T), write R MXFP8 rows
+    gmm1:     read W1 (codes + scales, packed once ahead of time) and the R
+              dispatch rows, write R MXFP8 rows of width I
+    gmm2:     read W2 (codes + scales) and those rows, write R bf16 rows
+    combine:  read R bf16 rows, slots and weights, write T bf16 rows
+    """
+    H, I, E, T, k = w.H, w.I, w.E_local, w.T, w.k
+    mx = lambda n: n + n // 32
+    b = {
+        "layout": T * k * 8 + E * 8 + (E + 1) * 4 + T * k * 4 + R * 4,
+        "dispatch": 2 * T * H + T * k * 4 + R * mx(H),
+        "gmm1": E * 2 * I * mx(H) + R * mx(H) + R * mx(I),
+        "gmm2": E * H * mx(I) + R * mx(I) + R * 2 * H,
+        "combine": R * 2 * H + T * k * 8 + 2 * T * H,
+    }
+    b["total"] = sum(b.values())
+    f = {"gmm1": 2.0 * R * H * 2 * I, "gmm2": 2.0 * R * I * H}
+    return {"bytes": b, "flops": f}
+
+
+def moe_main(args) -> int:
+    """layout + MXFP8 dispatch + GMM1/SwiGLU/requant + GMM2 + combine of one
+    MoE workload; one JSON line."""
+    import numpy as np
+    import torch
+    from combine_topk_idx_amd import ep, workloads as W
+
+    w = W.MOE_WORKLOADS[args.moe]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name}: T={w.T} H={w.H} I={w.I} E={w.E_local}/{w.E_total} k={w.k}",
+          file=sys.stderr, flush=True)
+    inp = W.make_moe_inputs(w)
+    rows = w.max_rows
+    xb, _ = ep.ep_buffer_bytes(rows, w.H, "mxfp8")
+    ab, _ = ep.ep_buffer_bytes(rows, w.I, "mxfp8")
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    # the weights are the bulk of each step's bytes: two copies (8 GB+ apart
+    # would be needed to defeat the 256 MB cache; two sets already exceed it)
+    nsets = args.sets or 2
+    sets = []
+    for i in range(nsets):
+        w1, w1s = ep.pack_moe_weights(d(inp["w1_codes"]), d(inp["w1_scales"]), True)
+        w2, w2s = ep.pack_moe_weights(d(inp["w2_codes"]), d(inp["w2_scales"]), False)
+        sets.append(dict(
+            x=d(inp["x"].view(np.int16)).view(torch.bfloat16), idx=d(inp["topk_idx"]), wt=d(inp["topk_weights"]),
+            w1=w1, w1s=w1s, w2=w2, w2s=w2s,
+            ws=torch.empty(ep.ep_workspace_bytes(w.T, w.k, w.E_local), dtype=torch.uint8, device=dev),
+            rc=torch.empty(w.E_local, dtype=torch.int64, device=dev),
+            recv=torch.empty(xb, dtype=torch.uint8, device=dev), a=torch.empty(ab, dtype=torch.uint8, device=dev),
+            y=torch.empty(rows * w.H * 2, dtype=torch.uint8, device=dev),
+            out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)))
+    stream = torch.cuda.current_stream()
+
+    def phases(s):
+        def lay():
+            s["h"] = ep.ep_layout(s["idx"], w.E_local, w.T, s["rc"], s["ws"])
+
+        def disp():
+            ep.ep_dispatch(s["h"], s["x"], w.H, "mxfp8", s["recv"])
+
+        def g1():
+            ep.ep_moe_gmm1(s["h"], s["recv"], w.H, w.I, s["w1"], s["w1s"], "mxfp8", s["a"], recv_count=s["rc"])
+
+        def g2():
+            ep.ep_moe_gmm2(s["h"], s["a"], w.I, w.H, s["w2"], s["w2s"], s["y"], recv_count=s["rc"])
+
+        def comb():
+            ep.ep_combine(s["h"], s["y"], "none", w.H, s["wt"], s["out"])
+        return [lay, disp, g1, g2, comb]
+
+    runners = [phases(s) for s in sets]
+    for i in range(max(args.warmup, nsets)):
+        for f in runners[i % nsets]:
+            f()
+    torch.cuda.synchronize()
+    R = int(sets[0]["rc"].sum().item())
+    names = ["layout", "dispatch", "gmm1", "gmm2", "combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        r = runners[i % nsets]
+        ev[i][0].record(stream)
+        for j, f in enumerate(r):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0][0].elapsed_time(ev[-1][5]) / args.steps
+    ph = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j, n in enumerate(names)}
+    alg = moe_algorithmic(w, R)
+    b, f = alg["bytes"], alg["flops"]
+    gbps = lambda n: b[n] / (ph[n] * 1e-3) / 1e9
+    tflops = lambda n: f[n] / (ph[n] * 1e-3) / 1e12
+    roof = {"bound": "hbm", "kernel": "gmm1", "achieved": round(gbps("gmm1"), 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(gbps("gmm1") / HBM_PEAK_GBPS, 4), "traffic": None,
+            "alg_bytes_per_launch": b["gmm1"], "avg_launch_ms": round(ph["gmm1"], 5),
+            "mfma_tflops": round(tflops("gmm1"), 1),
+            "mfma_frac": round(tflops("gmm1") / MFMA_FP8_PEAK_TFLOPS, 4)}
+    print(json.dumps({
+        "metric": "fused MoE step (dispatch, GMM1+SwiGLU+requant, GMM2, combine) tokens/s, H=7168 I=3072 k=6",
+        "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8", "data": "synthetic",
+        "config": {"workload": f"{w.name}: T={w.T} H={w.H} I={w.I} experts {w.E_local} of {w.E_total} k={w.k} "
+                               f"MXFP8 activations and weights", "rows": R, "buffer_sets": nsets},
+        "phase_ms": {n: round(v, 5) for n, v in ph.items()},
+        "phase_gbps": {n: round(gbps(n), 1) for n in names},
+        "gemm_tflops": {n: round(tflops(n), 1) for n in ("gmm1", "gmm2")},
+        "hbm_gbps": round(b["total"] / (ms * 1e-3) / 1e9, 1),
+        "roofline": roof, "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +345,9 @@ def main() -> int:
                     help="receive rows hold their data then their scales (EP_RECV_INTERLEAVED)")
     ap.add_argument("--quant", default=None,
                     help="dispatch quantisation in place of the workload's own (e.g. fp8_b128_ue8m0)")
+    ap.add_argument("--moe", default=None, metavar="WORKLOAD",
+                    help="time the expert-MLP path (layout, MXFP8 dispatch, GMM1+SwiGLU+requant, GMM2, combine) "
+                         "of a MoE workload, e.g. moe_share")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
@@ -234,6 +356,11 @@ def main() -> int:
         return 0
     if args.combine_backward:
         return backward_main(args)
+    if args.moe:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            return 2
+        return moe_main(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path has no "
               f"multi-GPU exchange)", file=sys.stderr)

@@ -266,6 +266,34 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
   return EP_OK;
 }
 
+ep_status_t ep_moe_packed_bytes(int32_t num_experts, int32_t rows, int32_t k, size_t *codes_bytes,
+                                size_t *scales_bytes) {
+  const char *fn = "ep_moe_packed_bytes";
+  if (num_experts <= 0 || num_experts > ep::kMaxExperts || rows <= 0 || rows % 32 != 0 || k <= 0 || k % 64 != 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: need 0 < experts <= 512, rows %% 32 == 0, k %% 64 == 0", fn);
+  size_t c, sc;
+  ep::moe_packed_bytes(num_experts, rows, k, &c, &sc);
+  if (codes_bytes) *codes_bytes = c;
+  if (scales_bytes) *scales_bytes = sc;
+  return EP_OK;
+}
+
+ep_status_t ep_moe_pack_weights(const void *codes, const void *scales, int32_t num_experts, int32_t rows, int32_t k,
+                                int32_t gate_up, void *packed_codes, void *packed_scales, void *stream) {
+  const char *fn = "ep_moe_pack_weights";
+  const ep_status_t st = ep_moe_packed_bytes(num_experts, rows, k, nullptr, nullptr);
+  if (st != EP_OK) return fail(st, "%s: need 0 < experts <= 512, rows %% 32 == 0, k %% 64 == 0", fn);
+  if (gate_up != 0 && gate_up != 1) return fail(EP_ERR_INVALID_ARG, "%s: gate_up must be 0 or 1", fn);
+  if (gate_up && rows % 64 != 0) return fail(EP_ERR_INVALID_ARG, "%s: gate/up weights need rows %% 64 == 0", fn);
+  if (!codes || !scales || !packed_codes || !packed_scales || !aligned(codes, 16) || !aligned(packed_codes, 16) ||
+      !aligned(packed_scales, 4))
+    return fail(EP_ERR_INVALID_ARG, "%s: NULL or misaligned buffer", fn);
+  const hipError_t e = ep::launch_moe_pack(codes, scales, num_experts, rows, k, gate_up, packed_codes, packed_scales,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return EP_OK;
+}
+
 ep_status_t ep_moe_gmm1(const ep_handle_t *handle, const int64_t *recv_count, const void *x_buf, size_t x_buf_bytes,
                         int32_t hidden, int32_t inter, const void *w1, const void *w1_scales, ep_quant_t out_quant,
                         void *out_buf, size_t out_buf_bytes, void *stream) {
@@ -281,8 +309,8 @@ ep_status_t ep_moe_gmm1(const ep_handle_t *handle, const int64_t *recv_count, co
     return fail(EP_ERR_INVALID_ARG, "%s: out_quant must be EP_QUANT_MXFP8 or EP_QUANT_NONE", fn);
   if (!x_buf || !aligned(x_buf, 16) || !out_buf || !aligned(out_buf, 16))
     return fail(EP_ERR_INVALID_ARG, "%s: x_buf / out_buf NULL or not 16-byte aligned", fn);
-  if (!w1 || !w1_scales || !aligned(w1, 16))
-    return fail(EP_ERR_INVALID_ARG, "%s: w1 NULL or not 16-byte aligned, or w1_scales NULL", fn);
+  if (!w1 || !w1_scales || !aligned(w1, 16) || !aligned(w1_scales, 4))
+    return fail(EP_ERR_INVALID_ARG, "%s: w1 / w1_scales NULL or misaligned", fn);
   if (recv_count && !aligned(recv_count, 8)) return fail(EP_ERR_INVALID_ARG, "%s: recv_count misaligned", fn);
   const size_t need_x = buffer_bytes(handle->max_rows, hidden, EP_QUANT_MXFP8, nullptr);
   const size_t need_o = buffer_bytes(handle->max_rows, inter, out_quant, nullptr);
@@ -307,8 +335,8 @@ ep_status_t ep_moe_gmm2(const ep_handle_t *handle, const int64_t *recv_count, co
     return fail(EP_ERR_UNSUPPORTED, "%s: hidden / inter above %d", fn, kMaxHidden);
   if (!a_buf || !aligned(a_buf, 16) || !out_buf || !aligned(out_buf, 16))
     return fail(EP_ERR_INVALID_ARG, "%s: a_buf / out_buf NULL or not 16-byte aligned", fn);
-  if (!w2 || !w2_scales || !aligned(w2, 16))
-    return fail(EP_ERR_INVALID_ARG, "%s: w2 NULL or not 16-byte aligned, or w2_scales NULL", fn);
+  if (!w2 || !w2_scales || !aligned(w2, 16) || !aligned(w2_scales, 4))
+    return fail(EP_ERR_INVALID_ARG, "%s: w2 / w2_scales NULL or misaligned", fn);
   if (recv_count && !aligned(recv_count, 8)) return fail(EP_ERR_INVALID_ARG, "%s: recv_count misaligned", fn);
   const size_t need_a = buffer_bytes(handle->max_rows, inter, EP_QUANT_MXFP8, nullptr);
   const size_t need_o = buffer_bytes(handle->max_rows, hidden, EP_QUANT_NONE, nullptr);

@@ -21,10 +21,10 @@
 // instruction, measured), which bounds how closely any result here can
 // follow an exact dot product.
 //
-// Mapping: a workgroup (4 waves) owns one (expert, chunk of up to 256 rows,
+// Mapping: a workgroup (4 waves) owns one (expert, chunk of up to 160 rows,
 // N tile).  The chunk's A rows are staged through double-buffered LDS one
 // 64-wide K step at a time and shared by the 4 waves; every wave streams its
-// own 32 weight rows (B) straight into registers, kPrefetch K steps ahead
+// own 32 weight rows (B) straight into registers, eight K steps ahead
 // (weights are read once from HBM: they are the traffic that bounds the
 // kernel at the shapes of the benchmark).  GMM1 gives each wave 16 gate and
 // the matching 16 up rows, so lane c < 16 and lane c + 16 hold g and u of the
@@ -43,13 +43,18 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxFrags = 8;                      // 32-row fragments per chunk
+constexpr int kMaxFrags = 5;                      // 32-row fragments per chunk
 constexpr int kChunkRows = kMaxFrags * 32;        // rows per work item
 constexpr int kKStep = 64;                        // K per matrix-core step
 constexpr int kRowStride = 80;                    // LDS bytes per staged A row (64 + pad)
-constexpr int kStage = kChunkRows * kRowStride;   // bytes of one staged A step
-constexpr int kScaleStage = kChunkRows * 2;       // scale bytes of one staged A step
-constexpr int kPrefetch = 4;                      // weight K steps in flight per wave
+// Every thread moves the same number of 16-byte A pieces per step, so a
+// stage holds slots for that many pieces of every thread (rows past the
+// chunk are loaded from its last row and never read), and one scale pair
+// per thread.
+constexpr int kPiecesMax = (kChunkRows * 4 + kThreads - 1) / kThreads;
+constexpr int kStageRows = kPiecesMax * kThreads / 4;
+constexpr int kStage = kStageRows * kRowStride;   // bytes of one staged A step
+constexpr int kScaleStage = kThreads * 2;         // scale bytes of one staged A step
 constexpr int kEpiCols = 64;                      // GMM1 SwiGLU columns per workgroup
 constexpr int kEpiStride = kEpiCols + 1;          // floats per LDS row of the epilogue tile
 
@@ -59,12 +64,19 @@ struct Item {
   int expert, row0, rows;                         // rows <= kChunkRows
 };
 
-// The work item of work index `item` (an (expert, 256-row chunk) pair in
-// expert order), or expert -1 past the last one.  Row counts are recv_count
-// when given, else the expert block sizes.  Every thread takes two experts;
-// their chunk counts are scanned across the workgroup (wave scans, then the
-// four wave totals through LDS).
-__device__ Item find_item(int item, int E, const int *__restrict__ offsets, const int64_t *__restrict__ recv_count) {
+// The work of this workgroup.  Work units are (expert, chunk of up to
+// kChunkRows rows, N tile) triples in expert-major order; their number comes
+// from a workgroup scan of the per-expert chunk counts (recv_count when
+// given, else the expert block sizes; every thread takes two experts).  The
+// hardware hands workgroups to the 8 XCDs round-robin, so workgroup b runs on
+// XCD b % 8; giving XCD x the contiguous units [x * per, (x + 1) * per) keeps
+// each XCD on one or two experts, whose activation rows then stay in that
+// XCD's L2 instead of being fetched by every XCD.  Returns expert -1 when the
+// workgroup has no unit.
+constexpr int kXcds = 8;
+
+__device__ Item find_item(int n_tiles, int E, const int *__restrict__ offsets, const int64_t *__restrict__ recv_count,
+                          int &ntile) {
   __shared__ int wsum[kWaves];
   __shared__ Item found;
   if (threadIdx.x == 0) found.expert = -1;
@@ -85,14 +97,23 @@ __device__ Item find_item(int item, int E, const int *__restrict__ offsets, cons
   }
   if (lane == kWave - 1) wsum[wv] = x;
   __syncthreads();
-  int before = 0;
+  int before = 0, chunks = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) before += i < wv ? wsum[i] : 0;
+  for (int i = 0; i < kWaves; ++i) {
+    before += i < wv ? wsum[i] : 0;
+    chunks += wsum[i];
+  }
+  const int units = chunks * n_tiles;
+  const int per = (units + kXcds - 1) / kXcds;
+  const int unit = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  const bool have = blockIdx.x / kXcds < per && unit < units;
+  const int item = unit / n_tiles;
+  ntile = unit - item * n_tiles;
   int start = before + x - ch[0] - ch[1];                          // exclusive prefix of expert 2t
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = 2 * threadIdx.x + q;
-    if (e < E && item >= start && item < start + ch[q]) {
+    if (have && e < E && item >= start && item < start + ch[q]) {
       const int c = item - start;
       found.expert = e;
       found.row0 = offsets[e] + c * kChunkRows;
@@ -106,131 +127,203 @@ __device__ Item find_item(int item, int E, const int *__restrict__ offsets, cons
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void mx_gmm_kernel(
-    const uint8_t *__restrict__ a_data, const uint8_t *__restrict__ a_scales, int K,
-    const uint8_t *__restrict__ w, const uint8_t *__restrict__ w_scales, int N_w, int n_tiles, int inter,
-    const int *__restrict__ offsets, const int64_t *__restrict__ recv_count, int E,
-    uint8_t *__restrict__ out_data, uint8_t *__restrict__ out_scales, int out_cols) {
-  constexpr int kStaging = 2 * (kStage + kScaleStage);
-  constexpr int kTile = MODE == kGmm2 ? 0 : kChunkRows * kEpiStride * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kTile ? kStaging : kTile];
-  const Item it = find_item(blockIdx.x / n_tiles, E, offsets, recv_count);
-  if (it.expert < 0 || it.rows <= 0) return;                     // uniform
-  const int ntile = blockIdx.x % n_tiles;
+// Packed weights.  A wave's 32 weight rows form a group: for GMM2 rows
+// 32j .. 32j+31; for GMM1 ("gate/up" groups) the gate rows 16j .. 16j+15 and
+// the matching up rows I+16j .. I+16j+15.  For each group and 64-wide K step
+// the group's fragment is 2048 bytes in matrix-core lane order: bytes
+// [0, 1024) hold, for lane l = 32g + r, K bytes [16g, 16g+16) of the
+// group's row r at offset 16l; bytes [1024, 2048) hold K bytes [32+16g,
+// 48+16g) at 1024 + 16l.  Each 16-byte load of a wave then reads 1 KB in
+// one piece.  Scale bytes: for each group and span of four K steps, 256
+// bytes where lane l's four bytes (offset 4l) are the e8m0 scales of K-block
+// 2(4t+u) + g of row r for u = 0..3 (zero past the last step).
+__host__ __device__ inline int packed_group_row(int j, int r, int gate_up, int inter) {
+  return gate_up ? (r < 16 ? 16 * j + r : inter + 16 * j + (r - 16)) : 32 * j + r;
+}
+
+__global__ void pack_weights_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int E, int N,
+                                    int K, int gate_up, uint8_t *__restrict__ pcodes, uint8_t *__restrict__ pscales) {
+  const int ksteps = K / kKStep, spans = (ksteps + 3) / 4, groups = N / 32, kb = K / 32;
+  const int inter = N / 2;
+  // one thread per (expert, group, step, half, lane): a 16-byte piece
+  const int64_t pieces = (int64_t)E * groups * ksteps * 128;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63), half = (int)((i >> 6) & 1);
+    const int64_t rest = i >> 7;
+    const int s = (int)(rest % ksteps);
+    const int64_t eg = rest / ksteps;
+    const int j = (int)(eg % groups), e = (int)(eg / groups);
+    const int r = lane & 31, g = lane >> 5;
+    const int row = packed_group_row(j, r, gate_up, inter);
+    const uint8_t *src = codes + ((int64_t)e * N + row) * K + s * kKStep + half * 32 + g * 16;
+    *(u32x4 *)(pcodes + i * 16) = *(const u32x4 *)src;
+  }
+  // one thread per (expert, group, span, lane): four scale bytes
+  const int64_t words = (int64_t)E * groups * spans * 64;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    const int64_t rest = i >> 6;
+    const int t = (int)(rest % spans);
+    const int64_t eg = rest / spans;
+    const int j = (int)(eg % groups), e = (int)(eg / groups);
+    const int r = lane & 31, g = lane >> 5;
+    const int row = packed_group_row(j, r, gate_up, inter);
+    uint32_t w = 0;
+    for (int u = 0; u < 4; ++u) {
+      const int step = 4 * t + u;
+      if (step < ksteps) w |= (uint32_t)scales[((int64_t)e * N + row) * kb + step * 2 + g] << (8 * u);
+    }
+    *(uint32_t *)(pscales + i * 4) = w;
+  }
+}
+
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() carries a
+// release fence, which on this target waits for every outstanding vector
+// memory operation -- loads included -- and so would drain the weight loads
+// in flight at every K step.  Every LDS write here is a ds_write whose data is
+// already in registers, so waiting for this wave's LDS operations and then
+// meeting at the barrier is enough; the "memory" clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct GemmArgs {
+  const uint8_t *a_data, *a_scales;
+  int K;
+  const uint8_t *w, *w_scales;
+  int N_w, n_tiles, inter;
+  uint8_t *out_data, *out_scales;
+  int out_cols;
+};
+
+// Main loop and epilogue for a chunk of NF 32-row fragments.
+template <int MODE, int NF>
+__device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, int ntile, uint8_t *smem) {
+  constexpr int kPieces = (NF * 32 * 4 + kThreads - 1) / kThreads;   // 16-byte A pieces per thread per step
+  static_assert(kPieces <= kPiecesMax && kPieces * kThreads / 4 <= kStageRows, "A slots fit the stage");
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int r = lane & 31, g = lane >> 5;
-  const int nfrag = (it.rows + 31) / 32;
-  const int ksteps = K / kKStep;
-  const int kb = K / 32;                                          // scale bytes per row
+  const int K = p.K, ksteps = K / kKStep, kb = K / 32;
 
-  // this lane's weight row
-  int wrow;
-  if constexpr (MODE == kGmm2) {
-    wrow = ntile * (kWaves * 32) + wv * 32 + r;
-  } else {
-    const int n0 = ntile * kEpiCols + wv * 16;
-    wrow = r < 16 ? n0 + r : inter + n0 + (r - 16);
-  }
-  const uint8_t *wp = w + ((size_t)it.expert * N_w + wrow) * (size_t)K;
-  const uint8_t *wsp = w_scales + ((size_t)it.expert * N_w + wrow) * (size_t)kb;
+  // this wave's packed weight group (see pack_weights_kernel): fragments of
+  // 2048 bytes per K step, scale dwords per span of four steps
+  const int group = ntile * kWaves + wv;
+  const int spans = (ksteps + 3) / 4;
+  const size_t gidx = (size_t)it.expert * (p.N_w / 32) + group;
+  const uint8_t *wp = p.w + gidx * (size_t)ksteps * 2048 + lane * 16;
+  const uint8_t *wsp = p.w_scales + gidx * (size_t)spans * 256 + lane * 4;
 
-  // staging of A step s into LDS buffer s & 1: each thread moves 16-byte
-  // pieces of the chunk's rows (4 per row per step) and one scale pair per row
-  auto a_piece_count = nfrag * 32 * 4;
-  auto load_a = [&](int s, u32x4 (&pieces)[4], uint32_t &sc) {
+  // A staging, branch-free: piece i of this thread is (row, quarter) =
+  // (idx >> 2, idx & 3) of the chunk; rows past the chunk read its last row
+  // (their LDS slots exist and are never used)
+  const uint8_t *apiece[kPieces];
+  int lpiece[kPieces];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      pieces[p] = u32x4{0u, 0u, 0u, 0u};
-      if (idx < a_piece_count) {
-        const int row = idx >> 2, q = idx & 3;
-        const int src = it.row0 + min(row, it.rows - 1);
-        pieces[p] = *(const u32x4 *)(a_data + (size_t)src * K + (size_t)s * kKStep + q * 16);
-      }
-    }
-    sc = 0;
-    if (threadIdx.x < nfrag * 32) {
-      const int src = it.row0 + min((int)threadIdx.x, it.rows - 1);
-      const uint8_t *sp = a_scales + (size_t)src * kb + (size_t)s * 2;
-      sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
-    }
+  for (int i = 0; i < kPieces; ++i) {
+    const int idx = threadIdx.x + i * kThreads;
+    const int row = idx >> 2, q = idx & 3;
+    apiece[i] = p.a_data + (size_t)(it.row0 + min(row, it.rows - 1)) * K + q * 16;
+    lpiece[i] = row * kRowStride + q * 16;
+  }
+  const uint8_t *ascale = p.a_scales + (size_t)(it.row0 + min((int)threadIdx.x, it.rows - 1)) * kb;
+
+  constexpr int kASets = 4;                                       // A loads run three steps ahead
+  u32x4 areg[kASets][kPieces];
+  uint32_t asreg[kASets];
+  auto load_a = [&](int s, int set) {
+    const int ss = min(s, ksteps - 1);
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) areg[set][i] = *(const u32x4 *)(apiece[i] + (size_t)ss * kKStep);
+    asreg[set] = *(const uint16_t *)(ascale + ss * 2);
   };
-  auto store_a = [&](int buf, const u32x4 (&pieces)[4], uint32_t sc) {
+  auto store_a = [&](int buf, int set) {
     uint8_t *base = smem + buf * (kStage + kScaleStage);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      if (idx < a_piece_count) {
-        const int row = idx >> 2, q = idx & 3;
-        *(u32x4 *)(base + row * kRowStride + q * 16) = pieces[p];
-      }
-    }
-    if (threadIdx.x < nfrag * 32) *(uint16_t *)(base + kStage + threadIdx.x * 2) = (uint16_t)sc;
+    for (int i = 0; i < kPieces; ++i) *(u32x4 *)(base + lpiece[i]) = areg[set][i];
+    *(uint16_t *)(base + kStage + threadIdx.x * 2) = (uint16_t)asreg[set];
   };
 
-  // weight ring: kPrefetch steps of (two 16-byte pieces, one scale byte)
-  u32x4 wb0[kPrefetch], wb1[kPrefetch];
-  uint32_t wsc[kPrefetch];
+  // weight ring: kRing K steps of two 16-byte pieces (each wave load reads
+  // 1 KB in one piece); scales one dword per span of four steps (current
+  // span and the next one in flight)
+  constexpr int kRing = 4;
+  static_assert(kRing == 4, "one scale span per ring cycle");
+  u32x4 wb0[kRing], wb1[kRing];
+  uint32_t wsc_cur, wsc_nxt;
   auto load_w = [&](int s, int slot) {
-    const int ss = min(s, ksteps - 1);                            // clamped: loads past the end are dropped
-    wb0[slot] = *(const u32x4 *)(wp + (size_t)ss * kKStep + g * 16);
-    wb1[slot] = *(const u32x4 *)(wp + (size_t)ss * kKStep + 32 + g * 16);
-    wsc[slot] = wsp[ss * 2 + g];
+    const int ss = min(s, ksteps - 1);                             // loads past the end are never used
+    wb0[slot] = *(const u32x4 *)(wp + (size_t)ss * 2048);
+    wb1[slot] = *(const u32x4 *)(wp + (size_t)ss * 2048 + 1024);
   };
+  auto load_ws = [&](int span) { return *(const uint32_t *)(wsp + (size_t)min(span, spans - 1) * 256); };
 
-  v16f acc[kMaxFrags];
+  v16f acc[NF];
 #pragma unroll
-  for (int f = 0; f < kMaxFrags; ++f) acc[f] = v16f{};
+  for (int f = 0; f < NF; ++f) acc[f] = v16f{};
 
-  u32x4 ap[4];
-  uint32_t asc;
-  load_a(0, ap, asc);
-  store_a(0, ap, asc);
-  if (ksteps > 1) load_a(1, ap, asc);
+  // prologue: A step 0 in LDS buffer 0, steps 1..3 in register sets 1..3;
+  // weight steps 0 .. kRing-1 in flight
+  load_a(0, 0);
+  store_a(0, 0);
+  load_a(1, 1);
+  load_a(2, 2);
+  load_a(3, 3);
 #pragma unroll
-  for (int p = 0; p < kPrefetch; ++p) load_w(p, p);
-  __syncthreads();
+  for (int q = 0; q < kRing; ++q) load_w(q, q);
+  wsc_cur = load_ws(0);
+  wsc_nxt = load_ws(1);
+  lds_barrier();
 
-  for (int s0 = 0; s0 < ksteps; s0 += kPrefetch) {
-#pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) {
-      const int s = s0 + u;
-      if (s >= ksteps) break;                                     // uniform
-      if (s + 1 < ksteps) store_a((s + 1) & 1, ap, asc);
-      if (s + 2 < ksteps) load_a(s + 2, ap, asc);
-      const u32x4 b0 = wb0[u], b1 = wb1[u];
-      const int bsc = (int)wsc[u];
-      load_w(s + kPrefetch, u);
-      const v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-      const uint8_t *base = smem + (s & 1) * (kStage + kScaleStage);
-#pragma unroll
-      for (int f = 0; f < kMaxFrags; ++f) {
-        if (f >= nfrag) break;                                    // uniform
-        const int row = f * 32 + r;
-        const u32x4 x0 = *(const u32x4 *)(base + row * kRowStride + g * 16);
-        const u32x4 x1 = *(const u32x4 *)(base + row * kRowStride + 32 + g * 16);
-        const int xs = (int)base[kStage + row * 2 + g];
-        const v8i av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[f], 0, 0, 0, xs, 0, bsc);
-      }
-      __syncthreads();
+  // step s: write A(s+1) (loaded three steps ago, register set (s+1) % 4) to
+  // LDS buffer (s+1)&1, load A(s+4) into set s % 4 (free since step s-1),
+  // compute step s from buffer s&1 with weight slot s % kRing and refill
+  // that slot with step s + kRing
+  auto step = [&](int s, int u) {
+    store_a((s + 1) & 1, (u + 1) % kASets);
+    load_a(s + 4, u % kASets);
+    const u32x4 b0 = wb0[u], b1 = wb1[u];
+    const int bsc = (int)((wsc_cur >> (8 * u)) & 0xffu);
+    load_w(s + kRing, u);
+    if (u == kRing - 1) {                                            // static: next span, and the one after in flight
+      wsc_cur = wsc_nxt;
+      wsc_nxt = load_ws(s / 4 + 2);
     }
+    const v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    const uint8_t *base = smem + (s & 1) * (kStage + kScaleStage);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int row = f * 32 + r;
+      const u32x4 x0 = *(const u32x4 *)(base + row * kRowStride + g * 16);
+      const u32x4 x1 = *(const u32x4 *)(base + row * kRowStride + 32 + g * 16);
+      const int xs = (int)base[kStage + row * 2 + g];
+      const v8i av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[f], 0, 0, 0, xs, 0, bsc);
+    }
+    lds_barrier();
+  };
+  int s0 = 0;
+  for (; s0 + kRing <= ksteps; s0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) step(s0 + u, u);
   }
+#pragma unroll
+  for (int u = 0; u < kRing; ++u)
+    if (s0 + u < ksteps) step(s0 + u, u);                           // uniform tail
+  // every load issued past the last step targets registers nobody reads;
+  // let them land before the registers and the kernel go away
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
   if constexpr (MODE == kGmm2) {
     // bf16 rows: column l % 32 of this wave's 32, rows 8b + 4g + i of each fragment
     const int col = ntile * (kWaves * 32) + wv * 32 + r;
 #pragma unroll
-    for (int f = 0; f < kMaxFrags; ++f) {
-      if (f >= nfrag) break;
+    for (int f = 0; f < NF; ++f) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = f * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
         if (row < it.rows) {
           const uint32_t bits = pack_bf16x2(acc[f][i], 0.0f) & 0xffffu;
-          *(uint16_t *)(out_data + ((size_t)(it.row0 + row) * out_cols + col) * 2) = (uint16_t)bits;
+          *(uint16_t *)(p.out_data + ((size_t)(it.row0 + row) * p.out_cols + col) * 2) = (uint16_t)bits;
         }
       }
     }
@@ -239,8 +332,7 @@ __global__ __launch_bounds__(kThreads) void mx_gmm_kernel(
     // column; the 16 results of each wave go to an LDS tile [rows][64]
     float *tile = (float *)smem;
 #pragma unroll
-    for (int f = 0; f < kMaxFrags; ++f) {
-      if (f >= nfrag) break;
+    for (int f = 0; f < NF; ++f) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float gate = acc[f][i];
@@ -249,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void mx_gmm_kernel(
         if (r < 16) tile[row * kEpiStride + wv * 16 + r] = silu(gate) * up;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // each thread: one (row, 32-column block) of the tile
     const int n0 = ntile * kEpiCols;
     for (int job = threadIdx.x; job < it.rows * 2; job += kThreads) {
@@ -260,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void mx_gmm_kernel(
         uint32_t o[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[e] = pack_bf16x2(src[2 * e], src[2 * e + 1]);
-        u32x4 *dst = (u32x4 *)(out_data + (orow * out_cols + n0 + blk * 32) * 2);
+        u32x4 *dst = (u32x4 *)(p.out_data + (orow * p.out_cols + n0 + blk * 32) * 2);
 #pragma unroll
         for (int q = 0; q < 4; ++q) dst[q] = u32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
       } else {
@@ -283,35 +375,59 @@ __global__ __launch_bounds__(kThreads) void mx_gmm_kernel(
           for (int e = 0; e < 8; ++e) v[e] = fminf(fmaxf(src[8 * c + e] * mult, -448.0f), 448.0f);
           q[c] = e4m3x8_encode(v);
         }
-        u32x4 *dst = (u32x4 *)(out_data + orow * out_cols + n0 + blk * 32);
+        u32x4 *dst = (u32x4 *)(p.out_data + orow * p.out_cols + n0 + blk * 32);
         dst[0] = u32x4{q[0].x, q[0].y, q[1].x, q[1].y};
         dst[1] = u32x4{q[2].x, q[2].y, q[3].x, q[3].y};
-        out_scales[orow * (out_cols / 32) + (n0 >> 5) + blk] = (uint8_t)(se + 127);
+        p.out_scales[orow * (p.out_cols / 32) + (n0 >> 5) + blk] = (uint8_t)(se + 127);
       }
     }
   }
 }
 
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void mx_gmm_kernel(GemmArgs p, const int *__restrict__ offsets,
+                                                          const int64_t *__restrict__ recv_count, int E) {
+  constexpr int kStaging = 2 * (kStage + kScaleStage);
+  constexpr int kTile = MODE == kGmm2 ? 0 : kChunkRows * kEpiStride * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kTile ? kStaging : kTile];
+  int ntile;
+  const Item it = find_item(p.n_tiles, E, offsets, recv_count, ntile);
+  if (it.expert < 0 || it.rows <= 0) return;                     // uniform
+  static_assert(kMaxFrags == 5, "one instantiation per fragment count 1..kMaxFrags");
+  switch ((it.rows + 31) / 32) {                                 // uniform: one instantiation per fragment count
+    case 1: gemm_chunk<MODE, 1>(p, it, ntile, smem); break;
+    case 2: gemm_chunk<MODE, 2>(p, it, ntile, smem); break;
+    case 3: gemm_chunk<MODE, 3>(p, it, ntile, smem); break;
+    case 4: gemm_chunk<MODE, 4>(p, it, ntile, smem); break;
+    default: gemm_chunk<MODE, 5>(p, it, ntile, smem); break;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_moe_pack(const void *codes, const void *scales, int E, int N, int K, int gate_up, void *pcodes,
+                           void *pscales, hipStream_t s) {
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(1024), dim3(256), 0, s, (const uint8_t *)codes, (const uint8_t *)scales,
+                     E, N, K, gate_up, (uint8_t *)pcodes, (uint8_t *)pscales);
+  return hipGetLastError();
+}
 
 hipError_t launch_moe_gmm1(const ep_handle_t &h, const int64_t *recv_count, const char *x_buf, int hidden, int inter,
                            const void *w1, const void *w1_scales, int out_quant, char *out_buf, hipStream_t s) {
   const RecvGeom gx = recv_geom(h.max_rows, hidden, EP_QUANT_MXFP8);
   const int n_tiles = inter / kEpiCols;
   const int64_t items = (h.max_rows + kChunkRows - 1) / kChunkRows + h.num_experts;
-  const int64_t blocks = items * n_tiles;
+  const int64_t blocks = (items * n_tiles + kXcds - 1) / kXcds * kXcds;
   if (h.num_tokens == 0 || blocks == 0) return hipSuccess;
+  GemmArgs p{(const uint8_t *)x_buf, (const uint8_t *)x_buf + gx.scale_off, hidden, (const uint8_t *)w1,
+             (const uint8_t *)w1_scales, 2 * inter, n_tiles, inter, (uint8_t *)out_buf, nullptr, inter};
   if (out_quant == EP_QUANT_MXFP8) {
-    const RecvGeom go = recv_geom(h.max_rows, inter, EP_QUANT_MXFP8);
-    hipLaunchKernelGGL(mx_gmm_kernel<kGmm1Mx>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       (const uint8_t *)x_buf, (const uint8_t *)x_buf + gx.scale_off, hidden, (const uint8_t *)w1,
-                       (const uint8_t *)w1_scales, 2 * inter, n_tiles, inter, h.offsets, recv_count, h.num_experts,
-                       (uint8_t *)out_buf, (uint8_t *)out_buf + go.scale_off, inter);
+    p.out_scales = (uint8_t *)out_buf + recv_geom(h.max_rows, inter, EP_QUANT_MXFP8).scale_off;
+    hipLaunchKernelGGL(mx_gmm_kernel<kGmm1Mx>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, h.offsets,
+                       recv_count, h.num_experts);
   } else {
-    hipLaunchKernelGGL(mx_gmm_kernel<kGmm1Bf16>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                       (const uint8_t *)x_buf, (const uint8_t *)x_buf + gx.scale_off, hidden, (const uint8_t *)w1,
-                       (const uint8_t *)w1_scales, 2 * inter, n_tiles, inter, h.offsets, recv_count, h.num_experts,
-                       (uint8_t *)out_buf, (uint8_t *)nullptr, inter);
+    hipLaunchKernelGGL(mx_gmm_kernel<kGmm1Bf16>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, h.offsets,
+                       recv_count, h.num_experts);
   }
   return hipGetLastError();
 }
@@ -321,12 +437,12 @@ hipError_t launch_moe_gmm2(const ep_handle_t &h, const int64_t *recv_count, cons
   const RecvGeom ga = recv_geom(h.max_rows, inter, EP_QUANT_MXFP8);
   const int n_tiles = hidden / (kWaves * 32);
   const int64_t items = (h.max_rows + kChunkRows - 1) / kChunkRows + h.num_experts;
-  const int64_t blocks = items * n_tiles;
+  const int64_t blocks = (items * n_tiles + kXcds - 1) / kXcds * kXcds;
   if (h.num_tokens == 0 || blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx_gmm_kernel<kGmm2>, dim3((unsigned)blocks), dim3(kThreads), 0, s, (const uint8_t *)a_buf,
-                     (const uint8_t *)a_buf + ga.scale_off, inter, (const uint8_t *)w2, (const uint8_t *)w2_scales,
-                     hidden, n_tiles, inter, h.offsets, recv_count, h.num_experts, (uint8_t *)out_buf,
-                     (uint8_t *)nullptr, hidden);
+  const GemmArgs p{(const uint8_t *)a_buf, (const uint8_t *)a_buf + ga.scale_off, inter, (const uint8_t *)w2,
+                   (const uint8_t *)w2_scales, hidden, n_tiles, inter, (uint8_t *)out_buf, nullptr, hidden};
+  hipLaunchKernelGGL(mx_gmm_kernel<kGmm2>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, h.offsets, recv_count,
+                     h.num_experts);
   return hipGetLastError();
 }
 

@@ -2,7 +2,8 @@
 
 The functions ``ep_workspace_bytes``, ``ep_workspace_bytes_ex``,
 ``ep_layout_rows``, ``ep_buffer_bytes``, ``ep_layout``, ``ep_layout_ex``,
-``ep_dispatch``, ``ep_combine``, ``ep_combine_backward``, ``ep_moe_gmm1``,
+``ep_dispatch``, ``ep_combine``, ``ep_combine_backward``,
+``ep_moe_packed_bytes``, ``ep_moe_pack_weights``, ``ep_moe_gmm1``,
 ``ep_moe_gmm2``, ``ep_read_status``,
 ``ep_last_error`` and ``ep_abi_version`` have the names and arguments of the C ABI in
 ``include/ep.h``; torch tensors stand in for device pointers and torch's
@@ -40,7 +41,7 @@ EP_STATUS_ID_OUT_OF_RANGE = 1
 EP_STATUS_CAPACITY_OVERFLOW = 2
 
 SYMBOLS = ("ep_workspace_bytes", "ep_workspace_bytes_ex", "ep_layout_rows", "ep_buffer_bytes", "ep_layout",
-           "ep_layout_ex", "ep_dispatch", "ep_combine", "ep_combine_backward", "ep_moe_gmm1", "ep_moe_gmm2",
+           "ep_layout_ex", "ep_dispatch", "ep_combine", "ep_combine_backward", "ep_moe_packed_bytes", "ep_moe_pack_weights", "ep_moe_gmm1", "ep_moe_gmm2",
            "ep_read_status", "ep_last_error", "ep_abi_version")
 
 
@@ -81,6 +82,10 @@ _lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int,
 _lib.ep_combine.restype = ctypes.c_int
 _lib.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp]
 _lib.ep_combine_backward.restype = ctypes.c_int
+_lib.ep_moe_packed_bytes.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+_lib.ep_moe_packed_bytes.restype = ctypes.c_int
+_lib.ep_moe_pack_weights.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+_lib.ep_moe_pack_weights.restype = ctypes.c_int
 _lib.ep_moe_gmm1.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _vp, _sz, _i32, _i32, _vp, _vp, ctypes.c_int, _vp,
                              _sz, _vp]
 _lib.ep_moe_gmm1.restype = ctypes.c_int
@@ -232,6 +237,29 @@ def ep_combine_backward(handle: ep_handle_t, grad_out, hidden: int, quant, grad_
     nbytes = _nbytes(grad_buf) if grad_buf_bytes is None else grad_buf_bytes
     _check(_lib.ep_combine_backward(ctypes.byref(handle), _ptr(grad_out), hidden, _ptr(topk_weights),
                                     _quant(quant, interleaved), _ptr(grad_buf), nbytes, _stream(stream)))
+
+
+def ep_moe_packed_bytes(num_experts: int, rows: int, k: int) -> tuple[int, int]:
+    c, sc = _sz(0), _sz(0)
+    _check(_lib.ep_moe_packed_bytes(num_experts, rows, k, ctypes.byref(c), ctypes.byref(sc)))
+    return c.value, sc.value
+
+
+def ep_moe_pack_weights(codes, scales, num_experts: int, rows: int, k: int, gate_up: bool, packed_codes,
+                        packed_scales, *, stream=None) -> None:
+    _check(_lib.ep_moe_pack_weights(_ptr(codes), _ptr(scales), num_experts, rows, k, int(gate_up), _ptr(packed_codes),
+                                    _ptr(packed_scales), _stream(stream)))
+
+
+def pack_moe_weights(codes, scales, gate_up: bool, *, stream=None):
+    """Device tensors codes [E, N, K] uint8 and scales [E, N, K/32] uint8 ->
+    (packed codes, packed scales) uint8 device tensors."""
+    E, N, K = codes.shape
+    cb, sb = ep_moe_packed_bytes(E, N, K)
+    pc = torch.empty(cb, dtype=torch.uint8, device=codes.device)
+    ps = torch.empty(sb, dtype=torch.uint8, device=codes.device)
+    ep_moe_pack_weights(codes, scales, E, N, K, gate_up, pc, ps, stream=stream)
+    return pc, ps
 
 
 def ep_moe_gmm1(handle: ep_handle_t, x_buf, hidden: int, inter: int, w1, w1_scales, out_quant, out_buf, *,

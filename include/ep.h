@@ -255,8 +255,10 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
  * GMM1 A operand is e4m3 with one e8m0 scale per 32 elements).  Each expert e
  * multiplies the receive rows of its block (the first recv_count[e] rows, or
  * the whole block when recv_count is NULL) by its own weights.  Weights are
- * MXFP8, dense and row-major: codes [E, N, K] (e4m3), scale bytes
- * [E, N, K/32] (e8m0, one per 32 consecutive codes of a row).  Products are
+ * MXFP8 -- codes [E, N, K] (e4m3) and scale bytes [E, N, K/32] (e8m0, one
+ * per 32 consecutive codes of a row) -- packed once by ep_moe_pack_weights
+ * into the matrix cores' fragment order (a permutation of the same bytes;
+ * the GEMMs read only the packed form).  Products are
  * summed by the MX-scaled matrix cores in float32 accumulators; the
  * instruction adds each 64-product block with less than float32 precision
  * (about 3e-4 of the block's sum of |products|).
@@ -265,8 +267,9 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
  *   x_buf      MXFP8 receive buffer of ep_dispatch (region form), rows = max_rows
  *   hidden     H (K of GMM1), H % 64 == 0
  *   inter      I, I % 64 == 0
- *   w1         codes [E, 2I, H]: rows 0..I-1 are the gate rows, I..2I-1 the up rows;
- *   w1_scales  [E, 2I, H/32]
+ *   w1         packed codes of [E, 2I, H] (gate_up = 1): rows 0..I-1 are the
+ *              gate rows, I..2I-1 the up rows;
+ *   w1_scales  packed scales of [E, 2I, H/32]
  *   out_quant  EP_QUANT_MXFP8: row r of out_buf (an MXFP8 receive buffer of
  *              width I, region form) gets MXFP8(a) with the MX rule of
  *              dispatch; EP_QUANT_NONE: bf16(a) [max_rows, I]
@@ -274,10 +277,29 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
  *   silu(z) = z / (1 + exp(-z)).  Rows holding no pair are not written.
  * ep_moe_gmm2: GMM2.
  *   a_buf      MXFP8 receive buffer of width I (ep_moe_gmm1's output)
- *   w2         codes [E, H, I], w2_scales [E, H, I/32]; H % 128 == 0
+ *   w2         packed codes of [E, H, I] (gate_up = 0), w2_scales packed
+ *              scales of [E, H, I/32]; H % 128 == 0
  *   out_buf    bf16 [max_rows, H]: row r gets bf16(W2[e] . a_r), the
  *              expert-output rows ep_combine reads (in_quant EP_QUANT_NONE)
  */
+/* Bytes of packed codes and packed scales for E experts of N rows of K
+ * codes (host only); EP_ERR_INVALID_ARG unless N % 32 == 0, K % 64 == 0. */
+ep_status_t ep_moe_packed_bytes(int32_t num_experts, int32_t rows, int32_t k, size_t *codes_bytes,
+                                size_t *scales_bytes);
+
+/* Packs MXFP8 weights codes [E, N, K] and scales [E, N, K/32] (device,
+ * dense) into packed_codes / packed_scales (device, sizes from
+ * ep_moe_packed_bytes, 16-byte aligned).  gate_up = 1 for W1 (N = 2I: a
+ * wave's 32 rows are 16 gate rows and the matching 16 up rows), 0 for W2.
+ * Layout: for each group of 32 rows and 64-wide K step a 2048-byte
+ * fragment, lane l = 32g + r holding K bytes [16g, 16g+16) of the group's
+ * row r at 16l and K bytes [32+16g, 48+16g) at 1024 + 16l; for each group
+ * and span of four K steps 256 scale bytes, lane l's four at 4l (step
+ * 4t+u's K-block 2(4t+u)+g of row r, zero past the last step). */
+ep_status_t ep_moe_pack_weights(const void *codes, const void *scales, int32_t num_experts, int32_t rows,
+                                int32_t k, int32_t gate_up, void *packed_codes, void *packed_scales,
+                                void *stream);
+
 ep_status_t ep_moe_gmm1(const ep_handle_t *handle, const int64_t *recv_count, const void *x_buf,
                         size_t x_buf_bytes, int32_t hidden, int32_t inter, const void *w1,
                         const void *w1_scales, ep_quant_t out_quant, void *out_buf, size_t out_buf_bytes,

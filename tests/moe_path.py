@@ -34,12 +34,12 @@ def gpu_moe(ep, w: W.MoeWorkload, inp: dict, *, out_quant="mxfp8", pass_count=Tr
     xb, _ = ep.ep_buffer_bytes(rows, w.H, "mxfp8")
     recv = canary_buffer(xb)
     ep.ep_dispatch(h, to_dev(inp["x"]), w.H, "mxfp8", recv)
-    w1c, w1s = to_dev(inp["w1_codes"]), to_dev(inp["w1_scales"])
-    w2c, w2s = to_dev(inp["w2_codes"]), to_dev(inp["w2_scales"])
+    w1c, w1s = ep.pack_moe_weights(to_dev(inp["w1_codes"]), to_dev(inp["w1_scales"]), True)
+    w2c, w2s = ep.pack_moe_weights(to_dev(inp["w2_codes"]), to_dev(inp["w2_scales"]), False)
     ab, _ = ep.ep_buffer_bytes(rows, w.I, out_quant)
     a = canary_buffer(ab)
     ep.ep_moe_gmm1(h, recv, w.H, w.I, w1c, w1s, out_quant, a, recv_count=rc if pass_count else None)
-    res = {"handle": h, "ws": ws, "rc": rc, "recv": recv, "a": a}
+    res = {"handle": h, "ws": ws, "rc": rc, "recv": recv, "a": a, "w2": (w2c, w2s)}
     if stop_after == "gmm1":
         torch.cuda.synchronize()
         return res

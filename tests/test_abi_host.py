@@ -275,3 +275,32 @@ def test_flag_mapping(ep):
                   dict(use_fp8=True, use_mxfp4=True)]:
         assert ep.quant_mode(**flags) == OV.check_flags(flags.get("use_fp8"), flags.get("use_ue8m0", False),
                                                         flags.get("use_mxfp4", False), False, False)
+
+
+def test_moe_packed_bytes(ep):
+    assert ep.ep_moe_packed_bytes(6, 6144, 7168) == (6 * 6144 * 7168, 6 * (6144 // 32) * 28 * 256)
+    assert ep.ep_moe_packed_bytes(1, 32, 320) == (32 * 320, 2 * 256)          # 5 steps -> 2 spans
+    for bad in ((0, 32, 64), (1, 48, 64), (1, 32, 96), (513, 32, 64)):
+        with pytest.raises(ep.EpError):
+            ep.ep_moe_packed_bytes(*bad)
+
+
+MOE_BAD = [(dict(hidden=96), 1), (dict(inter=100), 1), (dict(out_quant=2), 1), (dict(x=None), 1),
+           (dict(w1=FAKE + 8), 1), (dict(out_bytes=10), 3)]
+
+
+@pytest.mark.parametrize("kw,code", MOE_BAD)
+def test_moe_gmm1_rejects(ep, kw, code):
+    h = _handle(ep)
+    rc = ep._lib.ep_moe_gmm1(ctypes.byref(h), None, kw.get("x", FAKE), 1 << 30, kw.get("hidden", 256),
+                             kw.get("inter", 128), kw.get("w1", FAKE), FAKE, kw.get("out_quant", 3), FAKE,
+                             kw.get("out_bytes", 1 << 30), None)
+    assert rc == code, ep.ep_last_error()
+    assert ep.ep_last_error().startswith("ep_moe_gmm1")
+
+
+def test_moe_gmm2_rejects(ep):
+    h = _handle(ep)
+    assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 1 << 30, 128, 192, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 1 << 30, 96, 256, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 8, 128, 256, FAKE, FAKE, FAKE, 1 << 30, None) == 3

@@ -147,7 +147,7 @@ def test_gmm2_on_shared_input(ep):
     shared = OD.RecvBuffer("mxfp8", w.I, rows, ac[0], asc[0], None)
     a_buf = to_dev(shared.to_bytes())
     y = canary_buffer(rows * w.H * 2)
-    ep.ep_moe_gmm2(h, a_buf, w.I, w.H, to_dev(inp["w2_codes"]), to_dev(inp["w2_scales"]), y, recv_count=res["rc"])
+    ep.ep_moe_gmm2(h, a_buf, w.I, w.H, res["w2"][0], res["w2"][1], y, recv_count=res["rc"])
     torch.cuda.synchronize()
     got = codecs.bf16_bits_to_f32(_bf16_rows(y, rows, w.H)).astype(np.float64)
     rc = res["rc"].cpu().numpy()
@@ -230,3 +230,37 @@ def test_share_full_size_sampled(ep):
         print(f"expert {e}: {f:.4f} of the codes differ")
     worst = _check_end_to_end(res["out"][toks], out)
     print(f"worst row relative error {worst:.3g}")
+
+
+def _pack_reference(codes, scales, gate_up):
+    """The packed layout of ep_moe_pack_weights built with numpy indexing
+    from its description in include/ep.h (a permutation of the bytes)."""
+    E, N, K = codes.shape
+    ks, G, inter = K // 64, N // 32, N // 2
+    spans = (ks + 3) // 4
+    lanes = np.arange(64)
+    r, g = lanes % 32, lanes // 32
+    pc = np.zeros((E, G, ks, 2, 64, 16), np.uint8)
+    ps = np.zeros((E, G, spans, 64, 4), np.uint8)
+    for j in range(G):
+        rows = np.where(r < 16, 16 * j + r, inter + 16 * j + r - 16) if gate_up else 32 * j + r
+        for s in range(ks):
+            for half in range(2):
+                cols = s * 64 + half * 32 + g[:, None] * 16 + np.arange(16)[None, :]
+                pc[:, j, s, half] = codes[:, rows[:, None], cols]
+        for t in range(spans):
+            for u in range(4):
+                if 4 * t + u < ks:
+                    ps[:, j, t, :, u] = scales[:, rows, (4 * t + u) * 2 + g]
+    return pc.reshape(-1), ps.reshape(-1)
+
+
+@pytest.mark.parametrize("gate_up", [True, False])
+def test_pack_weights_layout(ep, gate_up):
+    _announce(f"pack weights layout gate_up={gate_up}")
+    codes, scales = W.make_mx_weights(77, 2, 128, 320)              # 5 K steps: a ragged last scale span
+    pc, ps = ep.pack_moe_weights(to_dev(codes), to_dev(scales), gate_up)
+    torch.cuda.synchronize()
+    want_c, want_s = _pack_reference(codes, scales, gate_up)
+    assert np.array_equal(pc.cpu().numpy(), want_c)
+    assert np.array_equal(ps.cpu().numpy(), want_s)
