@@ -177,6 +177,43 @@ __global__ void pack_weights_kernel(const uint8_t *__restrict__ codes, const uin
   }
 }
 
+// Weight loads are streamed (each weight byte is read once per launch);
+// activation rows are shared by the workgroups of an expert through L2.
+#ifndef EP_MOE_W_NT
+#define EP_MOE_W_NT 1
+#endif
+#ifndef EP_MOE_A_NT
+#define EP_MOE_A_NT 0
+#endif
+template <typename T>
+__device__ __forceinline__ T ld_w(const uint8_t *p) {
+#if EP_MOE_W_NT
+  return __builtin_nontemporal_load((const T *)p);
+#else
+  return *(const T *)p;
+#endif
+}
+template <typename T>
+__device__ __forceinline__ T ld_a(const uint8_t *p) {
+#if EP_MOE_A_NT
+  return __builtin_nontemporal_load((const T *)p);
+#else
+  return *(const T *)p;
+#endif
+}
+
+// The MX-scaled matrix-core step with the B scale taken from byte `u` of
+// `bsc` (the instruction's op_sel picks the byte, so no extraction is needed;
+// u is a constant wherever this is inlined in the unrolled loop).
+__device__ __forceinline__ v16f mfma_b_byte(int u, const v8i &a, const v8i &b, const v16f &c, int as, int bs) {
+  switch (u) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, as, 0, bs);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, as, 1, bs);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, as, 2, bs);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, as, 3, bs);
+  }
+}
+
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() carries a
 // release fence, which on this target waits for every outstanding vector
 // memory operation -- loads included -- and so would drain the weight loads
@@ -232,7 +269,7 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   auto load_a = [&](int s, int set) {
     const int ss = min(s, ksteps - 1);
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i) areg[set][i] = *(const u32x4 *)(apiece[i] + (size_t)ss * kKStep);
+    for (int i = 0; i < kPieces; ++i) areg[set][i] = ld_a<u32x4>(apiece[i] + (size_t)ss * kKStep);
     asreg[set] = *(const uint16_t *)(ascale + ss * 2);
   };
   auto store_a = [&](int buf, int set) {
@@ -243,18 +280,20 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   };
 
   // weight ring: kRing K steps of two 16-byte pieces (each wave load reads
-  // 1 KB in one piece); scales one dword per span of four steps (current
-  // span and the next one in flight)
+  // 1 KB in one piece) and the scale dword of the step's span of four.
+  // Slot u is refilled only after the matrix-core instructions that read it
+  // are issued, so a slot keeps one register across the loop: no copy of a
+  // register a load is still writing (a copy would wait for that load and
+  // every load before it).
   constexpr int kRing = 4;
-  static_assert(kRing == 4, "one scale span per ring cycle");
   u32x4 wb0[kRing], wb1[kRing];
-  uint32_t wsc_cur, wsc_nxt;
+  uint32_t wsc[kRing];
   auto load_w = [&](int s, int slot) {
     const int ss = min(s, ksteps - 1);                             // loads past the end are never used
-    wb0[slot] = *(const u32x4 *)(wp + (size_t)ss * 2048);
-    wb1[slot] = *(const u32x4 *)(wp + (size_t)ss * 2048 + 1024);
+    wb0[slot] = ld_w<u32x4>(wp + (size_t)ss * 2048);
+    wb1[slot] = ld_w<u32x4>(wp + (size_t)ss * 2048 + 1024);
+    wsc[slot] = ld_w<uint32_t>(wsp + (size_t)(ss >> 2) * 256);
   };
-  auto load_ws = [&](int span) { return *(const uint32_t *)(wsp + (size_t)min(span, spans - 1) * 256); };
 
   v16f acc[NF];
 #pragma unroll
@@ -269,25 +308,18 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   load_a(3, 3);
 #pragma unroll
   for (int q = 0; q < kRing; ++q) load_w(q, q);
-  wsc_cur = load_ws(0);
-  wsc_nxt = load_ws(1);
   lds_barrier();
 
   // step s: write A(s+1) (loaded three steps ago, register set (s+1) % 4) to
   // LDS buffer (s+1)&1, load A(s+4) into set s % 4 (free since step s-1),
-  // compute step s from buffer s&1 with weight slot s % kRing and refill
+  // compute step s from buffer s&1 with weight slot s % kRing, then refill
   // that slot with step s + kRing
   auto step = [&](int s, int u) {
     store_a((s + 1) & 1, (u + 1) % kASets);
     load_a(s + 4, u % kASets);
-    const u32x4 b0 = wb0[u], b1 = wb1[u];
-    const int bsc = (int)((wsc_cur >> (8 * u)) & 0xffu);
-    load_w(s + kRing, u);
-    if (u == kRing - 1) {                                            // static: next span, and the one after in flight
-      wsc_cur = wsc_nxt;
-      wsc_nxt = load_ws(s / 4 + 2);
-    }
-    const v8i bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    const v8i bv = {(int)wb0[u].x, (int)wb0[u].y, (int)wb0[u].z, (int)wb0[u].w,
+                    (int)wb1[u].x, (int)wb1[u].y, (int)wb1[u].z, (int)wb1[u].w};
+    const int bsc = (int)wsc[u];                                   // byte s & 3 == u, picked by op_sel
     const uint8_t *base = smem + (s & 1) * (kStage + kScaleStage);
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -296,8 +328,9 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
       const u32x4 x1 = *(const u32x4 *)(base + row * kRowStride + 32 + g * 16);
       const int xs = (int)base[kStage + row * 2 + g];
       const v8i av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      acc[f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[f], 0, 0, 0, xs, 0, bsc);
+      acc[f] = mfma_b_byte(u, av, bv, acc[f], xs, bsc);
     }
+    load_w(s + kRing, u);
     lds_barrier();
   };
   int s0 = 0;
