@@ -300,9 +300,9 @@ ep_status_t ep_moe_gmm1(const ep_handle_t *handle, const int64_t *recv_count, co
   const char *fn = "ep_moe_gmm1";
   ep_status_t st = check_handle(handle, fn);
   if (st != EP_OK) return st;
-  if (hidden <= 0 || hidden % 64 != 0 || inter <= 0 || inter % 64 != 0)
-    return fail(EP_ERR_INVALID_ARG, "%s: hidden and inter must be positive multiples of 64 (got %d, %d)", fn, hidden,
-                inter);
+  if (hidden <= 0 || hidden % 128 != 0 || inter <= 0 || inter % 64 != 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: need hidden a positive multiple of 128 and inter of 64 (got %d, %d)", fn,
+                hidden, inter);
   if (hidden > kMaxHidden || inter > kMaxHidden)
     return fail(EP_ERR_UNSUPPORTED, "%s: hidden / inter above %d", fn, kMaxHidden);
   if (out_quant != EP_QUANT_MXFP8 && out_quant != EP_QUANT_NONE)
@@ -328,9 +328,9 @@ ep_status_t ep_moe_gmm2(const ep_handle_t *handle, const int64_t *recv_count, co
   const char *fn = "ep_moe_gmm2";
   ep_status_t st = check_handle(handle, fn);
   if (st != EP_OK) return st;
-  if (inter <= 0 || inter % 64 != 0 || hidden <= 0 || hidden % 128 != 0)
-    return fail(EP_ERR_INVALID_ARG, "%s: inter must be a positive multiple of 64 and hidden of 128 (got %d, %d)", fn,
-                inter, hidden);
+  if (inter <= 0 || inter % 128 != 0 || hidden <= 0 || hidden % 128 != 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: inter and hidden must be positive multiples of 128 (got %d, %d)", fn, inter,
+                hidden);
   if (hidden > kMaxHidden || inter > kMaxHidden)
     return fail(EP_ERR_UNSUPPORTED, "%s: hidden / inter above %d", fn, kMaxHidden);
   if (!a_buf || !aligned(a_buf, 16) || !out_buf || !aligned(out_buf, 16))

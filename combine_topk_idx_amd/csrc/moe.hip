@@ -22,8 +22,8 @@
 // follow an exact dot product.
 //
 // Mapping: a workgroup (4 waves) owns one (expert, chunk of up to 160 rows,
-// N tile).  The chunk's A rows are staged through double-buffered LDS one
-// 64-wide K step at a time and shared by the 4 waves; every wave streams its
+// N tile).  The chunk's A rows are staged through double-buffered LDS two
+// 64-wide K steps at a time and shared by the 4 waves; every wave streams its
 // own 32 weight rows (B) straight into registers, eight K steps ahead
 // (weights are read once from HBM: they are the traffic that bounds the
 // kernel at the shapes of the benchmark).  GMM1 gives each wave 16 gate and
@@ -46,15 +46,21 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxFrags = 5;                      // 32-row fragments per chunk
 constexpr int kChunkRows = kMaxFrags * 32;        // rows per work item
 constexpr int kKStep = 64;                        // K per matrix-core step
-constexpr int kRowStride = 80;                    // LDS bytes per staged A row (64 + pad)
-// Every thread moves the same number of 16-byte A pieces per step, so a
-// stage holds slots for that many pieces of every thread (rows past the
-// chunk are loaded from its last row and never read), and one scale pair
-// per thread.
-constexpr int kPiecesMax = (kChunkRows * 4 + kThreads - 1) / kThreads;
-constexpr int kStageRows = kPiecesMax * kThreads / 4;
-constexpr int kStage = kStageRows * kRowStride;   // bytes of one staged A step
-constexpr int kScaleStage = kThreads * 2;         // scale bytes of one staged A step
+// The chunk's A rows are staged two K steps (128 bytes of a row, one full
+// cache line) at a time; a padded row stride of 144 bytes puts the 16-byte
+// fragment reads of 16 consecutive rows in distinct LDS banks.  Every thread
+// moves NF pieces of 16 bytes per stage (NF * 32 rows * 8 pieces / 256).
+constexpr int kStageSteps = 2;
+constexpr int kStageK = kStageSteps * kKStep;     // K bytes of a row per stage
+constexpr int kRowStride = kStageK + 16;          // LDS bytes per staged A row
+constexpr int kAStage = kChunkRows * kRowStride;  // bytes of one staged A block
+// A scale bytes are loaded 16 per row (eight K steps) at a time into a
+// double-buffered table of kThreads rows, padded to 20 bytes so that the
+// byte reads of 32 consecutive rows fall in distinct banks.
+constexpr int kBodySteps = 8;
+constexpr int kScaleStride = 20;
+constexpr int kScaleBuf = kThreads * kScaleStride;
+constexpr int kStaging = 2 * kAStage + 2 * kScaleBuf;
 constexpr int kEpiCols = 64;                      // GMM1 SwiGLU columns per workgroup
 constexpr int kEpiStride = kEpiCols + 1;          // floats per LDS row of the epilogue tile
 
@@ -232,14 +238,17 @@ struct GemmArgs {
   int out_cols;
 };
 
-// Main loop and epilogue for a chunk of NF 32-row fragments.
+// Main loop and epilogue for a chunk of NF 32-row fragments.  K is a
+// multiple of 128 (whole stages).
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 template <int MODE, int NF>
 __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, int ntile, uint8_t *smem) {
-  constexpr int kPieces = (NF * 32 * 4 + kThreads - 1) / kThreads;   // 16-byte A pieces per thread per step
-  static_assert(kPieces <= kPiecesMax && kPieces * kThreads / 4 <= kStageRows, "A slots fit the stage");
+  constexpr int kPieces = NF;                                     // 16-byte A pieces per thread per stage
+  static_assert(NF * 32 * (kStageK / 16) == kPieces * kThreads, "pieces cover the stage exactly");
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int r = lane & 31, g = lane >> 5;
-  const int K = p.K, ksteps = K / kKStep, kb = K / 32;
+  const int K = p.K, ksteps = K / kKStep, nstages = ksteps / kStageSteps, kb = K / 32;
 
   // this wave's packed weight group (see pack_weights_kernel): fragments of
   // 2048 bytes per K step, scale dwords per span of four steps
@@ -249,34 +258,48 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   const uint8_t *wp = p.w + gidx * (size_t)ksteps * 2048 + lane * 16;
   const uint8_t *wsp = p.w_scales + gidx * (size_t)spans * 256 + lane * 4;
 
-  // A staging, branch-free: piece i of this thread is (row, quarter) =
-  // (idx >> 2, idx & 3) of the chunk; rows past the chunk read its last row
-  // (their LDS slots exist and are never used)
+  // A staging, branch-free: piece i of this thread is (row, 16-byte piece) =
+  // (idx >> 3, idx & 7) of the stage, so 8 lanes read one 128-byte line;
+  // rows past the chunk read its last row (their LDS rows are never used)
   const uint8_t *apiece[kPieces];
   int lpiece[kPieces];
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
     const int idx = threadIdx.x + i * kThreads;
-    const int row = idx >> 2, q = idx & 3;
+    const int row = idx >> 3, q = idx & 7;
     apiece[i] = p.a_data + (size_t)(it.row0 + min(row, it.rows - 1)) * K + q * 16;
     lpiece[i] = row * kRowStride + q * 16;
   }
-  const uint8_t *ascale = p.a_scales + (size_t)(it.row0 + min((int)threadIdx.x, it.rows - 1)) * kb;
-
-  constexpr int kASets = 4;                                       // A loads run three steps ahead
-  u32x4 areg[kASets][kPieces];
-  uint32_t asreg[kASets];
-  auto load_a = [&](int s, int set) {
-    const int ss = min(s, ksteps - 1);
+  u32x4 areg[2][kPieces];                                         // A loads run two stages ahead
+  auto load_a = [&](int j, int set) {
+    const int jj = min(j, nstages - 1);                           // loads past the end are never used
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i) areg[set][i] = ld_a<u32x4>(apiece[i] + (size_t)ss * kKStep);
-    asreg[set] = *(const uint16_t *)(ascale + ss * 2);
+    for (int i = 0; i < kPieces; ++i) areg[set][i] = ld_a<u32x4>(apiece[i] + (size_t)jj * kStageK);
   };
   auto store_a = [&](int buf, int set) {
-    uint8_t *base = smem + buf * (kStage + kScaleStage);
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i) *(u32x4 *)(base + lpiece[i]) = areg[set][i];
-    *(uint16_t *)(base + kStage + threadIdx.x * 2) = (uint16_t)asreg[set];
+    for (int i = 0; i < kPieces; ++i) *(u32x4 *)(smem + buf * kAStage + lpiece[i]) = areg[set][i];
+  };
+
+  // A scales: thread t keeps row t's 16 scale bytes of the next eight K steps
+  // (body b covers steps [8b, 8b + 8)); the table row of thread t is t.  A
+  // body's 16 bytes start at byte min(16b, kb - 16) of the row, so a partial
+  // last body reads in bounds and its reader adds back the shift.
+  const uint8_t *srow = p.a_scales + (size_t)(it.row0 + min((int)threadIdx.x, it.rows - 1)) * kb;
+  uint32_t *sc_st = (uint32_t *)(smem + 2 * kAStage + threadIdx.x * kScaleStride);
+  u32x4_a4 sc;
+  auto load_sc = [&](int body) { sc = ld_a<u32x4_a4>(srow + min(16 * body, kb - 16)); };
+  auto store_sc = [&](int buf) {
+    uint32_t *d = sc_st + buf * (kScaleBuf / 4);
+    d[0] = sc.x;
+    d[1] = sc.y;
+    d[2] = sc.z;
+    d[3] = sc.w;
+  };
+  const uint8_t *sc_rd0 = smem + 2 * kAStage + r * kScaleStride + g;
+  auto sc_reader = [&](int body) {
+    const int shift = body == 0 ? 0 : 16 * body - min(16 * body, kb - 16);
+    return sc_rd0 + (body & 1) * kScaleBuf + shift;
   };
 
   // weight ring: kRing K steps of two 16-byte pieces (each wave load reads
@@ -286,6 +309,7 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   // register a load is still writing (a copy would wait for that load and
   // every load before it).
   constexpr int kRing = 4;
+  static_assert(kBodySteps % kRing == 0, "slots are fixed within a body");
   u32x4 wb0[kRing], wb1[kRing];
   uint32_t wsc[kRing];
   auto load_w = [&](int s, int slot) {
@@ -299,48 +323,65 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = v16f{};
 
-  // prologue: A step 0 in LDS buffer 0, steps 1..3 in register sets 1..3;
-  // weight steps 0 .. kRing-1 in flight
+  // prologue: A stage 0 and body 0's scales in LDS buffer 0 (the scales as
+  // four dword loads clamped to the row, which may be shorter than 16 bytes);
+  // A stage 1 in register set 1, stage 2 in set 0; weight steps 0 .. kRing-1
+  // in flight
   load_a(0, 0);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) sc[d] = *(const uint32_t *)(srow + min(4 * d, kb - 4));
   store_a(0, 0);
+  store_sc(0);
   load_a(1, 1);
-  load_a(2, 2);
-  load_a(3, 3);
+  load_a(2, 0);
 #pragma unroll
   for (int q = 0; q < kRing; ++q) load_w(q, q);
   lds_barrier();
 
-  // step s: write A(s+1) (loaded three steps ago, register set (s+1) % 4) to
-  // LDS buffer (s+1)&1, load A(s+4) into set s % 4 (free since step s-1),
-  // compute step s from buffer s&1 with weight slot s % kRing, then refill
-  // that slot with step s + kRing
-  auto step = [&](int s, int u) {
-    store_a((s + 1) & 1, (u + 1) % kASets);
-    load_a(s + 4, u % kASets);
-    const v8i bv = {(int)wb0[u].x, (int)wb0[u].y, (int)wb0[u].z, (int)wb0[u].w,
-                    (int)wb1[u].x, (int)wb1[u].y, (int)wb1[u].z, (int)wb1[u].w};
-    const int bsc = (int)wsc[u];                                   // byte s & 3 == u, picked by op_sel
-    const uint8_t *base = smem + (s & 1) * (kStage + kScaleStage);
+  // stage j (i = j % 4 within its body): write A(j+1) (register set
+  // (j+1) % 2, loaded two stages ago) to LDS buffer (j+1) & 1 and reload the
+  // set with A(j+3); in a full body, stage 0 loads the next body's scales and
+  // stage 3 writes them to their table; then the two K steps of stage j from
+  // buffer j & 1, each followed by the refill of its weight slot; one barrier
+  // per stage
+  auto stage = [&](int j, int i, bool full, int body, const uint8_t *sc_rd) {
+    store_a((i + 1) & 1, (i + 1) & 1);
+    load_a(j + 3, (i + 1) & 1);
+    if (full && i == 0) load_sc(body + 1);
+    if (full && i == 3) store_sc((body + 1) & 1);
+    const uint8_t *abase = smem + (i & 1) * kAStage;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int row = f * 32 + r;
-      const u32x4 x0 = *(const u32x4 *)(base + row * kRowStride + g * 16);
-      const u32x4 x1 = *(const u32x4 *)(base + row * kRowStride + 32 + g * 16);
-      const int xs = (int)base[kStage + row * 2 + g];
-      const v8i av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      acc[f] = mfma_b_byte(u, av, bv, acc[f], xs, bsc);
+    for (int h = 0; h < kStageSteps; ++h) {
+      const int sb = kStageSteps * i + h;                          // step within the body
+      const int u = sb % kRing;
+      const v8i bv = {(int)wb0[u].x, (int)wb0[u].y, (int)wb0[u].z, (int)wb0[u].w,
+                      (int)wb1[u].x, (int)wb1[u].y, (int)wb1[u].z, (int)wb1[u].w};
+      const int bsc = (int)wsc[u];                                 // byte sb & 3 of the span dword, by op_sel
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int row = f * 32 + r;
+        const u32x4 x0 = *(const u32x4 *)(abase + row * kRowStride + h * kKStep + g * 16);
+        const u32x4 x1 = *(const u32x4 *)(abase + row * kRowStride + h * kKStep + 32 + g * 16);
+        const int xs = (int)sc_rd[f * 32 * kScaleStride + 2 * sb];
+        const v8i av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        acc[f] = mfma_b_byte(sb & 3, av, bv, acc[f], xs, bsc);
+      }
+      load_w(kStageSteps * j + h + kRing, u);
     }
-    load_w(s + kRing, u);
     lds_barrier();
   };
-  int s0 = 0;
-  for (; s0 + kRing <= ksteps; s0 += kRing) {
+  int j0 = 0, body = 0;
+  for (; (j0 + 4) * kStageSteps <= ksteps; j0 += 4, ++body) {
+    const uint8_t *sc_rd = sc_reader(body);
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) step(s0 + u, u);
+    for (int i = 0; i < 4; ++i) stage(j0 + i, i, true, body, sc_rd);
   }
+  {
+    const uint8_t *sc_rd = sc_reader(body);
 #pragma unroll
-  for (int u = 0; u < kRing; ++u)
-    if (s0 + u < ksteps) step(s0 + u, u);                           // uniform tail
+    for (int i = 0; i < 3; ++i)
+      if (j0 + i < nstages) stage(j0 + i, i, false, body, sc_rd);  // uniform tail
+  }
   // every load issued past the last step targets registers nobody reads;
   // let them land before the registers and the kernel go away
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -420,7 +461,6 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void mx_gmm_kernel(GemmArgs p, const int *__restrict__ offsets,
                                                           const int64_t *__restrict__ recv_count, int E) {
-  constexpr int kStaging = 2 * (kStage + kScaleStage);
   constexpr int kTile = MODE == kGmm2 ? 0 : kChunkRows * kEpiStride * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kTile ? kStaging : kTile];
   int ntile;

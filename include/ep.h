@@ -265,7 +265,7 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
  *
  * ep_moe_gmm1: GMM1 + SwiGLU.
  *   x_buf      MXFP8 receive buffer of ep_dispatch (region form), rows = max_rows
- *   hidden     H (K of GMM1), H % 64 == 0
+ *   hidden     H (K of GMM1), H % 128 == 0
  *   inter      I, I % 64 == 0
  *   w1         packed codes of [E, 2I, H] (gate_up = 1): rows 0..I-1 are the
  *              gate rows, I..2I-1 the up rows;
@@ -276,7 +276,8 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
  *   where a_n = silu(g_n) * u_n in float32, g = gate rows . x, u = up rows . x,
  *   silu(z) = z / (1 + exp(-z)).  Rows holding no pair are not written.
  * ep_moe_gmm2: GMM2.
- *   a_buf      MXFP8 receive buffer of width I (ep_moe_gmm1's output)
+ *   a_buf      MXFP8 receive buffer of width I (ep_moe_gmm1's output);
+ *              I % 128 == 0
  *   w2         packed codes of [E, H, I] (gate_up = 0), w2_scales packed
  *              scales of [E, H, I/32]; H % 128 == 0
  *   out_buf    bf16 [max_rows, H]: row r gets bf16(W2[e] . a_r), the

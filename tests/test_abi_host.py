@@ -285,7 +285,7 @@ def test_moe_packed_bytes(ep):
             ep.ep_moe_packed_bytes(*bad)
 
 
-MOE_BAD = [(dict(hidden=96), 1), (dict(inter=100), 1), (dict(out_quant=2), 1), (dict(x=None), 1),
+MOE_BAD = [(dict(hidden=96), 1), (dict(hidden=192), 1), (dict(inter=100), 1), (dict(out_quant=2), 1), (dict(x=None), 1),
            (dict(w1=FAKE + 8), 1), (dict(out_bytes=10), 3)]
 
 
@@ -303,4 +303,5 @@ def test_moe_gmm2_rejects(ep):
     h = _handle(ep)
     assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 1 << 30, 128, 192, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 1 << 30, 96, 256, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 1 << 30, 192, 256, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 8, 128, 256, FAKE, FAKE, FAKE, 1 << 30, None) == 3
