@@ -13,6 +13,7 @@
 #include <cstring>
 
 #include "common.hpp"
+#include "moe.hpp"
 
 namespace {
 

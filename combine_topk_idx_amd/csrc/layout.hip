@@ -23,11 +23,11 @@
 // cap-th of an expert are dropped and set a status bit).  Rows that hold no
 // pair get row_src -1.
 //
-// Small problems (pairs <= 4096) run in one workgroup that also does the scan
+// Small problems (pairs <= 6144) run in one workgroup that also does the scan
 // over experts and writes every output: one launch (padded arrangements with
 // many rows add workgroups that only clear free rows).  (All of its waves share
 // one CU, so its cost grows by about a microsecond per 64-pair step of a
-// wave; past 4096 pairs two launches are faster.)  Larger ones run in two
+// wave, against about four for a second launch.)  Larger ones run in two
 // launches over 2048-pair chunks: rank (per-chunk counts and ranks), then
 // finalize (each workgroup redoes the small scan over chunk counts itself).
 #include "common.hpp"
@@ -39,7 +39,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kSingleItems = 4;                    // up to 4 * 1024 pairs in one workgroup
+constexpr int kSingleItems = 6;                    // up to 6 * 1024 pairs in one workgroup
 constexpr int kMultiItems = EP_LAYOUT_ITEMS;       // pairs per thread in a multi-block chunk
 constexpr int kMultiChunk = kMultiItems * kThreads;
 constexpr int64_t kSingleMaxPairs = (int64_t)kSingleItems * kThreads;

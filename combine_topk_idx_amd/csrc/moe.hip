@@ -32,6 +32,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "moe.hpp"
 #include "formats.hpp"
 
 namespace ep {
@@ -191,6 +192,14 @@ __global__ void pack_weights_kernel(const uint8_t *__restrict__ codes, const uin
 #ifndef EP_MOE_A_NT
 #define EP_MOE_A_NT 0
 #endif
+// stages of A in flight per thread
+#ifndef EP_MOE_ASETS
+#define EP_MOE_ASETS 2
+#endif
+// K steps of weights in flight per wave
+#ifndef EP_MOE_RING
+#define EP_MOE_RING 4
+#endif
 template <typename T>
 __device__ __forceinline__ T ld_w(const uint8_t *p) {
 #if EP_MOE_W_NT
@@ -270,7 +279,9 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
     apiece[i] = p.a_data + (size_t)(it.row0 + min(row, it.rows - 1)) * K + q * 16;
     lpiece[i] = row * kRowStride + q * 16;
   }
-  u32x4 areg[2][kPieces];                                         // A loads run two stages ahead
+  constexpr int kASets = EP_MOE_ASETS;                            // A loads run kASets stages ahead
+  static_assert(4 % kASets == 0, "sets are fixed within a body");
+  u32x4 areg[kASets][kPieces];
   auto load_a = [&](int j, int set) {
     const int jj = min(j, nstages - 1);                           // loads past the end are never used
 #pragma unroll
@@ -308,7 +319,7 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   // are issued, so a slot keeps one register across the loop: no copy of a
   // register a load is still writing (a copy would wait for that load and
   // every load before it).
-  constexpr int kRing = 4;
+  constexpr int kRing = EP_MOE_RING;
   static_assert(kBodySteps % kRing == 0, "slots are fixed within a body");
   u32x4 wb0[kRing], wb1[kRing];
   uint32_t wsc[kRing];
@@ -325,28 +336,29 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
 
   // prologue: A stage 0 and body 0's scales in LDS buffer 0 (the scales as
   // four dword loads clamped to the row, which may be shorter than 16 bytes);
-  // A stage 1 in register set 1, stage 2 in set 0; weight steps 0 .. kRing-1
-  // in flight
+  // A stages 1 .. kASets in register sets 1 .. kASets-1, 0; weight steps
+  // 0 .. kRing-1 in flight
   load_a(0, 0);
 #pragma unroll
   for (int d = 0; d < 4; ++d) sc[d] = *(const uint32_t *)(srow + min(4 * d, kb - 4));
   store_a(0, 0);
   store_sc(0);
-  load_a(1, 1);
-  load_a(2, 0);
+#pragma unroll
+  for (int q = 1; q < kASets; ++q) load_a(q, q);
+  load_a(kASets, 0);
 #pragma unroll
   for (int q = 0; q < kRing; ++q) load_w(q, q);
   lds_barrier();
 
   // stage j (i = j % 4 within its body): write A(j+1) (register set
-  // (j+1) % 2, loaded two stages ago) to LDS buffer (j+1) & 1 and reload the
-  // set with A(j+3); in a full body, stage 0 loads the next body's scales and
+  // (j+1) % kASets, loaded kASets stages ago) to LDS buffer (j+1) & 1 and
+  // reload the set with A(j+1+kASets); in a full body, stage 0 loads the next body's scales and
   // stage 3 writes them to their table; then the two K steps of stage j from
   // buffer j & 1, each followed by the refill of its weight slot; one barrier
   // per stage
   auto stage = [&](int j, int i, bool full, int body, const uint8_t *sc_rd) {
-    store_a((i + 1) & 1, (i + 1) & 1);
-    load_a(j + 3, (i + 1) & 1);
+    store_a((i + 1) & 1, (i + 1) % kASets);
+    load_a(j + 1 + kASets, (i + 1) % kASets);
     if (full && i == 0) load_sc(body + 1);
     if (full && i == 3) store_sc((body + 1) & 1);
     const uint8_t *abase = smem + (i & 1) * kAStage;

@@ -4,7 +4,7 @@ Covers: empty input (T = 0), capacity larger than T, tokens with no routed
 pair, duplicate experts in a row, out-of-range ids (status bit), k = 1 and
 k = 16, E = 1 and E = 512, hidden sizes that are and are not multiples of 128
 (MX scale packing), ragged tails of the row tiling, int32 and int64 ids, the
-multi-workgroup layout path (more than 16384 pairs), every bf16 bit pattern
+multi-workgroup layout path (more than 6144 pairs) and both sides of that limit, every bf16 bit pattern
 through every quantiser, blocks of zeros, subnormals and huge values (for the
 power-of-two per-128 scales this includes the last kept exponent, -127, and
 the zeroed blocks below it).
@@ -70,6 +70,8 @@ CASES = [
     (14, 3000, 512, 64, 8, "fp8_b128_ue8m0", "int32", 0.05, 3000, "identity"),  # multi-block layout
     (15, 7, 384, 8, 2, "fp8_b128_ue8m0", "int64", 0.0, 7, "identity"),     # 3 scale bytes per row
     (16, 128, 7168, 256, 8, "fp8_b128_pow2", "int64", 0.1, 128, "identity"),
+    (17, 768, 256, 48, 8, "mxfp8", "int64", 0.1, 768, "identity"),     # one-workgroup layout at 6144 pairs
+    (18, 769, 256, 48, 8, "none", "int32", 0.0, 769, "normal"),         # 6152 pairs: two launches
 ]
 
 
