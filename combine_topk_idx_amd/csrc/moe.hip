@@ -21,14 +21,14 @@
 // instruction, measured), which bounds how closely any result here can
 // follow an exact dot product.
 //
-// Mapping: a workgroup (4 waves) owns one (expert, chunk of up to 160 rows,
-// N tile).  The chunk's A rows are staged through double-buffered LDS two
-// 64-wide K steps at a time and shared by the 4 waves; every wave streams its
-// own 32 weight rows (B) straight into registers, eight K steps ahead
-// (weights are read once from HBM: they are the traffic that bounds the
-// kernel at the shapes of the benchmark).  GMM1 gives each wave 16 gate and
-// the matching 16 up rows, so lane c < 16 and lane c + 16 hold g and u of the
-// same output; GMM2 gives each wave 32 output columns.
+// Mapping: a workgroup (4 or 6 working waves) owns one (expert, chunk of up
+// to 160 rows, N tile of one 32-row weight group per wave).  The chunk's A
+// rows are staged through double-buffered LDS two 64-wide K steps at a time
+// and shared by the waves; every wave streams its own weight group (B)
+// straight into registers four K steps ahead (each weight byte is read once
+// from HBM).  GMM1 gives each wave 16 gate and the matching 16 up rows, so
+// lane c < 16 and lane c + 16 hold g and u of the same output; GMM2 gives
+// each wave 32 output columns.
 #include <math.h>
 
 #include "common.hpp"
@@ -42,19 +42,32 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+// A tile is 4 or 6 groups of 32 weight rows, one per wave (an even count,
+// so that a GMM1 tile covers whole 32-column MX blocks).  A CU moves data at
+// a bounded rate, and its time is about the weight bytes of its tiles plus
+// the activation bytes of their chunks, which every tile of a chunk reads
+// again: wide tiles read the activations fewer times, narrow tiles make more
+// work units.  Each launch takes narrow tiles when their units fit on the
+// CUs at once and wide ones otherwise; workgroups are launched with the wide
+// tile's waves, and with narrow tiles the last two waves leave at once.
+constexpr int kNarrow = 4, kWide = 6;
+constexpr int kThreads = kWide * kWave;
+constexpr int kWaves = kWide;                     // waves launched per workgroup
 constexpr int kMaxFrags = 5;                      // 32-row fragments per chunk
 constexpr int kChunkRows = kMaxFrags * 32;        // rows per work item
 constexpr int kKStep = 64;                        // K per matrix-core step
 // The chunk's A rows are staged two K steps (128 bytes of a row, one full
 // cache line) at a time; a padded row stride of 144 bytes puts the 16-byte
 // fragment reads of 16 consecutive rows in distinct LDS banks.  Every thread
-// moves NF pieces of 16 bytes per stage (NF * 32 rows * 8 pieces / 256).
+// moves the same number of 16-byte pieces per stage; pieces past the
+// chunk's rows land in spare LDS rows that are never read.
 constexpr int kStageSteps = 2;
 constexpr int kStageK = kStageSteps * kKStep;     // K bytes of a row per stage
 constexpr int kRowStride = kStageK + 16;          // LDS bytes per staged A row
-constexpr int kAStage = kChunkRows * kRowStride;  // bytes of one staged A block
+constexpr int a_pieces(int nf, int waves) { return (nf * 32 * (kStageK / 16) + waves * kWave - 1) / (waves * kWave); }
+constexpr int a_stage_rows(int waves) { return a_pieces(kMaxFrags, waves) * waves * kWave / (kStageK / 16); }
+constexpr int kAStageRows = a_stage_rows(kNarrow) > a_stage_rows(kWide) ? a_stage_rows(kNarrow) : a_stage_rows(kWide);
+constexpr int kAStage = kAStageRows * kRowStride; // bytes of one staged A block
 // A scale bytes are loaded 16 per row (eight K steps) at a time into a
 // double-buffered table of kThreads rows, padded to 20 bytes so that the
 // byte reads of 32 consecutive rows fall in distinct banks.
@@ -62,8 +75,7 @@ constexpr int kBodySteps = 8;
 constexpr int kScaleStride = 20;
 constexpr int kScaleBuf = kThreads * kScaleStride;
 constexpr int kStaging = 2 * kAStage + 2 * kScaleBuf;
-constexpr int kEpiCols = 64;                      // GMM1 SwiGLU columns per workgroup
-constexpr int kEpiStride = kEpiCols + 1;          // floats per LDS row of the epilogue tile
+constexpr int kEpiTileBytes = kChunkRows * (16 * kWide + 1) * 4;   // GMM1 SwiGLU tile of the wide tiles
 
 enum Mode { kGmm1Mx = 0, kGmm1Bf16 = 1, kGmm2 = 2 };
 
@@ -71,22 +83,28 @@ struct Item {
   int expert, row0, rows;                         // rows <= kChunkRows
 };
 
-// The work of this workgroup.  Work units are (expert, chunk of up to
-// kChunkRows rows, N tile) triples in expert-major order; their number comes
-// from a workgroup scan of the per-expert chunk counts (recv_count when
-// given, else the expert block sizes; every thread takes two experts).  The
-// hardware hands workgroups to the 8 XCDs round-robin, so workgroup b runs on
-// XCD b % 8; giving XCD x the contiguous units [x * per, (x + 1) * per) keeps
-// each XCD on one or two experts, whose activation rows then stay in that
-// XCD's L2 instead of being fetched by every XCD.  Returns expert -1 when the
-// workgroup has no unit.
+// The work of a launch.  Work units are (expert, chunk of up to kChunkRows
+// rows, N tile) triples in expert-major order; their number comes from a
+// workgroup scan of the per-expert chunk counts (recv_count when given, else
+// the expert block sizes; every thread takes two experts).  The grid is at
+// most one workgroup per CU and each workgroup walks its units with a
+// stride.  The hardware hands workgroups to the 8 XCDs round-robin, so
+// workgroup b runs on XCD b % 8; giving XCD x the contiguous units
+// [x * per, (x + 1) * per) keeps each XCD on one or two experts, whose
+// activation rows then stay in that XCD's L2 instead of being fetched by
+// every XCD.
 constexpr int kXcds = 8;
 
-__device__ Item find_item(int n_tiles, int E, const int *__restrict__ offsets, const int64_t *__restrict__ recv_count,
-                          int &ntile) {
+struct Plan {                                     // uniform over the launch
+  int units, per, n_tiles, waves;
+};
+
+// per-expert rows and first chunk, for the unit lookups
+__shared__ int s_rows[2 * kThreads], s_first[2 * kThreads];
+
+__device__ Plan make_plan(int nt_narrow, int nt_wide, int num_cus, int E, const int *__restrict__ offsets,
+                          const int64_t *__restrict__ recv_count) {
   __shared__ int wsum[kWaves];
-  __shared__ Item found;
-  if (threadIdx.x == 0) found.expert = -1;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   int cnt[2], ch[2];
 #pragma unroll
@@ -110,23 +128,42 @@ __device__ Item find_item(int n_tiles, int E, const int *__restrict__ offsets, c
     before += i < wv ? wsum[i] : 0;
     chunks += wsum[i];
   }
-  const int units = chunks * n_tiles;
-  const int per = (units + kXcds - 1) / kXcds;
-  const int unit = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  const bool have = blockIdx.x / kXcds < per && unit < units;
-  const int item = unit / n_tiles;
-  ntile = unit - item * n_tiles;
-  int start = before + x - ch[0] - ch[1];                          // exclusive prefix of expert 2t
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = 2 * threadIdx.x + q;
-    if (have && e < E && item >= start && item < start + ch[q]) {
-      const int c = item - start;
-      found.expert = e;
-      found.row0 = offsets[e] + c * kChunkRows;
-      found.rows = min(kChunkRows, cnt[q] - c * kChunkRows);
+  const int start = before + x - ch[0] - ch[1];
+  s_rows[2 * threadIdx.x] = cnt[0];
+  s_rows[2 * threadIdx.x + 1] = cnt[1];
+  s_first[2 * threadIdx.x] = start;
+  s_first[2 * threadIdx.x + 1] = start + ch[0];
+  Plan pl;
+  chunks = __builtin_amdgcn_readfirstlane(chunks);
+  pl.waves = chunks * nt_narrow <= num_cus ? kNarrow : kWide;
+  pl.n_tiles = pl.waves == kNarrow ? nt_narrow : nt_wide;
+  pl.units = chunks * pl.n_tiles;
+  pl.per = (pl.units + kXcds - 1) / kXcds;
+  return pl;
+}
+
+// The i-th unit of this workgroup, or expert -1 past its last one (uniform).
+// Starts with a barrier, so the previous unit's LDS is no longer in use.
+__device__ Item find_item(const Plan &pl, int E, const int *__restrict__ offsets, int i, int &ntile) {
+  __shared__ Item found;
+  __syncthreads();
+  if (threadIdx.x == 0) found.expert = -1;
+  __syncthreads();
+  const int slot = blockIdx.x / kXcds + i * (gridDim.x / kXcds);
+  const int unit = (blockIdx.x % kXcds) * pl.per + slot;
+  const bool have = slot < pl.per && unit < pl.units;
+  const int item = unit / pl.n_tiles;
+  ntile = unit - item * pl.n_tiles;
+  if (have) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      const int first = s_first[e], rows = s_rows[e];
+      const int c = item - first;
+      if (c >= 0 && c * kChunkRows < rows) {
+        found.expert = e;
+        found.row0 = offsets[e] + c * kChunkRows;
+        found.rows = min(kChunkRows, rows - c * kChunkRows);
+      }
     }
-    start += ch[q];
   }
   __syncthreads();
   return found;
@@ -196,10 +233,6 @@ __global__ void pack_weights_kernel(const uint8_t *__restrict__ codes, const uin
 #ifndef EP_MOE_ASETS
 #define EP_MOE_ASETS 2
 #endif
-// K steps of weights in flight per wave
-#ifndef EP_MOE_RING
-#define EP_MOE_RING 4
-#endif
 template <typename T>
 __device__ __forceinline__ T ld_w(const uint8_t *p) {
 #if EP_MOE_W_NT
@@ -217,16 +250,22 @@ __device__ __forceinline__ T ld_a(const uint8_t *p) {
 #endif
 }
 
-// The MX-scaled matrix-core step with the B scale taken from byte `u` of
-// `bsc` (the instruction's op_sel picks the byte, so no extraction is needed;
-// u is a constant wherever this is inlined in the unrolled loop).
+// The MX-scaled matrix-core step with the A scale taken from byte 2h of
+// `as` and the B scale from byte `u` of `bs` (the instruction's op_sel picks
+// the bytes, so no extraction is needed; h and u are constants wherever this
+// is inlined in the unrolled loop).
+template <int HA>
 __device__ __forceinline__ v16f mfma_b_byte(int u, const v8i &a, const v8i &b, const v16f &c, int as, int bs) {
   switch (u) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, as, 0, bs);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, as, 1, bs);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, as, 2, bs);
-    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, as, 3, bs);
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, HA, as, 0, bs);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, HA, as, 1, bs);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, HA, as, 2, bs);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, HA, as, 3, bs);
   }
+}
+__device__ __forceinline__ v16f mfma_ab_byte(int h, int u, const v8i &a, const v8i &b, const v16f &c, int as,
+                                             int bs) {
+  return h == 0 ? mfma_b_byte<0>(u, a, b, c, as, bs) : mfma_b_byte<2>(u, a, b, c, as, bs);
 }
 
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() carries a
@@ -242,7 +281,7 @@ struct GemmArgs {
   const uint8_t *a_data, *a_scales;
   int K;
   const uint8_t *w, *w_scales;
-  int N_w, n_tiles, inter;
+  int N_w, nt_narrow, nt_wide, num_cus, inter;
   uint8_t *out_data, *out_scales;
   int out_cols;
 };
@@ -251,17 +290,24 @@ struct GemmArgs {
 // multiple of 128 (whole stages).
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-template <int MODE, int NF>
-__device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, int ntile, uint8_t *smem) {
-  constexpr int kPieces = NF;                                     // 16-byte A pieces per thread per stage
-  static_assert(NF * 32 * (kStageK / 16) == kPieces * kThreads, "pieces cover the stage exactly");
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+template <int MODE, int NF, int WE>
+__device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, int ntile, uint8_t *smem, int tid) {
+  constexpr int kThr = WE * kWave;                                // threads of the working waves
+  constexpr int kPieces = a_pieces(NF, WE);                       // A pieces per thread per stage
+  static_assert(kPieces * kThr / (kStageK / 16) <= kAStageRows, "A pieces fit the staged block");
+  constexpr int kEpiCols = 16 * WE;                               // GMM1 SwiGLU columns of the tile
+  constexpr int kEpiStride = kEpiCols + 1;                        // floats per LDS row of the epilogue tile
+  const int lane = tid & (kWave - 1), wv = tid / kWave;
   const int r = lane & 31, g = lane >> 5;
   const int K = p.K, ksteps = K / kKStep, nstages = ksteps / kStageSteps, kb = K / 32;
 
   // this wave's packed weight group (see pack_weights_kernel): fragments of
   // 2048 bytes per K step, scale dwords per span of four steps
-  const int group = ntile * kWaves + wv;
+  // a tile's last waves may lie past N: they repeat the last group (their
+  // loads hit the cache lines of the wave that owns it) and store nothing
+  const int groups = p.N_w / 32;
+  const int group = min(ntile * WE + wv, groups - 1);
+  const bool owner = ntile * WE + wv < groups;
   const int spans = (ksteps + 3) / 4;
   const size_t gidx = (size_t)it.expert * (p.N_w / 32) + group;
   const uint8_t *wp = p.w + gidx * (size_t)ksteps * 2048 + lane * 16;
@@ -269,14 +315,15 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
 
   // A staging, branch-free: piece i of this thread is (row, 16-byte piece) =
   // (idx >> 3, idx & 7) of the stage, so 8 lanes read one 128-byte line;
-  // rows past the chunk read its last row (their LDS rows are never used)
-  const uint8_t *apiece[kPieces];
+  // rows past the chunk read its last row (their LDS rows are never read)
+  const uint8_t *a_chunk = p.a_data + (size_t)it.row0 * K;
+  uint32_t apiece[kPieces];                                       // byte offsets within the chunk
   int lpiece[kPieces];
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
-    const int idx = threadIdx.x + i * kThreads;
+    const int idx = tid + i * kThr;
     const int row = idx >> 3, q = idx & 7;
-    apiece[i] = p.a_data + (size_t)(it.row0 + min(row, it.rows - 1)) * K + q * 16;
+    apiece[i] = (uint32_t)(min(row, it.rows - 1) * K + q * 16);
     lpiece[i] = row * kRowStride + q * 16;
   }
   constexpr int kASets = EP_MOE_ASETS;                            // A loads run kASets stages ahead
@@ -285,7 +332,7 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   auto load_a = [&](int j, int set) {
     const int jj = min(j, nstages - 1);                           // loads past the end are never used
 #pragma unroll
-    for (int i = 0; i < kPieces; ++i) areg[set][i] = ld_a<u32x4>(apiece[i] + (size_t)jj * kStageK);
+    for (int i = 0; i < kPieces; ++i) areg[set][i] = ld_a<u32x4>(a_chunk + apiece[i] + (size_t)jj * kStageK);
   };
   auto store_a = [&](int buf, int set) {
 #pragma unroll
@@ -296,8 +343,8 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   // (body b covers steps [8b, 8b + 8)); the table row of thread t is t.  A
   // body's 16 bytes start at byte min(16b, kb - 16) of the row, so a partial
   // last body reads in bounds and its reader adds back the shift.
-  const uint8_t *srow = p.a_scales + (size_t)(it.row0 + min((int)threadIdx.x, it.rows - 1)) * kb;
-  uint32_t *sc_st = (uint32_t *)(smem + 2 * kAStage + threadIdx.x * kScaleStride);
+  const uint8_t *srow = p.a_scales + (size_t)(it.row0 + min(tid, it.rows - 1)) * kb;
+  uint32_t *sc_st = (uint32_t *)(smem + 2 * kAStage + tid * kScaleStride);
   u32x4_a4 sc;
   auto load_sc = [&](int body) { sc = ld_a<u32x4_a4>(srow + min(16 * body, kb - 16)); };
   auto store_sc = [&](int buf) {
@@ -307,28 +354,28 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
     d[2] = sc.z;
     d[3] = sc.w;
   };
-  const uint8_t *sc_rd0 = smem + 2 * kAStage + r * kScaleStride + g;
+  const uint8_t *sc_rd0 = smem + 2 * kAStage + r * kScaleStride;  // dword-aligned (shift is a multiple of 4)
   auto sc_reader = [&](int body) {
     const int shift = body == 0 ? 0 : 16 * body - min(16 * body, kb - 16);
     return sc_rd0 + (body & 1) * kScaleBuf + shift;
   };
 
   // weight ring: kRing K steps of two 16-byte pieces (each wave load reads
-  // 1 KB in one piece) and the scale dword of the step's span of four.
-  // Slot u is refilled only after the matrix-core instructions that read it
-  // are issued, so a slot keeps one register across the loop: no copy of a
-  // register a load is still writing (a copy would wait for that load and
-  // every load before it).
-  constexpr int kRing = EP_MOE_RING;
-  static_assert(kBodySteps % kRing == 0, "slots are fixed within a body");
+  // 1 KB in one piece), and the scale dwords of the current and the next
+  // span of four steps (span t in wspan[t & 1], loaded at the first step of
+  // span t - 1).  Slot u is refilled only after the matrix-core instructions
+  // that read it are issued, so a slot keeps one register across the loop:
+  // no copy of a register a load is still writing (a copy would wait for
+  // that load and every load before it).
+  constexpr int kRing = 4;                                        // K steps of weights in flight per wave
   u32x4 wb0[kRing], wb1[kRing];
-  uint32_t wsc[kRing];
+  uint32_t wspan[2];
   auto load_w = [&](int s, int slot) {
     const int ss = min(s, ksteps - 1);                             // loads past the end are never used
     wb0[slot] = ld_w<u32x4>(wp + (size_t)ss * 2048);
     wb1[slot] = ld_w<u32x4>(wp + (size_t)ss * 2048 + 1024);
-    wsc[slot] = ld_w<uint32_t>(wsp + (size_t)(ss >> 2) * 256);
   };
+  auto load_span = [&](int t, int slot) { wspan[slot] = ld_w<uint32_t>(wsp + (size_t)min(t, spans - 1) * 256); };
 
   v16f acc[NF];
 #pragma unroll
@@ -348,6 +395,7 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   load_a(kASets, 0);
 #pragma unroll
   for (int q = 0; q < kRing; ++q) load_w(q, q);
+  load_span(0, 0);
   lds_barrier();
 
   // stage j (i = j % 4 within its body): write A(j+1) (register set
@@ -362,23 +410,37 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
     if (full && i == 0) load_sc(body + 1);
     if (full && i == 3) store_sc((body + 1) & 1);
     const uint8_t *abase = smem + (i & 1) * kAStage;
+    // the stage's A scale bytes of each fragment row: one dword (blocks
+    // 4i .. 4i+3 of the body), shifted so that byte 2h is lane (r, g)'s
+    // block of step h
+    int xsw[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      xsw[f] = (int)(*(const uint32_t *)(sc_rd + f * 32 * kScaleStride + 4 * i) >> (8 * g));
 #pragma unroll
     for (int h = 0; h < kStageSteps; ++h) {
       const int sb = kStageSteps * i + h;                          // step within the body
       const int u = sb % kRing;
       const v8i bv = {(int)wb0[u].x, (int)wb0[u].y, (int)wb0[u].z, (int)wb0[u].w,
                       (int)wb1[u].x, (int)wb1[u].y, (int)wb1[u].z, (int)wb1[u].w};
-      const int bsc = (int)wsc[u];                                 // byte sb & 3 of the span dword, by op_sel
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
+      const int bsc = (int)wspan[(sb >> 2) & 1];                   // byte sb & 3 of the span dword, by op_sel
+      // A fragments in two register sets, so that the LDS read of fragment
+      // f + 1 is in flight while the matrix core works on fragment f
+      v8i av[2];
+      auto read_a = [&](int f) {
         const int row = f * 32 + r;
         const u32x4 x0 = *(const u32x4 *)(abase + row * kRowStride + h * kKStep + g * 16);
         const u32x4 x1 = *(const u32x4 *)(abase + row * kRowStride + h * kKStep + 32 + g * 16);
-        const int xs = (int)sc_rd[f * 32 * kScaleStride + 2 * sb];
-        const v8i av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        acc[f] = mfma_b_byte(sb & 3, av, bv, acc[f], xs, bsc);
+        av[f & 1] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      read_a(0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (f + 1 < NF) read_a(f + 1);
+        acc[f] = mfma_ab_byte(h, sb & 3, av[f & 1], bv, acc[f], xsw[f], bsc);
       }
       load_w(kStageSteps * j + h + kRing, u);
+      if ((sb & 3) == 0) load_span((kStageSteps * j + h) / 4 + 1, ((sb >> 2) + 1) & 1);
     }
     lds_barrier();
   };
@@ -401,13 +463,13 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   // ---------------------------------------------------------------- epilogue
   if constexpr (MODE == kGmm2) {
     // bf16 rows: column l % 32 of this wave's 32, rows 8b + 4g + i of each fragment
-    const int col = ntile * (kWaves * 32) + wv * 32 + r;
+    const int col = ntile * (WE * 32) + wv * 32 + r;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = f * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (row < it.rows) {
+        if (owner && row < it.rows) {
           const uint32_t bits = pack_bf16x2(acc[f][i], 0.0f) & 0xffffu;
           *(uint16_t *)(p.out_data + ((size_t)(it.row0 + row) * p.out_cols + col) * 2) = (uint16_t)bits;
         }
@@ -415,7 +477,7 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
     }
   } else {
     // SwiGLU: lane r < 16 holds gate column r, lane r + 16 the matching up
-    // column; the 16 results of each wave go to an LDS tile [rows][64]
+    // column; the 16 results of each wave go to an LDS tile [rows][16 * waves]
     float *tile = (float *)smem;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -430,8 +492,10 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
     lds_barrier();
     // each thread: one (row, 32-column block) of the tile
     const int n0 = ntile * kEpiCols;
-    for (int job = threadIdx.x; job < it.rows * 2; job += kThreads) {
-      const int row = job >> 1, blk = job & 1;
+    constexpr int kBlocks = kEpiCols / 32;
+    for (int job = tid; job < it.rows * kBlocks; job += kThr) {
+      const int row = job / kBlocks, blk = job - row * kBlocks;
+      if (n0 + blk * 32 >= p.out_cols) continue;                  // past I (a partial last tile)
       const float *src = tile + row * kEpiStride + blk * 32;
       const size_t orow = (size_t)(it.row0 + row);
       if constexpr (MODE == kGmm1Bf16) {
@@ -470,25 +534,67 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void mx_gmm_kernel(GemmArgs p, const int *__restrict__ offsets,
-                                                          const int64_t *__restrict__ recv_count, int E) {
-  constexpr int kTile = MODE == kGmm2 ? 0 : kChunkRows * kEpiStride * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kTile ? kStaging : kTile];
-  int ntile;
-  const Item it = find_item(p.n_tiles, E, offsets, recv_count, ntile);
-  if (it.expert < 0 || it.rows <= 0) return;                     // uniform
+template <int MODE, int WE>
+__device__ __forceinline__ void gemm_frags(const GemmArgs &p, const Item &it, int ntile, uint8_t *smem, int tid) {
   static_assert(kMaxFrags == 5, "one instantiation per fragment count 1..kMaxFrags");
   switch ((it.rows + 31) / 32) {                                 // uniform: one instantiation per fragment count
-    case 1: gemm_chunk<MODE, 1>(p, it, ntile, smem); break;
-    case 2: gemm_chunk<MODE, 2>(p, it, ntile, smem); break;
-    case 3: gemm_chunk<MODE, 3>(p, it, ntile, smem); break;
-    case 4: gemm_chunk<MODE, 4>(p, it, ntile, smem); break;
-    default: gemm_chunk<MODE, 5>(p, it, ntile, smem); break;
+    case 1: gemm_chunk<MODE, 1, WE>(p, it, ntile, smem, tid); break;
+    case 2: gemm_chunk<MODE, 2, WE>(p, it, ntile, smem, tid); break;
+    case 3: gemm_chunk<MODE, 3, WE>(p, it, ntile, smem, tid); break;
+    case 4: gemm_chunk<MODE, 4, WE>(p, it, ntile, smem, tid); break;
+    default: gemm_chunk<MODE, 5, WE>(p, it, ntile, smem, tid); break;
   }
 }
 
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void mx_gmm_kernel(GemmArgs p, const int *__restrict__ offsets,
+                                                          const int64_t *__restrict__ recv_count, int E) {
+  constexpr int kTile = MODE == kGmm2 ? 0 : kEpiTileBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kTile ? kStaging : kTile];
+  const Plan pl = make_plan(p.nt_narrow, p.nt_wide, p.num_cus, E, offsets, recv_count);
+  // with narrow tiles the last waves have no weight group; a wave that has
+  // ended no longer takes part in the workgroup's barriers
+  if ((int)(threadIdx.x / kWave) >= pl.waves) return;
+  for (int i = 0;; ++i) {
+    int ntile;
+    const Item it = find_item(pl, E, offsets, i, ntile);
+    if (it.expert < 0) return;                                   // uniform
+    // the thread index passes through an empty asm in every iteration, so
+    // that no address derived from it is hoisted out of this loop (held
+    // across a whole unit, those would crowd out the GEMM's registers)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    if (pl.waves == kNarrow)
+      gemm_frags<MODE, kNarrow>(p, it, ntile, smem, tid);
+    else
+      gemm_frags<MODE, kWide>(p, it, ntile, smem, tid);
+  }
+}
+
+// CUs of the current device (cached per device).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 }  // namespace
+
+// Workgroups of a GEMM launch: one per possible work unit, at most one per
+// CU (a multiple of the XCD count, so that every XCD walks its units with the
+// same stride); a workgroup with no unit leaves at once.
+int64_t persistent_grid(int64_t units_upper) {
+  const int cus = device_cus();
+  const int64_t cap = cus >= kXcds ? cus / kXcds * kXcds : kXcds;
+  const int64_t g = (units_upper + kXcds - 1) / kXcds * kXcds;
+  return g < cap ? g : cap;
+}
 
 hipError_t launch_moe_pack(const void *codes, const void *scales, int E, int N, int K, int gate_up, void *pcodes,
                            void *pscales, hipStream_t s) {
@@ -500,12 +606,14 @@ hipError_t launch_moe_pack(const void *codes, const void *scales, int E, int N, 
 hipError_t launch_moe_gmm1(const ep_handle_t &h, const int64_t *recv_count, const char *x_buf, int hidden, int inter,
                            const void *w1, const void *w1_scales, int out_quant, char *out_buf, hipStream_t s) {
   const RecvGeom gx = recv_geom(h.max_rows, hidden, EP_QUANT_MXFP8);
-  const int n_tiles = inter / kEpiCols;
+  const int groups = inter / 16;                                  // 2I weight rows in groups of 32
+  const int ntn = (groups + kNarrow - 1) / kNarrow, ntw = (groups + kWide - 1) / kWide;
   const int64_t items = (h.max_rows + kChunkRows - 1) / kChunkRows + h.num_experts;
-  const int64_t blocks = (items * n_tiles + kXcds - 1) / kXcds * kXcds;
+  const int64_t blocks = persistent_grid(items * ntn);
   if (h.num_tokens == 0 || blocks == 0) return hipSuccess;
   GemmArgs p{(const uint8_t *)x_buf, (const uint8_t *)x_buf + gx.scale_off, hidden, (const uint8_t *)w1,
-             (const uint8_t *)w1_scales, 2 * inter, n_tiles, inter, (uint8_t *)out_buf, nullptr, inter};
+             (const uint8_t *)w1_scales, 2 * inter, ntn, ntw, device_cus(), inter, (uint8_t *)out_buf, nullptr,
+             inter};
   if (out_quant == EP_QUANT_MXFP8) {
     p.out_scales = (uint8_t *)out_buf + recv_geom(h.max_rows, inter, EP_QUANT_MXFP8).scale_off;
     hipLaunchKernelGGL(mx_gmm_kernel<kGmm1Mx>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, h.offsets,
@@ -520,12 +628,14 @@ hipError_t launch_moe_gmm1(const ep_handle_t &h, const int64_t *recv_count, cons
 hipError_t launch_moe_gmm2(const ep_handle_t &h, const int64_t *recv_count, const char *a_buf, int inter, int hidden,
                            const void *w2, const void *w2_scales, char *out_buf, hipStream_t s) {
   const RecvGeom ga = recv_geom(h.max_rows, inter, EP_QUANT_MXFP8);
-  const int n_tiles = hidden / (kWaves * 32);
+  const int groups = hidden / 32;
+  const int ntn = (groups + kNarrow - 1) / kNarrow, ntw = (groups + kWide - 1) / kWide;
   const int64_t items = (h.max_rows + kChunkRows - 1) / kChunkRows + h.num_experts;
-  const int64_t blocks = (items * n_tiles + kXcds - 1) / kXcds * kXcds;
+  const int64_t blocks = persistent_grid(items * ntn);
   if (h.num_tokens == 0 || blocks == 0) return hipSuccess;
   const GemmArgs p{(const uint8_t *)a_buf, (const uint8_t *)a_buf + ga.scale_off, inter, (const uint8_t *)w2,
-                   (const uint8_t *)w2_scales, hidden, n_tiles, inter, (uint8_t *)out_buf, nullptr, hidden};
+                   (const uint8_t *)w2_scales, hidden, ntn, ntw, device_cus(), inter, (uint8_t *)out_buf, nullptr,
+                   hidden};
   hipLaunchKernelGGL(mx_gmm_kernel<kGmm2>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, h.offsets, recv_count,
                      h.num_experts);
   return hipGetLastError();

@@ -232,6 +232,40 @@ def test_share_full_size_sampled(ep):
     print(f"worst row relative error {worst:.3g}")
 
 
+def test_wide_tiles_many_experts(ep):
+    """192 small experts: more narrow work units than a 256-CU device has
+    CUs, so both GEMMs take the 6-wave tiles, whose last tile is partial
+    (GMM1: 16 weight groups = 6 + 6 + 4; GMM2: 8 = 6 + 2)."""
+    w = W.MoeWorkload("moe_wide", 768, 256, 256, 192, 192, 4, seed=1024)
+    _announce("moe wide tiles, 192 experts")
+    inp = W.make_moe_inputs(w)
+    res = gpu_moe(ep, w, inp)
+    lay, rb, per, out = oracle_moe(w, inp)
+    total, _ = ep.ep_buffer_bytes(lay.max_rows, w.I, "mxfp8")
+    a = OD.RecvBuffer.from_bytes(res["a"][:total].cpu().numpy(), lay.max_rows, w.I, "mxfp8", lay.num_rows)
+    for e, (rows, ent) in enumerate(per):
+        if ent is None:
+            continue
+        ab = _gmm1_bound(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e], ent["a"], 0.0)
+        _check_requant(a.data[rows], a.scales[rows], ent["q"], ent["qs"], ab, frac=0.05)
+    y = _bf16_rows(res["y"], lay.max_rows, w.H)
+    for e, (rows, ent) in enumerate(per):
+        if ent is None:
+            continue
+        got = codecs.bf16_bits_to_f32(y[rows]).astype(np.float64)
+        # GMM2 reads the GPU's own requantised rows (checked above against the
+        # oracle's), so its exact reference is the dot product with those rows
+        gv = OM.mx_dequant(a.data[rows], a.scales[rows])
+        wv = OM.mx_dequant(inp["w2_codes"][e], inp["w2_scales"][e])
+        want = gv @ wv.T
+        S = np.abs(gv) @ np.abs(wv).T
+        bound = MFMA_REL * S + 2.0 ** -8 * np.abs(want) + 1e-30
+        err = np.abs(got - want)
+        assert np.all(err <= bound), f"expert {e}: worst err/bound {np.max(err / bound):.3g}"
+    worst = _check_end_to_end(res["out"], out)
+    print(f"worst row relative error {worst:.3g}")
+
+
 def _pack_reference(codes, scales, gate_up):
     """The packed layout of ep_moe_pack_weights built with numpy indexing
     from its description in include/ep.h (a permutation of the bytes)."""
