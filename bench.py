@@ -109,6 +109,11 @@ def cpu_baseline_child(name: str, tokens: int) -> None:
     rb = D.dispatch(x, lay, w.mode)
     if w.combine_input == "identity":
         cin = rb
+    elif w.combine_input == "scaled_dispatch":                    # bf16 rows: the dispatched rows x 1.5
+        from oracle import codecs
+        ys = codecs.bf16_bits_to_f32(rb.data.view(np.uint16)).astype(np.float32) * np.float32(1.5)
+        cin = D.RecvBuffer("none", w.H, lay.num_rows, W.bf16_from_f32(ys).view(np.uint8),
+                           np.zeros((lay.max_rows, 0), np.uint8), None)
     else:
         cin = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8).reshape(tokens * w.k, -1),
                            np.zeros((tokens * w.k, 0), np.uint8), None)
@@ -117,17 +122,49 @@ def cpu_baseline_child(name: str, tokens: int) -> None:
     print(json.dumps({"tokens": tokens, "seconds": dt, "cores": len(os.sched_getaffinity(0))}))
 
 
-def cpu_baseline(name: str, tokens: int) -> dict:
-    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", name,
+def cpu_baseline_moe_child(name: str, tokens: int) -> None:
+    """The oracle's expert-MLP path (layout, MXFP8 dispatch, GMM1 + SwiGLU +
+    requant, GMM2, combine) on the first `tokens` tokens, on one core."""
+    os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    import numpy as np
+    from combine_topk_idx_amd import workloads as W
+    from oracle import combine as C, dispatch as D, layout as L, moe as M
+
+    w = W.MOE_WORKLOADS[name]
+    inp = W.make_moe_inputs(w)
+    x, idx, wts = inp["x"][:tokens], inp["topk_idx"][:tokens], inp["topk_weights"][:tokens]
+    t0 = time.perf_counter()
+    lay = L.layout(idx, w.E_local, tokens)
+    rb = D.dispatch(x, lay, "mxfp8")
+    y = np.zeros((lay.max_rows, w.H), np.uint16)
+    for e in range(w.E_local):
+        rows = np.arange(lay.offsets[e], lay.offsets[e] + lay.count[e])
+        if rows.size == 0:
+            continue
+        q, qs, _ = M.gmm1_swiglu_rows(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e])
+        y[rows], _ = M.gmm2_rows(q, qs, inp["w2_codes"][e], inp["w2_scales"][e])
+    cin = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8), np.zeros((lay.max_rows, 0), np.uint8), None)
+    C.combine(cin, lay, wts)
+    dt = time.perf_counter() - t0
+    print(json.dumps({"tokens": tokens, "rows": int(lay.num_rows), "seconds": dt,
+                      "cores": len(os.sched_getaffinity(0))}))
+
+
+def cpu_baseline(name: str, tokens: int, moe: bool = False) -> dict:
+    flag = "--cpu-baseline-moe-child" if moe else "--cpu-baseline-child"
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), flag, name,
                         "--cpu-tokens", str(tokens)], capture_output=True, text=True, env=dict(
                             os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
                             HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES=""))
     if r.returncode != 0:
         raise RuntimeError(f"cpu baseline failed:\n{r.stderr}")
     d = json.loads(r.stdout.strip().splitlines()[-1])
+    what = ("layout + MXFP8 dispatch + GMM1/SwiGLU/requant + GMM2 + combine, "
+            f"{d.get('rows', 0)} expert rows; the weights are dequantised in full" if moe else
+            "layout + dispatch + combine")
     return {"value": d["tokens"] / d["seconds"], "unit": "tokens/s", "cores": d["cores"], "kind": "oracle",
-            "sample": f"first {d['tokens']} tokens of the workload as one batch (layout + dispatch + "
-                      f"combine), {d['seconds']:.1f} s on one host core"}
+            "sample": f"first {d['tokens']} tokens of the workload as one batch ({what}), "
+                      f"{d['seconds']:.1f} s on one host core"}
 
 
 # ---------------------------------------------------------------------------
@@ -298,6 +335,10 @@ def moe_main(args) -> int:
     torch.cuda.synchronize()
     ms = ev[0][0].elapsed_time(ev[-1][5]) / args.steps
     ph = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j, n in enumerate(names)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w.name, args.cpu_tokens or 256, moe=True)
     alg = moe_algorithmic(w, R)
     b, f = alg["bytes"], alg["flops"]
     gbps = lambda n: b[n] / (ph[n] * 1e-3) / 1e9
@@ -318,7 +359,7 @@ def moe_main(args) -> int:
         "phase_gbps": {n: round(gbps(n), 1) for n in names},
         "gemm_tflops": {n: round(tflops(n), 1) for n in ("gmm1", "gmm2")},
         "hbm_gbps": round(b["total"] / (ms * 1e-3) / 1e9, 1),
-        "roofline": roof, "cpu_baseline": None}), flush=True)
+        "roofline": roof, "cpu_baseline": cpu}), flush=True)
     return 0
 
 
@@ -349,10 +390,14 @@ def main() -> int:
                     help="time the expert-MLP path (layout, MXFP8 dispatch, GMM1+SwiGLU+requant, GMM2, combine) "
                          "of a MoE workload, e.g. moe_share")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-baseline-moe-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     if args.cpu_baseline_child:
         cpu_baseline_child(args.cpu_baseline_child, args.cpu_tokens)
+        return 0
+    if args.cpu_baseline_moe_child:
+        cpu_baseline_moe_child(args.cpu_baseline_moe_child, args.cpu_tokens)
         return 0
     if args.combine_backward:
         return backward_main(args)
