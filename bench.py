@@ -37,6 +37,9 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_large_traffic.json")
 KERNEL_SOURCES = ["combine_topk_idx_amd/csrc/combine.hip", "combine_topk_idx_amd/csrc/formats.hpp",
                   "combine_topk_idx_amd/csrc/common.hpp"]
+MOE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gmm1_moe_share_traffic.json")
+MOE_KERNEL_SOURCES = ["combine_topk_idx_amd/csrc/moe.hip", "combine_topk_idx_amd/csrc/moe.hpp",
+                      "combine_topk_idx_amd/csrc/formats.hpp", "combine_topk_idx_amd/csrc/common.hpp"]
 
 
 def algorithmic_bytes(w, R: int) -> dict:
@@ -63,24 +66,24 @@ def _row_bytes(mode: str, H: int):
             "mxfp8": (H, H // 32), "mxfp4": (H // 2, H // 32)}[mode]
 
 
-def _source_hash() -> str:
+def _source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str):
-    """HBM bytes per combine launch from the committed rocprofv3 counter
-    summary, or None if it is missing, for another workload, or was taken
-    on a different kernel source."""
+def _traffic(workload: str, path: str = TRAFFIC_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per launch of the measured kernel from a committed rocprofv3
+    counter summary, or None if it is missing, for another workload, or was
+    taken on a different kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != _source_hash() or d.get("workload") != workload:
+    if d.get("source_hash") != _source_hash(sources) or d.get("workload") != workload:
         return None
     return d.get("bytes_per_launch")
 
@@ -299,6 +302,13 @@ def moe_main(args) -> int:
             y=torch.empty(rows * w.H * 2, dtype=torch.uint8, device=dev),
             out=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)))
     stream = torch.cuda.current_stream()
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def phases(s):
         def lay():
@@ -344,7 +354,8 @@ def moe_main(args) -> int:
     gbps = lambda n: b[n] / (ph[n] * 1e-3) / 1e9
     tflops = lambda n: f[n] / (ph[n] * 1e-3) / 1e12
     roof = {"bound": "hbm", "kernel": "gmm1", "achieved": round(gbps("gmm1"), 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(gbps("gmm1") / HBM_PEAK_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(gbps("gmm1") / HBM_PEAK_GBPS, 4),
+            "traffic": _traffic(w.name, MOE_TRAFFIC_FILE, MOE_KERNEL_SOURCES),
             "alg_bytes_per_launch": b["gmm1"], "avg_launch_ms": round(ph["gmm1"], 5),
             "mfma_tflops": round(tflops("gmm1"), 1),
             "mfma_frac": round(tflops("gmm1") / MFMA_FP8_PEAK_TFLOPS, 4)}
