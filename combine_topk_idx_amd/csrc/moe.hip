@@ -47,9 +47,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // a bounded rate, and its time is about the weight bytes of its tiles plus
 // the activation bytes of their chunks, which every tile of a chunk reads
 // again: wide tiles read the activations fewer times, narrow tiles make more
-// work units.  Each launch takes narrow tiles when their units fit on the
-// CUs at once and wide ones otherwise; workgroups are launched with the wide
-// tile's waves, and with narrow tiles the last two waves leave at once.
+// work units.  Each launch picks the width whose busiest CU moves fewer
+// bytes; workgroups are launched with the wide tile's waves, and with narrow
+// tiles the last two waves leave at once.
 constexpr int kNarrow = 4, kWide = 6;
 constexpr int kThreads = kWide * kWave;
 constexpr int kWaves = kWide;                     // waves launched per workgroup
@@ -111,7 +111,11 @@ __device__ Plan make_plan(int nt_narrow, int nt_wide, int num_cus, int E, const 
   for (int q = 0; q < 2; ++q) {
     const int e = 2 * threadIdx.x + q;
     cnt[q] = 0;
-    if (e < E) cnt[q] = recv_count ? (int)recv_count[e] : offsets[e + 1] - offsets[e];
+    if (e < E) {
+      // rows of expert e: recv_count when given, never more than its block
+      const int block = offsets[e + 1] - offsets[e];
+      cnt[q] = recv_count ? (int)min((int64_t)block, max(recv_count[e], (int64_t)0)) : block;
+    }
     ch[q] = (cnt[q] + kChunkRows - 1) / kChunkRows;
   }
   int x = ch[0] + ch[1];
@@ -135,7 +139,12 @@ __device__ Plan make_plan(int nt_narrow, int nt_wide, int num_cus, int E, const 
   s_first[2 * threadIdx.x + 1] = start + ch[0];
   Plan pl;
   chunks = __builtin_amdgcn_readfirstlane(chunks);
-  pl.waves = chunks * nt_narrow <= num_cus ? kNarrow : kWide;
+  // a CU's time ~ its units x (weight rows + activation rows) of K bytes
+  // each, with chunks taken as full: the tile width with the smaller
+  // busiest-CU cost wins (narrow on a tie)
+  const int rounds_n = (chunks * nt_narrow + num_cus - 1) / num_cus;
+  const int rounds_w = (chunks * nt_wide + num_cus - 1) / num_cus;
+  pl.waves = rounds_n * (32 * kNarrow + kChunkRows) <= rounds_w * (32 * kWide + kChunkRows) ? kNarrow : kWide;
   pl.n_tiles = pl.waves == kNarrow ? nt_narrow : nt_wide;
   pl.units = chunks * pl.n_tiles;
   pl.per = (pl.units + kXcds - 1) / kXcds;

@@ -253,8 +253,9 @@ ep_status_t ep_combine_backward(const ep_handle_t *handle, const void *grad_out,
 /* Expert MLP between dispatch and combine ("[feat] A5 deep fused moe": the
  * fused operator runs dispatch, GMM1, SwiGLU, requant, GMM2 and combine; its
  * GMM1 A operand is e4m3 with one e8m0 scale per 32 elements).  Each expert e
- * multiplies the receive rows of its block (the first recv_count[e] rows, or
- * the whole block when recv_count is NULL) by its own weights.  Weights are
+ * multiplies the receive rows of its block (the first recv_count[e] rows,
+ * clamped to [0, block size], or the whole block when recv_count is NULL) by
+ * its own weights.  Weights are
  * MXFP8 -- codes [E, N, K] (e4m3) and scale bytes [E, N, K/32] (e8m0, one
  * per 32 consecutive codes of a row) -- packed once by ep_moe_pack_weights
  * into the matrix cores' fragment order (a permutation of the same bytes;

@@ -266,6 +266,34 @@ def test_wide_tiles_many_experts(ep):
     print(f"worst row relative error {worst:.3g}")
 
 
+def test_recv_count_is_clamped_to_the_block(ep):
+    """recv_count entries above the block size (or negative) do not reach
+    past the expert's block: the GEMMs then run exactly as with the block
+    sizes (recv_count = NULL)."""
+    w = W.MOE_WORKLOADS["moe_small"]
+    _announce("recv_count clamped to the block")
+    inp = W.make_moe_inputs(w)
+    ref = gpu_moe(ep, w, inp, out_quant="none", pass_count=False, stop_after="gmm1")
+    h = ref["handle"]
+    bad = torch.tensor([1 << 40, -5, 1 << 20, 7][: w.E_local], dtype=torch.int64, device=DEV)
+    rows_kept = np.minimum(np.maximum(bad.cpu().numpy(), 0), np.diff(read_slots(ep, ref, w)[1]))
+    ab, _ = ep.ep_buffer_bytes(h.max_rows, w.I, "none")
+    a = canary_buffer(ab)
+    ep.ep_moe_gmm1(h, ref["recv"], w.H, w.I, *_packed_w1(ep, inp), "none", a, recv_count=bad)
+    torch.cuda.synchronize()
+    got = _bf16_rows(a, h.max_rows, w.I)
+    want = _bf16_rows(ref["a"], h.max_rows, w.I)
+    offs = read_slots(ep, ref, w)[1]
+    for e in range(w.E_local):
+        r0, n = int(offs[e]), int(rows_kept[e])
+        assert np.array_equal(got[r0:r0 + n], want[r0:r0 + n])
+        assert np.all(got[r0 + n:offs[e + 1]] == NAN_BF16)            # rows past the clamped count untouched
+
+
+def _packed_w1(ep, inp):
+    return ep.pack_moe_weights(to_dev(inp["w1_codes"]), to_dev(inp["w1_scales"]), True)
+
+
 def _pack_reference(codes, scales, gate_up):
     """The packed layout of ep_moe_pack_weights built with numpy indexing
     from its description in include/ep.h (a permutation of the bytes)."""
