@@ -232,12 +232,21 @@ def test_share_full_size_sampled(ep):
     print(f"worst row relative error {worst:.3g}")
 
 
-def test_wide_tiles_many_experts(ep):
-    """192 small experts: more narrow work units than a 256-CU device has
-    CUs, so both GEMMs take the 6-wave tiles, whose last tile is partial
-    (GMM1: 16 weight groups = 6 + 6 + 4; GMM2: 8 = 6 + 2)."""
-    w = W.MoeWorkload("moe_wide", 768, 256, 256, 192, 192, 4, seed=1024)
-    _announce("moe wide tiles, 192 experts")
+MANY = [
+    # 80 experts, H 512, I 256: 320 four-group units against 240 six-group
+    # ones, so on a 256-CU device both GEMMs take six-group tiles, the last
+    # one partial (16 weight groups = 6 + 6 + 4)
+    W.MoeWorkload("moe_wide", 480, 512, 256, 80, 80, 4, seed=1024),
+    # 192 experts, H = I = 256: four-group tiles, three units per workgroup
+    W.MoeWorkload("moe_rounds", 768, 256, 256, 192, 192, 4, seed=1025),
+]
+
+
+@pytest.mark.parametrize("w", MANY, ids=[m.name for m in MANY])
+def test_many_small_experts(ep, w):
+    """Many small experts: more work units than CUs (tile width chosen per
+    launch, partial last tiles, workgroups walking several units)."""
+    _announce(f"{w.name}: {w.E_local} experts, H={w.H}, I={w.I}")
     inp = W.make_moe_inputs(w)
     res = gpu_moe(ep, w, inp)
     lay, rb, per, out = oracle_moe(w, inp)
