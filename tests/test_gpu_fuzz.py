@@ -72,6 +72,8 @@ CASES = [
     (16, 128, 7168, 256, 8, "fp8_b128_pow2", "int64", 0.1, 128, "identity"),
     (17, 768, 256, 48, 8, "mxfp8", "int64", 0.1, 768, "identity"),     # one-workgroup layout at 6144 pairs
     (18, 769, 256, 48, 8, "none", "int32", 0.0, 769, "normal"),         # 6152 pairs: two launches
+    (19, 256, 512, 64, 8, "mxfp4", "int64", 0.05, 300, "identity"),     # spare receive rows past R
+    (20, 2049, 128, 32, 1, "int8_token", "int32", 0.0, 2049, "identity"),  # k = 1, smallest int8 row
 ]
 
 
