@@ -175,6 +175,38 @@ def cpu_baseline(name: str, tokens: int, moe: bool = False) -> dict:
 # ---------------------------------------------------------------------------
 
 
+def timed_steps(runners, steps: int, stream):
+    """Throughput pass: `steps` steps (runners[i % len] is the list of phase
+    calls of step i) between one event before the first and one after the
+    last, nothing in between, synchronised on both sides.  Then a phase
+    pass: the same steps again with an event between consecutive phases
+    (an event on the stream takes a few microseconds of its own, so the
+    throughput pass has none).  Returns (ms per step, [ms per phase],
+    wall seconds of the throughput pass)."""
+    import torch
+    nph = len(runners[0])
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        for f in runners[i % len(runners)]:
+            f()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, f in enumerate(runners[i % len(runners)]):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    ph = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(nph)]
+    return ms, ph, wall
+
+
 def backward_main(args) -> int:
     """layout + ep_combine_backward on one workload's routing; one JSON line."""
     if args.gpus != 1:
@@ -210,17 +242,8 @@ def backward_main(args) -> int:
         bwd(sets[i % len(sets)])
     torch.cuda.synchronize()
     R = int(sets[0]["rc"].sum().item())
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        s = sets[i % len(sets)]
-        ev[i][0].record(stream)
-        lay(s)
-        ev[i][1].record(stream)
-        bwd(s)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    runners = [[(lambda s=s: lay(s)), (lambda s=s: bwd(s))] for s in sets]
+    ms, (lay_ms, bwd_ms), _ = timed_steps(runners, args.steps, stream)
     dq, sqb = _row_bytes(q, w.H)
     b_idx = 4 if w.idx_dtype == "int32" else 8
     b_lay = w.T * w.k * b_idx + w.E * 8 + (w.E + 1) * 4 + w.T * w.k * 4 + R * 4
@@ -235,7 +258,7 @@ def backward_main(args) -> int:
         "config": {"workload": f"{w.name} routing: T={w.T} H={w.H} E={w.E} k={w.k}, weighted gradient rows "
                                f"quantised to {q}", "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-        "phase_ms": {"layout": round(ms - bwd_ms, 5), "combine_backward": round(bwd_ms, 5)},
+        "phase_ms": {"layout": round(lay_ms, 5), "combine_backward": round(bwd_ms, 5)},
         "roofline": {"bound": "hbm", "kernel": "combine_backward", "achieved": round(bwd_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "alg_bytes_per_launch": b_bwd, "avg_launch_ms": round(bwd_ms, 5)},
@@ -334,17 +357,8 @@ def moe_main(args) -> int:
     torch.cuda.synchronize()
     R = int(sets[0]["rc"].sum().item())
     names = ["layout", "dispatch", "gmm1", "gmm2", "combine"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        r = runners[i % nsets]
-        ev[i][0].record(stream)
-        for j, f in enumerate(r):
-            f()
-            ev[i][j + 1].record(stream)
-    torch.cuda.synchronize()
-    ms = ev[0][0].elapsed_time(ev[-1][5]) / args.steps
-    ph = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j, n in enumerate(names)}
+    ms, ph_list, _ = timed_steps(runners, args.steps, stream)
+    ph = dict(zip(names, ph_list))
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
@@ -518,27 +532,9 @@ def main() -> int:
             f()
     torch.cuda.synchronize()
     R = int(sets[0]["rc"].sum().item())
-    # timed region: events around each phase, on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        r = runners[i % nsets]
-        e = ev[i]
-        e[0].record(stream)
-        r[0]()
-        e[1].record(stream)
-        r[1]()
-        e[2].record(stream)
-        r[2]()
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall
-    total_ms = ev[0][0].elapsed_time(ev[-1][3])
-    lay_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    disp_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    comb_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
-    ms_per_step = total_ms / args.steps
+    # timed region: the throughput pass of timed_steps, on the launch stream;
+    # the per-phase times (and combine's launch time) come from its phase pass
+    ms_per_step, (lay_ms, disp_ms, comb_ms), wall_s = timed_steps(runners, args.steps, stream)
 
     b = algorithmic_bytes(w, R)
     gbps = b["total"] / (ms_per_step * 1e-3) / 1e9

@@ -275,6 +275,24 @@ def test_many_small_experts(ep, w):
     print(f"worst row relative error {worst:.3g}")
 
 
+def test_wide_tiles_bf16_output(ep):
+    """GMM1 with bf16 output in a launch that takes six-group tiles (the
+    partial last tile included), against the per-element bound."""
+    w = MANY[0]
+    _announce(f"{w.name}: GMM1 bf16 output")
+    inp = W.make_moe_inputs(w)
+    res = gpu_moe(ep, w, inp, out_quant="none", stop_after="gmm1")
+    lay, rb, per, _ = oracle_moe(w, inp, out_mode="bf16")
+    got = _bf16_rows(res["a"], lay.max_rows, w.I)
+    for e, (rows, ent) in enumerate(per):
+        if ent is None:
+            continue
+        bound = _gmm1_bound(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e], ent["a"])
+        _check_gmm1_bf16(got[rows], ent["a"], bound)
+    free = np.nonzero(lay.row_src < 0)[0]
+    assert np.all(got[free] == NAN_BF16)
+
+
 def test_recv_count_is_clamped_to_the_block(ep):
     """recv_count entries above the block size (or negative) do not reach
     past the expert's block: the GEMMs then run exactly as with the block
