@@ -70,7 +70,7 @@ constexpr int kAStageRows = a_stage_rows(kNarrow) > a_stage_rows(kWide) ? a_stag
 constexpr int kAStage = kAStageRows * kRowStride; // bytes of one staged A block
 // A scale bytes are loaded 16 per row (eight K steps) at a time into a
 // double-buffered table of kThreads rows, padded to 20 bytes so that the
-// byte reads of 32 consecutive rows fall in distinct banks.
+// dword reads of 32 consecutive rows fall in distinct banks.
 constexpr int kBodySteps = 8;
 constexpr int kScaleStride = 20;
 constexpr int kScaleBuf = kThreads * kScaleStride;
