@@ -229,6 +229,10 @@ MOE_WORKLOADS = {
     # tokens, 6 experts per device (48 in all), top-6, hidden 7168, inter 3072
     "moe_share": MoeWorkload("moe_share", 1024, 7168, 3072, 48, 6, 6, seed=1021),
     "moe_small": MoeWorkload("moe_small", 96, 512, 256, 12, 4, 3, seed=1022),
+    # the 32 / 64 / 96-tokens-per-device points of the same benchmark
+    "moe_share32": MoeWorkload("moe_share32", 256, 7168, 3072, 48, 6, 6, seed=1031),
+    "moe_share64": MoeWorkload("moe_share64", 512, 7168, 3072, 48, 6, 6, seed=1032),
+    "moe_share96": MoeWorkload("moe_share96", 768, 7168, 3072, 48, 6, 6, seed=1033),
 }
 
 
