@@ -74,6 +74,8 @@ CASES = [
     (18, 769, 256, 48, 8, "none", "int32", 0.0, 769, "normal"),         # 6152 pairs: two launches
     (19, 256, 512, 64, 8, "mxfp4", "int64", 0.05, 300, "identity"),     # spare receive rows past R
     (20, 2049, 128, 32, 1, "int8_token", "int32", 0.0, 2049, "identity"),  # k = 1, smallest int8 row
+    (21, 3, 65536, 4, 2, "int8_token", "int64", 0.0, 3, "identity"),    # largest hidden: 1024 threads x 8 vectors
+    (22, 5, 65504, 6, 3, "mxfp4", "int32", 0.0, 5, "normal"),           # largest hidden that is not a multiple of 128
 ]
 
 
