@@ -16,18 +16,19 @@ MFMA_REL = 5e-4
 
 
 def gpu_moe(ep, w: W.MoeWorkload, inp: dict, *, out_quant="mxfp8", pass_count=True, row_align=1,
-            stop_after=None):
+            expert_capacity=0, stop_after=None):
     """layout -> dispatch (MXFP8) -> GMM1 (+SwiGLU, out_quant) -> GMM2 -> combine."""
     E = w.E_local
-    if row_align > 1:
-        wsb = ep.ep_workspace_bytes_ex(w.T, w.k, E, row_align, 0)
+    padded = row_align > 1 or expert_capacity > 0
+    if padded:
+        wsb = ep.ep_workspace_bytes_ex(w.T, w.k, E, row_align, expert_capacity)
     else:
         wsb = ep.ep_workspace_bytes(w.T, w.k, E)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
     rc = torch.empty(E, dtype=torch.int64, device=DEV)
     idx = to_dev(inp["topk_idx"])
-    if row_align > 1:
-        h = ep.ep_layout_ex(idx, E, w.T, row_align, 0, rc, ws)
+    if padded:
+        h = ep.ep_layout_ex(idx, E, w.T, row_align, expert_capacity, rc, ws)
     else:
         h = ep.ep_layout(idx, E, w.T, rc, ws)
     rows = h.max_rows
@@ -59,10 +60,10 @@ def read_slots(ep, res, w):
     return slot, offs
 
 
-def oracle_moe(w: W.MoeWorkload, inp: dict, *, out_mode="mxfp8", tokens=None, row_align=1):
+def oracle_moe(w: W.MoeWorkload, inp: dict, *, out_mode="mxfp8", tokens=None, row_align=1, expert_capacity=0):
     """Oracle run; with `tokens`, only the rows of those tokens go through the
     MLP and only their combine rows are returned."""
-    lay = OL.layout(inp["topk_idx"], w.E_local, w.T, row_align=row_align)
+    lay = OL.layout(inp["topk_idx"], w.E_local, w.T, row_align=row_align, expert_capacity=expert_capacity)
     rb = OD.dispatch(inp["x"], lay, "mxfp8")
     want_rows = None
     if tokens is not None:

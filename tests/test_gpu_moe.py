@@ -28,7 +28,7 @@ import pytest
 import torch
 
 from combine_topk_idx_amd import workloads as W
-from oracle import codecs, dispatch as OD, moe as OM
+from oracle import codecs, combine as OC, dispatch as OD, moe as OM
 from tests.hip_path import DEV, canary_buffer, sample_tokens, to_dev, NAN_BF16
 from tests.moe_path import MFMA_REL, gpu_moe, oracle_moe, read_slots
 
@@ -208,6 +208,50 @@ def test_hot_expert_many_chunks_and_empty_experts(ep):
             _check_gmm1_bf16(got[rows], ent["a"], bound)
         free = np.nonzero(lay.row_src < 0)[0]
         assert np.all(got[free] == NAN_BF16)
+
+
+def test_capacity_padded_blocks(ep):
+    """The [E, C, ...] receive shape of the low-latency API: every expert
+    block has C rows, the hot expert's pairs past the C-th are dropped (slot
+    -1, never multiplied), the rest of each block is never written; the
+    whole path through combine."""
+    w = W.MoeWorkload("moe_cap", 200, 256, 128, 8, 4, 2, seed=1026)
+    _announce("moe capacity-padded blocks, C = 96")
+    inp = W.make_moe_inputs(w)
+    idx = inp["topk_idx"].copy()
+    idx[:, 0] = 0                                                  # expert 0 wants 200 rows, keeps 96
+    inp["topk_idx"] = idx
+    cap = 96
+    res = gpu_moe(ep, w, inp, expert_capacity=cap)
+    lay, rb, per, out = oracle_moe(w, inp, expert_capacity=cap)
+    assert lay.max_rows == w.E_local * cap and lay.count[0] == cap and lay.status & 2
+    slot, offs = read_slots(ep, res, w)
+    assert np.array_equal(slot, lay.slot) and np.array_equal(offs, lay.offsets.astype(np.int32))
+    total, _ = ep.ep_buffer_bytes(lay.max_rows, w.I, "mxfp8")
+    a = OD.RecvBuffer.from_bytes(res["a"][:total].cpu().numpy(), lay.max_rows, w.I, "mxfp8", lay.num_rows)
+    for e, (rows, ent) in enumerate(per):
+        if ent is None:
+            continue
+        ab = _gmm1_bound(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e], ent["a"], 0.0)
+        _check_requant(a.data[rows], a.scales[rows], ent["q"], ent["qs"], ab)
+    y = _bf16_rows(res["y"], lay.max_rows, w.H)
+    free = np.nonzero(lay.row_src < 0)[0]
+    assert free.size > 0 and np.all(y[free] == NAN_BF16)          # padding rows never written
+    # GMM2 against the exact products of the GPU's own requantised rows, then
+    # combine against the oracle's combine of the GPU's own expert rows (the
+    # requant may move a value by one e4m3 step, checked above; with few
+    # pairs per token and I = 128 one such step can show in a whole row)
+    for e, (rows, ent) in enumerate(per):
+        if ent is None:
+            continue
+        gv = OM.mx_dequant(a.data[rows], a.scales[rows])
+        wv = OM.mx_dequant(inp["w2_codes"][e], inp["w2_scales"][e])
+        want = gv @ wv.T
+        bound = MFMA_REL * (np.abs(gv) @ np.abs(wv).T) + 2.0 ** -8 * np.abs(want) + 1e-30
+        got = codecs.bf16_bits_to_f32(y[rows]).astype(np.float64)
+        assert np.all(np.abs(got - want) <= bound), f"expert {e}: GMM2 outside its bound"
+    cin = OD.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8), np.zeros((lay.max_rows, 0), np.uint8), None)
+    assert np.array_equal(res["out"], OC.combine(cin, lay, inp["topk_weights"]))
 
 
 def test_share_full_size_sampled(ep):
