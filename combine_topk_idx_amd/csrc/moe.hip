@@ -102,8 +102,8 @@ struct Plan {                                     // uniform over the launch
 // per-expert rows and first chunk, for the unit lookups
 __shared__ int s_rows[2 * kThreads], s_first[2 * kThreads];
 
-__device__ Plan make_plan(int nt_narrow, int nt_wide, int num_cus, int E, const int *__restrict__ offsets,
-                          const int64_t *__restrict__ recv_count) {
+__device__ __forceinline__ Plan make_plan(int nt_narrow, int nt_wide, int num_cus, int E,
+                                          const int *__restrict__ offsets, const int64_t *__restrict__ recv_count) {
   __shared__ int wsum[kWaves];
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   int cnt[2], ch[2];
@@ -153,7 +153,7 @@ __device__ Plan make_plan(int nt_narrow, int nt_wide, int num_cus, int E, const 
 
 // The i-th unit of this workgroup, or expert -1 past its last one (uniform).
 // Starts with a barrier, so the previous unit's LDS is no longer in use.
-__device__ Item find_item(const Plan &pl, int E, const int *__restrict__ offsets, int i, int &ntile) {
+__device__ __forceinline__ Item find_item(const Plan &pl, int E, const int *__restrict__ offsets, int i, int &ntile) {
   __shared__ Item found;
   __syncthreads();
   if (threadIdx.x == 0) found.expert = -1;
@@ -175,7 +175,11 @@ __device__ Item find_item(const Plan &pl, int E, const int *__restrict__ offsets
     }
   }
   __syncthreads();
-  return found;
+  Item it;                                        // the same in every lane: kept in scalar registers
+  it.expert = __builtin_amdgcn_readfirstlane(found.expert);
+  it.row0 = __builtin_amdgcn_readfirstlane(found.row0);
+  it.rows = __builtin_amdgcn_readfirstlane(found.rows);
+  return it;
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
