@@ -207,6 +207,30 @@ def timed_steps(runners, steps: int, stream):
     return ms, ph, wall
 
 
+def graph_steps(runners, steps: int, stream) -> float:
+    """The same `steps` steps captured once into one HIP graph (every phase
+    call of every step a kernel node, on the rotating buffer sets), replayed
+    once untimed and then once between two events on `stream`: the GPU's
+    time per step without the host's per-call launch cost.  Returns ms per
+    step."""
+    import torch
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            for f in runners[i % len(runners)]:
+                f()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def backward_main(args) -> int:
     """layout + ep_combine_backward on one workload's routing; one JSON line."""
     if args.gpus != 1:
@@ -414,6 +438,9 @@ def main() -> int:
     ap.add_argument("--moe", default=None, metavar="WORKLOAD",
                     help="time the expert-MLP path (layout, MXFP8 dispatch, GMM1+SwiGLU+requant, GMM2, combine) "
                          "of a MoE workload, e.g. moe_share")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as one captured HIP graph (no per-call host cost) instead of stream "
+                         "launches")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-baseline-moe-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -535,6 +562,11 @@ def main() -> int:
     # timed region: the throughput pass of timed_steps, on the launch stream;
     # the per-phase times (and combine's launch time) come from its phase pass
     ms_per_step, (lay_ms, disp_ms, comb_ms), wall_s = timed_steps(runners, args.steps, stream)
+    stream_ms = ms_per_step
+    if args.graph:
+        # the timed steps as one graph replay; the phases stay those of the
+        # stream pass
+        ms_per_step = graph_steps(runners, args.steps, stream)
 
     b = algorithmic_bytes(w, R)
     gbps = b["total"] / (ms_per_step * 1e-3) / 1e9
@@ -560,13 +592,14 @@ def main() -> int:
                                f"combine_input={w.combine_input}",
                    "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R, "buffer_sets": nsets,
                    "row_align": w.row_align, "expert_capacity": w.expert_capacity, "interleaved": w.interleaved,
-                   "receive_rows": w.max_rows},
+                   "receive_rows": w.max_rows, "launch": "graph" if args.graph else "stream"},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "alg_bytes_per_step": b["total"],
         "phase_ms": {"layout": round(lay_ms, 5), "dispatch": round(disp_ms, 5), "combine": round(comb_ms, 5)},
         "phase_gbps": {"dispatch": round(b["dispatch"] / (disp_ms * 1e-3) / 1e9, 1),
                        "combine": round(comb_gbps, 1)},
         "wall_s": round(wall_s, 4),
+        "stream_ms_per_step": round(stream_ms, 5),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
