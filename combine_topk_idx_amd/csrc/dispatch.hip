@@ -286,6 +286,17 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
   const int c = blockIdx.x - t * chunks;
   const int64_t pair0 = (int64_t)t * k;
 
+  // the token's span is loaded first and the routed rows right after, before
+  // either is needed, so the two loads are in flight together (at decode
+  // sizes each is a memory round trip of the kernel's short life)
+  const u32x4 *xr = x + (int64_t)t * nvec;
+  const int v0 = c * NT * VPT + threadIdx.x;
+  u32x4 raw[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = v0 + i * NT;
+    raw[i] = v < nvec ? xr[v] : u32x4{0u, 0u, 0u, 0u};
+  }
   // routed rows: loads from valid addresses first, then masking, so the loads
   // are in flight together (with k == KMAX they are one wide scalar load)
   int s[KMAX];
@@ -306,15 +317,6 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
   if (!WEIGHTED && recv_w != nullptr && c == 0 && threadIdx.x < k) {
     const int r = slot[pair0 + threadIdx.x];
     if (r >= 0) recv_w[r] = w[pair0 + threadIdx.x];
-  }
-
-  const u32x4 *xr = x + (int64_t)t * nvec;
-  const int v0 = c * NT * VPT + threadIdx.x;
-  u32x4 raw[VPT];
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int v = v0 + i * NT;
-    raw[i] = v < nvec ? xr[v] : u32x4{0u, 0u, 0u, 0u};
   }
 
   if constexpr (!WEIGHTED) {
