@@ -81,11 +81,12 @@ enum Mode { kGmm1Mx = 0, kGmm1Bf16 = 1, kGmm2 = 2 };
 
 struct Item {
   int expert, row0, rows;                         // rows <= kChunkRows
+  int waves;                                      // tile width of the unit
 };
 
 // The work of a launch.  Work units are (expert, chunk of up to kChunkRows
-// rows, N tile) triples in expert-major order; their number comes from a
-// workgroup scan of the per-expert chunk counts (recv_count when given, else
+// rows, N tile) triples in expert-major order; their number comes from
+// workgroup scans over the experts (rows from recv_count when given, else
 // the expert block sizes; every thread takes two experts).  The grid is at
 // most one workgroup per CU and each workgroup walks its units with a
 // stride.  The hardware hands workgroups to the 8 XCDs round-robin, so
@@ -93,19 +94,65 @@ struct Item {
 // [x * per, (x + 1) * per) keeps each XCD on one or two experts, whose
 // activation rows then stay in that XCD's L2 instead of being fetched by
 // every XCD.
+//
+// Tile widths.  A launch first takes one width for all chunks, counting
+// every chunk as full (the cost rule above).  When that is the wide tile
+// and every unit gets its own workgroup, chunks are then moved to narrow
+// tiles, those with the most 32-row fragments first (their units cost the
+// most), while the units still fit the grid: a 5-fragment chunk on narrow
+// tiles costs less than a 4-fragment one on wide tiles, so the busiest CU
+// gets cheaper at no cost to the others.  In such a mixed launch the
+// chunks with at least `nf_narrow` fragments take narrow tiles.
 constexpr int kXcds = 8;
 
 struct Plan {                                     // uniform over the launch
-  int units, per, n_tiles, waves;
+  int units, per, n_tiles, waves;                 // one width: n_tiles per chunk, `waves` its width
+  bool mixed;                                     // both widths (then the fields below)
+  int nt_narrow, nt_wide, nf_narrow;
 };
 
-// per-expert rows and first chunk, for the unit lookups
+// per-expert rows and first chunk (first unit when mixed), for the unit lookups
 __shared__ int s_rows[2 * kThreads], s_first[2 * kThreads];
 
+__device__ __forceinline__ int frags_of(int rows) { return (rows + 31) / 32; }
+
+// Units of an expert with `rows` rows in a mixed launch: its full chunks,
+// then a partial one.
+__device__ __forceinline__ int expert_units(int rows, int nf_narrow, int nt_narrow, int nt_wide) {
+  const int full = rows / kChunkRows, rest = rows - full * kChunkRows;
+  const int nt_full = kMaxFrags >= nf_narrow ? nt_narrow : nt_wide;
+  return full * nt_full + (rest > 0 ? (frags_of(rest) >= nf_narrow ? nt_narrow : nt_wide) : 0);
+}
+
+// Exclusive scan of x over the workgroup (every thread one value); returns
+// the thread's start and the total in `all`.  Ends with a barrier.
+__device__ __forceinline__ int block_scan(int x, int *wsum, int &all) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int x0 = x;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) wsum[wv] = x;
+  __syncthreads();
+  int before = 0;
+  all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    before += i < wv ? wsum[i] : 0;
+    all += wsum[i];
+  }
+  __syncthreads();
+  return before + x - x0;
+}
+
+// MIX: whether the launch may use both widths (see the kernel).
+template <bool MIX>
 __device__ __forceinline__ Plan make_plan(int nt_narrow, int nt_wide, int num_cus, int E,
                                           const int *__restrict__ offsets, const int64_t *__restrict__ recv_count) {
   __shared__ int wsum[kWaves];
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  __shared__ int bins[kMaxFrags + 1];             // chunks by fragment count
   int cnt[2], ch[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -118,21 +165,9 @@ __device__ __forceinline__ Plan make_plan(int nt_narrow, int nt_wide, int num_cu
     }
     ch[q] = (cnt[q] + kChunkRows - 1) / kChunkRows;
   }
-  int x = ch[0] + ch[1];
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == kWave - 1) wsum[wv] = x;
-  __syncthreads();
-  int before = 0, chunks = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    before += i < wv ? wsum[i] : 0;
-    chunks += wsum[i];
-  }
-  const int start = before + x - ch[0] - ch[1];
+  if (threadIdx.x <= kMaxFrags) bins[threadIdx.x] = 0;
+  int chunks;
+  const int start = block_scan(ch[0] + ch[1], wsum, chunks);
   s_rows[2 * threadIdx.x] = cnt[0];
   s_rows[2 * threadIdx.x + 1] = cnt[1];
   s_first[2 * threadIdx.x] = start;
@@ -147,6 +182,40 @@ __device__ __forceinline__ Plan make_plan(int nt_narrow, int nt_wide, int num_cu
   pl.waves = rounds_n * (32 * kNarrow + kChunkRows) <= rounds_w * (32 * kWide + kChunkRows) ? kNarrow : kWide;
   pl.n_tiles = pl.waves == kNarrow ? nt_narrow : nt_wide;
   pl.units = chunks * pl.n_tiles;
+  pl.mixed = false;
+  pl.nt_narrow = nt_narrow;
+  pl.nt_wide = nt_wide;
+  pl.nf_narrow = kMaxFrags + 1;
+  const int grid = (int)gridDim.x / kXcds * kXcds;   // units one round can take
+  if (MIX && pl.waves == kWide && pl.units <= grid && nt_narrow > nt_wide) {
+    // one unit per workgroup: move the chunks with the most fragments to
+    // narrow tiles while the units still fit
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int full = cnt[q] / kChunkRows, rest = cnt[q] - full * kChunkRows;
+      if (full > 0) atomicAdd(&bins[kMaxFrags], full);
+      if (rest > 0) atomicAdd(&bins[frags_of(rest)], 1);
+    }
+    __syncthreads();
+    int units = pl.units;
+    for (int nf = kMaxFrags; nf >= 1; --nf) {
+      const int more = bins[nf] * (nt_narrow - nt_wide);
+      if (units + more > grid) break;
+      units += more;
+      if (more > 0) pl.nf_narrow = nf;
+    }
+    pl.nf_narrow = __builtin_amdgcn_readfirstlane(pl.nf_narrow);
+    if (pl.nf_narrow <= kMaxFrags) {
+      // first unit of every expert
+      const int u0 = expert_units(cnt[0], pl.nf_narrow, nt_narrow, nt_wide);
+      const int u1 = expert_units(cnt[1], pl.nf_narrow, nt_narrow, nt_wide);
+      const int ustart = block_scan(u0 + u1, wsum, units);
+      s_first[2 * threadIdx.x] = ustart;
+      s_first[2 * threadIdx.x + 1] = ustart + u0;
+      pl.mixed = true;
+      pl.units = __builtin_amdgcn_readfirstlane(units);
+    }
+  }
   pl.per = (pl.units + kXcds - 1) / kXcds;
   return pl;
 }
@@ -155,22 +224,43 @@ __device__ __forceinline__ Plan make_plan(int nt_narrow, int nt_wide, int num_cu
 // Starts with a barrier, so the previous unit's LDS is no longer in use.
 __device__ __forceinline__ Item find_item(const Plan &pl, int E, const int *__restrict__ offsets, int i, int &ntile) {
   __shared__ Item found;
+  __shared__ int found_tile;
   __syncthreads();
   if (threadIdx.x == 0) found.expert = -1;
   __syncthreads();
   const int slot = blockIdx.x / kXcds + i * (gridDim.x / kXcds);
   const int unit = (blockIdx.x % kXcds) * pl.per + slot;
-  const bool have = slot < pl.per && unit < pl.units;
-  const int item = unit / pl.n_tiles;
-  ntile = unit - item * pl.n_tiles;
-  if (have) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      const int first = s_first[e], rows = s_rows[e];
-      const int c = item - first;
-      if (c >= 0 && c * kChunkRows < rows) {
-        found.expert = e;
-        found.row0 = offsets[e] + c * kChunkRows;
-        found.rows = min(kChunkRows, rows - c * kChunkRows);
+  if (slot < pl.per && unit < pl.units) {
+    if (!pl.mixed) {
+      const int item = unit / pl.n_tiles;
+      for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int first = s_first[e], rows = s_rows[e];
+        const int c = item - first;
+        if (c >= 0 && c * kChunkRows < rows) {
+          found.expert = e;
+          found.row0 = offsets[e] + c * kChunkRows;
+          found.rows = min(kChunkRows, rows - c * kChunkRows);
+          found.waves = pl.waves;
+          found_tile = unit - item * pl.n_tiles;
+        }
+      }
+    } else {
+      for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int first = s_first[e], rows = s_rows[e];
+        const int u = unit - first;
+        if (u >= 0 && u < expert_units(rows, pl.nf_narrow, pl.nt_narrow, pl.nt_wide)) {
+          // full chunks first, then the partial one
+          const int full = rows / kChunkRows;
+          const bool full_narrow = kMaxFrags >= pl.nf_narrow;
+          const int nt_full = full_narrow ? pl.nt_narrow : pl.nt_wide;
+          const bool in_full = u < full * nt_full;
+          const int c = in_full ? u / nt_full : full;
+          found.expert = e;
+          found.row0 = offsets[e] + c * kChunkRows;
+          found.rows = min(kChunkRows, rows - c * kChunkRows);
+          found.waves = (in_full ? full_narrow : frags_of(rows - full * kChunkRows) >= pl.nf_narrow) ? kNarrow : kWide;
+          found_tile = u - c * nt_full;
+        }
       }
     }
   }
@@ -179,6 +269,8 @@ __device__ __forceinline__ Item find_item(const Plan &pl, int E, const int *__re
   it.expert = __builtin_amdgcn_readfirstlane(found.expert);
   it.row0 = __builtin_amdgcn_readfirstlane(found.row0);
   it.rows = __builtin_amdgcn_readfirstlane(found.rows);
+  it.waves = __builtin_amdgcn_readfirstlane(found.waves);
+  ntile = __builtin_amdgcn_readfirstlane(found_tile);
   return it;
 }
 
@@ -564,20 +656,31 @@ __global__ __launch_bounds__(kThreads) void mx_gmm_kernel(GemmArgs p, const int 
                                                           const int64_t *__restrict__ recv_count, int E) {
   constexpr int kTile = MODE == kGmm2 ? 0 : kEpiTileBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kTile ? kStaging : kTile];
-  const Plan pl = make_plan(p.nt_narrow, p.nt_wide, p.num_cus, E, offsets, recv_count);
+  // GMM2 launches keep one width: the exit below that a launch with both
+  // widths needs made GMM2's compiled loop about 10 % slower, and at the
+  // sizes measured GMM2 never had room for narrow tiles anyway
+  constexpr bool kMix = MODE != kGmm2;
+  const Plan pl = make_plan<kMix>(p.nt_narrow, p.nt_wide, p.num_cus, E, offsets, recv_count);
   // with narrow tiles the last waves have no weight group; a wave that has
-  // ended no longer takes part in the workgroup's barriers
-  if ((int)(threadIdx.x / kWave) >= pl.waves) return;
+  // ended no longer takes part in the workgroup's barriers (the wave index
+  // is read as a scalar, so that these exits are branches of whole waves)
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  if (wave >= pl.waves) return;
   for (int i = 0;; ++i) {
     int ntile;
     const Item it = find_item(pl, E, offsets, i, ntile);
     if (it.expert < 0) return;                                   // uniform
+    // a launch with both widths gives every workgroup at most one unit, so
+    // the waves a narrow unit does not use are done
+    if constexpr (kMix) {
+      if (wave >= it.waves) return;
+    }
     // the thread index passes through an empty asm in every iteration, so
     // that no address derived from it is hoisted out of this loop (held
     // across a whole unit, those would crowd out the GEMM's registers)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    if (pl.waves == kNarrow)
+    if ((kMix ? it.waves : pl.waves) == kNarrow)
       gemm_frags<MODE, kNarrow>(p, it, ntile, smem, tid);
     else
       gemm_frags<MODE, kWide>(p, it, ntile, smem, tid);

@@ -210,6 +210,35 @@ def test_hot_expert_many_chunks_and_empty_experts(ep):
         assert np.all(got[free] == NAN_BF16)
 
 
+def test_mixed_tile_widths(ep):
+    """A launch with both tile widths (on a 256-CU device): GMM1 of I = 3072
+    has 96 four-group or 64 six-group tiles per chunk; with three chunks the
+    six-group plan fits one round and the chunk with the most fragments moves
+    to four-group tiles.  Expert 0 has 200 rows, a full 160-row chunk (five
+    fragments: narrow) and a 40-row one (two fragments: wide); expert 1 has
+    60 rows (wide).  bf16 and MXFP8 outputs against the oracle."""
+    w = W.MoeWorkload("moe_mixed", 260, 256, 3072, 2, 2, 1, seed=1026)
+    _announce("moe mixed tile widths: 200 + 60 rows, I=3072")
+    inp = W.make_moe_inputs(w)
+    idx = np.zeros((w.T, 1), dtype=inp["topk_idx"].dtype)
+    idx[200:] = 1
+    inp["topk_idx"] = idx
+    res = gpu_moe(ep, w, inp, out_quant="none", stop_after="gmm1")
+    lay, rb, per, _ = oracle_moe(w, inp, out_mode="bf16")
+    assert list(lay.count) == [200, 60]
+    got = _bf16_rows(res["a"], lay.max_rows, w.I)
+    for e, (rows, ent) in enumerate(per):
+        bound = _gmm1_bound(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e], ent["a"])
+        _check_gmm1_bf16(got[rows], ent["a"], bound)
+    res = gpu_moe(ep, w, inp, out_quant="mxfp8", stop_after="gmm1")
+    lay, rb, per, _ = oracle_moe(w, inp, out_mode="mxfp8")
+    total, _ = ep.ep_buffer_bytes(lay.max_rows, w.I, "mxfp8")
+    a = OD.RecvBuffer.from_bytes(res["a"][:total].cpu().numpy(), lay.max_rows, w.I, "mxfp8", lay.num_rows)
+    for e, (rows, ent) in enumerate(per):
+        ab = _gmm1_bound(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e], ent["a"], 0.0)
+        _check_requant(a.data[rows], a.scales[rows], ent["q"], ent["qs"], ab)
+
+
 def test_capacity_padded_blocks(ep):
     """The [E, C, ...] receive shape of the low-latency API: every expert
     block has C rows, the hot expert's pairs past the C-th are dropped (slot
