@@ -102,6 +102,9 @@ __device__ __forceinline__ uint32_t dpp_row_ror4(uint32_t v) {
 __device__ __forceinline__ uint32_t dpp_row_ror8(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
 }
+__device__ __forceinline__ uint32_t dpp_row_ror12(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x12C, 0xF, 0xF, false);
+}
 
 // max over the 4 lanes of a quad / the 16 lanes of a row, on unsigned values
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {

@@ -162,6 +162,66 @@ __device__ __forceinline__ u32x4 scale_bf16x8(const u32x4 &r, float w) {
   return o;
 }
 
+// Reverse dispatch in MXFP8: row s[j] receives, per 32-element block, the
+// MX codes of bf16(fl32(w[j] * g)).  Worked from the float32 products, with
+// no unpacking of rounded values: the block maximum of |w g| rounded to bf16
+// is the maximum of the rounded values (rounding is monotonic), and clamping
+// to +-448 * 2^se before the rounding gives what clamping after it gives
+// (448 * 2^se is itself a bf16 value), so the clamped, rounded pairs go
+// straight to the scaled e4m3 conversion, which divides by 2^se exactly and
+// rounds to nearest even (checked on the device against the unscaled encoder
+// of the exact quotient for every finite bf16 pattern and every se; past
+// +-448 it would give NaN, hence the clamp).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+template <int NT, int VPT, int KMAX, bool PACK>
+__device__ __forceinline__ void weighted_mxfp8_store(const u32x4 (&raw)[VPT], int v0, int nvec, const int (&s)[KMAX],
+                                                     const float (&wj)[KMAX], char *__restrict__ data,
+                                                     char *__restrict__ scales, int64_t dq, int64_t sq) {
+  float g[VPT][8];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) unpack8(raw[i], g[i]);
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (s[j] < 0) continue;   // uniform
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = v0 + i * NT;
+      float p[8];
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = wj[j] * g[i][e];
+        m = fmaxf(m, fabsf(p[e]));
+      }
+      float mult, scale;
+      const uint32_t sbyte = mx_scale(quad_max(pack_bf16x2(m, 0.0f) & 0xffffu), 8, mult, scale);
+      // scale bytes of the row's four blocks into its first lane (a row
+      // rotation by n hands lane l the value of lane l - n, modulo 16)
+      const uint32_t sword = PACK ? sbyte | (dpp_row_ror12(sbyte) << 8) | (dpp_row_ror8(sbyte) << 16) |
+                                        (dpp_row_ror4(sbyte) << 24)
+                                  : sbyte;
+      if (v >= nvec) continue;
+      const float lim = 448.0f * scale;
+      uint32_t wd[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        wd[k] = pack_bf16x2(__builtin_amdgcn_fmed3f(p[2 * k], -lim, lim), __builtin_amdgcn_fmed3f(p[2 * k + 1], -lim, lim));
+      s16x2 o0 = {0, 0}, o1 = {0, 0};
+      o0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o0, __builtin_bit_cast(bf16x2, wd[0]), scale, false);
+      o0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o0, __builtin_bit_cast(bf16x2, wd[1]), scale, true);
+      o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, __builtin_bit_cast(bf16x2, wd[2]), scale, false);
+      o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, __builtin_bit_cast(bf16x2, wd[3]), scale, true);
+      const u32x2 q = pin(u32x2{__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1)});
+      st_row(data + s[j] * dq + (int64_t)v * 8, q);
+      if (PACK ? (v & 15) == 0 : (v & 3) == 0) {
+        char *sp = scales + s[j] * sq + (int64_t)(v >> 2);
+        if constexpr (PACK) st_row(sp, sword);
+        else st_row(sp, (uint8_t)sbyte);
+      }
+    }
+  }
+}
+
 // Quantises this thread's VPT row vectors (vector v0 + i*NT of one token row)
 // and stores the packed codes and scales to every receive row s[j] >= 0 with
 // j0 <= j < j1.  Every thread of the workgroup calls it (the int8 row maximum
@@ -321,6 +381,8 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
 
   if constexpr (!WEIGHTED) {
     quantize_store<Q, NT, VPT, KMAX, PACK>(raw, v0, nvec, s, 0, KMAX, data, scales, dq, sq, red);
+  } else if constexpr (Q == EP_QUANT_MXFP8) {
+    weighted_mxfp8_store<NT, VPT, KMAX, PACK>(raw, v0, nvec, s, wj, data, scales, dq, sq);
   } else {
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {

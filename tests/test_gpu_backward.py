@@ -80,3 +80,42 @@ def test_backward_full_size_sampled(ep):
     data, scales = recv_rows(ep, run, w, rows)
     assert np.array_equal(data, rb.data[rows])
     assert np.array_equal(scales, rb.scales[rows])
+
+
+@pytest.mark.parametrize("mode", ["mxfp8", "mxfp4"])
+def test_backward_every_bf16_pattern(ep, mode):
+    """Weighted reverse dispatch of all 65536 bf16 patterns (NaN/Inf replaced
+    by 0), shuffled and sorted into rows, plus rows of zeros, subnormals and
+    near-overflow values, under weights that include 1, -1, tiny and
+    subnormal ones (no product overflows): every product rounded to bf16,
+    every block maximum and every clamp at the top of the code range is
+    compared with the oracle bit for bit."""
+    from oracle import codecs
+    print(f"\n[case] backward every bf16 pattern {mode}", flush=True)
+    H = 1024
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = codecs.bf16_bits_to_f32(pats)
+    pats[~np.isfinite(f)] = 0
+    rng = np.random.default_rng(13)
+    extra = np.zeros((4, H), np.uint16)
+    extra[1, :] = 0x0001
+    extra[2, :] = 0x7F7F
+    extra[3, ::2] = 0x8000
+    grad = np.concatenate([rng.permutation(pats).reshape(-1, H), np.sort(pats).reshape(-1, H), extra])
+    T, k, E = grad.shape[0], 2, 8
+    w = W.Workload("bp", T, H, E, k, "int64", mode, "uniform", seed=6100)
+    inp = W.make_inputs(w)
+    wts = inp["topk_weights"].copy()
+    wts[0::7, 0] = 1.0
+    wts[1::7, 1] = -1.0
+    wts[2::7, 0] = np.float32(2.0 ** -120)
+    wts[3::7, 1] = np.float32(0.75)
+    wts[4::7, 0] = np.float32(1.5 * 2.0 ** -140)
+    inp["topk_weights"] = wts
+    run = _run(ep, w, inp, grad, True)
+    lay = OL.layout(inp["topk_idx"], E, T)
+    rb = OB.combine_backward(grad, lay, mode, wts)
+    R = lay.num_rows
+    data, scales = recv_rows(ep, run, w)
+    assert np.array_equal(scales[:R], rb.scales[:R])
+    assert np.array_equal(data[:R], rb.data[:R])
