@@ -390,6 +390,22 @@ def test_recv_count_is_clamped_to_the_block(ep):
         assert np.all(got[r0 + n:offs[e + 1]] == NAN_BF16)            # rows past the clamped count untouched
 
 
+def test_no_routed_rows(ep):
+    """Every id -1: no expert has a row, both GEMMs launch with no work unit
+    and write nothing, and combine gives +0 rows."""
+    w = W.MOE_WORKLOADS["moe_small"]
+    _announce("moe with no routed rows")
+    inp = W.make_moe_inputs(w)
+    inp["topk_idx"] = np.full_like(inp["topk_idx"], -1)
+    res = gpu_moe(ep, w, inp)
+    h = res["handle"]
+    assert int(res["rc"].sum().item()) == 0
+    assert torch.all(res["a"].view(torch.int16) == NAN_BF16)
+    assert torch.all(res["y"].view(torch.int16) == NAN_BF16)
+    assert np.all(res["out"] == 0)
+    assert h.max_rows == w.T * w.k
+
+
 def _packed_w1(ep, inp):
     return ep.pack_moe_weights(to_dev(inp["w1_codes"]), to_dev(inp["w1_scales"]), True)
 
