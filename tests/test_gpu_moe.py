@@ -390,6 +390,51 @@ def test_recv_count_is_clamped_to_the_block(ep):
         assert np.all(got[r0 + n:offs[e + 1]] == NAN_BF16)            # rows past the clamped count untouched
 
 
+FUZZ = [
+    # T, H, I, E_total, E_local, k, seed: chunks of every fragment count,
+    # several chunks per expert, launches with one width or both
+    (300, 256, 3072, 4, 3, 2, 1101),
+    (500, 384, 1536, 8, 3, 4, 1102),
+    (200, 128, 768, 16, 16, 3, 1103),
+    (64, 512, 256, 8, 8, 1, 1104),
+    (1000, 128, 384, 2, 2, 1, 1105),
+    (96, 640, 640, 5, 5, 5, 1106),
+    # I = 3072: six-group tiles in one round; three 5-fragment chunks moved
+    # to four-group tiles (mixed), and seven chunks with no room to move any
+    (768, 256, 3072, 6, 6, 1, 1107),
+    (900, 128, 3072, 7, 7, 1, 1109),
+]
+
+
+@pytest.mark.parametrize("case", FUZZ, ids=[f"f{c[-1]}" for c in FUZZ])
+def test_gemm_shapes(ep, case):
+    """Assorted shapes through the whole path: GMM1's MXFP8 rows against the
+    oracle's requant, GMM2 against the exact product with the GPU's own GMM1
+    rows, rows holding no pair never written."""
+    T, H, I, Et, El, k, seed = case
+    w = W.MoeWorkload(f"fz{seed}", T, H, I, Et, El, k, seed=seed)
+    _announce(f"gemm shapes T={T} H={H} I={I} experts {El}/{Et} k={k}")
+    inp = W.make_moe_inputs(w)
+    res = gpu_moe(ep, w, inp)
+    lay, rb, per, out = oracle_moe(w, inp)
+    total, _ = ep.ep_buffer_bytes(lay.max_rows, w.I, "mxfp8")
+    a = OD.RecvBuffer.from_bytes(res["a"][:total].cpu().numpy(), lay.max_rows, w.I, "mxfp8", lay.num_rows)
+    y = _bf16_rows(res["y"], lay.max_rows, w.H)
+    for e, (rows, ent) in enumerate(per):
+        if ent is None:
+            continue
+        ab = _gmm1_bound(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e], ent["a"], 0.0)
+        _check_requant(a.data[rows], a.scales[rows], ent["q"], ent["qs"], ab, frac=0.05)
+        gv = OM.mx_dequant(a.data[rows], a.scales[rows])
+        wv = OM.mx_dequant(inp["w2_codes"][e], inp["w2_scales"][e])
+        want = gv @ wv.T
+        bound = MFMA_REL * (np.abs(gv) @ np.abs(wv).T) + 2.0 ** -8 * np.abs(want) + 1e-30
+        err = np.abs(codecs.bf16_bits_to_f32(y[rows]).astype(np.float64) - want)
+        assert np.all(err <= bound), f"expert {e}: worst GMM2 err/bound {np.max(err / bound):.3g}"
+    free = np.nonzero(lay.row_src < 0)[0]
+    assert np.all(y[free] == NAN_BF16)
+
+
 def test_no_routed_rows(ep):
     """Every id -1: no expert has a row, both GEMMs launch with no work unit
     and write nothing, and combine gives +0 rows."""
