@@ -55,3 +55,18 @@ def test_more_than_one_gpu_is_refused(extra):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", *extra],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_committed_counters_match_the_kernel_sources():
+    """profiles/ holds rocprofv3 HBM byte counts for the measured kernels,
+    stamped with a hash of the kernel sources they were taken on; bench.py
+    reports them as `roofline.traffic` only while the sources still match.
+    A kernel change must come with counters taken again."""
+    large = bench._traffic("large")
+    moe = bench._traffic("moe_share", bench.MOE_TRAFFIC_FILE, bench.MOE_KERNEL_SOURCES)
+    assert large is not None, "profiles/combine_large_traffic.json was taken on other kernel sources"
+    assert moe is not None, "profiles/gmm1_moe_share_traffic.json was taken on other kernel sources"
+    with open(os.path.join(ROOT, "profiles", "combine_large_traffic.json")) as f:
+        d = json.load(f)
+    # counter bytes within a few percent of the algorithmic bytes: no wasted re-reads
+    assert 1.0 <= d["traffic_over_alg"] < 1.05
