@@ -182,7 +182,8 @@ def timed_steps(runners, steps: int, stream):
     pass: the same steps again with an event between consecutive phases
     (an event on the stream takes a few microseconds of its own, so the
     throughput pass has none).  Returns (ms per step, [ms per phase],
-    wall seconds of the throughput pass)."""
+    wall seconds of the throughput pass, {p10, p50, p90} of the per-step
+    times of the phase pass, events included)."""
     import torch
     nph = len(runners[0])
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -204,7 +205,10 @@ def timed_steps(runners, steps: int, stream):
             ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     ph = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(nph)]
-    return ms, ph, wall
+    per = sorted(e[0].elapsed_time(e[nph]) for e in ev)
+    pick = lambda q: per[min(len(per) - 1, int(q * len(per)))]
+    dist = {"p10": round(pick(0.1), 5), "p50": round(pick(0.5), 5), "p90": round(pick(0.9), 5)}
+    return ms, ph, wall, dist
 
 
 def graph_steps(runners, steps: int, stream) -> float:
@@ -267,7 +271,7 @@ def backward_main(args) -> int:
     torch.cuda.synchronize()
     R = int(sets[0]["rc"].sum().item())
     runners = [[(lambda s=s: lay(s)), (lambda s=s: bwd(s))] for s in sets]
-    ms, (lay_ms, bwd_ms), _ = timed_steps(runners, args.steps, stream)
+    ms, (lay_ms, bwd_ms), _, dist = timed_steps(runners, args.steps, stream)
     dq, sqb = _row_bytes(q, w.H)
     b_idx = 4 if w.idx_dtype == "int32" else 8
     b_lay = w.T * w.k * b_idx + w.E * 8 + (w.E + 1) * 4 + w.T * w.k * 4 + R * 4
@@ -283,6 +287,7 @@ def backward_main(args) -> int:
                                f"quantised to {q}", "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "phase_ms": {"layout": round(lay_ms, 5), "combine_backward": round(bwd_ms, 5)},
+        "step_ms_phase_pass": dist,
         "roofline": {"bound": "hbm", "kernel": "combine_backward", "achieved": round(bwd_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(bwd_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "alg_bytes_per_launch": b_bwd, "avg_launch_ms": round(bwd_ms, 5)},
@@ -381,7 +386,7 @@ def moe_main(args) -> int:
     torch.cuda.synchronize()
     R = int(sets[0]["rc"].sum().item())
     names = ["layout", "dispatch", "gmm1", "gmm2", "combine"]
-    ms, ph_list, _ = timed_steps(runners, args.steps, stream)
+    ms, ph_list, _, dist = timed_steps(runners, args.steps, stream)
     ph = dict(zip(names, ph_list))
     cpu = None
     if not args.no_cpu_baseline:
@@ -405,6 +410,7 @@ def moe_main(args) -> int:
         "config": {"workload": f"{w.name}: T={w.T} H={w.H} I={w.I} experts {w.E_local} of {w.E_total} k={w.k} "
                                f"MXFP8 activations and weights", "rows": R, "buffer_sets": nsets},
         "phase_ms": {n: round(v, 5) for n, v in ph.items()},
+        "step_ms_phase_pass": dist,
         "phase_gbps": {n: round(gbps(n), 1) for n in names},
         "gemm_tflops": {n: round(tflops(n), 1) for n in ("gmm1", "gmm2")},
         "hbm_gbps": round(b["total"] / (ms * 1e-3) / 1e9, 1),
@@ -561,7 +567,7 @@ def main() -> int:
     R = int(sets[0]["rc"].sum().item())
     # timed region: the throughput pass of timed_steps, on the launch stream;
     # the per-phase times (and combine's launch time) come from its phase pass
-    ms_per_step, (lay_ms, disp_ms, comb_ms), wall_s = timed_steps(runners, args.steps, stream)
+    ms_per_step, (lay_ms, disp_ms, comb_ms), wall_s, dist = timed_steps(runners, args.steps, stream)
     stream_ms = ms_per_step
     if args.graph:
         # the timed steps as one graph replay; the phases stay those of the
@@ -599,6 +605,7 @@ def main() -> int:
         "phase_gbps": {"dispatch": round(b["dispatch"] / (disp_ms * 1e-3) / 1e9, 1),
                        "combine": round(comb_gbps, 1)},
         "wall_s": round(wall_s, 4),
+        "step_ms_phase_pass": dist,
         "stream_ms_per_step": round(stream_ms, 5),
         "roofline": roof,
         "cpu_baseline": cpu,
