@@ -167,7 +167,22 @@ def cpu_baseline(name: str, tokens: int, moe: bool = False) -> dict:
             "layout + dispatch + combine")
     return {"value": d["tokens"] / d["seconds"], "unit": "tokens/s", "cores": d["cores"], "kind": "oracle",
             "sample": f"first {d['tokens']} tokens of the workload as one batch ({what}), "
-                      f"{d['seconds']:.1f} s on one host core"}
+                      f"{d['seconds']:.1f} s on one host core",
+            "host": _host_cpu()}
+
+
+def _host_cpu() -> str:
+    """'1 core of N <model>' for the host the oracle ran on."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"1 core of {len(os.sched_getaffinity(0))} ({model})"
 
 
 # ---------------------------------------------------------------------------
