@@ -22,9 +22,8 @@
 // adjacent lanes and a 128-channel block 16 adjacent lanes, so block maxima
 // are DPP exchanges inside a quad or a 16-lane row; the int8 row maximum is a
 // workgroup reduction.  Routed rows and weights are read once per workgroup
-// (scalar loads).  Stores go through the cache hierarchy (which merges the
-// 4-8 byte lane stores into full lines); a non-temporal variant is a build
-// option in tuning.hpp.
+// (scalar loads).  Code rows are written with non-temporal stores, scale
+// pieces through L2.
 #include <type_traits>
 
 #include "common.hpp"
@@ -130,13 +129,21 @@ __device__ __forceinline__ u32x2 codes_mxfp8(const float (&f)[8], float mult) {
   return e4m3x8_encode(v);
 }
 
+// Code rows are written once and read by a later kernel: non-temporal stores
+// keep them from displacing other lines on the way.  A scale piece is 1-4
+// bytes of a 32-128 byte scale row that 4-16 workgroups on different XCDs
+// write, so it goes through L2, which merges the pieces into whole lines.
 template <typename T>
-__device__ __forceinline__ void st_row(char *p, const T &v) {
-#if EP_DISPATCH_NT_STORE
+__device__ __forceinline__ void st_data(char *p, const T &v) {
+#if EP_DISPATCH_NT_DATA
   __builtin_nontemporal_store(v, (T *)p);
 #else
   *(T *)p = v;
 #endif
+}
+template <typename T>
+__device__ __forceinline__ void st_scale(char *p, const T &v) {
+  *(T *)p = v;
 }
 
 // Workgroup max of one unsigned per thread (NT threads).
@@ -212,11 +219,11 @@ __device__ __forceinline__ void weighted_mxfp8_store(const u32x4 (&raw)[VPT], in
       o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, __builtin_bit_cast(bf16x2, wd[2]), scale, false);
       o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, __builtin_bit_cast(bf16x2, wd[3]), scale, true);
       const u32x2 q = pin(u32x2{__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1)});
-      st_row(data + s[j] * dq + (int64_t)v * 8, q);
+      st_data(data + s[j] * dq + (int64_t)v * 8, q);
       if (PACK ? (v & 15) == 0 : (v & 3) == 0) {
         char *sp = scales + s[j] * sq + (int64_t)(v >> 2);
-        if constexpr (PACK) st_row(sp, sword);
-        else st_row(sp, (uint8_t)sbyte);
+        if constexpr (PACK) st_scale(sp, sword);
+        else st_scale(sp, (uint8_t)sbyte);
       }
     }
   }
@@ -238,7 +245,7 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
       if (v >= nvec) continue;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (routed(j)) st_row(data + s[j] * dq + (int64_t)v * 16, raw[i]);
+        if (routed(j)) st_data(data + s[j] * dq + (int64_t)v * 16, raw[i]);
     }
   } else if constexpr (Q == EP_QUANT_INT8_TOKEN) {
     uint32_t am = 0;
@@ -254,12 +261,12 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
       const u32x2 q = pin(codes_int8(f, b));
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (routed(j)) st_row(data + s[j] * dq + (int64_t)v * 8, q);
+        if (routed(j)) st_data(data + s[j] * dq + (int64_t)v * 8, q);
     }
     if (threadIdx.x == 0) {
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
-        if (routed(j)) st_row(scales + s[j] * sq, b.scale);
+        if (routed(j)) st_scale(scales + s[j] * sq, b.scale);
     }
   } else {
 #pragma unroll
@@ -280,10 +287,10 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
           if (!routed(j)) continue;
-          st_row(data + s[j] * dq + (int64_t)v * 8, q);
+          st_data(data + s[j] * dq + (int64_t)v * 8, q);
           if (lead) {
-            if constexpr (Q == EP_QUANT_FP8_B128_UE8M0) st_row(scales + s[j] * sq + (int64_t)(v >> 4), (uint8_t)sbyte);
-            else st_row(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
+            if constexpr (Q == EP_QUANT_FP8_B128_UE8M0) st_scale(scales + s[j] * sq + (int64_t)(v >> 4), (uint8_t)sbyte);
+            else st_scale(scales + s[j] * sq + (int64_t)(v >> 4) * 4, b.scale);
           }
         }
       } else {
@@ -318,11 +325,11 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
           if (!routed(j)) continue;
-          st_row(data + s[j] * dq + (int64_t)v * kBytes, q);
+          st_data(data + s[j] * dq + (int64_t)v * kBytes, q);
           if (lead) {
             char *sp = scales + s[j] * sq + (int64_t)(v >> 2);
-            if constexpr (PACK) st_row(sp, sword);
-            else st_row(sp, (uint8_t)sbyte);
+            if constexpr (PACK) st_scale(sp, sword);
+            else st_scale(sp, (uint8_t)sbyte);
           }
         }
       }

@@ -9,8 +9,8 @@
 #ifndef EP_DISPATCH_VPT
 #define EP_DISPATCH_VPT 1         // 16-byte input vectors per thread
 #endif
-#ifndef EP_DISPATCH_NT_STORE
-#define EP_DISPATCH_NT_STORE 0    // non-temporal stores of receive rows
+#ifndef EP_DISPATCH_NT_DATA
+#define EP_DISPATCH_NT_DATA 1     // non-temporal stores of the code rows (scale pieces always go through L2)
 #endif
 #ifndef EP_COMBINE_THREADS
 #define EP_COMBINE_THREADS 128
