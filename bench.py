@@ -459,6 +459,9 @@ def main() -> int:
     ap.add_argument("--moe", default=None, metavar="WORKLOAD",
                     help="time the expert-MLP path (layout, MXFP8 dispatch, GMM1+SwiGLU+requant, GMM2, combine) "
                          "of a MoE workload, e.g. moe_share")
+    ap.add_argument("--fused", action="store_true",
+                    help="layout and dispatch through the one call ep_layout_dispatch (a single launch for compact "
+                         "layouts of at most 2048 pairs)")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as one captured HIP graph (no per-call host cost) instead of stream "
                          "launches")
@@ -562,6 +565,11 @@ def main() -> int:
         def disp():
             ep.ep_dispatch(s["h"], s["x"], w.H, w.mode, s["recv"], interleaved=w.interleaved)
 
+        def lay_disp():
+            s["h"] = ep.ep_layout_dispatch(s["idx"], w.E, w.t_max, s["rc"], s["ws"], s["x"], w.H, w.mode, s["recv"],
+                                           row_align=w.row_align, expert_capacity=w.expert_capacity,
+                                           interleaved=w.interleaved)
+
         def comb():
             if w.combine_input == "identity":
                 ep.ep_combine(s["h"], s["recv"], w.mode, w.H, s["w"], s["out"], interleaved=w.interleaved)
@@ -571,7 +579,7 @@ def main() -> int:
                 ep.ep_combine(s["h"], s["recv"], "none", w.H, s["w"], s["out"])
             else:
                 ep.ep_combine(s["h"], s["y"], "none", w.H, s["w"], s["out"])
-        return [lay, disp, comb]
+        return [lay_disp, comb] if args.fused else [lay, disp, comb]
 
     runners = [phases(s) for s in sets]
     print(f"[bench] {nsets} buffer sets, warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
@@ -582,7 +590,8 @@ def main() -> int:
     R = int(sets[0]["rc"].sum().item())
     # timed region: the throughput pass of timed_steps, on the launch stream;
     # the per-phase times (and combine's launch time) come from its phase pass
-    ms_per_step, (lay_ms, disp_ms, comb_ms), wall_s, dist = timed_steps(runners, args.steps, stream)
+    ms_per_step, ph, wall_s, dist = timed_steps(runners, args.steps, stream)
+    lay_ms, disp_ms, comb_ms = (ph[0], None, ph[1]) if args.fused else ph
     stream_ms = ms_per_step
     if args.graph:
         # the timed steps as one graph replay; the phases stay those of the
@@ -613,12 +622,14 @@ def main() -> int:
                                f"combine_input={w.combine_input}",
                    "T": w.T, "H": w.H, "E": w.E, "k": w.k, "rows": R, "buffer_sets": nsets,
                    "row_align": w.row_align, "expert_capacity": w.expert_capacity, "interleaved": w.interleaved,
-                   "receive_rows": w.max_rows, "launch": "graph" if args.graph else "stream"},
+                   "receive_rows": w.max_rows, "launch": "graph" if args.graph else "stream",
+                   "layout_dispatch": "one call (ep_layout_dispatch)" if args.fused else "two calls"},
         "hbm_gbps": round(gbps, 1), "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "alg_bytes_per_step": b["total"],
-        "phase_ms": {"layout": round(lay_ms, 5), "dispatch": round(disp_ms, 5), "combine": round(comb_ms, 5)},
-        "phase_gbps": {"dispatch": round(b["dispatch"] / (disp_ms * 1e-3) / 1e9, 1),
-                       "combine": round(comb_gbps, 1)},
+        "phase_ms": ({"layout_dispatch": round(lay_ms, 5), "combine": round(comb_ms, 5)} if args.fused else
+                     {"layout": round(lay_ms, 5), "dispatch": round(disp_ms, 5), "combine": round(comb_ms, 5)}),
+        "phase_gbps": ({"combine": round(comb_gbps, 1)} if args.fused else
+                       {"dispatch": round(b["dispatch"] / (disp_ms * 1e-3) / 1e9, 1), "combine": round(comb_gbps, 1)}),
         "wall_s": round(wall_s, 4),
         "step_ms_phase_pass": dist,
         "stream_ms_per_step": round(stream_ms, 5),

@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "dispatch.hpp"
 #include "formats.hpp"
 #include "tuning.hpp"
 
@@ -337,20 +338,192 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Layout fused into dispatch (compact receive rows, few pairs).
+//
+// In the compact arrangement the receive row of pair f with expert e is
+// (pairs with an expert below e) + (earlier pairs with expert e): the
+// exclusive scan of the expert counts plus the stable rank ("Low-Latency Mode
+// API", Return Values recv_count and the receive layout it describes).  Both
+// are counts over the ids, so a dispatch workgroup can find the rows of its
+// token's pairs by itself, with no wait on another workgroup, while its span
+// of the token row is in flight.  Workgroup 0 writes the per-expert outputs
+// (counts, block starts, running statistics, status) and marks the rows past
+// the last routed one free; the first span workgroup of each token writes the
+// token's slots, row_src entries and receive weights.
+struct FusedArgs {
+  const void *idx;     // [n] int32 or int64 ids
+  int idx64, n, E, max_rows;
+  int64_t *recv_count; // [E]
+  int32_t *cum;        // [E] or null
+  int32_t *offsets;    // [E + 1]
+  int32_t *slot;       // [n]
+  int32_t *row_src;    // [max_rows]
+  uint32_t *status;
+};
+
+// Expert of an id, or `none` for -1 and for ids outside [-1, E) (`bad`).
+template <typename IdT>
+__device__ __forceinline__ int expert_or(IdT v, int E, int none, bool &bad) {
+  if (v >= 0 && (int64_t)v < (int64_t)E) return (int)v;
+  bad |= v != -1;
+  return none;
+}
+constexpr int kIdBatch = 8;   // id loads a thread keeps in flight
+
+// Exclusive scan of one int per thread over an NT-thread workgroup; `total`
+// receives the sum.  `wsum` is LDS of NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_sum(int v, int *wsum, int &total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    const int c = wsum[i];
+    all += c;
+    before += i < w ? c : 0;
+  }
+  total = all;
+  return before + x - v;
+}
+
+// Workgroup 0 of the fused launch: expert histogram (LDS atomics), its
+// exclusive scan, the per-expert outputs, the status word and the free rows.
+template <int NT, typename IdT>
+__device__ __forceinline__ void fused_layout_outputs(const FusedArgs &a) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int wsum[NT / kWave];
+  __shared__ uint32_t sbad;
+  const IdT *idx = (const IdT *)a.idx;
+  for (int e = threadIdx.x; e < a.E; e += NT) cnt[e] = 0;
+  if (threadIdx.x == 0) sbad = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int base = threadIdx.x; base < a.n; base += kIdBatch * NT) {
+    IdT v[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) v[u] = idx[min(base + u * NT, a.n - 1)];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      if (base + u * NT >= a.n) break;
+      const int e = expert_or(v[u], a.E, -1, bad);
+      if (e >= 0) atomicAdd(&cnt[e], 1);
+    }
+  }
+  if (bad) atomicOr(&sbad, EP_STATUS_ID_OUT_OF_RANGE);
+  __syncthreads();
+  // thread i owns experts [i * per, (i + 1) * per)
+  const int per = (a.E + NT - 1) / NT;
+  const int e0 = threadIdx.x * per, e1 = min(e0 + per, a.E);
+  int mine = 0;
+  for (int e = e0; e < e1; ++e) mine += cnt[e];
+  int nrows;
+  int run = block_exclusive_sum<NT>(mine, wsum, nrows);
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt[e];
+    a.offsets[e] = run;
+    a.recv_count[e] = c;
+    if (a.cum) a.cum[e] += c;
+    run += c;
+  }
+  if (threadIdx.x == 0) {
+    a.offsets[a.E] = nrows;
+    *a.status = sbad;
+  }
+  for (int r = nrows + threadIdx.x; r < a.max_rows; r += NT) a.row_src[r] = -1;
+}
+
+// Receive rows of the pairs of token t (s[j] = -1 past k and for pairs with
+// no valid expert): every thread counts, over its share of the ids, the ids
+// that order before each pair, two 16-bit counts per word (n < 2^16); the
+// words are then summed over the workgroup.  `red` is LDS of NT / 64 *
+// KMAX / 2 words.
+template <int NT, int KMAX, bool EXACT, typename IdT>
+__device__ __forceinline__ void fused_slots(const FusedArgs &a, int t, int k, int (&s)[KMAX], uint32_t *red) {
+  const IdT *idx = (const IdT *)a.idx;
+  const int f0 = t * k;
+  bool bad = false;   // reported by workgroup 0
+  int ej[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int e = expert_or(idx[f0 + (EXACT ? j : min(j, k - 1))], a.E, -1, bad);
+    ej[j] = j < k ? e : -1;
+  }
+  uint32_t acc[KMAX / 2];
+#pragma unroll
+  for (int i = 0; i < KMAX / 2; ++i) acc[i] = 0;
+  for (int base = threadIdx.x; base < a.n; base += kIdBatch * NT) {
+    IdT v[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) v[u] = idx[min(base + u * NT, a.n - 1)];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int f = base + u * NT;
+      // ids past the end and invalid ones order before no pair
+      const int e = f < a.n ? expert_or(v[u], a.E, INT32_MAX, bad) : INT32_MAX;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const bool before = e < ej[j] || (e == ej[j] && f < f0 + j);
+        acc[j / 2] += (uint32_t)before << (16 * (j & 1));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KMAX / 2; ++i) {
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) acc[i] += (uint32_t)__shfl_xor((int)acc[i], d);
+  }
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+#pragma unroll
+    for (int i = 0; i < KMAX / 2; ++i) red[w * (KMAX / 2) + i] = acc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < KMAX / 2; ++i) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int ww = 0; ww < NT / kWave; ++ww) sum += red[ww * (KMAX / 2) + i];
+    acc[i] = sum;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) s[j] = ej[j] >= 0 ? (int)((acc[j / 2] >> (16 * (j & 1))) & 0xffffu) : -1;
+}
+
 // One workgroup per (token, span of its row).  WEIGHTED = false: dispatch --
 // the token row is quantised once and stored to every routed row (and, if
 // recv_w is given, row slot[t, j] receives w[t, j]).  WEIGHTED = true: the
 // reverse dispatch of combine's gradient -- row slot[t, j] receives the
 // quantised bf16(w[t, j] * x[t]), one quantisation per routed pair.
-template <int Q, int NT, int VPT, int KMAX, bool EXACT, bool PACK, bool WEIGHTED>
+// FUSED: workgroup 0 writes the layout's per-expert outputs and workgroup
+// b > 0 is span workgroup b - 1, which derives its token's slots from the ids
+// (above) instead of reading them.
+template <int Q, int NT, int VPT, int KMAX, bool EXACT, bool PACK, bool WEIGHTED, bool FUSED>
 __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ x, int nvec, int k, int chunks,
                                                       const int *__restrict__ slot,
                                                       const float *__restrict__ w, float *__restrict__ recv_w,
                                                       char *__restrict__ data, char *__restrict__ scales,
-                                                      int64_t dq, int64_t sq) {
-  __shared__ uint32_t red[NT / kWave];
-  const int t = blockIdx.x / chunks;
-  const int c = blockIdx.x - t * chunks;
+                                                      int64_t dq, int64_t sq, FusedArgs fa) {
+  __shared__ uint32_t red[NT / kWave * (FUSED ? KMAX / 2 : 1)];
+  int b = blockIdx.x;
+  if constexpr (FUSED) {
+    if (b == 0) {
+      if (fa.idx64) fused_layout_outputs<NT, int64_t>(fa);
+      else fused_layout_outputs<NT, int32_t>(fa);
+      return;
+    }
+    b -= 1;
+  }
+  const int t = b / chunks;
+  const int c = b - t * chunks;
   const int64_t pair0 = (int64_t)t * k;
 
   // the token's span is loaded first and the routed rows right after, before
@@ -368,11 +541,26 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
   // are in flight together (with k == KMAX they are one wide scalar load)
   int s[KMAX];
   float wj[KMAX];
+  if constexpr (FUSED) {
+    if (fa.idx64) fused_slots<NT, KMAX, EXACT, int64_t>(fa, t, k, s, red);
+    else fused_slots<NT, KMAX, EXACT, int32_t>(fa, t, k, s, red);
+    if (c == 0 && threadIdx.x < k) {
+      int r = -1;
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    const int jj = EXACT ? j : min(j, k - 1);
-    s[j] = slot[pair0 + jj];
-    if constexpr (WEIGHTED) wj[j] = w[pair0 + jj];
+      for (int j = 0; j < KMAX; ++j) r = j == (int)threadIdx.x ? s[j] : r;
+      fa.slot[pair0 + threadIdx.x] = r;
+      if (r >= 0) {
+        fa.row_src[r] = (int)pair0 + threadIdx.x;
+        if (recv_w != nullptr) recv_w[r] = w[pair0 + threadIdx.x];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const int jj = EXACT ? j : min(j, k - 1);
+      s[j] = slot[pair0 + jj];
+      if constexpr (WEIGHTED) wj[j] = w[pair0 + jj];
+    }
   }
   bool any = false;
 #pragma unroll
@@ -381,7 +569,7 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
     any |= s[j] >= 0;
   }
   if (!any) return;   // uniform: the token is routed nowhere
-  if (!WEIGHTED && recv_w != nullptr && c == 0 && threadIdx.x < k) {
+  if (!FUSED && !WEIGHTED && recv_w != nullptr && c == 0 && threadIdx.x < k) {
     const int r = slot[pair0 + threadIdx.x];
     if (r >= 0) recv_w[r] = w[pair0 + threadIdx.x];
   }
@@ -402,20 +590,30 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
   }
 }
 
+// fa != null: the fused launch (layout workgroup first), forward dispatch only.
 template <int Q, int NT, int VPT, bool PACK, bool WEIGHTED>
 hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *w, char *recv, float *recv_w,
-                    int64_t dq, int64_t sq, size_t scale_off, hipStream_t s) {
+                    int64_t dq, int64_t sq, size_t scale_off, const FusedArgs *fa, hipStream_t s) {
   const int chunks = (nvec + NT * VPT - 1) / (NT * VPT);
-  const int64_t blocks = h.num_tokens * chunks;
+  const int64_t blocks = h.num_tokens * chunks + (fa ? 1 : 0);
   if (blocks == 0) return hipSuccess;
-#define EP_LAUNCH_DISPATCH(KMAX, EXACT)                                                                     \
-  hipLaunchKernelGGL((dispatch_kernel<Q, NT, VPT, KMAX, EXACT, PACK, WEIGHTED>), dim3((unsigned)blocks), dim3(NT), \
-                     EP_DISPATCH_LDS_CAP, s, (const u32x4 *)x, nvec, h.num_topk, chunks, h.slot, w, recv_w, recv, \
-                     recv + scale_off, dq, sq)
-  if (h.num_topk == 8) EP_LAUNCH_DISPATCH(8, true);
-  else if (h.num_topk < 8) EP_LAUNCH_DISPATCH(8, false);
-  else if (h.num_topk == kMaxTopk) EP_LAUNCH_DISPATCH(kMaxTopk, true);
-  else EP_LAUNCH_DISPATCH(kMaxTopk, false);
+#define EP_LAUNCH_DISPATCH(KMAX, EXACT, FUSED)                                                                 \
+  hipLaunchKernelGGL((dispatch_kernel<Q, NT, VPT, KMAX, EXACT, PACK, WEIGHTED, FUSED>), dim3((unsigned)blocks), \
+                     dim3(NT), EP_DISPATCH_LDS_CAP, s, (const u32x4 *)x, nvec, h.num_topk, chunks, h.slot, w,    \
+                     recv_w, recv, recv + scale_off, dq, sq, fa ? *fa : FusedArgs{})
+#define EP_LAUNCH_K(FUSED)                                                  \
+  if (h.num_topk == 8) EP_LAUNCH_DISPATCH(8, true, FUSED);                  \
+  else if (h.num_topk < 8) EP_LAUNCH_DISPATCH(8, false, FUSED);             \
+  else if (h.num_topk == kMaxTopk) EP_LAUNCH_DISPATCH(kMaxTopk, true, FUSED); \
+  else EP_LAUNCH_DISPATCH(kMaxTopk, false, FUSED);
+  if constexpr (!WEIGHTED) {
+    if (fa) {
+      EP_LAUNCH_K(true)
+      return hipGetLastError();
+    }
+  }
+  EP_LAUNCH_K(false)
+#undef EP_LAUNCH_K
 #undef EP_LAUNCH_DISPATCH
   return hipGetLastError();
 }
@@ -424,33 +622,33 @@ hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *
 // row strides of data and scales (equal for interleaved rows) and the scale base.
 template <int Q, bool WEIGHTED>
 hipError_t launch_mode(const ep_handle_t &h, const void *x, int hidden, const float *w, char *recv,
-                       float *recv_w, int quant, hipStream_t s) {
+                       float *recv_w, int quant, const FusedArgs *fa, hipStream_t s) {
   const RecvGeom g = recv_geom(h.max_rows, hidden, quant);
   const int64_t dq = g.data_stride, sq = g.scale_stride;
   const size_t scale_off = g.scale_off;
   const int nvec = hidden / 8;
   if constexpr (Q == EP_QUANT_INT8_TOKEN) {
     // the whole row must sit in one workgroup (its amax is a row reduction)
-    if (nvec <= 256) return launch_q<Q, 256, 1, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    if (nvec <= 512) return launch_q<Q, 256, 2, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    if (nvec <= 1024) return launch_q<Q, 256, 4, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    if (nvec <= 2048) return launch_q<Q, 256, 8, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    return launch_q<Q, 1024, 8, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+    if (nvec <= 256) return launch_q<Q, 256, 1, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, fa, s);
+    if (nvec <= 512) return launch_q<Q, 256, 2, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, fa, s);
+    if (nvec <= 1024) return launch_q<Q, 256, 4, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, fa, s);
+    if (nvec <= 2048) return launch_q<Q, 256, 8, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, fa, s);
+    return launch_q<Q, 1024, 8, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, fa, s);
   } else if constexpr (Q == EP_QUANT_MXFP8 || Q == EP_QUANT_MXFP4) {
     constexpr int NT = EP_DISPATCH_THREADS, VPT = EP_DISPATCH_VPT;
     if (hidden % 128 == 0)
-      return launch_q<Q, NT, VPT, true, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
-    return launch_q<Q, NT, VPT, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, s);
+      return launch_q<Q, NT, VPT, true, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, fa, s);
+    return launch_q<Q, NT, VPT, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq, scale_off, fa, s);
   } else {
     return launch_q<Q, EP_DISPATCH_THREADS, EP_DISPATCH_VPT, false, WEIGHTED>(h, x, nvec, w, recv, recv_w, dq, sq,
-                                                                          scale_off, s);
+                                                                          scale_off, fa, s);
   }
 }
 
 template <bool WEIGHTED>
 hipError_t launch_any(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant, char *recv,
-                      float *recv_w, hipStream_t s) {
-#define EP_MODE(QQ) launch_mode<QQ, WEIGHTED>(h, x, hidden, w, recv, recv_w, quant, s)
+                      float *recv_w, const FusedArgs *fa, hipStream_t s) {
+#define EP_MODE(QQ) launch_mode<QQ, WEIGHTED>(h, x, hidden, w, recv, recv_w, quant, fa, s)
   switch (quant & kQuantMask) {
     case EP_QUANT_NONE: return EP_MODE(EP_QUANT_NONE);
     case EP_QUANT_INT8_TOKEN: return EP_MODE(EP_QUANT_INT8_TOKEN);
@@ -467,13 +665,31 @@ hipError_t launch_any(const ep_handle_t &h, const void *x, int hidden, const flo
 
 hipError_t launch_dispatch(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant,
                            char *recv, float *recv_w, hipStream_t s) {
-  return launch_any<false>(h, x, hidden, w, quant, recv, recv_w, s);
+  return launch_any<false>(h, x, hidden, w, quant, recv, recv_w, nullptr, s);
+}
+
+hipError_t launch_layout_dispatch(const ep_handle_t &h, const void *idx, int idx64, int64_t *recv_count,
+                                  int32_t *cum, const void *x, int hidden, const float *w, int quant, char *recv,
+                                  float *recv_w, hipStream_t s) {
+  FusedArgs fa;
+  fa.idx = idx;
+  fa.idx64 = idx64;
+  fa.n = (int)(h.num_tokens * h.num_topk);
+  fa.E = h.num_experts;
+  fa.max_rows = (int)h.max_rows;
+  fa.recv_count = recv_count;
+  fa.cum = cum;
+  fa.offsets = h.offsets;
+  fa.slot = h.slot;
+  fa.row_src = h.row_src;
+  fa.status = h.status;
+  return launch_any<false>(h, x, hidden, w, quant, recv, recv_w, &fa, s);
 }
 
 hipError_t launch_combine_backward(const ep_handle_t &h, const void *grad, int hidden, const float *w, int quant,
                                    char *buf, hipStream_t s) {
-  if (w == nullptr) return launch_any<false>(h, grad, hidden, nullptr, quant, buf, nullptr, s);
-  return launch_any<true>(h, grad, hidden, w, quant, buf, nullptr, s);
+  if (w == nullptr) return launch_any<false>(h, grad, hidden, nullptr, quant, buf, nullptr, nullptr, s);
+  return launch_any<true>(h, grad, hidden, w, quant, buf, nullptr, nullptr, s);
 }
 
 }  // namespace ep

@@ -13,6 +13,7 @@
 #include <cstring>
 
 #include "common.hpp"
+#include "dispatch.hpp"
 #include "moe.hpp"
 
 namespace {
@@ -115,10 +116,13 @@ ep_status_t ep_buffer_bytes(int64_t rows, int32_t hidden, ep_quant_t quant, size
 
 namespace {
 
-ep_status_t layout_impl(const char *fn, const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
-                        int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts, int32_t row_align,
-                        int32_t expert_capacity, int64_t *recv_count, int32_t *cumulative_recv_stats,
-                        void *workspace, size_t workspace_bytes, ep_handle_t *handle, void *stream) {
+// Checks the layout arguments and fills `h` (the handle the layout will
+// produce) and `wl`; launches nothing.
+ep_status_t layout_prepare(const char *fn, const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                           int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts, int32_t row_align,
+                           int32_t expert_capacity, int64_t *recv_count, int32_t *cumulative_recv_stats,
+                           void *workspace, size_t workspace_bytes, ep_handle_t *handle, ep_handle_t &h,
+                           ep::WsLayout &wl) {
   if (idx_dtype != EP_IDX_INT32 && idx_dtype != EP_IDX_INT64)
     return fail(EP_ERR_INVALID_ARG, "%s: topk_idx dtype must be int32 or int64", fn);
   if (num_topk <= 0 || num_topk > ep::kMaxTopk)
@@ -150,12 +154,11 @@ ep_status_t layout_impl(const char *fn, const void *topk_idx, ep_idx_dtype_t idx
   if (!workspace || !aligned(workspace, ep::kWsAlign))
     return fail(EP_ERR_INVALID_ARG, "%s: workspace is NULL or not 256-byte aligned", fn);
   if (!handle) return fail(EP_ERR_INVALID_ARG, "%s: handle is NULL", fn);
-  const ep::WsLayout wl = ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts, max_rows);
+  wl = ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts, max_rows);
   if (workspace_bytes < wl.total)
     return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, wl.total);
 
   char *ws = (char *)workspace;
-  ep_handle_t h;
   h.num_tokens = num_tokens;
   h.num_max_tokens = num_max_dispatch_tokens;
   h.max_rows = max_rows;
@@ -167,11 +170,46 @@ ep_status_t layout_impl(const char *fn, const void *topk_idx, ep_idx_dtype_t idx
   h.slot = (int32_t *)(ws + wl.slot);
   h.row_src = (int32_t *)(ws + wl.row_src);
   h.status = (uint32_t *)(ws + wl.status);
+  return EP_OK;
+}
+
+ep_status_t layout_impl(const char *fn, const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                        int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts, int32_t row_align,
+                        int32_t expert_capacity, int64_t *recv_count, int32_t *cumulative_recv_stats,
+                        void *workspace, size_t workspace_bytes, ep_handle_t *handle, void *stream) {
+  ep_handle_t h;
+  ep::WsLayout wl;
+  const ep_status_t st = layout_prepare(fn, topk_idx, idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
+                                        num_experts, row_align, expert_capacity, recv_count, cumulative_recv_stats,
+                                        workspace, workspace_bytes, handle, h, wl);
+  if (st != EP_OK) return st;
   const hipError_t e = ep::launch_layout(topk_idx, idx_dtype == EP_IDX_INT64, num_tokens, num_topk, num_experts,
                                          h.max_rows, row_align, expert_capacity, recv_count, cumulative_recv_stats,
-                                         ws, wl, (hipStream_t)stream);
+                                         (char *)workspace, wl, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   *handle = h;
+  return EP_OK;
+}
+
+// The dispatch arguments against a handle; launches nothing.
+ep_status_t check_dispatch(const char *fn, const ep_handle_t *handle, const void *x, int32_t hidden,
+                           const float *topk_weights, int quant, const void *recv_buf, size_t recv_buf_bytes,
+                           const float *recv_weights) {
+  ep_status_t st = check_handle(handle, fn);
+  if (st != EP_OK) return st;
+  st = check_hidden(hidden, quant, fn);
+  if (st != EP_OK) return st;
+  if (handle->num_tokens > 0 && !x) return fail(EP_ERR_INVALID_ARG, "%s: x is NULL", fn);
+  if (x && !aligned(x, 16)) return fail(EP_ERR_INVALID_ARG, "%s: x is not 16-byte aligned", fn);
+  if (!recv_buf || !aligned(recv_buf, 16))
+    return fail(EP_ERR_INVALID_ARG, "%s: recv_buf is NULL or not 16-byte aligned", fn);
+  const size_t need = buffer_bytes(handle->max_rows, hidden, quant, nullptr);
+  if (recv_buf_bytes < need)
+    return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: recv_buf has %zu bytes, needs %zu", fn, recv_buf_bytes, need);
+  if (recv_weights && !topk_weights && handle->num_tokens > 0)
+    return fail(EP_ERR_INVALID_ARG, "%s: recv_weights given without topk_weights", fn);
+  if ((topk_weights && !aligned(topk_weights, 4)) || (recv_weights && !aligned(recv_weights, 4)))
+    return fail(EP_ERR_INVALID_ARG, "%s: weights are misaligned", fn);
   return EP_OK;
 }
 
@@ -200,24 +238,43 @@ ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden
                         ep_quant_t quant, void *recv_buf, size_t recv_buf_bytes, float *recv_weights,
                         void *stream) {
   const char *fn = "ep_dispatch";
-  ep_status_t st = check_handle(handle, fn);
+  const ep_status_t st = check_dispatch(fn, handle, x, hidden, topk_weights, quant, recv_buf, recv_buf_bytes,
+                                        recv_weights);
   if (st != EP_OK) return st;
-  st = check_hidden(hidden, quant, fn);
-  if (st != EP_OK) return st;
-  if (handle->num_tokens > 0 && !x) return fail(EP_ERR_INVALID_ARG, "%s: x is NULL", fn);
-  if (x && !aligned(x, 16)) return fail(EP_ERR_INVALID_ARG, "%s: x is not 16-byte aligned", fn);
-  if (!recv_buf || !aligned(recv_buf, 16))
-    return fail(EP_ERR_INVALID_ARG, "%s: recv_buf is NULL or not 16-byte aligned", fn);
-  const size_t need = buffer_bytes(handle->max_rows, hidden, quant, nullptr);
-  if (recv_buf_bytes < need)
-    return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: recv_buf has %zu bytes, needs %zu", fn, recv_buf_bytes, need);
-  if (recv_weights && !topk_weights && handle->num_tokens > 0)
-    return fail(EP_ERR_INVALID_ARG, "%s: recv_weights given without topk_weights", fn);
-  if ((topk_weights && !aligned(topk_weights, 4)) || (recv_weights && !aligned(recv_weights, 4)))
-    return fail(EP_ERR_INVALID_ARG, "%s: weights are misaligned", fn);
   const hipError_t e = ep::launch_dispatch(*handle, x, hidden, topk_weights, quant, (char *)recv_buf,
                                            recv_weights, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);
+  return EP_OK;
+}
+
+ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens, int32_t num_topk,
+                               int64_t num_max_dispatch_tokens, int32_t num_experts, int32_t row_align,
+                               int32_t expert_capacity, int64_t *recv_count, int32_t *cumulative_recv_stats,
+                               void *workspace, size_t workspace_bytes, const void *x, int32_t hidden,
+                               const float *topk_weights, ep_quant_t quant, void *recv_buf, size_t recv_buf_bytes,
+                               float *recv_weights, ep_handle_t *handle, void *stream) {
+  const char *fn = "ep_layout_dispatch";
+  ep_handle_t h;
+  ep::WsLayout wl;
+  ep_status_t st = layout_prepare(fn, topk_idx, idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
+                                  num_experts, row_align, expert_capacity, recv_count, cumulative_recv_stats,
+                                  workspace, workspace_bytes, handle, h, wl);
+  if (st != EP_OK) return st;
+  st = check_dispatch(fn, &h, x, hidden, topk_weights, quant, recv_buf, recv_buf_bytes, recv_weights);
+  if (st != EP_OK) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (row_align == 1 && expert_capacity == 0 && num_tokens * num_topk <= ep::kFusedMaxPairs) {
+    e = ep::launch_layout_dispatch(h, topk_idx, idx_dtype == EP_IDX_INT64, recv_count, cumulative_recv_stats, x,
+                                   hidden, topk_weights, quant, (char *)recv_buf, recv_weights, s);
+  } else {
+    e = ep::launch_layout(topk_idx, idx_dtype == EP_IDX_INT64, num_tokens, num_topk, num_experts, h.max_rows,
+                          row_align, expert_capacity, recv_count, cumulative_recv_stats, (char *)workspace, wl, s);
+    if (e == hipSuccess)
+      e = ep::launch_dispatch(h, x, hidden, topk_weights, quant, (char *)recv_buf, recv_weights, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, fn);
+  *handle = h;
   return EP_OK;
 }
 

@@ -41,7 +41,7 @@ EP_STATUS_ID_OUT_OF_RANGE = 1
 EP_STATUS_CAPACITY_OVERFLOW = 2
 
 SYMBOLS = ("ep_workspace_bytes", "ep_workspace_bytes_ex", "ep_layout_rows", "ep_buffer_bytes", "ep_layout",
-           "ep_layout_ex", "ep_dispatch", "ep_combine", "ep_combine_backward", "ep_moe_packed_bytes", "ep_moe_pack_weights", "ep_moe_gmm1", "ep_moe_gmm2",
+           "ep_layout_ex", "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_combine_backward", "ep_moe_packed_bytes", "ep_moe_pack_weights", "ep_moe_gmm1", "ep_moe_gmm2",
            "ep_read_status", "ep_last_error", "ep_abi_version")
 
 
@@ -78,6 +78,9 @@ _lib.ep_layout_ex.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i64, _i32, _i32, _
 _lib.ep_layout_ex.restype = ctypes.c_int
 _lib.ep_dispatch.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp, _vp]
 _lib.ep_dispatch.restype = ctypes.c_int
+_lib.ep_layout_dispatch.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
+                                    _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp, ctypes.POINTER(ep_handle_t), _vp]
+_lib.ep_layout_dispatch.restype = ctypes.c_int
 _lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int, _i32, _vp, _vp, _vp]
 _lib.ep_combine.restype = ctypes.c_int
 _lib.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp]
@@ -225,6 +228,25 @@ def ep_dispatch(handle: ep_handle_t, x, hidden: int, quant, recv_buf, topk_weigh
                             _ptr(recv_buf), nbytes, _ptr(recv_weights), _stream(stream)))
 
 
+def ep_layout_dispatch(topk_idx, num_experts: int, num_max_dispatch_tokens: int, recv_count, workspace,
+                       x, hidden: int, quant, recv_buf, topk_weights=None, recv_weights=None,
+                       cumulative_recv_stats=None, *, row_align: int = 1, expert_capacity: int = 0,
+                       num_tokens=None, num_topk=None, idx_dtype=None, recv_buf_bytes=None, interleaved=False,
+                       stream=None) -> ep_handle_t:
+    """ep_layout_ex and ep_dispatch in one call (one launch for compact
+    layouts of at most 2048 pairs).  Returns the handle."""
+    num_tokens, num_topk, idx_dtype = _idx_args(topk_idx, num_tokens, num_topk, idx_dtype)
+    nbytes = _nbytes(recv_buf) if recv_buf_bytes is None else recv_buf_bytes
+    h = ep_handle_t()
+    _check(_lib.ep_layout_dispatch(_ptr(topk_idx), idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
+                                   num_experts, row_align, expert_capacity, _ptr(recv_count),
+                                   _ptr(cumulative_recv_stats), _ptr(workspace),
+                                   _nbytes(workspace) if isinstance(workspace, torch.Tensor) else 0,
+                                   _ptr(x), hidden, _ptr(topk_weights), _quant(quant, interleaved), _ptr(recv_buf),
+                                   nbytes, _ptr(recv_weights), ctypes.byref(h), _stream(stream)))
+    return h
+
+
 def ep_combine(handle: ep_handle_t, expert_out, in_quant, hidden: int, topk_weights, out, *,
                expert_out_bytes=None, interleaved=False, stream=None) -> None:
     nbytes = _nbytes(expert_out) if expert_out_bytes is None else expert_out_bytes
@@ -367,15 +389,17 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispat
     ws = torch.empty(max(ep_workspace_bytes_ex(num_max_dispatch_tokens_per_rank, k, num_experts, row_align,
                                                expert_capacity), 1), dtype=torch.uint8, device=dev)
     recv_count = torch.empty(num_experts, dtype=torch.int64, device=dev)
-    h = ep_layout_ex(topk_idx, num_experts, num_max_dispatch_tokens_per_rank, row_align, expert_capacity,
-                     recv_count, ws, cumulative_local_expert_recv_stats)
-    rows = h.max_rows
+    rows = ep_layout_rows(num_max_dispatch_tokens_per_rank, k, num_experts, row_align, expert_capacity)
+    if rows < 0:
+        raise EpError(EP_ERR_INVALID_ARG, "receive rows out of range")
     total, _ = ep_buffer_bytes(rows, H, q)
     buf = torch.empty(max(total, 16), dtype=torch.uint8, device=dev)
     recv_w = None
     if topk_weights is not None:
         recv_w = torch.empty(max(rows, 1), dtype=torch.float32, device=dev)
-    ep_dispatch(h, x, H, q, buf, topk_weights, recv_w)
+    h = ep_layout_dispatch(topk_idx, num_experts, num_max_dispatch_tokens_per_rank, recv_count, ws, x, H, q, buf,
+                           topk_weights, recv_w, cumulative_local_expert_recv_stats, row_align=row_align,
+                           expert_capacity=expert_capacity)
     handle = Handle(h, ws, H, q, tuple(topk_idx.shape), topk_idx.dtype)
     recv_x = split_recv(buf, rows, H, q)
     if expert_capacity > 0:

@@ -211,6 +211,25 @@ ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden
                         const float *topk_weights, ep_quant_t quant, void *recv_buf,
                         size_t recv_buf_bytes, float *recv_weights, void *stream);
 
+/* Layout and dispatch in one call ("Low-Latency Mode API",
+ * low_latency_dispatch, which takes the token rows and topk_idx together).
+ * Arguments as ep_layout_ex followed by ep_dispatch; the results (handle,
+ * recv_count, cumulative_recv_stats, status, receive buffer, receive
+ * weights) are identical to that pair of calls, and every argument of both
+ * is checked before anything is launched.  Compact layouts (row_align 1, no
+ * capacity) of at most 2048 (token, j) pairs run as a single launch, in
+ * which each dispatch workgroup derives its own receive rows from topk_idx
+ * (a decode-sized step saves one launch); the others run the two launches of
+ * the separate calls.  The workspace must outlive every call that uses the
+ * returned handle, as for ep_layout. */
+ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                               int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts,
+                               int32_t row_align, int32_t expert_capacity, int64_t *recv_count,
+                               int32_t *cumulative_recv_stats, void *workspace, size_t workspace_bytes,
+                               const void *x, int32_t hidden, const float *topk_weights, ep_quant_t quant,
+                               void *recv_buf, size_t recv_buf_bytes, float *recv_weights,
+                               ep_handle_t *handle, void *stream);
+
 /* Combine ("Low-Latency Mode API", low_latency_combine; "DeepEP FP8 Dispatch
  * and Combine Operations", The FP8 Combine Operation).
  *   handle          host, from the ep_layout of the matching dispatch

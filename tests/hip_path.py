@@ -85,16 +85,35 @@ def read_layout(ep, h, ws, recv_count, w):
     )
 
 
+def run_layout_dispatch(ep, w: W.Workload, idx: np.ndarray, x, wts, recv, recv_w, cum=None):
+    """ep_layout_dispatch (layout and dispatch in one call) on fresh,
+    garbage-filled workspace and counts."""
+    nbytes = ep.ep_workspace_bytes_ex(w.t_max, w.k, w.E, w.row_align, w.expert_capacity)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)
+    recv_count = torch.full((w.E,), -7, dtype=torch.int64, device=DEV)
+    h = ep.ep_layout_dispatch(to_dev(idx), w.E, w.t_max, recv_count, ws, x, w.H, w.mode, recv, wts, recv_w, cum,
+                              row_align=w.row_align, expert_capacity=w.expert_capacity, interleaved=w.interleaved)
+    assert h.max_rows == w.max_rows
+    return h, ws, recv_count
+
+
 def run_path(ep, w: W.Workload, inp: dict, *, expert_out: np.ndarray | None = None,
-             with_recv_weights=True, do_combine=True) -> HipRun:
-    """layout -> dispatch -> (expert step) -> combine on the GPU."""
-    h, ws, recv_count = run_layout(ep, w, inp["topk_idx"])
+             with_recv_weights=True, do_combine=True, fused=False) -> HipRun:
+    """layout -> dispatch -> (expert step) -> combine on the GPU (fused: the
+    first two through ep_layout_dispatch)."""
     x = to_dev(inp["x"])
     wts = to_dev(inp["topk_weights"])
     total, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode, w.interleaved)
     recv = canary_buffer(total)
     recv_w = torch.full((max(w.max_rows, 1),), float("nan"), device=DEV) if with_recv_weights else None
-    ep.ep_dispatch(h, x, w.H, w.mode, recv, wts if with_recv_weights else None, recv_w, interleaved=w.interleaved)
+    if fused:
+        h, ws, recv_count = run_layout_dispatch(ep, w, inp["topk_idx"], x, wts if with_recv_weights else None,
+                                                recv, recv_w)
+    else:
+        h, ws, recv_count = run_layout(ep, w, inp["topk_idx"])
+        ep.ep_dispatch(h, x, w.H, w.mode, recv, wts if with_recv_weights else None, recv_w,
+                       interleaved=w.interleaved)
     lay = read_layout(ep, h, ws, recv_count, w)
     out = None
     if do_combine:
