@@ -442,42 +442,53 @@ __device__ __forceinline__ void fused_layout_outputs(const FusedArgs &a) {
 }
 
 // Receive rows of the pairs of token t (s[j] = -1 past k and for pairs with
-// no valid expert): every thread counts, over its share of the ids, the ids
-// that order before each pair, two 16-bit counts per word (n < 2^16); the
-// words are then summed over the workgroup.  `red` is LDS of NT / 64 *
-// KMAX / 2 words.
+// no valid expert).  With n < 4096, pair f with expert e has the order key
+// e * 4096 + f, and the ids that order before pair j are those with a smaller
+// key (ids with no valid expert get a key above all others).  Every thread counts,
+// over its share of the ids, the keys below each pair's key (one compare and
+// one add per id and pair); the counts are packed two per word (16 bits
+// each) and summed over the wave and then, through `red` (LDS of NT / 64 *
+// KMAX / 2 words), over the workgroup.
 template <int NT, int KMAX, bool EXACT, typename IdT>
 __device__ __forceinline__ void fused_slots(const FusedArgs &a, int t, int k, int (&s)[KMAX], uint32_t *red) {
+  static_assert(kFusedMaxPairs < 4096, "order keys hold the pair index in 12 bits; counts fit 16 bits");
   const IdT *idx = (const IdT *)a.idx;
   const int f0 = t * k;
-  bool bad = false;   // reported by workgroup 0
-  int ej[KMAX];
+  // the first batch of ids is loaded before the token's own ids, so that the
+  // two loads are in flight together (this workgroup is called with n >= 1)
+  IdT v[kIdBatch];
+#pragma unroll
+  for (int u = 0; u < kIdBatch; ++u) v[u] = idx[min(u * NT + (int)threadIdx.x, a.n - 1)];
+  int key[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    const int e = expert_or(idx[f0 + (EXACT ? j : min(j, k - 1))], a.E, -1, bad);
-    ej[j] = j < k ? e : -1;
+    const IdT e = idx[f0 + (EXACT ? j : min(j, k - 1))];
+    const bool ok = j < k && e >= 0 && (int64_t)e < (int64_t)a.E;
+    key[j] = ok ? (int)e * 4096 + f0 + j : -1;   // -1: nothing orders before it
+  }
+  int cnt[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) cnt[j] = 0;
+  for (int b0 = 0;;) {
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int f = b0 + u * NT + threadIdx.x;
+      const bool ok = f < a.n && v[u] >= 0 && (int64_t)v[u] < (int64_t)a.E;
+      const int kf = ok ? (int)v[u] * 4096 + f : 1 << 30;   // above every valid key
+      // kf < key[j] as the sign of a difference that cannot overflow (keys
+      // lie in [-1, 2^21)): plain vector arithmetic, no lane masks
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) cnt[j] += (int)(((uint32_t)kf - (uint32_t)key[j]) >> 31);
+    }
+    b0 += kIdBatch * NT;
+    if (b0 >= a.n) break;
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) v[u] = idx[min(b0 + u * NT + (int)threadIdx.x, a.n - 1)];
   }
   uint32_t acc[KMAX / 2];
 #pragma unroll
-  for (int i = 0; i < KMAX / 2; ++i) acc[i] = 0;
-  for (int base = threadIdx.x; base < a.n; base += kIdBatch * NT) {
-    IdT v[kIdBatch];
-#pragma unroll
-    for (int u = 0; u < kIdBatch; ++u) v[u] = idx[min(base + u * NT, a.n - 1)];
-#pragma unroll
-    for (int u = 0; u < kIdBatch; ++u) {
-      const int f = base + u * NT;
-      // ids past the end and invalid ones order before no pair
-      const int e = f < a.n ? expert_or(v[u], a.E, INT32_MAX, bad) : INT32_MAX;
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        const bool before = e < ej[j] || (e == ej[j] && f < f0 + j);
-        acc[j / 2] += (uint32_t)before << (16 * (j & 1));
-      }
-    }
-  }
-#pragma unroll
   for (int i = 0; i < KMAX / 2; ++i) {
+    acc[i] = (uint32_t)cnt[2 * i] | ((uint32_t)cnt[2 * i + 1] << 16);
 #pragma unroll
     for (int d = kWave / 2; d >= 1; d >>= 1) acc[i] += (uint32_t)__shfl_xor((int)acc[i], d);
   }
@@ -495,14 +506,9 @@ __device__ __forceinline__ void fused_slots(const FusedArgs &a, int t, int k, in
     acc[i] = sum;
   }
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) s[j] = ej[j] >= 0 ? (int)((acc[j / 2] >> (16 * (j & 1))) & 0xffffu) : -1;
+  for (int j = 0; j < KMAX; ++j) s[j] = key[j] >= 0 ? (int)((acc[j / 2] >> (16 * (j & 1))) & 0xffffu) : -1;
 }
 
-// One workgroup per (token, span of its row).  WEIGHTED = false: dispatch --
-// the token row is quantised once and stored to every routed row (and, if
-// recv_w is given, row slot[t, j] receives w[t, j]).  WEIGHTED = true: the
-// reverse dispatch of combine's gradient -- row slot[t, j] receives the
-// quantised bf16(w[t, j] * x[t]), one quantisation per routed pair.
 // FUSED: workgroup 0 writes the layout's per-expert outputs and workgroup
 // b > 0 is span workgroup b - 1, which derives its token's slots from the ids
 // (above) instead of reading them.
