@@ -308,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
 // offsets, statistics and status; all of them clear row_src past R.  `tile`
 // is LDS of kTileInts ints, `base` of E ints.
 constexpr int kTileInts = 8192;
+static_assert(kTileInts % kThreads == 0, "a tile is whole loads per thread");
 
 __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int align, int cap, int nblocks, int b,
                                                const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
@@ -336,7 +337,16 @@ __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int a
   int tot = 0, pre = 0;
   for (int b0 = 0; b0 < nblocks; b0 += tile_rows) {
     const int rows = min(tile_rows, nblocks - b0);
-    for (int i = threadIdx.x; i < rows * E; i += kThreads) tile[i] = hist[(int64_t)b0 * E + i];
+    // all of this thread's share of the tile is loaded before any of it is
+    // stored, so the loads are in flight together (rows * E <= kTileInts)
+    const int m = rows * E;
+    int part[kTileInts / kThreads];
+#pragma unroll
+    for (int u = 0; u < kTileInts / kThreads; ++u)
+      part[u] = hist[(int64_t)b0 * E + min(u * kThreads + (int)threadIdx.x, m - 1)];
+#pragma unroll
+    for (int u = 0; u < kTileInts / kThreads; ++u)
+      if (u * kThreads + (int)threadIdx.x < m) tile[u * kThreads + threadIdx.x] = part[u];
     __syncthreads();
     if (e < E) {
       const int mine = min(max(b - b0, 0), rows);   // rows of this tile before chunk b
