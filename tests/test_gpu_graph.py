@@ -1,8 +1,10 @@
 """HIP-graph capture of the whole path.
 
-layout -> dispatch -> combine is captured once into a graph and replayed
+layout -> dispatch -> combine (layout and dispatch as two calls, or as the
+one call ep_layout_dispatch) is captured once into a graph and replayed
 several times; between replays the test does its own eager work (another
-layout on other inputs, fills of the output buffers) and synchronises, and it
+layout on other inputs, fills of the output buffers and of the workspace)
+and synchronises, and it
 checks every replay against the eager run of the same inputs.  The path
 records no memset nodes (its kernels write every output they own).
 """
@@ -25,9 +27,10 @@ def ep():
     return _ep
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "layout_dispatch"])
 @pytest.mark.parametrize("name", ["decode", "decode8", "small"])
-def test_graph_replays_match_eager(ep, name):
-    print(f"\n[case] graph replay {name}", flush=True)
+def test_graph_replays_match_eager(ep, name, fused):
+    print(f"\n[case] graph replay {name} fused={fused}", flush=True)
     sys.stdout.flush()
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w)
@@ -40,8 +43,11 @@ def test_graph_replays_match_eager(ep, name):
     out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
 
     def path():
-        h = ep.ep_layout(idx, w.E, w.t_max, rc, ws)
-        ep.ep_dispatch(h, x, w.H, w.mode, recv)
+        if fused:
+            h = ep.ep_layout_dispatch(idx, w.E, w.t_max, rc, ws, x, w.H, w.mode, recv)
+        else:
+            h = ep.ep_layout(idx, w.E, w.t_max, rc, ws)
+            ep.ep_dispatch(h, x, w.H, w.mode, recv)
         if y is None:
             ep.ep_combine(h, recv, w.mode if w.combine_input == "identity" else "none", w.H, wts, out)
         else:
@@ -71,6 +77,7 @@ def test_graph_replays_match_eager(ep, name):
         out.fill_(float("nan"))
         rc.fill_(-1)
         recv.fill_(0xAB)
+        ws.fill_(0xA5)                                 # every replay must write the layout again
         ep.ep_layout(idx2, w.E, 64, rc2, ws2)          # unrelated eager work in between
         torch.cuda.synchronize()
         g.replay()
