@@ -371,6 +371,21 @@ __device__ __forceinline__ int expert_or(IdT v, int E, int none, bool &bad) {
 }
 constexpr int kIdBatch = 8;   // id loads a thread keeps in flight
 
+// Sum of v over the 64 lanes of the wave (every lane gets it), by DPP steps:
+// row_shr 1, 2, 4, 8 leave in lane 15 of each 16-lane row the row's sum
+// (with zero for sources past the row start), row_bcast 15 adds row r's last
+// lane into row r + 1 and row_bcast 31 adds lane 31 into rows 2 and 3, so
+// lane 63 ends with the total.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Exclusive scan of one int per thread over an NT-thread workgroup; `total`
 // receives the sum.  `wsum` is LDS of NT / 64 ints.
 template <int NT>
@@ -447,7 +462,7 @@ __device__ __forceinline__ void fused_layout_outputs(const FusedArgs &a) {
 // key (ids with no valid expert get a key above all others).  Every thread counts,
 // over its share of the ids, the keys below each pair's key (one compare and
 // one add per id and pair); the counts are packed two per word (16 bits
-// each) and summed over the wave and then, through `red` (LDS of NT / 64 *
+// each) and summed over the wave (DPP) and then, through `red` (LDS of NT / 64 *
 // KMAX / 2 words), over the workgroup.
 template <int NT, int KMAX, bool EXACT, typename IdT>
 __device__ __forceinline__ void fused_slots(const FusedArgs &a, int t, int k, int (&s)[KMAX], uint32_t *red) {
@@ -488,9 +503,7 @@ __device__ __forceinline__ void fused_slots(const FusedArgs &a, int t, int k, in
   uint32_t acc[KMAX / 2];
 #pragma unroll
   for (int i = 0; i < KMAX / 2; ++i) {
-    acc[i] = (uint32_t)cnt[2 * i] | ((uint32_t)cnt[2 * i + 1] << 16);
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) acc[i] += (uint32_t)__shfl_xor((int)acc[i], d);
+    acc[i] = wave_sum((uint32_t)cnt[2 * i] | ((uint32_t)cnt[2 * i + 1] << 16));
   }
   const int w = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) {
