@@ -335,19 +335,25 @@ __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int a
 
   const int tile_rows = kTileInts / E;
   int tot = 0, pre = 0;
+  // this thread's share of a tile (rows * E <= kTileInts ints) is loaded
+  // whole before any of it is stored, so the loads are in flight together;
+  // the next tile's share is loaded before the current tile is summed
+  constexpr int kPart = kTileInts / kThreads;
+  int part[kPart];
+  auto load_part = [&](int b0) {
+    const int m = min(tile_rows, nblocks - b0) * E;
+#pragma unroll
+    for (int u = 0; u < kPart; ++u) part[u] = hist[(int64_t)b0 * E + min(u * kThreads + (int)threadIdx.x, m - 1)];
+  };
+  if (nblocks > 0) load_part(0);
   for (int b0 = 0; b0 < nblocks; b0 += tile_rows) {
     const int rows = min(tile_rows, nblocks - b0);
-    // all of this thread's share of the tile is loaded before any of it is
-    // stored, so the loads are in flight together (rows * E <= kTileInts)
     const int m = rows * E;
-    int part[kTileInts / kThreads];
 #pragma unroll
-    for (int u = 0; u < kTileInts / kThreads; ++u)
-      part[u] = hist[(int64_t)b0 * E + min(u * kThreads + (int)threadIdx.x, m - 1)];
-#pragma unroll
-    for (int u = 0; u < kTileInts / kThreads; ++u)
+    for (int u = 0; u < kPart; ++u)
       if (u * kThreads + (int)threadIdx.x < m) tile[u * kThreads + threadIdx.x] = part[u];
     __syncthreads();
+    if (b0 + tile_rows < nblocks) load_part(b0 + tile_rows);
     if (e < E) {
       const int mine = min(max(b - b0, 0), rows);   // rows of this tile before chunk b
       int r = 0;
