@@ -176,6 +176,30 @@ def test_dispatch_rejects(ep, kw, code):
     assert ep.ep_last_error().startswith("ep_dispatch")
 
 
+# ep_layout_dispatch checks the layout arguments and then the dispatch ones;
+# either kind of failure launches nothing and names the call
+LAYOUT_DISPATCH_BAD = [
+    (dict(dtype=2), 1), (dict(k=17), 1), (dict(E=513), 1), (dict(T=9), 1), (dict(idx=None), 1),
+    (dict(rc=None), 1), (dict(ws=FAKE + 16), 1), (dict(wsb=100), 3), (dict(align=2, cap=4), 1),
+    (dict(handle=False), 1), (dict(hidden=48), 1), (dict(quant=7), 1), (dict(x=None), 1),
+    (dict(x=FAKE + 8), 1), (dict(recv=None), 1), (dict(recv_bytes=10), 3), (dict(rw=FAKE, w=None), 1),
+    (dict(w=FAKE + 2), 1),
+]
+
+
+@pytest.mark.parametrize("kw,code", LAYOUT_DISPATCH_BAD)
+def test_layout_dispatch_rejects(ep, kw, code):
+    h = ep.ep_handle_t()
+    rc = ep._lib.ep_layout_dispatch(kw.get("idx", FAKE), kw.get("dtype", 1), kw.get("T", 4), kw.get("k", 2), 8,
+                                    kw.get("E", 8), kw.get("align", 1), kw.get("cap", 0), kw.get("rc", FAKE), None,
+                                    kw.get("ws", FAKE), kw.get("wsb", 1 << 30), kw.get("x", FAKE),
+                                    kw.get("hidden", 256), kw.get("w", None), kw.get("quant", 3),
+                                    kw.get("recv", FAKE), kw.get("recv_bytes", 1 << 30), kw.get("rw", None),
+                                    None if kw.get("handle") is False else ctypes.byref(h), None)
+    assert rc == code, ep.ep_last_error()
+    assert ep.ep_last_error().startswith("ep_layout_dispatch")
+
+
 COMBINE_BAD = [
     (dict(hidden=40), 1), (dict(quant=-1), 1), (dict(inp=None), 1), (dict(inp=FAKE + 4), 1),
     (dict(in_bytes=5), 3), (dict(w=None), 1), (dict(out=None), 1), (dict(out=FAKE + 2), 1),
