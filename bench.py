@@ -47,7 +47,7 @@ def algorithmic_bytes(w, R: int) -> dict:
 
     layout:   read ids, write counts/offsets, slot map and row sources
     dispatch: read x once and the slot map, write every routed packed row
-    combine:  read every routed row, the slot map and the weights, write out
+    combine:  read every routed row, the ids and the weights, write out
     """
     b_idx = 4 if w.idx_dtype == "int32" else 8
     H, T, k, E = w.H, w.T, w.k, w.E
@@ -56,7 +56,7 @@ def algorithmic_bytes(w, R: int) -> dict:
     dc, sc = _row_bytes(cin, H)
     lay = T * k * b_idx + E * 8 + (E + 1) * 4 + T * k * 4 + R * 4
     disp = 2 * T * H + T * k * 4 + R * (dq + sq)
-    comb = R * (dc + sc) + T * k * (4 + 4) + 2 * T * H
+    comb = R * (dc + sc) + T * k * (b_idx + 4) + 2 * T * H
     return {"layout": lay, "dispatch": disp, "combine": comb, "total": lay + disp + comb}
 
 
@@ -93,7 +93,26 @@ def _traffic(workload: str, path: str = TRAFFIC_FILE, sources=KERNEL_SOURCES):
 # ---------------------------------------------------------------------------
 
 
+CPU_RUNS = 3             # timed oracle runs of the sample; the median is reported
+CPU_ONE_RUN_S = 60.0     # ... or one run, when a run takes longer than this
+
+
+def _timed_runs(run) -> list:
+    """Times `run()` CPU_RUNS times, or once if that run exceeds CPU_ONE_RUN_S."""
+    times = []
+    for _ in range(CPU_RUNS):
+        t0 = time.perf_counter()
+        run()
+        times.append(time.perf_counter() - t0)
+        if times[0] > CPU_ONE_RUN_S:
+            break
+    return times
+
+
 def cpu_baseline_child(name: str, tokens: int) -> None:
+    """The oracle's layout + dispatch + combine on the first `tokens` tokens
+    as one batch, on one core, timed CPU_RUNS times (inputs drawn once,
+    outside the timed region)."""
     os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
     import numpy as np
     from combine_topk_idx_amd import workloads as W
@@ -107,27 +126,30 @@ def cpu_baseline_child(name: str, tokens: int) -> None:
     y = None
     if w.combine_input == "normal":
         y = W.make_expert_out(w, rows=tokens * w.k)
-    t0 = time.perf_counter()
-    lay = L.layout(idx, w.E, tokens)
-    rb = D.dispatch(x, lay, w.mode)
-    if w.combine_input == "identity":
-        cin = rb
-    elif w.combine_input == "scaled_dispatch":                    # bf16 rows: the dispatched rows x 1.5
-        from oracle import codecs
-        ys = codecs.bf16_bits_to_f32(rb.data.view(np.uint16)).astype(np.float32) * np.float32(1.5)
-        cin = D.RecvBuffer("none", w.H, lay.num_rows, W.bf16_from_f32(ys).view(np.uint8),
-                           np.zeros((lay.max_rows, 0), np.uint8), None)
-    else:
-        cin = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8).reshape(tokens * w.k, -1),
-                           np.zeros((tokens * w.k, 0), np.uint8), None)
-    C.combine(cin, lay, wts)
-    dt = time.perf_counter() - t0
-    print(json.dumps({"tokens": tokens, "seconds": dt, "cores": len(os.sched_getaffinity(0))}))
+
+    def run():
+        lay = L.layout(idx, w.E, tokens)
+        rb = D.dispatch(x, lay, w.mode)
+        if w.combine_input == "identity":
+            cin = rb
+        elif w.combine_input == "scaled_dispatch":                # bf16 rows: the dispatched rows x 1.5
+            from oracle import codecs
+            ys = codecs.bf16_bits_to_f32(rb.data.view(np.uint16)).astype(np.float32) * np.float32(1.5)
+            cin = D.RecvBuffer("none", w.H, lay.num_rows, W.bf16_from_f32(ys).view(np.uint8),
+                               np.zeros((lay.max_rows, 0), np.uint8), None)
+        else:
+            cin = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8).reshape(tokens * w.k, -1),
+                               np.zeros((tokens * w.k, 0), np.uint8), None)
+        C.combine(cin, lay, wts)
+
+    times = _timed_runs(run)
+    print(json.dumps({"tokens": tokens, "times": times, "cores": len(os.sched_getaffinity(0))}))
 
 
 def cpu_baseline_moe_child(name: str, tokens: int) -> None:
     """The oracle's expert-MLP path (layout, MXFP8 dispatch, GMM1 + SwiGLU +
-    requant, GMM2, combine) on the first `tokens` tokens, on one core."""
+    requant, GMM2, combine) on the first `tokens` tokens, on one core, timed
+    CPU_RUNS times."""
     os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
     import numpy as np
     from combine_topk_idx_amd import workloads as W
@@ -136,20 +158,25 @@ def cpu_baseline_moe_child(name: str, tokens: int) -> None:
     w = W.MOE_WORKLOADS[name]
     inp = W.make_moe_inputs(w)
     x, idx, wts = inp["x"][:tokens], inp["topk_idx"][:tokens], inp["topk_weights"][:tokens]
-    t0 = time.perf_counter()
-    lay = L.layout(idx, w.E_local, tokens)
-    rb = D.dispatch(x, lay, "mxfp8")
-    y = np.zeros((lay.max_rows, w.H), np.uint16)
-    for e in range(w.E_local):
-        rows = np.arange(lay.offsets[e], lay.offsets[e] + lay.count[e])
-        if rows.size == 0:
-            continue
-        q, qs, _ = M.gmm1_swiglu_rows(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e])
-        y[rows], _ = M.gmm2_rows(q, qs, inp["w2_codes"][e], inp["w2_scales"][e])
-    cin = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8), np.zeros((lay.max_rows, 0), np.uint8), None)
-    C.combine(cin, lay, wts)
-    dt = time.perf_counter() - t0
-    print(json.dumps({"tokens": tokens, "rows": int(lay.num_rows), "seconds": dt,
+    rows_seen = []
+
+    def run():
+        lay = L.layout(idx, w.E_local, tokens)
+        rb = D.dispatch(x, lay, "mxfp8")
+        y = np.zeros((lay.max_rows, w.H), np.uint16)
+        for e in range(w.E_local):
+            rows = np.arange(lay.offsets[e], lay.offsets[e] + lay.count[e])
+            if rows.size == 0:
+                continue
+            q, qs, _ = M.gmm1_swiglu_rows(rb.data[rows], rb.scales[rows], inp["w1_codes"][e], inp["w1_scales"][e])
+            y[rows], _ = M.gmm2_rows(q, qs, inp["w2_codes"][e], inp["w2_scales"][e])
+        cin = D.RecvBuffer("none", w.H, lay.num_rows, y.view(np.uint8), np.zeros((lay.max_rows, 0), np.uint8),
+                           None)
+        C.combine(cin, lay, wts)
+        rows_seen.append(int(lay.num_rows))
+
+    times = _timed_runs(run)
+    print(json.dumps({"tokens": tokens, "rows": rows_seen[0], "times": times,
                       "cores": len(os.sched_getaffinity(0))}))
 
 
@@ -162,13 +189,17 @@ def cpu_baseline(name: str, tokens: int, moe: bool = False) -> dict:
     if r.returncode != 0:
         raise RuntimeError(f"cpu baseline failed:\n{r.stderr}")
     d = json.loads(r.stdout.strip().splitlines()[-1])
+    times = sorted(d["times"])
+    med = times[len(times) // 2]
     what = ("layout + MXFP8 dispatch + GMM1/SwiGLU/requant + GMM2 + combine, "
             f"{d.get('rows', 0)} expert rows; the weights are dequantised in full" if moe else
             "layout + dispatch + combine")
-    return {"value": d["tokens"] / d["seconds"], "unit": "tokens/s", "cores": d["cores"], "kind": "oracle",
-            "sample": f"first {d['tokens']} tokens of the workload as one batch ({what}), "
-                      f"{d['seconds']:.1f} s on one host core",
-            "host": _host_cpu()}
+    runs = (f"median of {len(times)} runs ({', '.join(f'{t:.2f}' for t in d['times'])} s)" if len(times) > 1
+            else f"one run of {times[0]:.1f} s (over {CPU_ONE_RUN_S:.0f} s)")
+    return {"value": d["tokens"] / med, "unit": "tokens/s", "cores": d["cores"], "kind": "oracle",
+            "sample": f"first {d['tokens']} tokens of the workload as one batch ({what}), {runs}, "
+                      f"on one host core",
+            "seconds": round(med, 3), "host": _host_cpu()}
 
 
 def _host_cpu() -> str:
@@ -320,7 +351,7 @@ def moe_algorithmic(w, R: int) -> dict:
     gmm1:     read W1 (codes + scales, packed once ahead of time) and the R
               dispatch rows, write R MXFP8 rows of width I
     gmm2:     read W2 (codes + scales) and those rows, write R bf16 rows
-    combine:  read R bf16 rows, slots and weights, write T bf16 rows
+    combine:  read R bf16 rows, the (int64) ids and the weights, write T bf16 rows
     """
     H, I, E, T, k = w.H, w.I, w.E_local, w.T, w.k
     mx = lambda n: n + n // 32
@@ -329,7 +360,7 @@ def moe_algorithmic(w, R: int) -> dict:
         "dispatch": 2 * T * H + T * k * 4 + R * mx(H),
         "gmm1": E * 2 * I * mx(H) + R * mx(H) + R * mx(I),
         "gmm2": E * H * mx(I) + R * mx(I) + R * 2 * H,
-        "combine": R * 2 * H + T * k * 8 + 2 * T * H,
+        "combine": R * 2 * H + T * k * (8 + 4) + 2 * T * H,
     }
     b["total"] = sum(b.values())
     f = {"gmm1": 2.0 * R * H * 2 * I, "gmm2": 2.0 * R * I * H}
@@ -391,7 +422,7 @@ def moe_main(args) -> int:
             ep.ep_moe_gmm2(s["h"], s["a"], w.I, w.H, s["w2"], s["w2s"], s["y"], recv_count=s["rc"])
 
         def comb():
-            ep.ep_combine(s["h"], s["y"], "none", w.H, s["wt"], s["out"])
+            ep.ep_combine(s["h"], s["y"], "none", w.H, s["idx"], s["wt"], s["out"])
         return [lay, disp, g1, g2, comb]
 
     runners = [phases(s) for s in sets]
@@ -433,6 +464,88 @@ def moe_main(args) -> int:
     return 0
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 counter summaries (HBM bytes per launch)
+# ---------------------------------------------------------------------------
+
+# kernels of each measured path: (label, substring of the kernel name)
+PMC_KERNELS = {
+    "path": [("combine", "combine_kernel"), ("dispatch", "dispatch_kernel"), ("layout_rank", "layout_rank_kernel"),
+             ("layout_finalize", "layout_finalize_kernel"), ("layout_single", "layout_single_kernel")],
+    "moe": [("gmm1", "mx_gmm_kernel<0>"), ("gmm2", "mx_gmm_kernel<2>"), ("dispatch", "dispatch_kernel"),
+            ("combine", "combine_kernel")],
+}
+
+
+def _pmc_rows(path: str, counter: str) -> list:
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {path}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    return rows
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, moe: bool, copy_mib: int = 1024) -> dict:
+    """HBM bytes per launch of the path's kernels from two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what
+    the same counter reads for a device-to-device copy of `copy_mib` MiB in
+    the same run (`--copy-probe-mib`), against the algorithmic bytes."""
+    import numpy as np
+    from combine_topk_idx_amd import workloads as W
+    fetch, write = _pmc_rows(fetch_dir, "FETCH_SIZE"), _pmc_rows(write_dir, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+
+    def calib(rows):
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise ValueError("no copy kernel in the counter run (run it with --copy-probe-mib)")
+        return copies
+
+    # the probe copy is the copy whose WRITE_SIZE is the copy's size; the
+    # fetch run's copies come in the same order
+    wcopies, fcopies = calib(write), calib(fetch)
+    i = min(range(len(wcopies)), key=lambda j: abs(wcopies[j] - copy_kib))
+    w_scale, f_scale = copy_kib / wcopies[i], copy_kib / fcopies[i]
+
+    def per_launch(rows, sub):
+        v = [float(r["Counter_Value"]) for r in rows if sub in r["Kernel_Name"]]
+        return (sum(v) / len(v), len(v)) if v else (None, 0)
+
+    if moe:
+        w = W.MOE_WORKLOADS[workload]
+        R = int((W.make_moe_inputs(w)["topk_idx"] >= 0).sum())
+        alg = moe_algorithmic(w, R)["bytes"]
+        measured, sources = "gmm1", MOE_KERNEL_SOURCES
+    else:
+        w = W.WORKLOADS[workload]
+        idx = W.make_inputs(w)["topk_idx"]
+        R = int(((idx >= 0) & (idx < w.E)).sum())
+        alg = algorithmic_bytes(w, R)
+        measured, sources = "combine", KERNEL_SOURCES
+    kernels = {}
+    for label, sub in PMC_KERNELS["moe" if moe else "path"]:
+        fk, n = per_launch(fetch, sub)
+        wk, _ = per_launch(write, sub)
+        if fk is None:
+            continue
+        b = (fk * f_scale + wk * w_scale) * 1024.0
+        a = alg.get(label)
+        kernels[label] = {"launches": n, "fetch_kib_raw": round(fk, 3), "write_kib_raw": round(wk, 3),
+                          "bytes": int(round(b)), "alg_bytes": a, "ratio": round(b / a, 4) if a else None}
+    m = kernels[measured]
+    return {"workload": workload, "kernel": measured, "source_hash": _source_hash(sources),
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "calibration": f"{copy_mib} MiB device-to-device copy read FETCH_SIZE {fcopies[i]:.0f} KiB and "
+                           f"WRITE_SIZE {wcopies[i]:.0f} KiB",
+            "bytes_per_launch": m["bytes"], "alg_bytes_per_launch": m["alg_bytes"],
+            "traffic_over_alg": m["bytes"] / m["alg_bytes"], "kernels": kernels}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +578,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as one captured HIP graph (no per-call host cost) instead of stream "
                          "launches")
+    ap.add_argument("--pmc-summary", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "bench (with --copy-probe-mib) into HBM bytes per launch; prints JSON")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--cpu-baseline-moe-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -474,6 +590,10 @@ def main() -> int:
         return 0
     if args.cpu_baseline_moe_child:
         cpu_baseline_moe_child(args.cpu_baseline_moe_child, args.cpu_tokens)
+        return 0
+    if args.pmc_summary:
+        d = pmc_summary(*args.pmc_summary, args.moe or args.workload, bool(args.moe), args.copy_probe_mib or 1024)
+        print(json.dumps(d, indent=1))
         return 0
     if args.combine_backward:
         return backward_main(args)
@@ -572,13 +692,13 @@ def main() -> int:
 
         def comb():
             if w.combine_input == "identity":
-                ep.ep_combine(s["h"], s["recv"], w.mode, w.H, s["w"], s["out"], interleaved=w.interleaved)
+                ep.ep_combine(s["h"], s["recv"], w.mode, w.H, s["idx"], s["w"], s["out"], interleaved=w.interleaved)
             elif w.combine_input == "scaled_dispatch":
                 # the x1.5 expert step is not part of the path: combine reads
                 # the dispatched bf16 rows (same bytes, same work)
-                ep.ep_combine(s["h"], s["recv"], "none", w.H, s["w"], s["out"])
+                ep.ep_combine(s["h"], s["recv"], "none", w.H, s["idx"], s["w"], s["out"])
             else:
-                ep.ep_combine(s["h"], s["y"], "none", w.H, s["w"], s["out"])
+                ep.ep_combine(s["h"], s["y"], "none", w.H, s["idx"], s["w"], s["out"])
         return [lay_disp, comb] if args.fused else [lay, disp, comb]
 
     runners = [phases(s) for s in sets]
@@ -608,7 +728,9 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline and not variant:
-        tokens = args.cpu_tokens or {"large": 1536, "prefill": 1024}.get(w.name, w.T)
+        # one 1024-token chunk of the large workloads (about 5 s per run of
+        # the oracle; three runs keep the default bench within minutes)
+        tokens = args.cpu_tokens or {"large": 1024, "prefill": 1024}.get(w.name, w.T)
         print(f"[bench] cpu oracle on {tokens} tokens", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w.name, tokens)
 

@@ -15,6 +15,16 @@
 // (scalar loads).  All k row loads of a lane are issued before the first add,
 // so a lane has up to k independent 4-16 byte loads in flight; the adds then
 // run in ascending j.
+//
+// The topk_idx given to combine must be the one dispatch was given ("Low-
+// Latency Mode API", low_latency_combine Parameters).  The first span
+// workgroup of each token checks its k pairs against the handle: a valid id e
+// must have its slot inside expert e's block [offsets[e], offsets[e+1]) (or
+// slot -1 when blocks have a capacity, for a pair dropped past it), and any
+// other id must have slot -1.  A mismatch sets EP_STATUS_COMBINE_MISMATCH; the
+// reduction itself always follows the handle's slots.  The ids' loads are
+// issued before the row loads and the block bounds' loads after them, so the
+// check adds no memory round trip of its own.
 #include "common.hpp"
 #include "formats.hpp"
 #include "tuning.hpp"
@@ -62,14 +72,29 @@ __device__ __forceinline__ void dequant8(const typename Raw<Q>::T &r, float scal
   }
 }
 
+// What the routing check needs: the ids and the handle's block bounds.
+struct IdCheck {
+  const void *idx;              // [T, k] int32 or int64
+  int idx64, E, cap;            // cap: the handle's expert_capacity (0: none)
+  const int *offsets;           // [E + 1] block starts
+  uint32_t *status;
+};
+
 template <int Q, int NT, int KMAX, int CV, bool EXACT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void combine_kernel(
     const char *__restrict__ data, const char *__restrict__ scales, int64_t dq, int64_t sq, int nvec, int k,
-    int chunks, const int *__restrict__ slot, const float *__restrict__ w, u32x4 *__restrict__ out) {
+    int chunks, const int *__restrict__ slot, const float *__restrict__ w, u32x4 *__restrict__ out, IdCheck ic) {
   using RawT = typename Raw<Q>::T;
   const int t = blockIdx.x / chunks;
   const int c = blockIdx.x - t * chunks;
   const int64_t pair0 = (int64_t)t * k;
+  // lane j < k of the token's first span workgroup checks pair j
+  const bool checker = c == 0 && (int)threadIdx.x < k;
+  int64_t my_id = -1;
+  if (checker) {
+    my_id = ic.idx64 ? ((const int64_t *)ic.idx)[pair0 + threadIdx.x]
+                     : (int64_t)((const int32_t *)ic.idx)[pair0 + threadIdx.x];
+  }
 
   // routed rows and weights: loads from valid addresses first, then masking,
   // so the loads are in flight together (with k == KMAX they are contiguous
@@ -93,7 +118,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void co
 
   // this lane's CV consecutive 8-element vectors
   const int v0 = (c * NT + threadIdx.x) * CV;
-  if (v0 >= nvec) return;
+  const bool active = v0 < nvec;
+  if (!active && !checker) return;
 
   // phase 1: issue every row load (data and scale)
   RawT raw[KMAX][CV];
@@ -105,7 +131,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void co
       raw[j][h] = RawT{};
       sraw[j][h] = 0;
     }
-    if (s[j] < 0) continue;
+    if (s[j] < 0 || !active) continue;
 #pragma unroll
     for (int h = 0; h < CV; ++h) {
       const int v = v0 + h;
@@ -124,6 +150,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void co
       }
     }
   }
+  // the routing check: this lane's slot is s[threadIdx.x] (uniform values)
+  if (checker) {
+    int my_slot = -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) my_slot = j == (int)threadIdx.x ? s[j] : my_slot;
+    bool bad;
+    if (my_id >= 0 && my_id < (int64_t)ic.E) {
+      const int lo = ic.offsets[my_id], hi = ic.offsets[my_id + 1];
+      bad = my_slot < 0 ? ic.cap == 0 : (my_slot < lo || my_slot >= hi);
+    } else {
+      bad = my_slot >= 0;
+    }
+    if (bad) atomicOr(ic.status, (uint32_t)EP_STATUS_COMBINE_MISMATCH);
+  }
+  if (!active) return;
+
   // phase 2: dequantise and accumulate in ascending j
   float acc[CV][8];
 #pragma unroll
@@ -163,7 +205,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void co
 // row strides of data and scales (equal for interleaved rows) and the scale base.
 template <int Q, int NT, int KMAX, int CV, bool EXACT>
 hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out, int quant,
-                    hipStream_t s) {
+                    const IdCheck &ic, hipStream_t s) {
   const RecvGeom g = recv_geom(h.max_rows, hidden, quant);
   const int64_t dq = g.data_stride, sq = g.scale_stride;
   const size_t scale_off = g.scale_off;
@@ -173,34 +215,35 @@ hipError_t launch_q(const ep_handle_t &h, const char *in, int hidden, const floa
   const int64_t blocks = h.num_tokens * chunks;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((combine_kernel<Q, NT, KMAX, CV, EXACT>), dim3((unsigned)blocks), dim3(NT), EP_COMBINE_LDS_CAP, s, in,
-                     in + scale_off, (int64_t)dq, (int64_t)sq, nvec, h.num_topk, chunks, h.slot, w, (u32x4 *)out);
+                     in + scale_off, (int64_t)dq, (int64_t)sq, nvec, h.num_topk, chunks, h.slot, w, (u32x4 *)out, ic);
   return hipGetLastError();
 }
 
 template <int Q>
 hipError_t launch_mode(const ep_handle_t &h, const char *in, int hidden, const float *w, void *out, int quant,
-                       hipStream_t s) {
+                       const IdCheck &ic, hipStream_t s) {
   constexpr int NT = EP_COMBINE_THREADS, CV = EP_COMBINE_CV;
   if (EP_COMBINE_KMAX_MIN <= 8 && h.num_topk == 8)
-    return launch_q<Q, NT, 8, CV, true>(h, in, hidden, w, out, quant, s);
+    return launch_q<Q, NT, 8, CV, true>(h, in, hidden, w, out, quant, ic, s);
   if (EP_COMBINE_KMAX_MIN <= 8 && h.num_topk < 8)
-    return launch_q<Q, NT, 8, CV, false>(h, in, hidden, w, out, quant, s);
-  if (h.num_topk == kMaxTopk) return launch_q<Q, NT, kMaxTopk, CV, true>(h, in, hidden, w, out, quant, s);
-  return launch_q<Q, NT, kMaxTopk, CV, false>(h, in, hidden, w, out, quant, s);
+    return launch_q<Q, NT, 8, CV, false>(h, in, hidden, w, out, quant, ic, s);
+  if (h.num_topk == kMaxTopk) return launch_q<Q, NT, kMaxTopk, CV, true>(h, in, hidden, w, out, quant, ic, s);
+  return launch_q<Q, NT, kMaxTopk, CV, false>(h, in, hidden, w, out, quant, ic, s);
 }
 
 }  // namespace
 
-hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const float *w, void *out,
-                          hipStream_t s) {
+hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const void *idx, int idx64,
+                          const float *w, void *out, hipStream_t s) {
+  const IdCheck ic{idx, idx64, h.num_experts, h.expert_capacity, h.offsets, h.status};
   switch (quant & kQuantMask) {
-    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE>(h, in, hidden, w, out, quant, s);
-    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN>(h, in, hidden, w, out, quant, s);
-    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128>(h, in, hidden, w, out, quant, s);
-    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8>(h, in, hidden, w, out, quant, s);
-    case EP_QUANT_FP8_B128_POW2: return launch_mode<EP_QUANT_FP8_B128_POW2>(h, in, hidden, w, out, quant, s);
-    case EP_QUANT_FP8_B128_UE8M0: return launch_mode<EP_QUANT_FP8_B128_UE8M0>(h, in, hidden, w, out, quant, s);
-    default: return launch_mode<EP_QUANT_MXFP4>(h, in, hidden, w, out, quant, s);
+    case EP_QUANT_NONE: return launch_mode<EP_QUANT_NONE>(h, in, hidden, w, out, quant, ic, s);
+    case EP_QUANT_INT8_TOKEN: return launch_mode<EP_QUANT_INT8_TOKEN>(h, in, hidden, w, out, quant, ic, s);
+    case EP_QUANT_FP8_B128: return launch_mode<EP_QUANT_FP8_B128>(h, in, hidden, w, out, quant, ic, s);
+    case EP_QUANT_MXFP8: return launch_mode<EP_QUANT_MXFP8>(h, in, hidden, w, out, quant, ic, s);
+    case EP_QUANT_FP8_B128_POW2: return launch_mode<EP_QUANT_FP8_B128_POW2>(h, in, hidden, w, out, quant, ic, s);
+    case EP_QUANT_FP8_B128_UE8M0: return launch_mode<EP_QUANT_FP8_B128_UE8M0>(h, in, hidden, w, out, quant, ic, s);
+    default: return launch_mode<EP_QUANT_MXFP4>(h, in, hidden, w, out, quant, ic, s);
   }
 }
 

@@ -147,8 +147,8 @@ hipError_t launch_layout(const void *idx, int idx64, int64_t T, int32_t k, int32
 hipError_t launch_dispatch(const ep_handle_t &h, const void *x, int hidden, const float *w, int quant,
                            char *recv, float *recv_w, hipStream_t s);
 
-hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const float *w,
-                          void *out, hipStream_t s);
+hipError_t launch_combine(const ep_handle_t &h, const char *in, int quant, int hidden, const void *idx, int idx64,
+                          const float *w, void *out, hipStream_t s);
 
 hipError_t launch_combine_backward(const ep_handle_t &h, const void *grad, int hidden, const float *w, int quant,
                                    char *buf, hipStream_t s);

@@ -349,8 +349,9 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
 // token's pairs by itself, with no wait on another workgroup, while its span
 // of the token row is in flight.  Workgroup 0 writes the per-expert outputs
 // (counts, block starts, running statistics, status) and marks the rows past
-// the last routed one free; the first span workgroup of each token writes the
-// token's slots, row_src entries and receive weights.
+// the last routed one free up to n = T * k; every span workgroup marks a share
+// of the rows from n to the capacity's end free; the first span workgroup of
+// each token writes the token's slots, row_src entries and receive weights.
 struct FusedArgs {
   const void *idx;     // [n] int32 or int64 ids
   int idx64, n, E, max_rows;
@@ -411,7 +412,8 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum, int &total)
 }
 
 // Workgroup 0 of the fused launch: expert histogram (LDS atomics), its
-// exclusive scan, the per-expert outputs, the status word and the free rows.
+// exclusive scan, the per-expert outputs, the status word and the free rows
+// below n (all of them when there is no token, hence no span workgroup).
 template <int NT, typename IdT>
 __device__ __forceinline__ void fused_layout_outputs(const FusedArgs &a) {
   __shared__ int cnt[kMaxExperts];
@@ -453,7 +455,10 @@ __device__ __forceinline__ void fused_layout_outputs(const FusedArgs &a) {
     a.offsets[a.E] = nrows;
     *a.status = sbad;
   }
-  for (int r = nrows + threadIdx.x; r < a.max_rows; r += NT) a.row_src[r] = -1;
+  // free rows below n; the span workgroups clear [n, max_rows), unless there
+  // are none (no tokens)
+  const int end = gridDim.x > 1 ? a.n : a.max_rows;
+  for (int r = nrows + threadIdx.x; r < end; r += NT) a.row_src[r] = -1;
 }
 
 // Receive rows of the pairs of token t (s[j] = -1 past k and for pairs with
@@ -540,6 +545,10 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
       return;
     }
     b -= 1;
+    // rows at or past n (= T * k) never hold a pair; with a capacity far
+    // above T there can be many, so every span workgroup clears a share
+    const int stride = ((int)gridDim.x - 1) * NT;
+    for (int r = fa.n + b * NT + (int)threadIdx.x; r < fa.max_rows; r += stride) fa.row_src[r] = -1;
   }
   const int t = b / chunks;
   const int c = b - t * chunks;

@@ -247,13 +247,17 @@ ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden
   return EP_OK;
 }
 
-ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens, int32_t num_topk,
-                               int64_t num_max_dispatch_tokens, int32_t num_experts, int32_t row_align,
-                               int32_t expert_capacity, int64_t *recv_count, int32_t *cumulative_recv_stats,
-                               void *workspace, size_t workspace_bytes, const void *x, int32_t hidden,
-                               const float *topk_weights, ep_quant_t quant, void *recv_buf, size_t recv_buf_bytes,
-                               float *recv_weights, ep_handle_t *handle, void *stream) {
-  const char *fn = "ep_layout_dispatch";
+}  // extern "C"
+
+namespace {
+
+ep_status_t layout_dispatch_impl(const char *fn, const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                                 int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts,
+                                 int32_t row_align, int32_t expert_capacity, int64_t *recv_count,
+                                 int32_t *cumulative_recv_stats, void *workspace, size_t workspace_bytes,
+                                 const void *x, int32_t hidden, const float *topk_weights, ep_quant_t quant,
+                                 void *recv_buf, size_t recv_buf_bytes, float *recv_weights, ep_handle_t *handle,
+                                 void *stream) {
   ep_handle_t h;
   ep::WsLayout wl;
   ep_status_t st = layout_prepare(fn, topk_idx, idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
@@ -278,13 +282,36 @@ ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, i
   return EP_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens, int32_t num_topk,
+                               int64_t num_max_dispatch_tokens, int32_t num_experts, int32_t row_align,
+                               int32_t expert_capacity, int64_t *recv_count, int32_t *cumulative_recv_stats,
+                               void *workspace, size_t workspace_bytes, const void *x, int32_t hidden,
+                               const float *topk_weights, ep_quant_t quant, void *recv_buf, size_t recv_buf_bytes,
+                               float *recv_weights, ep_handle_t *handle, void *stream) {
+  return layout_dispatch_impl("ep_layout_dispatch", topk_idx, idx_dtype, num_tokens, num_topk,
+                              num_max_dispatch_tokens, num_experts, row_align, expert_capacity, recv_count,
+                              cumulative_recv_stats, workspace, workspace_bytes, x, hidden, topk_weights, quant,
+                              recv_buf, recv_buf_bytes, recv_weights, handle, stream);
+}
+
 ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t expert_out_bytes,
-                       ep_quant_t in_quant, int32_t hidden, const float *topk_weights, void *out, void *stream) {
+                       ep_quant_t in_quant, int32_t hidden, const void *topk_idx, ep_idx_dtype_t idx_dtype,
+                       const float *topk_weights, void *out, void *stream) {
   const char *fn = "ep_combine";
   ep_status_t st = check_handle(handle, fn);
   if (st != EP_OK) return st;
   st = check_hidden(hidden, in_quant, fn);
   if (st != EP_OK) return st;
+  if (idx_dtype != EP_IDX_INT32 && idx_dtype != EP_IDX_INT64)
+    return fail(EP_ERR_INVALID_ARG, "%s: topk_idx dtype must be int32 or int64", fn);
+  if (handle->num_tokens > 0 && !topk_idx)
+    return fail(EP_ERR_INVALID_ARG, "%s: topk_idx is NULL (it must be the one given to dispatch)", fn);
+  if (topk_idx && !aligned(topk_idx, idx_dtype == EP_IDX_INT64 ? 8 : 4))
+    return fail(EP_ERR_INVALID_ARG, "%s: topk_idx is not aligned to its dtype", fn);
   if (!expert_out || !aligned(expert_out, 16))
     return fail(EP_ERR_INVALID_ARG, "%s: expert_out is NULL or not 16-byte aligned", fn);
   const size_t need = buffer_bytes(handle->max_rows, hidden, in_quant, nullptr);
@@ -294,8 +321,8 @@ ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t
     return fail(EP_ERR_INVALID_ARG, "%s: topk_weights is NULL or misaligned (it is required)", fn);
   if (handle->num_tokens > 0 && (!out || !aligned(out, 16)))
     return fail(EP_ERR_INVALID_ARG, "%s: out is NULL or not 16-byte aligned", fn);
-  const hipError_t e = ep::launch_combine(*handle, (const char *)expert_out, in_quant, hidden, topk_weights, out,
-                                          (hipStream_t)stream);
+  const hipError_t e = ep::launch_combine(*handle, (const char *)expert_out, in_quant, hidden, topk_idx,
+                                          idx_dtype == EP_IDX_INT64, topk_weights, out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   return EP_OK;
 }

@@ -2,7 +2,7 @@
 
 The functions ``ep_workspace_bytes``, ``ep_workspace_bytes_ex``,
 ``ep_layout_rows``, ``ep_buffer_bytes``, ``ep_layout``, ``ep_layout_ex``,
-``ep_dispatch``, ``ep_combine``, ``ep_combine_backward``,
+``ep_dispatch``, ``ep_layout_dispatch``, ``ep_combine``, ``ep_combine_backward``,
 ``ep_moe_packed_bytes``, ``ep_moe_pack_weights``, ``ep_moe_gmm1``,
 ``ep_moe_gmm2``, ``ep_read_status``,
 ``ep_last_error`` and ``ep_abi_version`` have the names and arguments of the C ABI in
@@ -39,9 +39,11 @@ QUANT = {"none": 0, "int8_token": 1, "fp8_b128": 2, "mxfp8": 3, "mxfp4": 4, "fp8
 EP_RECV_INTERLEAVED = 0x100
 EP_STATUS_ID_OUT_OF_RANGE = 1
 EP_STATUS_CAPACITY_OVERFLOW = 2
+EP_STATUS_COMBINE_MISMATCH = 4
 
 SYMBOLS = ("ep_workspace_bytes", "ep_workspace_bytes_ex", "ep_layout_rows", "ep_buffer_bytes", "ep_layout",
-           "ep_layout_ex", "ep_dispatch", "ep_layout_dispatch", "ep_combine", "ep_combine_backward", "ep_moe_packed_bytes", "ep_moe_pack_weights", "ep_moe_gmm1", "ep_moe_gmm2",
+           "ep_layout_ex", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
+           "ep_combine_backward", "ep_moe_packed_bytes", "ep_moe_pack_weights", "ep_moe_gmm1", "ep_moe_gmm2",
            "ep_read_status", "ep_last_error", "ep_abi_version")
 
 
@@ -81,7 +83,8 @@ _lib.ep_dispatch.restype = ctypes.c_int
 _lib.ep_layout_dispatch.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                     _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp, ctypes.POINTER(ep_handle_t), _vp]
 _lib.ep_layout_dispatch.restype = ctypes.c_int
-_lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int, _i32, _vp, _vp, _vp]
+_lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int, _i32, _vp, ctypes.c_int, _vp, _vp,
+                            _vp]
 _lib.ep_combine.restype = ctypes.c_int
 _lib.ep_combine_backward.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp]
 _lib.ep_combine_backward.restype = ctypes.c_int
@@ -146,6 +149,34 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
+def _check_args(*specs) -> None:
+    """Host checks of tensor arguments before their pointers reach the
+    library, which can only check pointers and byte counts.  Each spec is
+    (tensor, name, dtype, shape, min_numel) with None for "any"; raw integer
+    pointers and None tensors pass unchecked.  First every tensor's dtype,
+    shape, density and size, then that all of them are on one GPU."""
+    ts = []
+    for t, name, dtype, shape, min_numel in specs:
+        if t is None or isinstance(t, int):
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise EpError(EP_ERR_INVALID_ARG, f"{name} must be a tensor")
+        if dtype is not None and t.dtype != dtype:
+            raise EpError(EP_ERR_INVALID_ARG, f"{name} must be {dtype} (got {t.dtype})")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise EpError(EP_ERR_INVALID_ARG, f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+        if not t.is_contiguous():
+            raise EpError(EP_ERR_INVALID_ARG, f"{name} must be contiguous")
+        if min_numel is not None and t.numel() < min_numel:
+            raise EpError(EP_ERR_INVALID_ARG, f"{name} holds {t.numel()} elements, needs {min_numel}")
+        ts.append((t, name))
+    for t, name in ts:
+        if not t.is_cuda:
+            raise EpError(EP_ERR_INVALID_ARG, f"{name} must be a GPU tensor (got {t.device})")
+        if t.device != ts[0][0].device:
+            raise EpError(EP_ERR_INVALID_ARG, f"{name} is on {t.device}, {ts[0][1]} on {ts[0][0].device}")
+
+
 # ---------------------------------------------------------------------------
 # C ABI, one function each
 # ---------------------------------------------------------------------------
@@ -192,12 +223,20 @@ def _idx_args(topk_idx, num_tokens, num_topk, idx_dtype):
     return num_tokens, num_topk, idx_dtype
 
 
+def _layout_specs(topk_idx, num_experts, recv_count, workspace, cum) -> list:
+    return [(topk_idx, "topk_idx", None, None, None),
+            (recv_count, "recv_count", torch.int64, None, num_experts),
+            (workspace, "workspace", None, None, None),
+            (cum, "cumulative_recv_stats", torch.int32, None, num_experts)]
+
+
 def ep_layout(topk_idx, num_experts: int, num_max_dispatch_tokens: int, recv_count, workspace,
               cumulative_recv_stats=None, *, num_tokens=None, num_topk=None, idx_dtype=None,
               stream=None) -> ep_handle_t:
     """topk_idx: device tensor [T, k] int32/int64 (or a raw pointer with
     num_tokens / num_topk / idx_dtype given).  Returns the handle."""
     num_tokens, num_topk, idx_dtype = _idx_args(topk_idx, num_tokens, num_topk, idx_dtype)
+    _check_args(*_layout_specs(topk_idx, num_experts, recv_count, workspace, cumulative_recv_stats))
     h = ep_handle_t()
     _check(_lib.ep_layout(_ptr(topk_idx), idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
                           num_experts, _ptr(recv_count), _ptr(cumulative_recv_stats), _ptr(workspace),
@@ -212,6 +251,7 @@ def ep_layout_ex(topk_idx, num_experts: int, num_max_dispatch_tokens: int, row_a
     """As ep_layout, with aligned (row_align) or capacity-padded
     (expert_capacity) expert blocks."""
     num_tokens, num_topk, idx_dtype = _idx_args(topk_idx, num_tokens, num_topk, idx_dtype)
+    _check_args(*_layout_specs(topk_idx, num_experts, recv_count, workspace, cumulative_recv_stats))
     h = ep_handle_t()
     _check(_lib.ep_layout_ex(_ptr(topk_idx), idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
                              num_experts, row_align, expert_capacity, _ptr(recv_count),
@@ -221,8 +261,17 @@ def ep_layout_ex(topk_idx, num_experts: int, num_max_dispatch_tokens: int, row_a
     return h
 
 
+def _dispatch_specs(T: int, k: int, max_rows: int, x, hidden: int, recv_buf, topk_weights, recv_weights) -> list:
+    return [(x, "x", torch.bfloat16, (T, hidden), None),
+            (recv_buf, "recv_buf", None, None, None),
+            (topk_weights, "topk_weights", torch.float32, (T, k), None),
+            (recv_weights, "recv_weights", torch.float32, None, max_rows)]
+
+
 def ep_dispatch(handle: ep_handle_t, x, hidden: int, quant, recv_buf, topk_weights=None,
                 recv_weights=None, *, recv_buf_bytes=None, interleaved=False, stream=None) -> None:
+    _check_args(*_dispatch_specs(handle.num_tokens, handle.num_topk, handle.max_rows, x, hidden, recv_buf,
+                                 topk_weights, recv_weights))
     nbytes = _nbytes(recv_buf) if recv_buf_bytes is None else recv_buf_bytes
     _check(_lib.ep_dispatch(ctypes.byref(handle), _ptr(x), hidden, _ptr(topk_weights), _quant(quant, interleaved),
                             _ptr(recv_buf), nbytes, _ptr(recv_weights), _stream(stream)))
@@ -236,6 +285,9 @@ def ep_layout_dispatch(topk_idx, num_experts: int, num_max_dispatch_tokens: int,
     """ep_layout_ex and ep_dispatch in one call (one launch for compact
     layouts of at most 2048 pairs).  Returns the handle."""
     num_tokens, num_topk, idx_dtype = _idx_args(topk_idx, num_tokens, num_topk, idx_dtype)
+    rows = max(ep_layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity), 0)
+    _check_args(*_layout_specs(topk_idx, num_experts, recv_count, workspace, cumulative_recv_stats),
+                *_dispatch_specs(num_tokens, num_topk, rows, x, hidden, recv_buf, topk_weights, recv_weights))
     nbytes = _nbytes(recv_buf) if recv_buf_bytes is None else recv_buf_bytes
     h = ep_handle_t()
     _check(_lib.ep_layout_dispatch(_ptr(topk_idx), idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
@@ -247,15 +299,31 @@ def ep_layout_dispatch(topk_idx, num_experts: int, num_max_dispatch_tokens: int,
     return h
 
 
-def ep_combine(handle: ep_handle_t, expert_out, in_quant, hidden: int, topk_weights, out, *,
-               expert_out_bytes=None, interleaved=False, stream=None) -> None:
+def ep_combine(handle: ep_handle_t, expert_out, in_quant, hidden: int, topk_idx, topk_weights, out, *,
+               idx_dtype=None, expert_out_bytes=None, interleaved=False, stream=None) -> None:
+    """topk_idx: the [T, k] ids given to the layout (a device tensor, or a
+    raw pointer with idx_dtype); a mismatch with the handle sets
+    EP_STATUS_COMBINE_MISMATCH."""
+    T, k = handle.num_tokens, handle.num_topk
+    if isinstance(topk_idx, torch.Tensor):
+        _, _, idx_dtype = _idx_args(topk_idx, None, None, None)
+        if tuple(topk_idx.shape) != (T, k):
+            raise EpError(EP_ERR_INVALID_ARG, f"topk_idx must have shape {(T, k)} (got {tuple(topk_idx.shape)})")
+    elif idx_dtype is None:
+        raise EpError(EP_ERR_INVALID_ARG, "idx_dtype is required with a raw topk_idx pointer")
+    _check_args((expert_out, "expert_out", None, None, None), (topk_idx, "topk_idx", None, None, None),
+                (topk_weights, "topk_weights", torch.float32, (T, k), None),
+                (out, "out", torch.bfloat16, (T, hidden), None))
     nbytes = _nbytes(expert_out) if expert_out_bytes is None else expert_out_bytes
     _check(_lib.ep_combine(ctypes.byref(handle), _ptr(expert_out), nbytes, _quant(in_quant, interleaved), hidden,
-                           _ptr(topk_weights), _ptr(out), _stream(stream)))
+                           _ptr(topk_idx), idx_dtype, _ptr(topk_weights), _ptr(out), _stream(stream)))
 
 
 def ep_combine_backward(handle: ep_handle_t, grad_out, hidden: int, quant, grad_buf, topk_weights=None, *,
                         grad_buf_bytes=None, interleaved=False, stream=None) -> None:
+    _check_args((grad_out, "grad_out", torch.bfloat16, (handle.num_tokens, hidden), None),
+                (grad_buf, "grad_buf", None, None, None),
+                (topk_weights, "topk_weights", torch.float32, (handle.num_tokens, handle.num_topk), None))
     nbytes = _nbytes(grad_buf) if grad_buf_bytes is None else grad_buf_bytes
     _check(_lib.ep_combine_backward(ctypes.byref(handle), _ptr(grad_out), hidden, _ptr(topk_weights),
                                     _quant(quant, interleaved), _ptr(grad_buf), nbytes, _stream(stream)))
@@ -284,8 +352,14 @@ def pack_moe_weights(codes, scales, gate_up: bool, *, stream=None):
     return pc, ps
 
 
+def _check_moe_args(handle: ep_handle_t, recv_count, **bufs) -> None:
+    _check_args(*[(b, n, None, None, None) for n, b in bufs.items()],
+                (recv_count, "recv_count", torch.int64, None, handle.num_experts))
+
+
 def ep_moe_gmm1(handle: ep_handle_t, x_buf, hidden: int, inter: int, w1, w1_scales, out_quant, out_buf, *,
                 recv_count=None, x_buf_bytes=None, out_buf_bytes=None, stream=None) -> None:
+    _check_moe_args(handle, recv_count, x_buf=x_buf, w1=w1, w1_scales=w1_scales, out_buf=out_buf)
     _check(_lib.ep_moe_gmm1(ctypes.byref(handle), _ptr(recv_count), _ptr(x_buf),
                             _nbytes(x_buf) if x_buf_bytes is None else x_buf_bytes, hidden, inter, _ptr(w1),
                             _ptr(w1_scales), _quant(out_quant), _ptr(out_buf),
@@ -294,6 +368,7 @@ def ep_moe_gmm1(handle: ep_handle_t, x_buf, hidden: int, inter: int, w1, w1_scal
 
 def ep_moe_gmm2(handle: ep_handle_t, a_buf, inter: int, hidden: int, w2, w2_scales, out_buf, *,
                 recv_count=None, a_buf_bytes=None, out_buf_bytes=None, stream=None) -> None:
+    _check_moe_args(handle, recv_count, a_buf=a_buf, w2=w2, w2_scales=w2_scales, out_buf=out_buf)
     _check(_lib.ep_moe_gmm2(ctypes.byref(handle), _ptr(recv_count), _ptr(a_buf),
                             _nbytes(a_buf) if a_buf_bytes is None else a_buf_bytes, inter, hidden, _ptr(w2),
                             _ptr(w2_scales), _ptr(out_buf), _nbytes(out_buf) if out_buf_bytes is None else out_buf_bytes,
@@ -386,6 +461,8 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_max_dispat
         raise EpError(EP_ERR_INVALID_ARG, "topk_idx must be [num_tokens, num_topk]")
     k = topk_idx.shape[1]
     dev = x.device
+    _check_args((x, "x", None, None, None), (topk_idx, "topk_idx", None, None, None),
+                (topk_weights, "topk_weights", torch.float32, (T, k), None))
     ws = torch.empty(max(ep_workspace_bytes_ex(num_max_dispatch_tokens_per_rank, k, num_experts, row_align,
                                                expert_capacity), 1), dtype=torch.uint8, device=dev)
     recv_count = torch.empty(num_experts, dtype=torch.int64, device=dev)
@@ -424,6 +501,6 @@ def low_latency_combine(x, topk_idx: torch.Tensor, topk_weights: torch.Tensor, h
         raise EpError(EP_ERR_INVALID_ARG, "topk_idx does not match the one given to dispatch")
     T, H = handle.topk_idx_shape[0], handle.hidden
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=topk_weights.device)
-    ep_combine(handle.c, x, in_quant, H, topk_weights, out)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=handle.workspace.device)
+    ep_combine(handle.c, x, in_quant, H, topk_idx, topk_weights, out)
     return out, None, None

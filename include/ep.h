@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 2
+#define EP_ABI_VERSION 3
 
 typedef enum {
   EP_OK = 0,
@@ -123,10 +123,14 @@ typedef struct {
   uint32_t *status;       /* device [1]: EP_STATUS_* bits                    */
 } ep_handle_t;
 
-/* Status bits written by the layout calls into *handle.status. */
+/* Status bits of *handle.status.  The layout calls write the word (bits 0
+ * and 1); ep_combine ORs in bit 2, which then stays set until the next layout
+ * call on the same workspace. */
 #define EP_STATUS_ID_OUT_OF_RANGE 1u   /* some id outside [-1, E), dropped     */
 #define EP_STATUS_CAPACITY_OVERFLOW 2u /* some expert got more pairs than its  */
                                        /* capacity; the later ones dropped     */
+#define EP_STATUS_COMBINE_MISMATCH 4u  /* ep_combine was given a topk_idx that */
+                                       /* does not match the handle's layout   */
 
 /* Bytes of workspace ep_layout needs for the given capacity; 0 if the
  * arguments are out of range.  Host-only; no device work. */
@@ -235,6 +239,11 @@ ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, i
  *   handle          host, from the ep_layout of the matching dispatch
  *   expert_out      device receive-format buffer (format above, rows =
  *                   max_rows) of in_quant, 16-byte aligned
+ *   hidden          H, as for ep_dispatch
+ *   topk_idx        device [T, k] of idx_dtype: the ids given to the layout
+ *                   call that made the handle (low_latency_combine
+ *                   Parameters: topk_idx must match dispatch).  Aligned to
+ *                   its dtype; may be NULL when T == 0.
  *   topk_weights    device float32 [T, k], required
  *   out             device bf16 [T, H], 16-byte aligned, written
  * out[t] = bf16_rne( sum over j = 0..k-1 with slot[t, j] >= 0 of
@@ -244,10 +253,14 @@ ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, i
  * times their float32 scale (one rounding); MX and per-128 e8m0 codes times
  * 2^(byte-127) (exact unless the product leaves float32's range); e8m0 byte
  * 0xFF is NaN.
- * The routing comes from the handle (the topk_idx that produced it). */
+ * The rows reduced are the handle's.  The kernel checks topk_idx against
+ * them: pair (t, j) with a valid id e must sit in expert e's block (or be
+ * dropped, slot -1, when blocks have a capacity) and a pair with any other
+ * id must hold no row.  A pair that fails sets EP_STATUS_COMBINE_MISMATCH
+ * (read it with ep_read_status); the output is still the handle's sum. */
 ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t expert_out_bytes,
-                       ep_quant_t in_quant, int32_t hidden, const float *topk_weights, void *out,
-                       void *stream);
+                       ep_quant_t in_quant, int32_t hidden, const void *topk_idx, ep_idx_dtype_t idx_dtype,
+                       const float *topk_weights, void *out, void *stream);
 
 /* Backward of combine with respect to the expert outputs, as a reverse
  * dispatch ("EP dispatch with unfused MXFP8 quantization", Description and
@@ -329,7 +342,8 @@ ep_status_t ep_moe_gmm2(const ep_handle_t *handle, const int64_t *recv_count, co
                         size_t a_buf_bytes, int32_t inter, int32_t hidden, const void *w2,
                         const void *w2_scales, void *out_buf, size_t out_buf_bytes, void *stream);
 
-/* Waits for `stream` and copies the status word of `handle` to host *flags. */
+/* Waits for `stream` and copies the status word of `handle` (EP_STATUS_*
+ * bits) to host *flags. */
 ep_status_t ep_read_status(const ep_handle_t *handle, uint32_t *flags, void *stream);
 
 /* Text of the last failed check or runtime error on the calling thread. */

@@ -70,8 +70,10 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     xv = mag.view(np.float32).astype(np.float64)
     vlo = _bf16_value(lo)
     vhi = np.where(hi == 0x7F80, 2.0 ** 128, _bf16_value(np.minimum(hi, 0x7F80)))
-    dlo = xv - vlo
-    dhi = vhi - xv
+    # infinite inputs give inf - inf here; they are handled by `is_inf` below
+    with np.errstate(invalid="ignore"):
+        dlo = xv - vlo
+        dhi = vhi - xv
     take_hi = (dhi < dlo) | ((dhi == dlo) & ((lo & np.uint32(1)) == 1))
     take_hi &= mag != (lo << np.uint32(16))         # exact values stay put
     res = np.where(take_hi, hi, lo)

@@ -281,7 +281,9 @@ def dequantize_row(mode: str, data: np.ndarray, scales: np.ndarray, hidden: int)
     if mode in ("fp8_b128", "fp8_b128_pow2"):
         s = np.repeat(scales.view("<f4").astype(np.float32), 128)
         val = codecs.e4m3_decode(data).astype(np.float32)     # exact
-        return (val * s).astype(np.float32)
+        # a power-of-two scale can take a code past float32's range: +-inf (IEEE)
+        with np.errstate(over="ignore"):
+            return (val * s).astype(np.float32)
     if mode == "fp8_b128_ue8m0":
         sc = np.repeat(codecs.e8m0_decode(scales), 128)
         with np.errstate(over="ignore", invalid="ignore"):

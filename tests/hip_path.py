@@ -132,9 +132,13 @@ def run_path(ep, w: W.Workload, inp: dict, *, expert_out: np.ndarray | None = No
             y[lay["row_src"] < 0] = NAN_BF16             # rows holding no pair: canaries
             src, q = to_dev(y).view(torch.uint8).reshape(-1), "none"
         o = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
-        ep.ep_combine(h, src, q, w.H, wts, o, interleaved=il)
+        ep.ep_combine(h, src, q, w.H, to_dev(inp["topk_idx"]), wts, o, interleaved=il)
         torch.cuda.synchronize()
         out = bf16_bits(o)
+        # the ids given to combine are dispatch's: the routing check must
+        # leave the layout's status word as it was
+        after = ep.ep_read_status(h)
+        assert after == lay["status"], f"combine changed the status word {lay['status']:#x} -> {after:#x}"
     return HipRun(h, ws, lay["recv_count"], lay["offsets"], lay["slot"], lay["row_src"], lay["status"],
                   recv, recv_w, out)
 
@@ -167,16 +171,32 @@ def recv_rows(ep, run: HipRun, w: W.Workload, rows=None):
     return data.cpu().numpy(), scales.cpu().numpy()
 
 
-def sample_tokens(w: W.Workload, idx: np.ndarray, n: int = 48, seed: int = 0) -> np.ndarray:
-    """First and last tokens, random ones, and some routed to the busiest expert."""
+LAYOUT_CHUNK_PAIRS = 2048   # pairs per workgroup of the multi-workgroup layout
+
+
+def sample_tokens(w: W.Workload, idx: np.ndarray, n: int = 640, seed: int = 0, window: int = 256,
+                  hot_cap: int = 256) -> np.ndarray:
+    """Tokens to compare at full size: the first and last 8, `n` random ones,
+    every token of two `window`-token spans centred on boundaries between
+    the layout's 2048-pair chunks (the middle one and the last one), and up
+    to `hot_cap` tokens routed to the busiest expert (evenly spaced, its
+    first and last included).  At 4096 tokens and more this is over 1024
+    tokens."""
     rng = np.random.default_rng(seed)
     T = w.T
     picks = set(range(min(8, T))) | set(range(max(0, T - 8), T))
     picks |= set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    chunk_tokens = max(LAYOUT_CHUNK_PAIRS // max(w.k, 1), 1)
+    nchunks = (T + chunk_tokens - 1) // chunk_tokens
+    if nchunks > 1 and window > 0:
+        for b in sorted({chunk_tokens * (nchunks // 2), chunk_tokens * (nchunks - 1)}):
+            picks |= set(range(max(0, b - window // 2), min(T, b + window // 2)))
     flat = idx.reshape(-1)
     valid = flat[(flat >= 0) & (flat < w.E)]
-    if valid.size:
+    if valid.size and hot_cap > 0:
         hot = np.bincount(valid, minlength=w.E).argmax()
         hot_tok = np.nonzero((idx == hot).any(axis=1))[0]
-        picks |= set(hot_tok[:8].tolist()) | set(hot_tok[-8:].tolist())
+        if hot_tok.size > hot_cap:
+            hot_tok = hot_tok[np.unique(np.linspace(0, hot_tok.size - 1, hot_cap).round().astype(np.int64))]
+        picks |= set(hot_tok.tolist())
     return np.array(sorted(picks), np.int64)

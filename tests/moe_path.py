@@ -47,7 +47,7 @@ def gpu_moe(ep, w: W.MoeWorkload, inp: dict, *, out_quant="mxfp8", pass_count=Tr
     y = canary_buffer(rows * w.H * 2)
     ep.ep_moe_gmm2(h, a, w.I, w.H, w2c, w2s, y, recv_count=rc if pass_count else None)
     out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
-    ep.ep_combine(h, y, "none", w.H, to_dev(inp["topk_weights"]), out)
+    ep.ep_combine(h, y, "none", w.H, idx, to_dev(inp["topk_weights"]), out)
     torch.cuda.synchronize()
     res.update(y=y, out=bf16_bits(out))
     return res

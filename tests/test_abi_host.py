@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(ep):
 
 
 def test_abi_version(ep):
-    assert ep.ep_abi_version() == 2
+    assert ep.ep_abi_version() == 3
 
 
 FAKE = 1 << 40          # 256-byte aligned, never dereferenced on the host
@@ -205,15 +205,20 @@ COMBINE_BAD = [
     (dict(in_bytes=5), 3), (dict(w=None), 1), (dict(out=None), 1), (dict(out=FAKE + 2), 1),
     (dict(hidden=128 + 32, quant=2), 1), (dict(hidden=128 + 64, quant=5), 1), (dict(hidden=96, quant=6), 1),
     (dict(quant=7), 1),
+    # topk_idx must be the dispatch ids: present, of a known dtype, aligned to it
+    (dict(idx=None), 1), (dict(idx_dtype=2), 1), (dict(idx_dtype=-1), 1), (dict(idx=FAKE + 4), 1),
+    (dict(idx=FAKE + 2, idx_dtype=0), 1), (dict(idx=FAKE + 4, idx_dtype=0), None),
 ]
 
 
 @pytest.mark.parametrize("kw,code", COMBINE_BAD)
 def test_combine_rejects(ep, kw, code):
+    if code is None:
+        pytest.skip("valid arguments (int32 ids need only 4-byte alignment): would launch")
     h = _handle(ep)
     rc = ep._lib.ep_combine(ctypes.byref(h), kw.get("inp", FAKE), kw.get("in_bytes", 1 << 30),
-                            kw.get("quant", 0), kw.get("hidden", 256), kw.get("w", FAKE), kw.get("out", FAKE),
-                            None)
+                            kw.get("quant", 0), kw.get("hidden", 256), kw.get("idx", FAKE), kw.get("idx_dtype", 1),
+                            kw.get("w", FAKE), kw.get("out", FAKE), None)
     assert rc == code, ep.ep_last_error()
     assert ep.ep_last_error().startswith("ep_combine")
 

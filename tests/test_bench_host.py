@@ -22,7 +22,7 @@ def test_large_workload_bytes_by_hand():
     T, H, k, E = 16384, 7168, 8, 256
     assert b["layout"] == T * k * 8 + E * 8 + (E + 1) * 4 + T * k * 4 + R * 4
     assert b["dispatch"] == 2 * T * H + T * k * 4 + R * (H // 2 + H // 32)      # 3584 codes + 224 scale bytes
-    assert b["combine"] == R * 2 * H + T * k * 8 + 2 * T * H                      # bf16 expert rows in
+    assert b["combine"] == R * 2 * H + T * k * (8 + 4) + 2 * T * H                # bf16 rows, int64 ids, weights
     assert b["total"] == b["layout"] + b["dispatch"] + b["combine"]
 
 

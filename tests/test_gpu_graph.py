@@ -49,9 +49,9 @@ def test_graph_replays_match_eager(ep, name, fused):
             h = ep.ep_layout(idx, w.E, w.t_max, rc, ws)
             ep.ep_dispatch(h, x, w.H, w.mode, recv)
         if y is None:
-            ep.ep_combine(h, recv, w.mode if w.combine_input == "identity" else "none", w.H, wts, out)
+            ep.ep_combine(h, recv, w.mode if w.combine_input == "identity" else "none", w.H, idx, wts, out)
         else:
-            ep.ep_combine(h, y, "none", w.H, wts, out)
+            ep.ep_combine(h, y, "none", w.H, idx, wts, out)
         return h
 
     h = path()

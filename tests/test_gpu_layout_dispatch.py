@@ -108,6 +108,30 @@ def test_out_of_range_ids_set_status(ep):
     assert run.slot[3, 1] == -1 and run.slot[7, 0] == -1 and run.slot[20, 3] == -1 and run.slot[21, 2] == -1
 
 
+@pytest.mark.parametrize("T,tmax", [(128, 16384), (0, 4096), (1, 2048)])
+def test_capacity_far_above_tokens(ep, T, tmax):
+    """A decode-sized batch with a large num_max_dispatch_tokens: the one
+    launch leaves up to 131072 rows free, cleared by every span workgroup
+    (or, with no token, by the layout workgroup); row_src and the whole
+    receive buffer equal those of the separate calls."""
+    _announce(f"layout_dispatch T={T} t_max={tmax}")
+    w = W.Workload("tmax", T, 7168, 256, 8, "int64", "fp8_b128", "uniform", neg_frac=0.1, seed=83,
+                   num_max_tokens=tmax)
+    inp = W.make_inputs(w)
+    x, wts = to_dev(inp["x"]), to_dev(inp["topk_weights"])
+    total, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    ra, rb = canary_buffer(total), canary_buffer(total)
+    ha, wsa, rca = run_layout_dispatch(ep, w, inp["topk_idx"], x, wts, ra, None)
+    hb, wsb, rcb = run_layout(ep, w, inp["topk_idx"])
+    ep.ep_dispatch(hb, x, w.H, w.mode, rb)
+    la, lb = read_layout(ep, ha, wsa, rca, w), read_layout(ep, hb, wsb, rcb, w)
+    for key in ("recv_count", "offsets", "slot", "row_src"):
+        assert np.array_equal(la[key], lb[key]), key
+    assert np.all(la["row_src"][T * w.k:] == -1)
+    assert la["status"] == lb["status"]
+    assert torch.equal(ra, rb)
+
+
 def test_same_bytes_as_separate_calls(ep):
     """Whole receive buffer (canaries of unused rows included), receive
     weights, layout arrays and running statistics equal those of
