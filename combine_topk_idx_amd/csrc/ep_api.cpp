@@ -15,6 +15,7 @@
 #include "common.hpp"
 #include "dispatch.hpp"
 #include "moe.hpp"
+#include "static_ws.hpp"
 
 namespace {
 
@@ -296,6 +297,32 @@ ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, i
                               num_max_dispatch_tokens, num_experts, row_align, expert_capacity, recv_count,
                               cumulative_recv_stats, workspace, workspace_bytes, x, hidden, topk_weights, quant,
                               recv_buf, recv_buf_bytes, recv_weights, handle, stream);
+}
+
+ep_status_t ep_layout_dispatch_noalloc(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                                       int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts,
+                                       int32_t row_align, int32_t expert_capacity, int64_t *recv_count,
+                                       int32_t *cumulative_recv_stats, const void *x, int32_t hidden,
+                                       const float *topk_weights, ep_quant_t quant, void *recv_buf,
+                                       size_t recv_buf_bytes, float *recv_weights, ep_handle_t *handle,
+                                       void *stream) {
+  const char *fn = "ep_layout_dispatch_noalloc";
+  // the workspace this layout needs, against the library's static one
+  // (argument errors are reported by the shared checks below)
+  const int64_t rows = ep_layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity);
+  if (rows >= 0) {
+    const size_t need = ep::workspace_layout(num_max_dispatch_tokens, num_topk, num_experts, rows).total;
+    if (need > ep::static_workspace_bytes())
+      return fail(EP_ERR_BUFFER_TOO_SMALL, "%s: the layout needs %zu bytes of workspace, the static one holds %zu",
+                  fn, need, ep::static_workspace_bytes());
+  }
+  void *ws = nullptr;
+  const hipError_t e = ep::static_workspace(&ws);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return layout_dispatch_impl(fn, topk_idx, idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens, num_experts,
+                              row_align, expert_capacity, recv_count, cumulative_recv_stats, ws,
+                              ep::static_workspace_bytes(), x, hidden, topk_weights, quant, recv_buf,
+                              recv_buf_bytes, recv_weights, handle, stream);
 }
 
 ep_status_t ep_combine(const ep_handle_t *handle, const void *expert_out, size_t expert_out_bytes,

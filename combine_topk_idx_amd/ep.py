@@ -2,7 +2,8 @@
 
 The functions ``ep_workspace_bytes``, ``ep_workspace_bytes_ex``,
 ``ep_layout_rows``, ``ep_buffer_bytes``, ``ep_layout``, ``ep_layout_ex``,
-``ep_dispatch``, ``ep_layout_dispatch``, ``ep_combine``, ``ep_combine_backward``,
+``ep_dispatch``, ``ep_layout_dispatch``, ``ep_layout_dispatch_noalloc``,
+``ep_combine``, ``ep_combine_backward``,
 ``ep_moe_packed_bytes``, ``ep_moe_pack_weights``, ``ep_moe_gmm1``,
 ``ep_moe_gmm2``, ``ep_read_status``,
 ``ep_last_error`` and ``ep_abi_version`` have the names and arguments of the C ABI in
@@ -42,9 +43,10 @@ EP_STATUS_CAPACITY_OVERFLOW = 2
 EP_STATUS_COMBINE_MISMATCH = 4
 
 SYMBOLS = ("ep_workspace_bytes", "ep_workspace_bytes_ex", "ep_layout_rows", "ep_buffer_bytes", "ep_layout",
-           "ep_layout_ex", "ep_dispatch", "ep_layout_dispatch", "ep_combine",
+           "ep_layout_ex", "ep_dispatch", "ep_layout_dispatch", "ep_layout_dispatch_noalloc", "ep_combine",
            "ep_combine_backward", "ep_moe_packed_bytes", "ep_moe_pack_weights", "ep_moe_gmm1", "ep_moe_gmm2",
            "ep_read_status", "ep_last_error", "ep_abi_version")
+STATIC_WORKSPACE_BYTES = 4 << 20   # the static workspace of ep_layout_dispatch_noalloc
 
 
 class ep_handle_t(ctypes.Structure):
@@ -83,6 +85,10 @@ _lib.ep_dispatch.restype = ctypes.c_int
 _lib.ep_layout_dispatch.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _sz,
                                     _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp, ctypes.POINTER(ep_handle_t), _vp]
 _lib.ep_layout_dispatch.restype = ctypes.c_int
+_lib.ep_layout_dispatch_noalloc.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
+                                            _vp, _i32, _vp, ctypes.c_int, _vp, _sz, _vp, ctypes.POINTER(ep_handle_t),
+                                            _vp]
+_lib.ep_layout_dispatch_noalloc.restype = ctypes.c_int
 _lib.ep_combine.argtypes = [ctypes.POINTER(ep_handle_t), _vp, _sz, ctypes.c_int, _i32, _vp, ctypes.c_int, _vp, _vp,
                             _vp]
 _lib.ep_combine.restype = ctypes.c_int
@@ -296,6 +302,28 @@ def ep_layout_dispatch(topk_idx, num_experts: int, num_max_dispatch_tokens: int,
                                    _nbytes(workspace) if isinstance(workspace, torch.Tensor) else 0,
                                    _ptr(x), hidden, _ptr(topk_weights), _quant(quant, interleaved), _ptr(recv_buf),
                                    nbytes, _ptr(recv_weights), ctypes.byref(h), _stream(stream)))
+    return h
+
+
+def ep_layout_dispatch_noalloc(topk_idx, num_experts: int, num_max_dispatch_tokens: int, recv_count, x,
+                               hidden: int, quant, recv_buf, topk_weights=None, recv_weights=None,
+                               cumulative_recv_stats=None, *, row_align: int = 1, expert_capacity: int = 0,
+                               num_tokens=None, num_topk=None, idx_dtype=None, recv_buf_bytes=None,
+                               interleaved=False, stream=None) -> ep_handle_t:
+    """ep_layout_dispatch with the library's static workspace (no workspace
+    argument, nothing allocated).  The handle is valid until the next call of
+    this function on the same device."""
+    num_tokens, num_topk, idx_dtype = _idx_args(topk_idx, num_tokens, num_topk, idx_dtype)
+    rows = max(ep_layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity), 0)
+    _check_args(*_layout_specs(topk_idx, num_experts, recv_count, None, cumulative_recv_stats),
+                *_dispatch_specs(num_tokens, num_topk, rows, x, hidden, recv_buf, topk_weights, recv_weights))
+    nbytes = _nbytes(recv_buf) if recv_buf_bytes is None else recv_buf_bytes
+    h = ep_handle_t()
+    _check(_lib.ep_layout_dispatch_noalloc(_ptr(topk_idx), idx_dtype, num_tokens, num_topk, num_max_dispatch_tokens,
+                                           num_experts, row_align, expert_capacity, _ptr(recv_count),
+                                           _ptr(cumulative_recv_stats), _ptr(x), hidden, _ptr(topk_weights),
+                                           _quant(quant, interleaved), _ptr(recv_buf), nbytes, _ptr(recv_weights),
+                                           ctypes.byref(h), _stream(stream)))
     return h
 
 

@@ -234,6 +234,30 @@ ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, i
                                void *recv_buf, size_t recv_buf_bytes, float *recv_weights,
                                ep_handle_t *handle, void *stream);
 
+/* ep_layout_dispatch for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call without the workspace arguments.  The
+ * workspace is the library's own static device array of 4 MiB (4194304
+ * bytes) per GPU, held from the first call until the process ends; a layout
+ * whose ep_workspace_bytes_ex(num_max_dispatch_tokens, num_topk,
+ * num_experts, row_align, expert_capacity) exceeds it returns
+ * EP_ERR_BUFFER_TOO_SMALL and launches nothing (4 MiB holds a compact
+ * layout of up to 465472 (token, j) pairs with 512 experts, e.g. 58184
+ * tokens at top-8, and 493120 with 256 experts).  The call allocates nothing
+ * (no hipMalloc, no allocating library routine); it uses the current
+ * device's array.  Every call on one device shares that array and leaves
+ * its contents behind: the returned handle (its offsets, slot, row_src and
+ * status point into the array) is valid until the next call of this
+ * function on the same device, and calls that overlap on one device (other
+ * streams or threads) race.  Results are those of ep_layout_dispatch. */
+ep_status_t ep_layout_dispatch_noalloc(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
+                                       int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts,
+                                       int32_t row_align, int32_t expert_capacity, int64_t *recv_count,
+                                       int32_t *cumulative_recv_stats, const void *x, int32_t hidden,
+                                       const float *topk_weights, ep_quant_t quant, void *recv_buf,
+                                       size_t recv_buf_bytes, float *recv_weights, ep_handle_t *handle,
+                                       void *stream);
+
 /* Combine ("Low-Latency Mode API", low_latency_combine; "DeepEP FP8 Dispatch
  * and Combine Operations", The FP8 Combine Operation).
  *   handle          host, from the ep_layout of the matching dispatch

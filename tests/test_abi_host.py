@@ -334,3 +334,16 @@ def test_moe_gmm2_rejects(ep):
     assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 1 << 30, 96, 256, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 1 << 30, 192, 256, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert ep._lib.ep_moe_gmm2(ctypes.byref(h), None, FAKE, 8, 128, 256, FAKE, FAKE, FAKE, 1 << 30, None) == 3
+
+
+def test_noalloc_refuses_a_layout_beyond_its_static_workspace(ep):
+    """ep_layout_dispatch_noalloc: num_max_dispatch_tokens * k = 2^20 pairs
+    needs over 8 MiB of workspace, more than the library's static 4 MiB; the
+    call returns EP_ERR_BUFFER_TOO_SMALL before touching the device."""
+    tmax, k, E = 1 << 17, 8, 256
+    assert ep.ep_workspace_bytes(tmax, k, E) > ep.STATIC_WORKSPACE_BYTES
+    h = ep.ep_handle_t()
+    rc = ep._lib.ep_layout_dispatch_noalloc(FAKE, 1, 16, k, tmax, E, 1, 0, FAKE, None, FAKE, 7168, None, 3, FAKE,
+                                            1 << 40, None, ctypes.byref(h), None)
+    assert rc == ep.EP_ERR_BUFFER_TOO_SMALL
+    assert ep.ep_last_error().startswith("ep_layout_dispatch_noalloc") and "static" in ep.ep_last_error()
