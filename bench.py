@@ -281,6 +281,115 @@ def graph_steps(runners, steps: int, stream) -> float:
     return start.elapsed_time(end) / steps
 
 
+def probes_main(args) -> int:
+    """Floors and ceilings of the path's access patterns, from the probe
+    kernels of libep_probe.so (an empty grid, combine's gather with no
+    dequantisation, 16-byte streams); one JSON line.  Decode-sized probes are
+    timed as graph replays over rotating buffer sets (cache-cold, no host
+    cost per launch), the large ones as stream launches between events."""
+    import ctypes
+    import numpy as np
+    import torch
+    from combine_topk_idx_amd import build as B
+
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    vp = ctypes.c_void_p
+    lib.ep_probe_empty.argtypes = [ctypes.c_int, ctypes.c_int, vp]
+    lib.ep_probe_gather.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.ep_probe_stream.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int, vp]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cur = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError("probe launch failed")
+
+    def graph_ms(calls, reps):
+        """ms per call: `reps` calls (rotating over `calls`) in one graph."""
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                calls[i % len(calls)]()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def stream_ms(call, reps):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    res = {}
+    T, k, H, rows = 128, 8, 7168, 1024                 # the decode workload: 896 span workgroups
+    chunks = (H // 8 + 127) // 128
+    for name, blocks in (("empty_1wg", 1), ("empty_decode_combine_grid", T * chunks),
+                         ("empty_decode_layout_dispatch_grid", T * chunks + 1)):
+        res[name] = {"us": round(1e3 * graph_ms([lambda b=blocks: ok(lib.ep_probe_empty(b, 128, cur()))], 200), 3),
+                     "grid": blocks}
+    rng = np.random.default_rng(7)
+    nsets = 42                                       # > 1 GB of rows over the sets, as the decode bench
+    sets = []
+    for _ in range(nsets):
+        sl = rng.permutation(rows)[: T * k].astype(np.int32)
+        sl[rng.choice(T * k, size=round(0.1 * T * k), replace=False)] = -1
+        sets.append({"rows": torch.empty((rows, H), dtype=torch.bfloat16, device=dev).normal_(),
+                     "slot": torch.from_numpy(sl).to(dev),
+                     "slot1": torch.from_numpy(sl.reshape(T, k)[:, :1].copy()).to(dev),
+                     "out": torch.empty((T, H), dtype=torch.bfloat16, device=dev)})
+    for kk in (1, 8):
+        calls = [lambda s=s, kk=kk: ok(lib.ep_probe_gather(s["rows"].data_ptr(), s["slot" if kk == 8 else "slot1"]
+                                                           .data_ptr(), T, kk, H, s["out"].data_ptr(), cur()))
+                 for s in sets]
+        ms = graph_ms(calls, 210)
+        R = int((sets[0]["slot"] >= 0).sum()) if kk == 8 else T
+        nbytes = R * 2 * H + T * kk * 4 + 2 * T * H
+        res[f"gather_decode_k{kk}"] = {"us": round(1e3 * ms, 3), "bytes": nbytes,
+                                       "gbps": round(nbytes / ms / 1e6, 1)}
+    del sets
+    torch.cuda.empty_cache()
+    # the large workload's combine pattern: 16384 tokens, 8 random rows each
+    T, rows = 16384, 131072
+    y = torch.empty((rows, H), dtype=torch.bfloat16, device=dev).normal_()
+    sl = rng.permutation(rows).astype(np.int32)
+    sl[rng.choice(rows, size=round(0.05 * rows), replace=False)] = -1
+    slot = torch.from_numpy(sl).to(dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ms = stream_ms(lambda: ok(lib.ep_probe_gather(y.data_ptr(), slot.data_ptr(), T, 8, H, out.data_ptr(), cur())), 20)
+    R = int((slot >= 0).sum())
+    nbytes = R * 2 * H + T * 8 * 4 + 2 * T * H
+    res["gather_large_k8"] = {"us": round(1e3 * ms, 2), "bytes": nbytes, "gbps": round(nbytes / ms / 1e6, 1)}
+    del y, out
+    torch.cuda.empty_cache()
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    for mode, name, moved in ((0, "read_1GiB", n), (1, "write_1GiB", n), (2, "copy_1GiB", 2 * n)):
+        best = None
+        for blocks in (1024, 2048, 4096, 8192, 16384, 65536):   # the best grid of each stream
+            ms = stream_ms(lambda m=mode, b=blocks: ok(lib.ep_probe_stream(m, src.data_ptr(), dst.data_ptr(), n, b,
+                                                                           cur())), 10)
+            if best is None or ms < best[0]:
+                best = (ms, blocks)
+        ms, blocks = best
+        res[name] = {"us": round(1e3 * ms, 1), "bytes": moved, "gbps": round(moved / ms / 1e6, 1), "grid": blocks}
+    print(json.dumps({"probes": res, "peak_gbps": HBM_PEAK_GBPS}), flush=True)
+    return 0
+
+
 def backward_main(args) -> int:
     """layout + ep_combine_backward on one workload's routing; one JSON line."""
     if args.gpus != 1:
@@ -546,6 +655,28 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str, moe: bool, copy_m
             "traffic_over_alg": m["bytes"] / m["alg_bytes"], "kernels": kernels}
 
 
+def trace_summary(path: str) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace --stats --output-format
+    csv run (its *kernel_stats.csv): calls and average / min / max duration
+    per kernel, longest total first."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *kernel_stats.csv under {path}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                   f"{float(r['MaxNs']) / 1e3:.2f} |")
+    return "\n".join(out)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -578,6 +709,11 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as one captured HIP graph (no per-call host cost) instead of stream "
                          "launches")
+    ap.add_argument("--probes", action="store_true",
+                    help="time the probe kernels of libep_probe.so: launch floors at decode grids, combine's "
+                         "gather pattern at decode and large sizes, 1 GiB read / write / copy streams")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="no GPU work: markdown table of a rocprofv3 --kernel-trace --stats csv run under DIR")
     ap.add_argument("--pmc-summary", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench (with --copy-probe-mib) into HBM bytes per launch; prints JSON")
@@ -591,10 +727,15 @@ def main() -> int:
     if args.cpu_baseline_moe_child:
         cpu_baseline_moe_child(args.cpu_baseline_moe_child, args.cpu_tokens)
         return 0
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
     if args.pmc_summary:
         d = pmc_summary(*args.pmc_summary, args.moe or args.workload, bool(args.moe), args.copy_probe_mib or 1024)
         print(json.dumps(d, indent=1))
         return 0
+    if args.probes:
+        return probes_main(args)
     if args.combine_backward:
         return backward_main(args)
     if args.moe:

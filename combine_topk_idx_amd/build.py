@@ -22,6 +22,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libep.so")
+PROBE_LIB = os.path.join(HERE, "libep_probe.so")   # measurement probes of bench.py --probes
+PROBE_SOURCES = ["probes.hip"]
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "moe.hip", "static_ws.hip", "ep_api.cpp"]
 
@@ -46,22 +48,30 @@ def _compile(src: str, build_dir: str, defines: tuple) -> str:
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
-    """Compile every source and link the library (default: libep.so next to
-    this file; ``defines`` are extra -D macros, e.g. launch-shape overrides
-    from csrc/tuning.hpp); returns the library path."""
-    build_dir = BUILD if out == LIB else out + ".build"
-    os.makedirs(build_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, tuple(defines)), SOURCES))
+def _link(objs: list, out: str) -> None:
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+
+
+def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+    """Compile every source and link the library (default: libep.so next to
+    this file; ``defines`` are extra -D macros, e.g. launch-shape overrides
+    from csrc/tuning.hpp); returns the library path.  The default build also
+    links the measurement probes of ``bench.py --probes`` (libep_probe.so)."""
+    build_dir = BUILD if out == LIB else out + ".build"
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = SOURCES + (PROBE_SOURCES if out == LIB else [])
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, build_dir, tuple(defines)), srcs)))
+    _link([objs[s] for s in SOURCES], out)
+    if out == LIB:
+        _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {out}")
+        print(f"built {out}" + (f" and {PROBE_LIB}" if out == LIB else ""))
     return out
 
 

@@ -10,10 +10,6 @@ from combine_topk_idx_amd import workloads as W
 from oracle import combine as OC, dispatch as OD, layout as OL, moe as OM
 from tests.hip_path import DEV, canary_buffer, ws_view, to_dev, bf16_bits
 
-# the matrix cores add each 64-product block with about 3e-4 of its sum of
-# |products| (worst seen over random full-range e4m3 inputs); 5e-4 leaves margin
-MFMA_REL = 5e-4
-
 
 def gpu_moe(ep, w: W.MoeWorkload, inp: dict, *, out_quant="mxfp8", pass_count=True, row_align=1,
             expert_capacity=0, stop_after=None):
