@@ -67,10 +67,16 @@ def _row_bytes(mode: str, H: int):
 
 
 def _source_hash(sources=KERNEL_SOURCES) -> str:
+    """Hash of the kernel sources' code: comments and whitespace are left
+    out, so that a comment edit does not retire measured counters."""
+    import re
     h = hashlib.sha256()
     for p in sources:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -386,6 +392,36 @@ def probes_main(args) -> int:
                 best = (ms, blocks)
         ms, blocks = best
         res[name] = {"us": round(1e3 * ms, 1), "bytes": moved, "gbps": round(moved / ms / 1e6, 1), "grid": blocks}
+    del dst
+    # the expert GEMMs' weight stream: every wave its own contiguous range in
+    # 2 KB steps, 4 or 8 steps in flight, one workgroup per CU (or two)
+    lib.ep_probe_wave_stream.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                         vp]
+    wout = torch.empty((4096, 16), dtype=torch.uint8, device=dev)
+    span = 512 << 20                                   # beyond the 256 MB last-level cache
+    for blocks, waves, depth, one in ((256, 6, 4, 1), (256, 6, 8, 1), (240, 6, 4, 1), (192, 6, 4, 1), (48, 6, 4, 1),
+                                      (256, 8, 4, 1), (256, 4, 4, 1), (512, 4, 4, 0), (512, 6, 4, 0)):
+        steps = span // (blocks * waves * 2048) // depth * depth
+        moved = blocks * waves * steps * 2048
+        ms = stream_ms(lambda b=blocks, wv=waves, st=steps, d=depth, o=one: ok(lib.ep_probe_wave_stream(
+            src.data_ptr(), b, wv, st, d, o, wout.data_ptr(), cur())), 10)
+        cus = blocks if one else blocks // 2
+        res[f"wave_stream_{blocks}x{waves}_d{depth}" + ("" if one else "_2perCU")] = {
+            "us": round(1e3 * ms, 1), "bytes": moved, "gbps": round(moved / ms / 1e6, 1),
+            "gbps_per_cu": round(moved / ms / 1e6 / cus, 1)}
+    # the matrix cores: back-to-back independent instructions on every wave,
+    # one workgroup per CU; a SIMD carries ceil(waves / 4) of them
+    lib.ep_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    mout = torch.empty(256 * 8 * 64, dtype=torch.float32, device=dev)
+    iters = 1000
+    for kind, name, flop in ((0, "mx_e4m3_32x32x64", 2 * 32 * 32 * 64), (1, "bf16_32x32x16", 2 * 32 * 32 * 16)):
+        for waves in (4, 6, 8):
+            ms = stream_ms(lambda k=kind, wv=waves: ok(lib.ep_probe_mfma_rate(k, 256, wv, iters, 1, mout.data_ptr(),
+                                                                              cur())), 5)
+            per_simd = -(-waves // 4) * iters * 8
+            res[f"mfma_{name}_{waves}waves"] = {
+                "us": round(1e3 * ms, 1), "tflops": round(256 * waves * iters * 8 * flop / ms / 1e9, 1),
+                "ns_per_instr_per_simd": round(1e6 * ms / per_simd, 2)}
     print(json.dumps({"probes": res, "peak_gbps": HBM_PEAK_GBPS}), flush=True)
     return 0
 
@@ -655,25 +691,45 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str, moe: bool, copy_m
             "traffic_over_alg": m["bytes"] / m["alg_bytes"], "kernels": kernels}
 
 
-def trace_summary(path: str) -> str:
+def _short_kernel_name(name: str) -> str:
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def trace_summary(path: str, by_grid: bool = False) -> str:
     """Markdown table of a rocprofv3 --kernel-trace --stats --output-format
-    csv run (its *kernel_stats.csv): calls and average / min / max duration
-    per kernel, longest total first."""
+    csv run: calls and average / min / max duration per kernel (from its
+    *kernel_stats.csv), longest total first; with by_grid, per kernel and
+    grid (workgroups x threads, from *kernel_trace.csv) with the median."""
     import csv
     import glob
-    files = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+
+    import numpy as np
+    pattern = "*kernel_trace.csv" if by_grid else "*kernel_stats.csv"
+    files = glob.glob(os.path.join(path, "**", pattern), recursive=True)
     if not files:
-        raise FileNotFoundError(f"no *kernel_stats.csv under {path}")
+        raise FileNotFoundError(f"no {pattern} under {path}")
     rows = []
     for f in files:
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
-    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    out = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    if not by_grid:
+        rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+        out = ["| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for r in rows:
+            out.append(f"| `{_short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                       f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        return "\n".join(out)
+    groups = {}
     for r in rows:
-        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
-        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                   f"{float(r['MaxNs']) / 1e3:.2f} |")
+        wg = int(r["Workgroup_Size_X"])
+        key = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(wg, 1), wg)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| kernel | workgroups x threads | calls | avg us | median us | min us | max us |",
+           "|---|---|---|---|---|---|---|"]
+    for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(d)
+        out.append(f"| `{key[0]}` | {key[1]} x {key[2]} | {a.size} | {a.mean():.2f} | {np.median(a):.2f} | "
+                   f"{a.min():.2f} | {a.max():.2f} |")
     return "\n".join(out)
 
 
@@ -711,9 +767,12 @@ def main() -> int:
                          "launches")
     ap.add_argument("--probes", action="store_true",
                     help="time the probe kernels of libep_probe.so: launch floors at decode grids, combine's "
-                         "gather pattern at decode and large sizes, 1 GiB read / write / copy streams")
+                         "gather pattern at decode and large sizes, 1 GiB read / write / copy streams, the "
+                         "GEMMs' per-wave weight stream")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
                     help="no GPU work: markdown table of a rocprofv3 --kernel-trace --stats csv run under DIR")
+    ap.add_argument("--by-grid", action="store_true",
+                    help="with --trace-summary: one row per kernel and grid, with the median")
     ap.add_argument("--pmc-summary", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "bench (with --copy-probe-mib) into HBM bytes per launch; prints JSON")
@@ -728,7 +787,7 @@ def main() -> int:
         cpu_baseline_moe_child(args.cpu_baseline_moe_child, args.cpu_tokens)
         return 0
     if args.trace_summary:
-        print(trace_summary(args.trace_summary))
+        print(trace_summary(args.trace_summary, args.by_grid))
         return 0
     if args.pmc_summary:
         d = pmc_summary(*args.pmc_summary, args.moe or args.workload, bool(args.moe), args.copy_probe_mib or 1024)

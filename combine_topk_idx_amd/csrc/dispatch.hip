@@ -177,9 +177,9 @@ __device__ __forceinline__ u32x4 scale_bf16x8(const u32x4 &r, float w) {
 // to +-448 * 2^se before the rounding gives what clamping after it gives
 // (448 * 2^se is itself a bf16 value), so the clamped, rounded pairs go
 // straight to the scaled e4m3 conversion, which divides by 2^se exactly and
-// rounds to nearest even (checked on the device against the unscaled encoder
-// of the exact quotient for every finite bf16 pattern and every se; past
-// +-448 it would give NaN, hence the clamp).
+// rounds to nearest even (tests/test_gpu_codecs.py compares it with the
+// software encoder of the exact quotient for every finite bf16 pattern and
+// every se; past +-448 it would give NaN, hence the clamp).
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 template <int NT, int VPT, int KMAX, bool PACK>
 __device__ __forceinline__ void weighted_mxfp8_store(const u32x4 (&raw)[VPT], int v0, int nvec, const int (&s)[KMAX],

@@ -3,9 +3,11 @@
 // The formats are the OCP ones the "Low-Latency Mode API" page names for its
 // receive buffers (float8_e4m3fn data, float4_e2m1fn_x2 data, float8_e8m0fnu
 // scales) and IEEE bf16.  All roundings are round-to-nearest, ties to even.
-// The conversions use gfx950's hardware convert instructions; each wrapper
-// states the input range for which it was checked bit-exact, over every input
-// of that range, against a software implementation of the format definition.
+// The conversions use gfx950's hardware convert instructions.  Each wrapper
+// states the inputs it is exact for; tests/test_gpu_codecs.py runs every
+// wrapper over that whole domain (every code with every scale byte, every
+// finite bf16 with every scale exponent, every rounding tie) and compares it
+// bit for bit with the oracle's software codecs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -100,8 +102,8 @@ __device__ __forceinline__ void e4m3x8_decode_scaled(const u32x2 &w, float scale
 
 // 8 bf16 (4 words, element 2i in the low half of word i) divided by the power
 // of two `scale` and rounded to e2m1, nearest even, saturating at +-6, sign
-// kept.  One instruction per pair; exact for every bf16 input and every
-// scale 2^-127 .. 2^126.
+// kept.  One instruction per pair; exact for every finite bf16 input and
+// every scale 2^-127 .. 2^126.
 __device__ __forceinline__ uint32_t e2m1x8_encode_bf16(const u32x4 &r, float scale) {
   // copy the words to scalars first: bit-casting a vector element in place
   // makes this compiler pass element 0 to every call

@@ -12,9 +12,20 @@
 //   ep_probe_stream     grid-stride 16-byte accesses over n bytes: read only
 //                       (one 16-byte value per workgroup written), write only,
 //                       or copy
+//   ep_probe_wave_stream  each wave reads its own contiguous range in 2 KB
+//                       steps (two 1 KB loads per step) with a fixed number
+//                       of steps in flight -- the expert GEMMs' weight
+//                       stream, without the matrix-core work
+//   ep_probe_mfma_rate  back-to-back independent matrix-core instructions
+//                       (MX-scaled e4m3 32x32x64, or bf16 32x32x16) on
+//                       every wave of a grid: the sustained rate per SIMD
 //   ep_probe_mfma       one v_mfma_scale_f32_32x32x64_f8f6f4 step (e4m3 x
 //                       e4m3) per case: the raw float32 result of a given
 //                       64-product block, to check a model of its precision
+//   ep_probe_codec      the element converters of formats.hpp (and the
+//                       scaled bf16 -> e4m3 conversion of the weighted reverse
+//                       dispatch) over arrays of inputs, to check them against
+//                       software codecs over their whole input domains
 //
 // All pointers are device pointers; every call is asynchronous on `stream`.
 // Sizes are checked on the host (a call with a bad size launches nothing and
@@ -22,9 +33,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "formats.hpp"
+
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using ep::u32x2;
+
+using ep::u32x4;
 
 __global__ void empty_kernel() {}
 
@@ -99,8 +114,103 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4 *__restrict__ s
   }
 }
 
+// Each wave w of the grid reads steps x 2 KB from src + w * steps * 2 KB:
+// lane l loads bytes [16l, 16l + 16) and [1024 + 16l, ...) of every step,
+// DEPTH steps ahead; lane 0 of each wave writes the XOR of what it read to
+// out[w].  ONE_PER_CU reserves 96 KB of LDS, so that no two workgroups share
+// a CU (160 KB of LDS per CU).  steps is a multiple of DEPTH.
+template <int DEPTH, bool ONE_PER_CU>
+__global__ __launch_bounds__(1024) void wave_stream_kernel(const u32x4 *__restrict__ src, int steps,
+                                                           u32x4 *__restrict__ out) {
+  __shared__ u32x4 pad[ONE_PER_CU ? 6144 : 1];
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const u32x4 *p = src + w * (int64_t)steps * 128 + lane;
+  u32x4 r0[DEPTH], r1[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    r0[d] = __builtin_nontemporal_load(p + d * 128);
+    r1[d] = __builtin_nontemporal_load(p + d * 128 + 64);
+  }
+  u32x4 x = {0u, 0u, 0u, 0u};
+  for (int s = DEPTH; s < steps; s += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      x ^= r0[d] ^ r1[d];
+      r0[d] = __builtin_nontemporal_load(p + (int64_t)(s + d) * 128);
+      r1[d] = __builtin_nontemporal_load(p + (int64_t)(s + d) * 128 + 64);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) x ^= r0[d] ^ r1[d];
+  if (steps < 0) {                              // never taken: keeps the LDS reservation
+    pad[threadIdx.x % (ONE_PER_CU ? 6144 : 1)] = x;
+    __syncthreads();
+    x = pad[(threadIdx.x + 1) % (ONE_PER_CU ? 6144 : 1)];
+  }
+  if (lane == 0) out[w] = x;
+}
+
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Every wave issues iters x 8 matrix-core instructions on eight independent
+// accumulators (KIND 0: MX-scaled e4m3 32x32x64, scale bytes 127; KIND 1:
+// bf16 32x32x16) and writes one float per lane.  ONE_PER_CU reserves 96 KB
+// of LDS so that no two workgroups share a CU.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+template <int KIND, bool ONE_PER_CU>
+__global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, float *__restrict__ out) {
+  __shared__ float pad[ONE_PER_CU ? 24576 : 1];
+  const int l = threadIdx.x & 63;
+  v16f c[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {                  // distinct, so that no two chains can be merged
+    c[u] = v16f{};
+    c[u][0] = (float)(u + 8 * l);
+  }
+  if constexpr (KIND == 0) {
+    const int x = 0x38383838 ^ (l & 7) ^ (iters << 8);
+    const v8i a = {x, x + 1, x + 2, x + 3, x + 4, x + 5, x + 6, x + 7};
+    const v8i b = {x ^ 1, x ^ 2, x ^ 3, x ^ 4, x ^ 5, x ^ 6, x ^ 7, x};
+    v8i au[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) au[u] = a ^ u;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        c[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(au[u], b, c[u], 0, 0, 0, 127, 0, 127);
+    }
+  } else {
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = (__bf16)(float)(l + e + iters);
+      b[e] = (__bf16)(float)(l - e);
+    }
+    bf16x8 au[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      au[u] = a;
+      au[u][0] = (__bf16)(float)(u + l);
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(au[u], b, c[u], 0, 0, 0);
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum += c[u][e];
+  if (iters < 0) {                               // never taken: keeps the LDS reservation
+    pad[threadIdx.x] = sum;
+    __syncthreads();
+    sum = pad[(threadIdx.x + 1) % (ONE_PER_CU ? 24576 : 1)];
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
 
 // One case: row 0 of A holds a[0..63] and column 0 of B holds b[0..63]
 // (e4m3 codes), the K-blocks [0, 32) and [32, 64) scaled by the e8m0 bytes
@@ -142,9 +252,86 @@ __global__ __launch_bounds__(64) void mfma_kernel(const MfmaCase *__restrict__ c
   out[(size_t)blockIdx.x * 64 + l] = acc[0];
 }
 
+// Converter checks; thread i handles input group i (see ep_probe_codec).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 scaled_e4m3(const u32x4 &r, float scale) {
+  const uint32_t w0 = r.x, w1 = r.y, w2 = r.z, w3 = r.w;
+  s16x2 o0 = {0, 0}, o1 = {0, 0};
+  o0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o0, __builtin_bit_cast(ep::bf16x2, w0), scale, false);
+  o0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o0, __builtin_bit_cast(ep::bf16x2, w1), scale, true);
+  o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, __builtin_bit_cast(ep::bf16x2, w2), scale, false);
+  o1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o1, __builtin_bit_cast(ep::bf16x2, w3), scale, true);
+  return u32x2{__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1)};
+}
+
+__global__ void codec_kernel(int kind, const void *__restrict__ in, void *__restrict__ out, int64_t groups,
+                             float scale_arg) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= groups) return;
+  // the kernels compute their scales per lane, so the instructions read them
+  // from vector registers; kind 6 passes the same value as a scalar operand
+  float scale = scale_arg;
+  asm volatile("" : "+v"(scale));
+  switch (kind) {
+    case 0: {   // e4m3 encode: 8 float32 (already within +-448) -> 8 codes
+      const float *f = (const float *)in + 8 * i;
+      float v[8];
+      for (int e = 0; e < 8; ++e) v[e] = f[e];
+      ((u32x2 *)out)[i] = ep::e4m3x8_encode(v);
+      break;
+    }
+    case 1: {   // e4m3 decode scaled: (code | scale byte << 8) -> float32
+      const uint16_t c = ((const uint16_t *)in)[i];
+      float y[8];
+      ep::e4m3x8_decode_scaled(u32x2{(uint32_t)(c & 0xff), 0u}, ep::e8m0_decode(c >> 8), y);
+      ((float *)out)[i] = y[0];
+      break;
+    }
+    case 2: {   // e2m1 encode: 8 bf16 divided by `scale` -> 8 nibbles
+      ((uint32_t *)out)[i] = ep::e2m1x8_encode_bf16(((const u32x4 *)in)[i], scale);
+      break;
+    }
+    case 3: {   // e2m1 decode scaled: (nibble | scale byte << 8) -> float32
+      const uint16_t c = ((const uint16_t *)in)[i];
+      float y[8];
+      ep::e2m1x8_decode_scaled((uint32_t)(c & 0xf), ep::e8m0_decode(c >> 8), y);
+      ((float *)out)[i] = y[0];
+      break;
+    }
+    case 4: {   // bf16 pack: 2 float32 -> 2 bf16 in one word
+      const float *f = (const float *)in + 2 * i;
+      ((uint32_t *)out)[i] = ep::pack_bf16x2(f[0], f[1]);
+      break;
+    }
+    case 5:     // scaled e4m3 from bf16 (the reverse dispatch's conversion): 8 bf16 / `scale` -> 8 codes
+      ((u32x2 *)out)[i] = scaled_e4m3(((const u32x4 *)in)[i], scale);
+      break;
+    default:    // the same with the scale as a scalar operand
+      ((u32x2 *)out)[i] = scaled_e4m3(((const u32x4 *)in)[i], scale_arg);
+      break;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// kind 0: e4m3 encode, in float32[8 groups], out bytes[8 groups]
+// kind 1: e4m3 decode scaled, in uint16 (code | byte << 8)[groups], out float32[groups]
+// kind 2: e2m1 encode of bf16 / scale, in bf16[8 groups], out uint32 (8 nibbles)[groups]
+// kind 3: e2m1 decode scaled, in uint16 (nibble | byte << 8)[groups], out float32[groups]
+// kind 4: bf16 pack, in float32[2 groups], out uint32[groups]
+// kind 5: scaled e4m3 of bf16 / scale, in bf16[8 groups], out bytes[8 groups]
+// kind 6: kind 5 with the scale read from a scalar register
+// `scale` (kinds 2, 5 and 6) is the float32 power of two the instructions take.
+int ep_probe_codec(int kind, const void *in, void *out, int64_t groups, float scale, void *stream) {
+  if (kind < 0 || kind > 6 || groups <= 0 || groups > (int64_t)1 << 31) return -1;
+  const int threads = 256;
+  hipLaunchKernelGGL(codec_kernel, dim3((unsigned)((groups + threads - 1) / threads)), dim3(threads), 0,
+                     (hipStream_t)stream, kind, in, out, groups, scale);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 // cases: n records of 136 bytes (64 A codes, 64 B codes, 2 A scale bytes,
 // 2 B scale bytes, float32 c0); out: n * 64 floats, out[64 i] the result of
@@ -189,6 +376,43 @@ int ep_probe_stream(int mode, const void *src, void *dst, int64_t n, int blocks,
     hipLaunchKernelGGL(stream_kernel<1>, grid, block, 0, (hipStream_t)stream, (const u32x4 *)src, (u32x4 *)dst, n16);
   else
     hipLaunchKernelGGL(stream_kernel<2>, grid, block, 0, (hipStream_t)stream, (const u32x4 *)src, (u32x4 *)dst, n16);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// out: blocks * waves * 64 floats; kind 0 (MX e4m3) or 1 (bf16); waves 1..8.
+int ep_probe_mfma_rate(int kind, int blocks, int waves, int iters, int one_per_cu, float *out, void *stream) {
+  if (blocks <= 0 || waves <= 0 || waves > 8 || iters <= 0 || kind < 0 || kind > 1) return -1;
+  const dim3 grid((unsigned)blocks), block((unsigned)(64 * waves));
+  const hipStream_t st = (hipStream_t)stream;
+  if (kind == 0 && one_per_cu)
+    hipLaunchKernelGGL((mfma_rate_kernel<0, true>), grid, block, 0, st, iters, out);
+  else if (kind == 0)
+    hipLaunchKernelGGL((mfma_rate_kernel<0, false>), grid, block, 0, st, iters, out);
+  else if (one_per_cu)
+    hipLaunchKernelGGL((mfma_rate_kernel<1, true>), grid, block, 0, st, iters, out);
+  else
+    hipLaunchKernelGGL((mfma_rate_kernel<1, false>), grid, block, 0, st, iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// src: blocks * waves * steps * 2048 bytes; out: blocks * waves vectors;
+// waves 1..16, depth 4 or 8, steps a positive multiple of depth.
+int ep_probe_wave_stream(const void *src, int blocks, int waves, int steps, int depth, int one_per_cu, void *out,
+                         void *stream) {
+  if (blocks <= 0 || waves <= 0 || waves > 16 || steps <= 0 || (depth != 4 && depth != 8) || steps % depth != 0)
+    return -1;
+  const dim3 grid((unsigned)blocks), block((unsigned)(64 * waves));
+  const u32x4 *s = (const u32x4 *)src;
+  u32x4 *o = (u32x4 *)out;
+  const hipStream_t st = (hipStream_t)stream;
+  if (depth == 4 && one_per_cu)
+    hipLaunchKernelGGL((wave_stream_kernel<4, true>), grid, block, 0, st, s, steps, o);
+  else if (depth == 4)
+    hipLaunchKernelGGL((wave_stream_kernel<4, false>), grid, block, 0, st, s, steps, o);
+  else if (one_per_cu)
+    hipLaunchKernelGGL((wave_stream_kernel<8, true>), grid, block, 0, st, s, steps, o);
+  else
+    hipLaunchKernelGGL((wave_stream_kernel<8, false>), grid, block, 0, st, s, steps, o);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
