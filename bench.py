@@ -411,13 +411,15 @@ def probes_main(args) -> int:
             "gbps_per_cu": round(moved / ms / 1e6 / cus, 1)}
     # the matrix cores: back-to-back independent instructions on every wave,
     # one workgroup per CU; a SIMD carries ceil(waves / 4) of them
-    lib.ep_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.ep_probe_mfma_rate.argtypes = [ctypes.c_int] * 6 + [vp, vp]
     mout = torch.empty(256 * 8 * 64, dtype=torch.float32, device=dev)
     iters = 1000
-    for kind, name, flop in ((0, "mx_e4m3_32x32x64", 2 * 32 * 32 * 64), (1, "bf16_32x32x16", 2 * 32 * 32 * 16)):
+    for kind, name, flop, chains in ((0, "mx_e4m3_32x32x64", 2 * 32 * 32 * 64, 8),
+                                     (0, "mx_e4m3_32x32x64_4chains", 2 * 32 * 32 * 64, 4),
+                                     (1, "bf16_32x32x16", 2 * 32 * 32 * 16, 8)):
         for waves in (4, 6, 8):
-            ms = stream_ms(lambda k=kind, wv=waves: ok(lib.ep_probe_mfma_rate(k, 256, wv, iters, 1, mout.data_ptr(),
-                                                                              cur())), 5)
+            ms = stream_ms(lambda k=kind, c=chains, wv=waves: ok(lib.ep_probe_mfma_rate(k, c, 256, wv, iters, 1,
+                                                                                        mout.data_ptr(), cur())), 5)
             per_simd = -(-waves // 4) * iters * 8
             res[f"mfma_{name}_{waves}waves"] = {
                 "us": round(1e3 * ms, 1), "tflops": round(256 * waves * iters * 8 * flop / ms / 1e9, 1),

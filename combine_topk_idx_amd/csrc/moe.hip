@@ -76,6 +76,10 @@ constexpr int kScaleStride = 20;
 constexpr int kScaleBuf = kThreads * kScaleStride;
 constexpr int kStaging = 2 * kAStage + 2 * kScaleBuf;
 constexpr int kEpiTileBytes = kChunkRows * (16 * kWide + 1) * 4;   // GMM1 SwiGLU tile of the wide tiles
+// GMM2's bf16 tile: dwords per row, 16 past the data of the wide tiles so
+// that the two rows one dword store writes start 16 banks apart
+constexpr int kGmm2Stride = 16 * kWide + 16;
+constexpr int kGmm2TileBytes = kChunkRows * kGmm2Stride * 4;
 
 enum Mode { kGmm1Mx = 0, kGmm1Bf16 = 1, kGmm2 = 2 };
 
@@ -412,7 +416,6 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   // loads hit the cache lines of the wave that owns it) and store nothing
   const int groups = p.N_w / 32;
   const int group = min(ntile * WE + wv, groups - 1);
-  const bool owner = ntile * WE + wv < groups;
   const int spans = (ksteps + 3) / 4;
   const size_t gidx = (size_t)it.expert * (p.N_w / 32) + group;
   const uint8_t *wp = p.w + gidx * (size_t)ksteps * 2048 + lane * 16;
@@ -567,31 +570,50 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
 
   // ---------------------------------------------------------------- epilogue
   if constexpr (MODE == kGmm2) {
-    // bf16 rows: column l % 32 of this wave's 32, rows 8b + 4g + i of each fragment
-    const int col = ntile * (WE * 32) + wv * 32 + r;
+    // bf16 rows through an LDS tile [rows][32 * WE], so that the stores to
+    // HBM are 16-byte pieces of whole row segments.  Lane (r, g) holds
+    // column r of this wave's 32 at rows 8b + 4g + i of each fragment.  The
+    // last stage's barrier has retired every read of the staging buffers
+    // this tile overwrites.
+    uint32_t *tile = (uint32_t *)smem;
+    constexpr int kDw = 16 * WE;                                  // dwords of a tile row's data
+    uint16_t *tcol = (uint16_t *)smem + wv * 32 + r;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = f * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (owner && row < it.rows) {
-          const uint32_t bits = pack_bf16x2(acc[f][i], 0.0f) & 0xffffu;
-          *(uint16_t *)(p.out_data + ((size_t)(it.row0 + row) * p.out_cols + col) * 2) = (uint16_t)bits;
-        }
+        tcol[row * (2 * kGmm2Stride)] = (uint16_t)(pack_bf16x2(acc[f][i], 0.0f) & 0xffffu);
       }
+    }
+    lds_barrier();
+    // each thread: 16-byte pieces (8 columns) of the tile's rows; pieces of
+    // a wave group past N are not stored
+    constexpr int kRowPieces = kDw / 4;
+    const int c0 = ntile * (WE * 32);
+    for (int job = tid; job < it.rows * kRowPieces; job += kThr) {
+      const int row = job / kRowPieces, q = job - row * kRowPieces;
+      if (ntile * WE + (q >> 2) >= groups) continue;
+      const u32x4 v = *(const u32x4 *)(tile + row * kGmm2Stride + 4 * q);
+      *(u32x4 *)(p.out_data + ((size_t)(it.row0 + row) * p.out_cols + c0 + 8 * q) * 2) = v;
     }
   } else {
     // SwiGLU: lane r < 16 holds gate column r, lane r + 16 the matching up
-    // column; the 16 results of each wave go to an LDS tile [rows][16 * waves]
+    // column.  For each pair of rows (i, i + 1), v_permlane16_swap exchanges
+    // lanes 16..31 of row i with lanes 0..15 of row i + 1 (in each 32-lane
+    // half), so that lane r < 16 then holds the gate and up of row i and
+    // lane r + 16 those of row i + 1: every lane evaluates one silu per two
+    // rows.  The 16 results of each wave go to an LDS tile [rows][16 * waves].
     float *tile = (float *)smem;
+    const int hi = r >> 4;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float gate = acc[f][i];
-        const float up = __shfl_xor(gate, 16);
-        const int row = f * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (r < 16) tile[row * kEpiStride + wv * 16 + r] = silu(gate) * up;
+      for (int i = 0; i < 16; i += 2) {
+        const auto gu = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[f][i]), __float_as_uint(acc[f][i + 1]),
+                                                         false, false);
+        const int row = f * 32 + (i >> 2) * 8 + g * 4 + (i & 3) + hi;
+        tile[row * kEpiStride + wv * 16 + (r & 15)] = silu(__uint_as_float(gu[0])) * __uint_as_float(gu[1]);
       }
     }
     lds_barrier();
@@ -654,7 +676,7 @@ __device__ __forceinline__ void gemm_frags(const GemmArgs &p, const Item &it, in
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void mx_gmm_kernel(GemmArgs p, const int *__restrict__ offsets,
                                                           const int64_t *__restrict__ recv_count, int E) {
-  constexpr int kTile = MODE == kGmm2 ? 0 : kEpiTileBytes;
+  constexpr int kTile = MODE == kGmm2 ? kGmm2TileBytes : kEpiTileBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStaging > kTile ? kStaging : kTile];
   // GMM2 launches keep one width: the exit below that a launch with both
   // widths needs made GMM2's compiled loop about 10 % slower, and at the

@@ -154,12 +154,13 @@ __global__ __launch_bounds__(1024) void wave_stream_kernel(const u32x4 *__restri
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// Every wave issues iters x 8 matrix-core instructions on eight independent
-// accumulators (KIND 0: MX-scaled e4m3 32x32x64, scale bytes 127; KIND 1:
-// bf16 32x32x16) and writes one float per lane.  ONE_PER_CU reserves 96 KB
-// of LDS so that no two workgroups share a CU.
+// Every wave issues iters x 8 matrix-core instructions on CHAINS independent
+// accumulators (8 or 4; with 4 each accumulator takes two instructions per
+// iteration, four instructions apart) -- KIND 0: MX-scaled e4m3 32x32x64,
+// scale bytes 127; KIND 1: bf16 32x32x16 -- and writes one float per lane.
+// ONE_PER_CU reserves 96 KB of LDS so that no two workgroups share a CU.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-template <int KIND, bool ONE_PER_CU>
+template <int KIND, int CHAINS, bool ONE_PER_CU>
 __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, float *__restrict__ out) {
   __shared__ float pad[ONE_PER_CU ? 24576 : 1];
   const int l = threadIdx.x & 63;
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, float *__rest
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        c[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(au[u], b, c[u], 0, 0, 0, 127, 0, 127);
+        c[u % CHAINS] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(au[u], b, c[u % CHAINS], 0, 0, 0, 127, 0, 127);
     }
   } else {
     bf16x8 a, b;
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(512) void mfma_rate_kernel(int iters, float *__rest
     }
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(au[u], b, c[u], 0, 0, 0);
+      for (int u = 0; u < 8; ++u) c[u % CHAINS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(au[u], b, c[u % CHAINS], 0, 0, 0);
     }
   }
   float sum = 0.0f;
@@ -379,19 +380,23 @@ int ep_probe_stream(int mode, const void *src, void *dst, int64_t n, int blocks,
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// out: blocks * waves * 64 floats; kind 0 (MX e4m3) or 1 (bf16); waves 1..8.
-int ep_probe_mfma_rate(int kind, int blocks, int waves, int iters, int one_per_cu, float *out, void *stream) {
-  if (blocks <= 0 || waves <= 0 || waves > 8 || iters <= 0 || kind < 0 || kind > 1) return -1;
+// out: blocks * waves * 64 floats; kind 0 (MX e4m3) or 1 (bf16); chains 8
+// or 4; waves 1..8.
+int ep_probe_mfma_rate(int kind, int chains, int blocks, int waves, int iters, int one_per_cu, float *out,
+                       void *stream) {
+  if (blocks <= 0 || waves <= 0 || waves > 8 || iters <= 0 || kind < 0 || kind > 1 || (chains != 4 && chains != 8))
+    return -1;
   const dim3 grid((unsigned)blocks), block((unsigned)(64 * waves));
   const hipStream_t st = (hipStream_t)stream;
-  if (kind == 0 && one_per_cu)
-    hipLaunchKernelGGL((mfma_rate_kernel<0, true>), grid, block, 0, st, iters, out);
-  else if (kind == 0)
-    hipLaunchKernelGGL((mfma_rate_kernel<0, false>), grid, block, 0, st, iters, out);
-  else if (one_per_cu)
-    hipLaunchKernelGGL((mfma_rate_kernel<1, true>), grid, block, 0, st, iters, out);
-  else
-    hipLaunchKernelGGL((mfma_rate_kernel<1, false>), grid, block, 0, st, iters, out);
+#define EP_RATE(K, C, O) hipLaunchKernelGGL((mfma_rate_kernel<K, C, O>), grid, block, 0, st, iters, out)
+  if (one_per_cu) {
+    if (kind == 0) { if (chains == 8) EP_RATE(0, 8, true); else EP_RATE(0, 4, true); }
+    else { if (chains == 8) EP_RATE(1, 8, true); else EP_RATE(1, 4, true); }
+  } else {
+    if (kind == 0) { if (chains == 8) EP_RATE(0, 8, false); else EP_RATE(0, 4, false); }
+    else { if (chains == 8) EP_RATE(1, 8, false); else EP_RATE(1, 4, false); }
+  }
+#undef EP_RATE
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
