@@ -159,28 +159,37 @@ def _check_args(*specs) -> None:
     """Host checks of tensor arguments before their pointers reach the
     library, which can only check pointers and byte counts.  Each spec is
     (tensor, name, dtype, shape, min_numel) with None for "any"; raw integer
-    pointers and None tensors pass unchecked.  First every tensor's dtype,
-    shape, density and size, then that all of them are on one GPU."""
-    ts = []
+    pointers and None tensors pass unchecked.  Every tensor's dtype, shape,
+    density and size, then that all of them are on one GPU.  The common case
+    (everything valid) reads each attribute once; the messages are built
+    only on failure."""
+    dev, dev_name = -2, None
     for t, name, dtype, shape, min_numel in specs:
-        if t is None or isinstance(t, int):
+        if t is None or type(t) is int:
             continue
         if not isinstance(t, torch.Tensor):
             raise EpError(EP_ERR_INVALID_ARG, f"{name} must be a tensor")
-        if dtype is not None and t.dtype != dtype:
-            raise EpError(EP_ERR_INVALID_ARG, f"{name} must be {dtype} (got {t.dtype})")
-        if shape is not None and tuple(t.shape) != tuple(shape):
-            raise EpError(EP_ERR_INVALID_ARG, f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
-        if not t.is_contiguous():
-            raise EpError(EP_ERR_INVALID_ARG, f"{name} must be contiguous")
-        if min_numel is not None and t.numel() < min_numel:
-            raise EpError(EP_ERR_INVALID_ARG, f"{name} holds {t.numel()} elements, needs {min_numel}")
-        ts.append((t, name))
-    for t, name in ts:
-        if not t.is_cuda:
-            raise EpError(EP_ERR_INVALID_ARG, f"{name} must be a GPU tensor (got {t.device})")
-        if t.device != ts[0][0].device:
-            raise EpError(EP_ERR_INVALID_ARG, f"{name} is on {t.device}, {ts[0][1]} on {ts[0][0].device}")
+        if not ((dtype is None or t.dtype is dtype) and (shape is None or t.shape == shape) and t.is_contiguous()
+                and (min_numel is None or t.numel() >= min_numel)):
+            _explain(t, name, dtype, shape, min_numel)
+        d = t.get_device()
+        if dev == -2:
+            dev, dev_name = d, name
+        elif d != dev:
+            raise EpError(EP_ERR_INVALID_ARG, f"{name} is on {t.device}, {dev_name} on another device")
+    if dev == -1:
+        raise EpError(EP_ERR_INVALID_ARG, f"{dev_name} must be a GPU tensor (got cpu)")
+
+
+def _explain(t, name, dtype, shape, min_numel) -> None:
+    """Raises the error for a tensor that failed the checks of _check_args."""
+    if dtype is not None and t.dtype != dtype:
+        raise EpError(EP_ERR_INVALID_ARG, f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise EpError(EP_ERR_INVALID_ARG, f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise EpError(EP_ERR_INVALID_ARG, f"{name} must be contiguous")
+    raise EpError(EP_ERR_INVALID_ARG, f"{name} holds {t.numel()} elements, needs {min_numel}")
 
 
 # ---------------------------------------------------------------------------
@@ -334,12 +343,15 @@ def ep_combine(handle: ep_handle_t, expert_out, in_quant, hidden: int, topk_idx,
     EP_STATUS_COMBINE_MISMATCH."""
     T, k = handle.num_tokens, handle.num_topk
     if isinstance(topk_idx, torch.Tensor):
-        _, _, idx_dtype = _idx_args(topk_idx, None, None, None)
-        if tuple(topk_idx.shape) != (T, k):
-            raise EpError(EP_ERR_INVALID_ARG, f"topk_idx must have shape {(T, k)} (got {tuple(topk_idx.shape)})")
+        if topk_idx.dtype is torch.int64:
+            idx_dtype = EP_IDX_INT64
+        elif topk_idx.dtype is torch.int32:
+            idx_dtype = EP_IDX_INT32
+        else:
+            raise EpError(EP_ERR_INVALID_ARG, "topk_idx dtype must be int32 or int64")
     elif idx_dtype is None:
         raise EpError(EP_ERR_INVALID_ARG, "idx_dtype is required with a raw topk_idx pointer")
-    _check_args((expert_out, "expert_out", None, None, None), (topk_idx, "topk_idx", None, None, None),
+    _check_args((expert_out, "expert_out", None, None, None), (topk_idx, "topk_idx", None, (T, k), None),
                 (topk_weights, "topk_weights", torch.float32, (T, k), None),
                 (out, "out", torch.bfloat16, (T, hidden), None))
     nbytes = _nbytes(expert_out) if expert_out_bytes is None else expert_out_bytes
