@@ -70,3 +70,24 @@ def test_committed_counters_match_the_kernel_sources():
         d = json.load(f)
     # counter bytes within a few percent of the algorithmic bytes: no wasted re-reads
     assert 1.0 <= d["traffic_over_alg"] < 1.05
+
+
+def test_trace_summary_groups_by_kernel_and_grid(tmp_path):
+    """--trace-summary --by-grid: one row per (kernel, workgroups x threads),
+    durations from the start and end timestamps, longest total first."""
+    import csv
+    cols = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Grid_Size_X"]
+    rows = [("KERNEL_DISPATCH", "void (anonymous namespace)::gather_kernel<8>(int const*)", 0, 5000, 128, 896 * 128),
+            ("KERNEL_DISPATCH", "void (anonymous namespace)::gather_kernel<8>(int const*)", 0, 7000, 128, 896 * 128),
+            ("KERNEL_DISPATCH", "void (anonymous namespace)::gather_kernel<8>(int const*)", 0, 340000, 128,
+             114688 * 128),
+            ("KERNEL_DISPATCH", "void empty_kernel()", 10, 1310, 128, 128)]
+    (tmp_path / "run").mkdir()
+    with open(tmp_path / "run" / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        w.writerows(rows)
+    lines = bench.trace_summary(str(tmp_path), by_grid=True).splitlines()
+    assert lines[2] == "| `gather_kernel<8>` | 114688 x 128 | 1 | 340.00 | 340.00 | 340.00 | 340.00 |"
+    assert lines[3] == "| `gather_kernel<8>` | 896 x 128 | 2 | 6.00 | 6.00 | 5.00 | 7.00 |"
+    assert lines[4] == "| `empty_kernel` | 1 x 128 | 1 | 1.30 | 1.30 | 1.30 | 1.30 |"
