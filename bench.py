@@ -365,6 +365,21 @@ def probes_main(args) -> int:
         nbytes = R * 2 * H + T * kk * 4 + 2 * T * H
         res[f"gather_decode_k{kk}"] = {"us": round(1e3 * ms, 3), "bytes": nbytes,
                                        "gbps": round(nbytes / ms / 1e6, 1)}
+    # dispatch's pattern at decode: each token's span read once and written
+    # as one byte per element to each of its routed rows
+    lib.ep_probe_scatter.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    for s in sets:
+        s["x"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev).normal_()
+        s["codes"] = s["rows"].view(-1).view(torch.uint8)[: rows * H].view(rows, H)
+    for kk in (1, 8):
+        calls = [lambda s=s, kk=kk: ok(lib.ep_probe_scatter(s["x"].data_ptr(), s["slot" if kk == 8 else "slot1"]
+                                                            .data_ptr(), T, kk, H, s["codes"].data_ptr(), cur()))
+                 for s in sets]
+        ms = graph_ms(calls, 210)
+        R = int((sets[0]["slot"] >= 0).sum()) if kk == 8 else T
+        nbytes = 2 * T * H + T * kk * 4 + R * H
+        res[f"scatter_decode_k{kk}"] = {"us": round(1e3 * ms, 3), "bytes": nbytes,
+                                        "gbps": round(nbytes / ms / 1e6, 1)}
     del sets
     torch.cuda.empty_cache()
     # the large workload's combine pattern: 16384 tokens, 8 random rows each
@@ -769,8 +784,8 @@ def main() -> int:
                          "launches")
     ap.add_argument("--probes", action="store_true",
                     help="time the probe kernels of libep_probe.so: launch floors at decode grids, combine's "
-                         "gather pattern at decode and large sizes, 1 GiB read / write / copy streams, the "
-                         "GEMMs' per-wave weight stream")
+                         "gather and dispatch's scatter patterns at decode, the gather at the large size, 1 GiB "
+                         "read / write / copy streams, the GEMMs' per-wave weight stream, the matrix-core rate")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
                     help="no GPU work: markdown table of a rocprofv3 --kernel-trace --stats csv run under DIR")
     ap.add_argument("--by-grid", action="store_true",

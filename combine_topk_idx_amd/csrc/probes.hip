@@ -9,6 +9,12 @@
 //                       numbers of token t, then k row spans of 2 KB (16
 //                       bytes per lane), add them in float32, write 2 KB --
 //                       combine's dependent loads with no dequantisation
+//   ep_probe_scatter    per workgroup (token t, span c): read the k row
+//                       numbers of token t and the token's 2 KB span (16
+//                       bytes per lane), write one byte per element (8
+//                       bytes per lane) to each of the k rows -- dispatch's
+//                       access pattern for one-byte codes, with no
+//                       quantisation and no scale bytes
 //   ep_probe_stream     grid-stride 16-byte accesses over n bytes: read only
 //                       (one 16-byte value per workgroup written), write only,
 //                       or copy
@@ -70,6 +76,26 @@ __global__ __launch_bounds__(128) void gather_kernel(const u32x4 *__restrict__ r
 #pragma unroll
   for (int e = 0; e < 4; ++e) o[e] = (__float_as_uint(acc[2 * e]) >> 16) | (__float_as_uint(acc[2 * e + 1]) & 0xffff0000u);
   __builtin_nontemporal_store(o, out + (int64_t)t * nvec + v);
+}
+
+// x: [T, nvec] 16-byte vectors (bf16 x 8); slot: [T, K] int32; rows:
+// [max_rows, nvec] 8-byte pieces.  Lane v of workgroup (t, c) writes the
+// high bytes of its eight bf16 values to every routed row of token t.
+template <int K>
+__global__ __launch_bounds__(128) void scatter_kernel(const u32x4 *__restrict__ x, const int *__restrict__ slot,
+                                                     int nvec, int chunks, u32x2 *__restrict__ rows) {
+  const int t = blockIdx.x / chunks, c = blockIdx.x - t * chunks;
+  const int v = c * 128 + threadIdx.x;
+  int s[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) s[j] = slot[t * K + j];
+  if (v >= nvec) return;
+  const u32x4 r = __builtin_nontemporal_load(x + (int64_t)t * nvec + v);
+  const u32x2 o = {(r.x >> 8 & 0xffu) | (r.x >> 16 & 0xff00u) | (r.y << 8 & 0xff0000u) | (r.y & 0xff000000u),
+                   (r.z >> 8 & 0xffu) | (r.z >> 16 & 0xff00u) | (r.w << 8 & 0xff0000u) | (r.w & 0xff000000u)};
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    if (s[j] >= 0) __builtin_nontemporal_store(o, rows + (int64_t)s[j] * nvec + v);
 }
 
 // mode 0: read `src` (each workgroup writes one vector to dst[blockIdx]);
@@ -362,6 +388,21 @@ int ep_probe_gather(const void *rows, const int *slot, int T, int k, int hidden,
   else
     hipLaunchKernelGGL(gather_kernel<8>, grid, dim3(128), 0, (hipStream_t)stream, (const u32x4 *)rows, slot, nvec,
                        chunks, (u32x4 *)out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// x: [T, hidden] bf16; slot: [T, k] int32 with values in [-1, max_rows);
+// rows: [max_rows, hidden] bytes; hidden % 8 == 0; k in {1, 8}.
+int ep_probe_scatter(const void *x, const int *slot, int T, int k, int hidden, void *rows, void *stream) {
+  if (T <= 0 || hidden <= 0 || hidden % 8 != 0 || (k != 1 && k != 8)) return -1;
+  const int nvec = hidden / 8, chunks = (nvec + 127) / 128;
+  const dim3 grid((unsigned)(T * chunks));
+  if (k == 1)
+    hipLaunchKernelGGL(scatter_kernel<1>, grid, dim3(128), 0, (hipStream_t)stream, (const u32x4 *)x, slot, nvec,
+                       chunks, (u32x2 *)rows);
+  else
+    hipLaunchKernelGGL(scatter_kernel<8>, grid, dim3(128), 0, (hipStream_t)stream, (const u32x4 *)x, slot, nvec,
+                       chunks, (u32x2 *)rows);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
