@@ -38,43 +38,56 @@ COMMON = [
 ]
 
 
-def _compile(src: str, build_dir: str, defines: tuple) -> str:
+# AddressSanitizer for the host code only (the device code cannot carry it
+# here): each -fsanitize= goes to the host pass alone
+HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, build_dir: str, defines: tuple, extra: tuple = ()) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *extra, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def _link(objs: list, out: str) -> None:
+def _link(objs: list, out: str, extra: tuple = ()) -> None:
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
 
 
-def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+def build(verbose: bool = False, out: str = LIB, defines: tuple = (), host_asan: bool = False) -> str:
     """Compile every source and link the library (default: libep.so next to
     this file; ``defines`` are extra -D macros, e.g. launch-shape overrides
     from csrc/tuning.hpp); returns the library path.  The default build also
-    links the measurement probes of ``bench.py --probes`` (libep_probe.so)."""
-    build_dir = BUILD if out == LIB else out + ".build"
+    links the measurement probes of ``bench.py --probes`` (libep_probe.so).
+
+    host_asan: the host code (argument checks, handles, launch set-up) with
+    AddressSanitizer, for the host-only ABI tests on a machine without a
+    GPU; load it with the ASan runtime preloaded (the runtime's path is
+    ``hipcc -print-file-name=libclang_rt.asan-x86_64.so``) and
+    ASAN_OPTIONS=detect_leaks=0, and build again without it afterwards."""
+    build_dir = (BUILD if out == LIB else out + ".build") + ("_asan" if host_asan else "")
     os.makedirs(build_dir, exist_ok=True)
     srcs = SOURCES + (PROBE_SOURCES if out == LIB else [])
+    cflags = tuple(HOST_ASAN) if host_asan else ()
+    lflags = ("-Xarch_host", "-fsanitize=address", "-shared-libasan") if host_asan else ()
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, build_dir, tuple(defines)), srcs)))
-    _link([objs[s] for s in SOURCES], out)
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, build_dir, tuple(defines), cflags), srcs)))
+    _link([objs[s] for s in SOURCES], out, lflags)
     if out == LIB:
-        _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
+        _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, lflags)
     if verbose:
-        print(f"built {out}" + (f" and {PROBE_LIB}" if out == LIB else ""))
+        print(f"built {out}" + (f" and {PROBE_LIB}" if out == LIB else "") + (" (host ASan)" if host_asan else ""))
     return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, host_asan="--host-asan" in sys.argv[1:])
     sys.exit(0)
