@@ -424,6 +424,20 @@ def probes_main(args) -> int:
         res[f"wave_stream_{blocks}x{waves}_d{depth}" + ("" if one else "_2perCU")] = {
             "us": round(1e3 * ms, 1), "bytes": moved, "gbps": round(moved / ms / 1e6, 1),
             "gbps_per_cu": round(moved / ms / 1e6 / cus, 1)}
+    # the GEMMs' whole fetch per CU: the weight stream plus 12 KB of shared
+    # activations per step (two 16-byte pieces per thread), from L2
+    lib.ep_probe_mixed_stream.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    act = torch.empty(1 << 20, dtype=torch.uint8, device=dev).fill_(3)
+    for blocks in (240, 256):
+        waves, depth = 6, 4
+        steps = span // (blocks * waves * 2048) // depth * depth
+        wbytes = blocks * waves * steps * 2048
+        abytes = blocks * waves * 64 * steps * 2 * 16
+        ms = stream_ms(lambda b=blocks, st=steps: ok(lib.ep_probe_mixed_stream(
+            src.data_ptr(), act.data_ptr(), act.numel(), b, waves, st, wout.data_ptr(), cur())), 10)
+        res[f"mixed_stream_{blocks}x{waves}"] = {
+            "us": round(1e3 * ms, 1), "weight_bytes": wbytes, "activation_bytes": abytes,
+            "weight_gbps": round(wbytes / ms / 1e6, 1), "gbps_per_cu": round((wbytes + abytes) / ms / 1e6 / blocks, 1)}
     # the matrix cores: back-to-back independent instructions on every wave,
     # one workgroup per CU; a SIMD carries ceil(waves / 4) of them
     lib.ep_probe_mfma_rate.argtypes = [ctypes.c_int] * 6 + [vp, vp]

@@ -22,6 +22,9 @@
 //                       steps (two 1 KB loads per step) with a fixed number
 //                       of steps in flight -- the expert GEMMs' weight
 //                       stream, without the matrix-core work
+//   ep_probe_mixed_stream  the weight stream plus, per step, two 16-byte
+//                       pieces per thread of an activation buffer shared by
+//                       all workgroups -- the GEMMs' whole fetch per CU
 //   ep_probe_mfma_rate  back-to-back independent matrix-core instructions
 //                       (MX-scaled e4m3 32x32x64, or bf16 32x32x16) on
 //                       every wave of a grid: the sustained rate per SIMD
@@ -145,30 +148,49 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4 *__restrict__ s
 // DEPTH steps ahead; lane 0 of each wave writes the XOR of what it read to
 // out[w].  ONE_PER_CU reserves 96 KB of LDS, so that no two workgroups share
 // a CU (160 KB of LDS per CU).  steps is a multiple of DEPTH.
-template <int DEPTH, bool ONE_PER_CU>
+// APIECES > 0 adds the activation side of the GEMMs' fetch: with every
+// weight step each thread also loads APIECES 16-byte pieces of a shared
+// buffer `a` (a_vecs vectors, a power of two) that every workgroup walks in
+// the same order, so that after the first workgroup of an XCD they come from
+// its L2.
+template <int DEPTH, bool ONE_PER_CU, int APIECES = 0>
 __global__ __launch_bounds__(1024) void wave_stream_kernel(const u32x4 *__restrict__ src, int steps,
-                                                           u32x4 *__restrict__ out) {
+                                                           u32x4 *__restrict__ out, const u32x4 *__restrict__ a = nullptr,
+                                                           int a_vecs = 1) {
   __shared__ u32x4 pad[ONE_PER_CU ? 6144 : 1];
   const int lane = threadIdx.x & 63;
   const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const u32x4 *p = src + w * (int64_t)steps * 128 + lane;
-  u32x4 r0[DEPTH], r1[DEPTH];
+  u32x4 r0[DEPTH], r1[DEPTH], ra[DEPTH][APIECES > 0 ? APIECES : 1];
+  auto load_a = [&](int step, int d) {
+#pragma unroll
+    for (int q = 0; q < APIECES; ++q)
+      ra[d][q] = a[((step * APIECES + q) * (int)blockDim.x + (int)threadIdx.x) & (a_vecs - 1)];
+  };
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     r0[d] = __builtin_nontemporal_load(p + d * 128);
     r1[d] = __builtin_nontemporal_load(p + d * 128 + 64);
+    load_a(d, d);
   }
   u32x4 x = {0u, 0u, 0u, 0u};
   for (int s = DEPTH; s < steps; s += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       x ^= r0[d] ^ r1[d];
+#pragma unroll
+      for (int q = 0; q < APIECES; ++q) x ^= ra[d][q];
       r0[d] = __builtin_nontemporal_load(p + (int64_t)(s + d) * 128);
       r1[d] = __builtin_nontemporal_load(p + (int64_t)(s + d) * 128 + 64);
+      load_a(s + d, d);
     }
   }
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) x ^= r0[d] ^ r1[d];
+  for (int d = 0; d < DEPTH; ++d) {
+    x ^= r0[d] ^ r1[d];
+#pragma unroll
+    for (int q = 0; q < APIECES; ++q) x ^= ra[d][q];
+  }
   if (steps < 0) {                              // never taken: keeps the LDS reservation
     pad[threadIdx.x % (ONE_PER_CU ? 6144 : 1)] = x;
     __syncthreads();
@@ -459,6 +481,20 @@ int ep_probe_wave_stream(const void *src, int blocks, int waves, int steps, int 
     hipLaunchKernelGGL((wave_stream_kernel<8, true>), grid, block, 0, st, s, steps, o);
   else
     hipLaunchKernelGGL((wave_stream_kernel<8, false>), grid, block, 0, st, s, steps, o);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// src as for ep_probe_wave_stream (depth 4, one workgroup per CU); a:
+// a_bytes of activations, a power of two and at least 16; out: blocks *
+// waves vectors.
+int ep_probe_mixed_stream(const void *src, const void *a, int64_t a_bytes, int blocks, int waves, int steps,
+                          void *out, void *stream) {
+  if (blocks <= 0 || waves <= 0 || waves > 16 || steps <= 0 || steps % 4 != 0 || a_bytes < 16 ||
+      (a_bytes & (a_bytes - 1)) != 0 || a_bytes / 16 > (int64_t)1 << 30)
+    return -1;
+  hipLaunchKernelGGL((wave_stream_kernel<4, true, 2>), dim3((unsigned)blocks), dim3((unsigned)(64 * waves)), 0,
+                     (hipStream_t)stream, (const u32x4 *)src, steps, (u32x4 *)out, (const u32x4 *)a,
+                     (int)(a_bytes / 16));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
