@@ -278,7 +278,13 @@ __device__ __forceinline__ Item find_item(const Plan &pl, int E, const int *__re
   return it;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z), the quotient taken as z times the hardware
+// reciprocal (v_rcp_f32, within 1 ulp) instead of a correctly rounded
+// division: expf, the add, the reciprocal and the two products stay within a
+// few float32 ulps of the exact a = silu(g)·u, far inside the 2^-20·|a|
+// the tests allow for its float32 evaluation, at a sixth of the division's
+// instructions (the epilogue is ALU-bound)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + expf(-z)); }
 
 // Packed weights.  A wave's 32 weight rows form a group: for GMM2 rows
 // 32j .. 32j+31; for GMM1 ("gate/up" groups) the gate rows 16j .. 16j+15 and
