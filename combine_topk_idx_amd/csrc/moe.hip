@@ -338,13 +338,15 @@ __global__ void pack_weights_kernel(const uint8_t *__restrict__ codes, const uin
 
 // Weight loads are streamed (each weight byte is read once per launch);
 // activation rows are shared by the workgroups of an expert through L2.
+// Build-time knobs (-D...) for measuring alternatives; the defaults are the
+// measured best: EP_MOE_W_NT / EP_MOE_A_NT non-temporal weight / activation
+// loads, EP_MOE_ASETS stages of A loads in flight per thread (1, 2 or 4).
 #ifndef EP_MOE_W_NT
 #define EP_MOE_W_NT 1
 #endif
 #ifndef EP_MOE_A_NT
 #define EP_MOE_A_NT 0
 #endif
-// stages of A in flight per thread
 #ifndef EP_MOE_ASETS
 #define EP_MOE_ASETS 2
 #endif
