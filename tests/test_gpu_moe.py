@@ -150,6 +150,41 @@ def test_gmm1_mxfp8_small(ep):
     check_chain(ep, w, inp, res, lay, rb, per, None, gmm2=False)
 
 
+@pytest.mark.parametrize("out_quant", ["none", "mxfp8"])
+def test_gmm1_silu_extremes(ep, out_quant):
+    """The gate rows' scale bytes raised by 5 (x32): |g| reaches the
+    hundreds, so in float32 e^-g overflows (silu -> -0; the exact value is
+    below 1e-36), underflows (silu -> g), and near g = -88 its reciprocal
+    1 / (1 + e^-g) is subnormal.  Every element stays within the derived
+    bound of the oracle's exact a."""
+    w = W.MOE_WORKLOADS["moe_small"]
+    _announce(f"gmm1 silu extremes moe_small {out_quant}")
+    inp = dict(W.make_moe_inputs(w))
+    s = inp["w1_scales"].copy()
+    s[:, : w.I] = np.minimum(s[:, : w.I].astype(np.int32) + 5, 254).astype(np.uint8)
+    inp["w1_scales"] = s
+    res = gpu_moe(ep, w, inp, out_quant=out_quant, stop_after="gmm1")
+    lay, rb, per, _ = oracle_moe(w, inp, out_mode="bf16" if out_quant == "none" else "mxfp8")
+    g_all = []
+    for e, (rows, ent) in enumerate(per):
+        if ent is not None:
+            xv, w1v, _ = _expert_mats(inp, e, rb, rows)
+            g_all.append((xv @ w1v[: w.I].T).ravel())
+    g_all = np.concatenate(g_all)
+    # the regimes are reached: overflow of e^-g, its underflow, and the
+    # subnormal reciprocal window
+    assert (g_all < -88.8).sum() > 100 and (g_all > 88.8).sum() > 100
+    assert ((g_all > -88.7) & (g_all < -87.4)).sum() > 10
+    if out_quant == "none":
+        got = _bf16_rows(res["a"], lay.max_rows, w.I)
+        for e, (rows, ent) in enumerate(per):
+            if ent is not None:
+                xv, w1v, _ = _expert_mats(inp, e, rb, rows)
+                _check_gmm1_bf16(got[rows], xv, w1v, ent["a"])
+    else:
+        check_chain(ep, w, inp, res, lay, rb, per, None, gmm2=False)
+
+
 def test_gmm2_on_shared_input(ep):
     """GMM2 alone: both sides read the same synthetic MXFP8 activations."""
     w = W.MOE_WORKLOADS["moe_small"]
