@@ -1,0 +1,107 @@
+"""Every call runs on the stream it is given.
+
+The buffers the calls read hold a fill pattern (ids -1, zero rows and
+weights) while the real inputs wait in staging buffers on the device.  A
+side stream is kept busy with a queue of matrix products, and the real
+inputs are copied over the fill pattern on that stream behind them; then
+layout, dispatch and combine are issued on the side stream -- by the
+explicit `stream=` argument, as torch's current stream, or through the
+one-call layout + dispatch.  A launch on any other stream would run before
+the copies land, read the fill pattern (no token routed anywhere) and differ
+from the oracle; on the side stream the results are the oracle's, bit for
+bit.  Streams keep the default priority.
+"""
+
+import sys
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+from combine_topk_idx_amd import workloads as W
+from tests.hip_path import DEV, bf16_bits, canary_buffer, recv_rows, to_dev, ws_view
+from tests.oracle_path import oracle_run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ep():
+    from combine_topk_idx_amd import ep as _ep
+    return _ep
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _keep_busy(s: torch.cuda.Stream, n: int = 12) -> None:
+    """About ten milliseconds of matrix products queued on s."""
+    a = torch.rand((4096, 4096), device=DEV)
+    b = torch.rand((4096, 4096), device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(n):
+            a = torch.mm(a, b) * (1.0 / 4096)
+
+
+@pytest.mark.parametrize("how", ["argument", "current", "fused"])
+def test_calls_follow_their_stream(ep, how):
+    w = W.WORKLOADS["decode"]
+    _announce(f"stream ordering ({how}) {w.name} T={w.T} H={w.H} E={w.E} k={w.k} {w.mode}")
+    inp = W.make_inputs(w)
+    y = W.make_expert_out(w)
+    lay, rb, want = oracle_run(w, inp, y)
+
+    idx_real, x_real = to_dev(inp["topk_idx"]), to_dev(inp["x"])
+    wts_real, y_real = to_dev(inp["topk_weights"]), to_dev(y)
+    idx = torch.full_like(idx_real, -1)
+    x = torch.zeros_like(x_real)
+    wts = torch.zeros_like(wts_real)
+    ysrc = torch.zeros_like(y_real)
+    nbytes = ep.ep_workspace_bytes(w.t_max, w.k, w.E)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)
+    recv_count = torch.full((w.E,), -7, dtype=torch.int64, device=DEV)
+    total, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    recv = canary_buffer(total)
+    recv_w = torch.full((w.max_rows,), float("nan"), device=DEV)
+    out = torch.zeros((w.T, w.H), dtype=torch.bfloat16, device=DEV)
+    torch.cuda.synchronize()
+
+    s = torch.cuda.Stream()
+    _keep_busy(s)
+    with torch.cuda.stream(s):
+        for dst, src in ((idx, idx_real), (x, x_real), (wts, wts_real), (ysrc, y_real)):
+            dst.copy_(src, non_blocking=True)
+    yb = ysrc.view(torch.uint8).reshape(-1)
+    if how == "argument":
+        h = ep.ep_layout(idx, w.E, w.t_max, recv_count, ws, stream=s)
+        ep.ep_dispatch(h, x, w.H, w.mode, recv, wts, recv_w, stream=s)
+        ep.ep_combine(h, yb, "none", w.H, idx, wts, out, stream=s)
+    elif how == "current":
+        with torch.cuda.stream(s):
+            h = ep.ep_layout(idx, w.E, w.t_max, recv_count, ws)
+            ep.ep_dispatch(h, x, w.H, w.mode, recv, wts, recv_w)
+            ep.ep_combine(h, yb, "none", w.H, idx, wts, out)
+    else:
+        h = ep.ep_layout_dispatch(idx, w.E, w.t_max, recv_count, ws, x, w.H, w.mode, recv, wts, recv_w, stream=s)
+        ep.ep_combine(h, yb, "none", w.H, idx, wts, out, stream=s)
+    # the side stream was still busy when the last call was issued, so a
+    # launch on another stream would have run before the copies
+    assert not s.query(), "the queued work ended before the calls were issued; the test would not see a wrong stream"
+    s.synchronize()
+
+    assert np.array_equal(recv_count.cpu().numpy(), lay.count)
+    assert np.array_equal(ws_view(ws, h.offsets, w.E + 1, torch.int32).cpu().numpy(), lay.offsets.astype(np.int32))
+    assert np.array_equal(ws_view(ws, h.slot, w.T * w.k, torch.int32).cpu().numpy().reshape(w.T, w.k), lay.slot)
+    assert np.array_equal(ws_view(ws, h.row_src, w.max_rows, torch.int32).cpu().numpy(), lay.row_src)
+    assert ep.ep_read_status(h) == lay.status
+    R = lay.num_rows
+    data, scales = recv_rows(ep, SimpleNamespace(recv=recv), w)
+    assert np.array_equal(data[:R], rb.data[:R])
+    assert np.array_equal(scales[:R], rb.scales[:R])
+    assert np.array_equal(recv_w[:R].cpu().numpy(), rb.weights[:R])
+    assert np.array_equal(bf16_bits(out), want)
