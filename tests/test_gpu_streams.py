@@ -105,3 +105,62 @@ def test_calls_follow_their_stream(ep, how):
     assert np.array_equal(scales[:R], rb.scales[:R])
     assert np.array_equal(recv_w[:R].cpu().numpy(), rb.weights[:R])
     assert np.array_equal(bf16_bits(out), want)
+
+
+def test_moe_chain_and_backward_follow_their_stream(ep):
+    """layout -> dispatch (MXFP8) -> GMM1 -> GMM2 -> combine, then combine's
+    backward, all with `stream=` a side stream whose inputs land behind
+    queued work; the chain is held to the oracle's with the derived bounds
+    of the expert-MLP tests, the backward rows bit for bit."""
+    from oracle import backward as OB
+    from tests.moe_path import oracle_moe
+    from tests.test_gpu_moe import check_chain
+
+    w = W.MOE_WORKLOADS["moe_small"]
+    _announce(f"stream ordering, expert MLP chain and backward {w.name} T={w.T} H={w.H} I={w.I} k={w.k}")
+    inp = W.make_moe_inputs(w)
+    lay, rb, per, want = oracle_moe(w, inp)
+    grad = W.make_inputs(W.Workload("g", w.T, w.H, w.E_local, w.k, "int64", "mxfp8", "uniform", seed=7100))["x"]
+    want_b = OB.combine_backward(grad, lay, "mxfp8", inp["topk_weights"])
+
+    E = w.E_local
+    max_rows = w.T * w.k                                 # compact blocks
+    idx_real, x_real = to_dev(inp["topk_idx"]), to_dev(inp["x"])
+    wts_real, g_real = to_dev(inp["topk_weights"]), to_dev(grad)
+    w1c, w1s = ep.pack_moe_weights(to_dev(inp["w1_codes"]), to_dev(inp["w1_scales"]), True)
+    w2c, w2s = ep.pack_moe_weights(to_dev(inp["w2_codes"]), to_dev(inp["w2_scales"]), False)
+    idx = torch.full_like(idx_real, -1)
+    x = torch.zeros_like(x_real)
+    wts = torch.zeros_like(wts_real)
+    g = torch.zeros_like(g_real)
+    ws = torch.empty(max(ep.ep_workspace_bytes(w.T, w.k, E), 256), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)
+    rc = torch.full((E,), -7, dtype=torch.int64, device=DEV)
+    recv = canary_buffer(ep.ep_buffer_bytes(max_rows, w.H, "mxfp8")[0])
+    a = canary_buffer(ep.ep_buffer_bytes(max_rows, w.I, "mxfp8")[0])
+    y = canary_buffer(max_rows * w.H * 2)
+    back = canary_buffer(ep.ep_buffer_bytes(max_rows, w.H, "mxfp8")[0])
+    out = torch.zeros((w.T, w.H), dtype=torch.bfloat16, device=DEV)
+    torch.cuda.synchronize()
+
+    s = torch.cuda.Stream()
+    _keep_busy(s)
+    with torch.cuda.stream(s):
+        for dst, src in ((idx, idx_real), (x, x_real), (wts, wts_real), (g, g_real)):
+            dst.copy_(src, non_blocking=True)
+    h = ep.ep_layout(idx, E, w.T, rc, ws, stream=s)
+    assert h.max_rows == max_rows
+    ep.ep_dispatch(h, x, w.H, "mxfp8", recv, stream=s)
+    ep.ep_moe_gmm1(h, recv, w.H, w.I, w1c, w1s, "mxfp8", a, recv_count=rc, stream=s)
+    ep.ep_moe_gmm2(h, a, w.I, w.H, w2c, w2s, y, recv_count=rc, stream=s)
+    ep.ep_combine(h, y, "none", w.H, idx, wts, out, stream=s)
+    ep.ep_combine_backward(h, g, w.H, "mxfp8", back, wts, stream=s)
+    assert not s.query(), "the queued work ended before the calls were issued; the test would not see a wrong stream"
+    s.synchronize()
+
+    check_chain(ep, w, inp, {"a": a, "y": y, "out": bf16_bits(out)}, lay, rb, per, want)
+    R = lay.num_rows
+    data, scales = recv_rows(ep, SimpleNamespace(recv=back), SimpleNamespace(max_rows=max_rows, H=w.H,
+                                                                              mode="mxfp8", interleaved=False))
+    assert np.array_equal(data[:R], want_b.data[:R])
+    assert np.array_equal(scales[:R], want_b.scales[:R])
