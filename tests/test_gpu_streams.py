@@ -42,6 +42,8 @@ def _keep_busy(s: torch.cuda.Stream, n: int = 12) -> None:
     a = torch.rand((4096, 4096), device=DEV)
     b = torch.rand((4096, 4096), device=DEV)
     torch.cuda.synchronize()
+    a.record_stream(s)                 # used on s after this function returns
+    b.record_stream(s)
     with torch.cuda.stream(s):
         for _ in range(n):
             a = torch.mm(a, b) * (1.0 / 4096)
