@@ -24,6 +24,7 @@
 // workgroup reduction.  Routed rows and weights are read once per workgroup
 // (scalar loads).  Code rows are written with non-temporal stores, scale
 // pieces through L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -339,22 +340,31 @@ __device__ __forceinline__ void quantize_store(const u32x4 (&raw)[VPT], int v0, 
 }
 
 // ---------------------------------------------------------------------------
-// Layout fused into dispatch (compact receive rows, few pairs).
+// Layout fused into dispatch (compact rows or capacity blocks, few pairs).
 //
 // In the compact arrangement the receive row of pair f with expert e is
 // (pairs with an expert below e) + (earlier pairs with expert e): the
 // exclusive scan of the expert counts plus the stable rank ("Low-Latency Mode
-// API", Return Values recv_count and the receive layout it describes).  Both
-// are counts over the ids, so a dispatch workgroup can find the rows of its
-// token's pairs by itself, with no wait on another workgroup, while its span
-// of the token row is in flight.  Workgroup 0 writes the per-expert outputs
-// (counts, block starts, running statistics, status) and marks the rows past
-// the last routed one free up to n = T * k; every span workgroup marks a share
-// of the rows from n to the capacity's end free; the first span workgroup of
-// each token writes the token's slots, row_src entries and receive weights.
+// API", Return Values recv_count and the receive layout it describes).  With
+// blocks of a fixed capacity C (the page's [experts, max tokens, hidden]
+// receive buffer) it is e * C + (earlier pairs with expert e), and a pair whose
+// rank reaches C is dropped.  Both are counts over the ids, so a dispatch
+// workgroup can find the rows of its token's pairs by itself, with no wait on
+// another workgroup, while its span of the token row is in flight.
+//
+// The first `lwg` workgroups are layout workgroups.  Compact (lwg = 1): it
+// writes the per-expert outputs (counts, block starts, running statistics,
+// status) and marks the rows past the last routed one free up to n = T * k;
+// every span workgroup marks a share of the rows from n to the end free.
+// Capacity: each layout workgroup counts the ids per expert and marks the
+// free tail of every lwg-th block; the first also writes the per-expert
+// outputs.  The first span workgroup of each token writes the token's slots,
+// row_src entries and receive weights.
 struct FusedArgs {
   const void *idx;     // [n] int32 or int64 ids
   int idx64, n, E, max_rows;
+  int cap;             // 0 (compact rows) or the rows of every expert block
+  int lwg;             // layout workgroups at the front of the grid
   int64_t *recv_count; // [E]
   int32_t *cum;        // [E] or null
   int32_t *offsets;    // [E + 1]
@@ -411,11 +421,13 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum, int &total)
   return before + x - v;
 }
 
-// Workgroup 0 of the fused launch: expert histogram (LDS atomics), its
-// exclusive scan, the per-expert outputs, the status word and the free rows
-// below n (all of them when there is no token, hence no span workgroup).
-template <int NT, typename IdT>
-__device__ __forceinline__ void fused_layout_outputs(const FusedArgs &a) {
+// Layout workgroup lw of the fused launch: expert histogram (LDS atomics).
+// Compact (lw = 0 only): its exclusive scan, the per-expert outputs, the
+// status word and the free rows below n (all of them when there is no token,
+// hence no span workgroup).  Capacity: the free tail of every lwg-th block
+// from block lw, and from lw = 0 the per-expert outputs and the status word.
+template <int NT, bool CAPM, typename IdT>
+__device__ __forceinline__ void fused_layout_outputs(const FusedArgs &a, int lw) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int wsum[NT / kWave];
   __shared__ uint32_t sbad;
@@ -437,6 +449,30 @@ __device__ __forceinline__ void fused_layout_outputs(const FusedArgs &a) {
   }
   if (bad) atomicOr(&sbad, EP_STATUS_ID_OUT_OF_RANGE);
   __syncthreads();
+  if constexpr (CAPM) {
+    // block e holds rows [e * cap, (e + 1) * cap); the first min(count, cap)
+    // hold pairs
+    for (int e = lw; e < a.E; e += a.lwg) {
+      const int hi = (e + 1) * a.cap;
+      for (int r = e * a.cap + min(cnt[e], a.cap) + (int)threadIdx.x; r < hi; r += NT) a.row_src[r] = -1;
+    }
+    if (lw != 0) return;
+    bool over = false;
+    for (int e = threadIdx.x; e < a.E; e += NT) {
+      const int c = cnt[e];
+      a.offsets[e] = e * a.cap;
+      a.recv_count[e] = min(c, a.cap);
+      if (a.cum) a.cum[e] += c;
+      over |= c > a.cap;
+    }
+    if (over) atomicOr(&sbad, EP_STATUS_CAPACITY_OVERFLOW);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      a.offsets[a.E] = a.E * a.cap;
+      *a.status = sbad;
+    }
+    return;
+  }
   // thread i owns experts [i * per, (i + 1) * per)
   const int per = (a.E + NT - 1) / NT;
   const int e0 = threadIdx.x * per, e1 = min(e0 + per, a.E);
@@ -527,9 +563,81 @@ __device__ __forceinline__ void fused_slots(const FusedArgs &a, int t, int k, in
   for (int j = 0; j < KMAX; ++j) s[j] = key[j] >= 0 ? (int)((acc[j / 2] >> (16 * (j & 1))) & 0xffffu) : -1;
 }
 
-// FUSED: workgroup 0 writes the layout's per-expert outputs and workgroup
-// b > 0 is span workgroup b - 1, which derives its token's slots from the ids
-// (above) instead of reading them.
+// Capacity blocks: the receive rows of the pairs of token t as above, but
+// counting only the keys in [e * 4096, key) -- the earlier pairs with the same
+// expert -- so that the row is e * cap + that rank, or -1 once the rank
+// reaches cap.  (Kept apart from the compact form, whose code it would
+// otherwise change.)
+template <int NT, int KMAX, bool EXACT, typename IdT>
+__device__ __forceinline__ void fused_slots_cap(const FusedArgs &a, int t, int k, int (&s)[KMAX], uint32_t *red) {
+  static_assert(kFusedMaxPairs < 4096, "order keys hold the pair index in 12 bits; counts fit 16 bits");
+  const IdT *idx = (const IdT *)a.idx;
+  const int f0 = t * k;
+  // the first batch of ids is loaded before the token's own ids, so that the
+  // two loads are in flight together (this workgroup is called with n >= 1)
+  IdT v[kIdBatch];
+#pragma unroll
+  for (int u = 0; u < kIdBatch; ++u) v[u] = idx[min(u * NT + (int)threadIdx.x, a.n - 1)];
+  int key[KMAX], lo[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const IdT e = idx[f0 + (EXACT ? j : min(j, k - 1))];
+    const bool ok = j < k && e >= 0 && (int64_t)e < (int64_t)a.E;
+    key[j] = ok ? (int)e * 4096 + f0 + j : -1;   // -1: nothing orders before it
+    lo[j] = ok ? (int)e * 4096 : 0;
+  }
+  int cnt[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) cnt[j] = 0;
+  for (int b0 = 0;;) {
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int f = b0 + u * NT + threadIdx.x;
+      const bool ok = f < a.n && v[u] >= 0 && (int64_t)v[u] < (int64_t)a.E;
+      const int kf = ok ? (int)v[u] * 4096 + f : 1 << 30;   // above every valid key
+      // kf < key[j] as the sign of a difference that cannot overflow (keys
+      // lie in [-1, 2^21)): plain vector arithmetic, no lane masks
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)   // lo[j] <= kf < key[j], both as signs of differences
+        cnt[j] += (int)((((uint32_t)kf - (uint32_t)key[j]) >> 31) & ~(((uint32_t)kf - (uint32_t)lo[j]) >> 31));
+    }
+    b0 += kIdBatch * NT;
+    if (b0 >= a.n) break;
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) v[u] = idx[min(b0 + u * NT + (int)threadIdx.x, a.n - 1)];
+  }
+  uint32_t acc[KMAX / 2];
+#pragma unroll
+  for (int i = 0; i < KMAX / 2; ++i) {
+    acc[i] = wave_sum((uint32_t)cnt[2 * i] | ((uint32_t)cnt[2 * i + 1] << 16));
+  }
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+#pragma unroll
+    for (int i = 0; i < KMAX / 2; ++i) red[w * (KMAX / 2) + i] = acc[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < KMAX / 2; ++i) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int ww = 0; ww < NT / kWave; ++ww) sum += red[ww * (KMAX / 2) + i];
+    acc[i] = sum;
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int c = (int)((acc[j / 2] >> (16 * (j & 1))) & 0xffffu);
+    s[j] = key[j] >= 0 && c < a.cap ? (key[j] >> 12) * a.cap + c : -1;
+  }
+}
+
+
+// FUSED: workgroups b < lwg are the layout workgroups (above) and workgroup
+// b >= lwg is span workgroup b - lwg, which derives its token's slots from
+// the ids instead of reading them.
+// FUSED (compact rows): workgroup 0 writes the layout's per-expert outputs
+// and workgroup b > 0 is span workgroup b - 1, which derives its token's
+// slots from the ids (above) instead of reading them.
 template <int Q, int NT, int VPT, int KMAX, bool EXACT, bool PACK, bool WEIGHTED, bool FUSED>
 __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ x, int nvec, int k, int chunks,
                                                       const int *__restrict__ slot,
@@ -540,8 +648,8 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
   int b = blockIdx.x;
   if constexpr (FUSED) {
     if (b == 0) {
-      if (fa.idx64) fused_layout_outputs<NT, int64_t>(fa);
-      else fused_layout_outputs<NT, int32_t>(fa);
+      if (fa.idx64) fused_layout_outputs<NT, false, int64_t>(fa, 0);
+      else fused_layout_outputs<NT, false, int32_t>(fa, 0);
       return;
     }
     b -= 1;
@@ -618,12 +726,65 @@ __global__ __launch_bounds__(NT) void dispatch_kernel(const u32x4 *__restrict__ 
   }
 }
 
-// fa != null: the fused launch (layout workgroup first), forward dispatch only.
+// The one launch of layout + dispatch for capacity blocks: workgroups b <
+// fa.lwg are layout workgroups, workgroup b >= fa.lwg is span workgroup
+// b - fa.lwg.  The same steps as the fused form of dispatch_kernel, with the
+// capacity rows; kept as a kernel of its own (rather than a flag of a shared
+// body) because sharing the body changed the compact kernel's register
+// allocation and cost it 0.3 us per decode step.
+template <int Q, int NT, int VPT, int KMAX, bool EXACT, bool PACK>
+__global__ __launch_bounds__(NT) void dispatch_cap_kernel(const u32x4 *__restrict__ x, int nvec, int k, int chunks,
+                                                          const float *__restrict__ w, float *__restrict__ recv_w,
+                                                          char *__restrict__ data, char *__restrict__ scales,
+                                                          int64_t dq, int64_t sq, FusedArgs fa) {
+  __shared__ uint32_t red[NT / kWave * (KMAX / 2)];
+  int b = blockIdx.x;
+  if (b < fa.lwg) {
+    if (fa.idx64) fused_layout_outputs<NT, true, int64_t>(fa, b);
+    else fused_layout_outputs<NT, true, int32_t>(fa, b);
+    return;
+  }
+  b -= fa.lwg;
+  const int t = b / chunks;
+  const int c = b - t * chunks;
+  const int64_t pair0 = (int64_t)t * k;
+  const u32x4 *xr = x + (int64_t)t * nvec;
+  const int v0 = c * NT * VPT + threadIdx.x;
+  u32x4 raw[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = v0 + i * NT;
+    raw[i] = v < nvec ? xr[v] : u32x4{0u, 0u, 0u, 0u};
+  }
+  int s[KMAX];
+  if (fa.idx64) fused_slots_cap<NT, KMAX, EXACT, int64_t>(fa, t, k, s, red);
+  else fused_slots_cap<NT, KMAX, EXACT, int32_t>(fa, t, k, s, red);
+  if (c == 0 && threadIdx.x < k) {
+    int r = -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) r = j == (int)threadIdx.x ? s[j] : r;
+    fa.slot[pair0 + threadIdx.x] = r;
+    if (r >= 0) {
+      fa.row_src[r] = (int)pair0 + threadIdx.x;
+      if (recv_w != nullptr) recv_w[r] = w[pair0 + threadIdx.x];
+    }
+  }
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    s[j] = j < k ? s[j] : -1;
+    any |= s[j] >= 0;
+  }
+  if (!any) return;   // uniform: every pair of the token dropped or routed nowhere
+  quantize_store<Q, NT, VPT, KMAX, PACK>(raw, v0, nvec, s, 0, KMAX, data, scales, dq, sq, red);
+}
+
+// fa != null: the fused launch (layout workgroups first), forward dispatch only.
 template <int Q, int NT, int VPT, bool PACK, bool WEIGHTED>
 hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *w, char *recv, float *recv_w,
                     int64_t dq, int64_t sq, size_t scale_off, const FusedArgs *fa, hipStream_t s) {
   const int chunks = (nvec + NT * VPT - 1) / (NT * VPT);
-  const int64_t blocks = h.num_tokens * chunks + (fa ? 1 : 0);
+  const int64_t blocks = h.num_tokens * chunks + (fa ? fa->lwg : 0);
   if (blocks == 0) return hipSuccess;
 #define EP_LAUNCH_DISPATCH(KMAX, EXACT, FUSED)                                                                 \
   hipLaunchKernelGGL((dispatch_kernel<Q, NT, VPT, KMAX, EXACT, PACK, WEIGHTED, FUSED>), dim3((unsigned)blocks), \
@@ -634,13 +795,25 @@ hipError_t launch_q(const ep_handle_t &h, const void *x, int nvec, const float *
   else if (h.num_topk < 8) EP_LAUNCH_DISPATCH(8, false, FUSED);             \
   else if (h.num_topk == kMaxTopk) EP_LAUNCH_DISPATCH(kMaxTopk, true, FUSED); \
   else EP_LAUNCH_DISPATCH(kMaxTopk, false, FUSED);
+#define EP_LAUNCH_CAP(KMAX, EXACT)                                                                          \
+  hipLaunchKernelGGL((dispatch_cap_kernel<Q, NT, VPT, KMAX, EXACT, PACK>), dim3((unsigned)blocks), dim3(NT),  \
+                     EP_DISPATCH_LDS_CAP, s, (const u32x4 *)x, nvec, h.num_topk, chunks, w, recv_w, recv,     \
+                     recv + scale_off, dq, sq, *fa)
   if constexpr (!WEIGHTED) {
+    if (fa && fa->cap > 0) {
+      if (h.num_topk == 8) EP_LAUNCH_CAP(8, true);
+      else if (h.num_topk < 8) EP_LAUNCH_CAP(8, false);
+      else if (h.num_topk == kMaxTopk) EP_LAUNCH_CAP(kMaxTopk, true);
+      else EP_LAUNCH_CAP(kMaxTopk, false);
+      return hipGetLastError();
+    }
     if (fa) {
       EP_LAUNCH_K(true)
       return hipGetLastError();
     }
   }
   EP_LAUNCH_K(false)
+#undef EP_LAUNCH_CAP
 #undef EP_LAUNCH_K
 #undef EP_LAUNCH_DISPATCH
   return hipGetLastError();
@@ -705,6 +878,12 @@ hipError_t launch_layout_dispatch(const ep_handle_t &h, const void *idx, int idx
   fa.n = (int)(h.num_tokens * h.num_topk);
   fa.E = h.num_experts;
   fa.max_rows = (int)h.max_rows;
+  fa.cap = h.expert_capacity;
+  fa.lwg = h.expert_capacity > 0
+               ? (int)std::min<int64_t>(std::max<int64_t>((h.max_rows + kFusedRowsPerLayoutWg - 1) /
+                                                               kFusedRowsPerLayoutWg, 1),
+                                        h.num_experts)
+               : 1;
   fa.recv_count = recv_count;
   fa.cum = cum;
   fa.offsets = h.offsets;

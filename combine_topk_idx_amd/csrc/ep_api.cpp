@@ -269,7 +269,7 @@ ep_status_t layout_dispatch_impl(const char *fn, const void *topk_idx, ep_idx_dt
   if (st != EP_OK) return st;
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (row_align == 1 && expert_capacity == 0 && num_tokens * num_topk <= ep::kFusedMaxPairs) {
+  if (ep::fused_layout_dispatch_fits(num_tokens * num_topk, row_align, expert_capacity, h.max_rows)) {
     e = ep::launch_layout_dispatch(h, topk_idx, idx_dtype == EP_IDX_INT64, recv_count, cumulative_recv_stats, x,
                                    hidden, topk_weights, quant, (char *)recv_buf, recv_weights, s);
   } else {

@@ -298,7 +298,7 @@ def ep_layout_dispatch(topk_idx, num_experts: int, num_max_dispatch_tokens: int,
                        num_tokens=None, num_topk=None, idx_dtype=None, recv_buf_bytes=None, interleaved=False,
                        stream=None) -> ep_handle_t:
     """ep_layout_ex and ep_dispatch in one call (one launch for compact
-    layouts of at most 2048 pairs).  Returns the handle."""
+    layouts and capacity blocks of at most 2048 pairs).  Returns the handle."""
     num_tokens, num_topk, idx_dtype = _idx_args(topk_idx, num_tokens, num_topk, idx_dtype)
     rows = max(ep_layout_rows(num_max_dispatch_tokens, num_topk, num_experts, row_align, expert_capacity), 0)
     _check_args(*_layout_specs(topk_idx, num_experts, recv_count, workspace, cumulative_recv_stats),

@@ -221,11 +221,12 @@ ep_status_t ep_dispatch(const ep_handle_t *handle, const void *x, int32_t hidden
  * recv_count, cumulative_recv_stats, status, receive buffer, receive
  * weights) are identical to that pair of calls, and every argument of both
  * is checked before anything is launched.  Compact layouts (row_align 1, no
- * capacity) of at most 2048 (token, j) pairs run as a single launch, in
- * which each dispatch workgroup derives its own receive rows from topk_idx
- * (a decode-sized step saves one launch); the others run the two launches of
- * the separate calls.  The workspace must outlive every call that uses the
- * returned handle, as for ep_layout. */
+ * capacity) and capacity blocks (row_align 1, at most 2^18 receive rows) of
+ * at most 2048 (token, j) pairs run as a single launch, in which each
+ * dispatch workgroup derives its own receive rows from topk_idx (a
+ * decode-sized step saves one launch); aligned blocks and larger inputs run
+ * the two launches of the separate calls.  The workspace must outlive every
+ * call that uses the returned handle, as for ep_layout. */
 ep_status_t ep_layout_dispatch(const void *topk_idx, ep_idx_dtype_t idx_dtype, int64_t num_tokens,
                                int32_t num_topk, int64_t num_max_dispatch_tokens, int32_t num_experts,
                                int32_t row_align, int32_t expert_capacity, int64_t *recv_count,

@@ -1,9 +1,11 @@
 """GPU parity of ep_layout_dispatch (layout and dispatch in one call) against
 the CPU oracle, and against the separate ep_layout_ex + ep_dispatch calls.
 
-Compact layouts of at most 2048 (token, j) pairs take the one-launch path,
-in which every dispatch workgroup counts its own receive rows from the ids;
-the rest take the two launches of the separate calls.  Every case below is
+Compact layouts and capacity blocks of at most 2048 (token, j) pairs take
+the one-launch path, in which every dispatch workgroup counts its own
+receive rows from the ids (with capacity blocks also layout workgroups that
+mark each block's free rows); aligned blocks and larger inputs take the two
+launches of the separate calls.  Every case below is
 compared with the oracle bit-exactly (layout, codes, scales, receive
 weights, combine), on both sides of the 2048-pair limit, with the edge cases
 of the fuzz set (empty input, capacity above T, pairs routed nowhere,
@@ -12,6 +14,7 @@ int64 ids, the widest int8 rows).
 """
 
 import sys
+from types import SimpleNamespace
 
 import numpy as np
 import pytest
@@ -84,6 +87,14 @@ EDGES = [
     ("k16_at_limit", 128, 512, 512, 16, "mxfp4", "int32", 0.1, 200, 1, 0),
     ("aligned", 64, 1024, 16, 8, "mxfp8", "int64", 0.1, 64, 128, 0),
     ("capacity", 64, 1024, 16, 8, "int8_token", "int64", 0.1, 64, 1, 24),
+    # capacity blocks: the page's [experts, max tokens, hidden] at decode
+    # (32768 rows, 8 layout workgroups), overflowing blocks, both sides of
+    # the pair limit, one expert
+    ("capacity_decode", 128, 7168, 256, 8, "fp8_b128", "int64", 0.1, 128, 1, 128),
+    ("capacity_overflow", 200, 512, 8, 8, "mxfp8", "int32", 0.05, 200, 1, 150),
+    ("capacity_at_limit", 256, 1024, 64, 8, "mxfp4", "int64", 0.0, 256, 1, 40),
+    ("capacity_past_limit", 257, 256, 64, 8, "int8_token", "int64", 0.0, 257, 1, 48),
+    ("capacity_one_expert", 100, 256, 1, 1, "none", "int32", 0.2, 100, 1, 64),
 ]
 
 
@@ -159,3 +170,46 @@ def test_same_bytes_as_separate_calls(ep):
         assert torch.equal(ra, rb)
         assert np.array_equal(wa.cpu().numpy(), wb.cpu().numpy(), equal_nan=True)
         assert torch.equal(cum_a, cum_b)
+
+
+@pytest.mark.parametrize("T,E,k,cap,mode,idt", [
+    (100, 40, 6, 20, "mxfp4", "int32"),       # overflowing blocks, duplicate experts, out-of-range ids
+    (128, 256, 8, 128, "fp8_b128", "int64"),  # decode shape, 8 layout workgroups
+    (0, 16, 4, 32, "mxfp8", "int64"),         # no token: the layout workgroups mark every row free
+], ids=["overflow", "decode", "empty"])
+def test_capacity_same_bytes_as_separate_calls(ep, T, E, k, cap, mode, idt):
+    """Capacity blocks through the one launch: whole receive buffer (canaries
+    of unused rows included), receive weights, layout arrays, status and
+    running statistics equal those of ep_layout_ex + ep_dispatch, over three
+    calls in a row."""
+    _announce(f"layout_dispatch capacity vs separate calls T={T} E={E} k={k} cap={cap} {mode} {idt}")
+    w = W.Workload("capsep", T, 1024, E, k, idt, mode, "uniform", neg_frac=0.1, combine_input="identity",
+                   seed=91 + T, num_max_tokens=max(T, 1), expert_capacity=cap)
+    inp = W.make_inputs(w)
+    if T and k > 1:
+        inp["topk_idx"] = W.with_duplicates(inp["topk_idx"], 5)
+    if T >= 30:
+        idx = inp["topk_idx"].copy()
+        idx[3, 0], idx[17, k - 1] = E, -5               # out of range: status bit, pair dropped
+        inp["topk_idx"] = idx
+    x, wts = to_dev(inp["x"]), to_dev(inp["topk_weights"])
+    total, _ = ep.ep_buffer_bytes(w.max_rows, w.H, w.mode)
+    cum_a = torch.full((w.E,), 3, dtype=torch.int32, device=DEV)
+    cum_b = cum_a.clone()
+    for it in range(3):
+        ra, rb = canary_buffer(total), canary_buffer(total)
+        wa = torch.full((w.max_rows,), float("nan"), device=DEV)
+        wb = wa.clone()
+        ha, wsa, rca = run_layout_dispatch(ep, w, inp["topk_idx"], x, wts, ra, wa, cum_a)
+        hb, wsb, rcb = run_layout(ep, w, inp["topk_idx"], cum_b)
+        ep.ep_dispatch(hb, x, w.H, w.mode, rb, wts, wb)
+        la, lb = read_layout(ep, ha, wsa, rca, w), read_layout(ep, hb, wsb, rcb, w)
+        for key in ("recv_count", "offsets", "slot", "row_src"):
+            assert np.array_equal(la[key], lb[key]), key
+        assert la["status"] == lb["status"]
+        assert torch.equal(ra, rb)
+        assert np.array_equal(wa.cpu().numpy(), wb.cpu().numpy(), equal_nan=True)
+        assert torch.equal(cum_a, cum_b)
+    lay, _, _ = oracle_run(w, inp)
+    check_layout(SimpleNamespace(recv_count=la["recv_count"], offsets=la["offsets"], slot=la["slot"],
+                                 row_src=la["row_src"], status=la["status"]), lay)
