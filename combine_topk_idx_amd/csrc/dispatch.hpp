@@ -12,7 +12,7 @@ namespace ep {
 // the free rows of every block, kFusedRowsPerLayoutWg each).
 constexpr int64_t kFusedMaxPairs = 2048;
 constexpr int64_t kFusedMaxCapRows = 1 << 18;
-constexpr int64_t kFusedRowsPerLayoutWg = 4096;
+constexpr int64_t kFusedRowsPerLayoutWg = 1024;
 inline bool fused_layout_dispatch_fits(int64_t pairs, int32_t row_align, int32_t cap, int64_t max_rows) {
   return row_align == 1 && pairs <= kFusedMaxPairs && (cap == 0 || max_rows <= kFusedMaxCapRows);
 }
