@@ -79,6 +79,23 @@ def test_fuzz_case(ep, case):
     _check(ep, w, inp, y)
 
 
+@pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}" for c in CASES])
+def test_fuzz_case_capacity(ep, case):
+    """The fuzz set with capacity blocks of about the average load per expert
+    (at least one row), so that many blocks overflow and drop pairs: the one
+    launch up to 2048 pairs, the separate calls above."""
+    seed, T, H, E, k, mode, idt, neg, tmax, cin = case
+    cap = max(1, (T * k) // E)
+    _announce(f"layout_dispatch capacity fuzz seed={seed} T={T} H={H} E={E} k={k} {mode} {idt} cap={cap}")
+    w = W.Workload(f"fc{seed}", T, H, E, k, idt, mode, "uniform", neg_frac=neg, combine_input=cin,
+                   seed=5000 + seed, num_max_tokens=tmax, expert_capacity=cap)
+    inp = W.make_inputs(w)
+    if seed % 3 == 0 and k > 1 and T:
+        inp["topk_idx"] = W.with_duplicates(inp["topk_idx"], seed)
+    y = W.make_expert_out(w) if cin == "normal" else None
+    _check(ep, w, inp, y)
+
+
 # both sides of the 2048-pair limit, compact and padded layouts
 EDGES = [
     # name, T, H, E, k, mode, idx_dtype, neg_frac, t_max, row_align, capacity
