@@ -298,12 +298,14 @@ def test_capacity_padded_blocks(ep):
     check_chain(ep, w, inp, res, lay, rb, per, out)
 
 
-def test_share_full_size_sampled(ep):
-    """The 1024-token, 6-local-expert share at full size (hidden 7168,
-    intermediate 3072), sampled tokens through the whole path; every routed
-    row within the 2e-2 relative error of a quantised combine."""
-    w = W.MOE_WORKLOADS["moe_share"]
-    _announce("moe_share full size, sampled tokens")
+@pytest.mark.parametrize("name", ["moe_share", "moe_share32"])
+def test_share_full_size_sampled(ep, name):
+    """The share at full size (hidden 7168, intermediate 3072, 6 local
+    experts; 1024 tokens, and 256 whose 1- and 2-fragment chunks put the
+    plan on mixed tile widths), sampled tokens through the whole path; every
+    routed row within the 2e-2 relative error of a quantised combine."""
+    w = W.MOE_WORKLOADS[name]
+    _announce(f"{name} full size, sampled tokens")
     inp = W.make_moe_inputs(w)
     res = gpu_moe(ep, w, inp)
     toks = sample_tokens(W.Workload("s", w.T, w.H, w.E_local, w.k, "int64", "mxfp8", "uniform"), inp["topk_idx"],
