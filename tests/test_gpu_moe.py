@@ -390,6 +390,10 @@ FUZZ = [
     # to four-group tiles (mixed), and seven chunks with no room to move any
     (768, 256, 3072, 6, 6, 1, 1107),
     (900, 128, 3072, 7, 7, 1, 1109),
+    # one expert whose 161 rows make a full chunk and a one-row chunk, and
+    # I = 128 (eight GMM1 groups: a full tile and a partial one)
+    (161, 256, 256, 1, 1, 1, 1112),
+    (130, 128, 128, 3, 3, 2, 1111),
 ]
 
 
@@ -407,6 +411,20 @@ def test_gemm_shapes(ep, case):
     y = _bf16_rows(res["y"], lay.max_rows, w.H)
     free = np.nonzero(lay.row_src < 0)[0]
     assert np.all(y[free] == NAN_BF16)
+
+
+@pytest.mark.parametrize("inter", [64, 192])
+def test_gmm1_inter_not_multiple_of_128(ep, inter):
+    """GMM1 takes an intermediate size that is a multiple of 64 (GMM2, which
+    reduces over it, needs 128): 64 is one four-group tile, 192 a six-group
+    tile and a four-group one; the requant against the oracle's chain, and
+    161 + 159 rows (a one-row chunk)."""
+    w = W.MoeWorkload(f"i{inter}", 320, 256, inter, 2, 2, 1, seed=1113)
+    _announce(f"gmm1 I={inter}")
+    inp = W.make_moe_inputs(w)
+    res = gpu_moe(ep, w, inp, out_quant="mxfp8", stop_after="gmm1")
+    lay, rb, per, _ = oracle_moe(w, inp, out_mode="mxfp8")
+    check_chain(ep, w, inp, res, lay, rb, per, None, gmm2=False)
 
 
 def test_no_routed_rows(ep):
