@@ -72,17 +72,20 @@ def _run(ep, w, inp, noalloc):
 
 CALLS = [
     # the decode workload (one launch), then a smaller one (fewer tokens,
-    # experts and rows), then aligned blocks (two launches)
+    # experts and rows), then capacity blocks that overflow (one launch), then
+    # aligned blocks (two launches)
     W.replace(W.WORKLOADS["decode"], combine_input="identity"),
     W.Workload("smaller", 40, 1024, 16, 4, "int32", "mxfp8", "uniform", neg_frac=0.1, combine_input="identity",
                seed=3301),
+    W.Workload("capacity", 60, 512, 8, 4, "int64", "fp8_b128", "uniform", neg_frac=0.05, combine_input="identity",
+               seed=3303, expert_capacity=20),
     W.Workload("aligned", 30, 512, 8, 2, "int64", "mxfp4", "uniform", combine_input="identity", seed=3302,
                num_max_tokens=33, row_align=32),
 ]
 
 
 def test_noalloc_matches_layout_dispatch(ep):
-    print("\n[case] ep_layout_dispatch_noalloc vs ep_layout_dispatch, three calls in a row", flush=True)
+    print("\n[case] ep_layout_dispatch_noalloc vs ep_layout_dispatch, four calls in a row", flush=True)
     sys.stdout.flush()
     for w in CALLS:
         inp = W.make_inputs(w)
