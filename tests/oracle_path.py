@@ -33,3 +33,12 @@ def oracle_run(w: W.Workload, inp: dict, expert_out: np.ndarray | None = None, t
                            np.zeros((w.max_rows, 0), np.uint8), None)
     out = C.combine(cin, lay, inp["topk_weights"], tokens)
     return lay, rb, out
+
+
+def oracle_combine_bf16_rows(w: W.Workload, inp: dict, lay, expert_out: np.ndarray, tokens=None) -> np.ndarray:
+    """The oracle's combine of bf16 expert rows (a workload whose combine
+    input does not depend on the dispatched rows), for every token or a
+    sample; the rows are read as they are, so no dispatch is needed."""
+    cin = D.RecvBuffer("none", w.H, lay.num_rows, expert_out.view(np.uint8).reshape(w.max_rows, -1),
+                       np.zeros((w.max_rows, 0), np.uint8), None)
+    return C.combine(cin, lay, inp["topk_weights"], tokens)

@@ -74,7 +74,7 @@ def test_backward_full_size_sampled(ep):
     grad = W.make_expert_out(w, rows=w.T)
     run = _run(ep, w, inp, grad, True)
     lay = OL.layout(inp["topk_idx"], w.E, w.T)
-    toks = sample_tokens(w, inp["topk_idx"], n=32)
+    toks = sample_tokens(w, inp["topk_idx"])
     rb = OB.combine_backward(grad, lay, w.mode, inp["topk_weights"], tokens=toks)
     rows = sorted({int(r) for t in toks for r in lay.slot[t] if r >= 0})
     data, scales = recv_rows(ep, run, w, rows)

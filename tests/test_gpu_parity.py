@@ -11,7 +11,9 @@ Workloads with at most a few hundred tokens are compared in full; the
 4096- and 16384-token ones are compared in full for the layout and on a
 sample of tokens (first, last, random, and tokens of the busiest expert) for
 dispatch and combine, at full size and in the launch configuration the
-benchmark uses.
+benchmark uses.  Where the combine input is a set of bf16 expert rows of its
+own (the 16384-token workload), combine is compared on every token: the
+oracle's combine of such rows costs well under a millisecond per token.
 """
 
 import sys
@@ -23,7 +25,7 @@ import torch
 from combine_topk_idx_amd import workloads as W
 from oracle import codecs, quant as Q
 from tests.hip_path import run_path, recv_rows, sample_tokens
-from tests.oracle_path import oracle_run
+from tests.oracle_path import oracle_combine_bf16_rows, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -111,6 +113,8 @@ def test_workload_full_size_sampled(ep, name):
     assert np.array_equal(data, rb.data[rows])
     assert np.array_equal(scales, rb.scales[rows])
     check_combine(w, run.out[toks], out)
+    if w.combine_input == "normal":                  # every token's combine, against the oracle
+        check_combine(w, run.out, oracle_combine_bf16_rows(w, inp, lay, y))
     if name == "prefill":                            # Zipf: hot experts hold > 10x the mean
         assert lay.count.max() > 10 * lay.count.mean()
 
