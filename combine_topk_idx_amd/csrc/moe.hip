@@ -295,7 +295,12 @@ __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcp
 // 48+16g) at 1024 + 16l.  Each 16-byte load of a wave then reads 1 KB in
 // one piece.  Scale bytes: for each group and span of four K steps, 256
 // bytes where lane l's four bytes (offset 4l) are the e8m0 scales of K-block
-// 2(4t+u) + g of row r for u = 0..3 (zero past the last step).
+// 2(4t+u) + g of row r for u = 0..3 (zero past the last step).  Fragments
+// are stored step-major: the fragments of K step s of every group of every
+// expert (expert-major, then group) lie together, and so do the scale
+// blocks of span t.  The waves of a launch all start at step 0 and advance
+// in step, so at any time they read one contiguous stretch of the weights
+// (measured 1 % faster than one contiguous stream per group).
 __host__ __device__ inline int packed_group_row(int j, int r, int gate_up, int inter) {
   return gate_up ? (r < 16 ? 16 * j + r : inter + 16 * j + (r - 16)) : 32 * j + r;
 }
@@ -315,7 +320,8 @@ __global__ void pack_weights_kernel(const uint8_t *__restrict__ codes, const uin
     const int r = lane & 31, g = lane >> 5;
     const int row = packed_group_row(j, r, gate_up, inter);
     const uint8_t *src = codes + ((int64_t)e * N + row) * K + s * kKStep + half * 32 + g * 16;
-    *(u32x4 *)(pcodes + i * 16) = *(const u32x4 *)src;
+    const int64_t d = ((int64_t)s * E * groups + eg) * 128 + (i & 127);   // step-major
+    *(u32x4 *)(pcodes + d * 16) = *(const u32x4 *)src;
   }
   // one thread per (expert, group, span, lane): four scale bytes
   const int64_t words = (int64_t)E * groups * spans * 64;
@@ -332,7 +338,8 @@ __global__ void pack_weights_kernel(const uint8_t *__restrict__ codes, const uin
       const int step = 4 * t + u;
       if (step < ksteps) w |= (uint32_t)scales[((int64_t)e * N + row) * kb + step * 2 + g] << (8 * u);
     }
-    *(uint32_t *)(pscales + i * 4) = w;
+    const int64_t d = ((int64_t)t * E * groups + eg) * 64 + lane;          // span-major
+    *(uint32_t *)(pscales + d * 4) = w;
   }
 }
 
@@ -399,6 +406,7 @@ struct GemmArgs {
   int K;
   const uint8_t *w, *w_scales;
   int N_w, nt_narrow, nt_wide, num_cus, inter;
+  int groups_all;                                 // weight groups of all experts (E * N_w / 32)
   uint8_t *out_data, *out_scales;
   int out_cols;
 };
@@ -419,15 +427,17 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   const int K = p.K, ksteps = K / kKStep, nstages = ksteps / kStageSteps, kb = K / 32;
 
   // this wave's packed weight group (see pack_weights_kernel): fragments of
-  // 2048 bytes per K step, scale dwords per span of four steps
+  // 2048 bytes per K step, groups_all fragments apart, scale dwords per span
+  // of four steps, groups_all blocks of 256 bytes apart
   // a tile's last waves may lie past N: they repeat the last group (their
   // loads hit the cache lines of the wave that owns it) and store nothing
   const int groups = p.N_w / 32;
   const int group = min(ntile * WE + wv, groups - 1);
   const int spans = (ksteps + 3) / 4;
   const size_t gidx = (size_t)it.expert * (p.N_w / 32) + group;
-  const uint8_t *wp = p.w + gidx * (size_t)ksteps * 2048 + lane * 16;
-  const uint8_t *wsp = p.w_scales + gidx * (size_t)spans * 256 + lane * 4;
+  const uint8_t *wp = p.w + gidx * (size_t)2048 + lane * 16;
+  const uint8_t *wsp = p.w_scales + gidx * (size_t)256 + lane * 4;
+  const size_t wstep = (size_t)p.groups_all * 2048, wspan_stride = (size_t)p.groups_all * 256;
 
   // A staging, branch-free: piece i of this thread is (row, 16-byte piece) =
   // (idx >> 3, idx & 7) of the stage, so 8 lanes read one 128-byte line;
@@ -488,10 +498,10 @@ __device__ __forceinline__ void gemm_chunk(const GemmArgs &p, const Item &it, in
   uint32_t wspan[2];
   auto load_w = [&](int s, int slot) {
     const int ss = min(s, ksteps - 1);                             // loads past the end are never used
-    wb0[slot] = ld_w<u32x4>(wp + (size_t)ss * 2048);
-    wb1[slot] = ld_w<u32x4>(wp + (size_t)ss * 2048 + 1024);
+    wb0[slot] = ld_w<u32x4>(wp + (size_t)ss * wstep);
+    wb1[slot] = ld_w<u32x4>(wp + (size_t)ss * wstep + 1024);
   };
-  auto load_span = [&](int t, int slot) { wspan[slot] = ld_w<uint32_t>(wsp + (size_t)min(t, spans - 1) * 256); };
+  auto load_span = [&](int t, int slot) { wspan[slot] = ld_w<uint32_t>(wsp + (size_t)min(t, spans - 1) * wspan_stride); };
 
   v16f acc[NF];
 #pragma unroll
@@ -758,8 +768,8 @@ hipError_t launch_moe_gmm1(const ep_handle_t &h, const int64_t *recv_count, cons
   const int64_t blocks = persistent_grid(items * ntn);
   if (h.num_tokens == 0 || blocks == 0) return hipSuccess;
   GemmArgs p{(const uint8_t *)x_buf, (const uint8_t *)x_buf + gx.scale_off, hidden, (const uint8_t *)w1,
-             (const uint8_t *)w1_scales, 2 * inter, ntn, ntw, device_cus(), inter, (uint8_t *)out_buf, nullptr,
-             inter};
+             (const uint8_t *)w1_scales, 2 * inter, ntn, ntw, device_cus(), inter, h.num_experts * (2 * inter / 32),
+             (uint8_t *)out_buf, nullptr, inter};
   if (out_quant == EP_QUANT_MXFP8) {
     p.out_scales = (uint8_t *)out_buf + recv_geom(h.max_rows, inter, EP_QUANT_MXFP8).scale_off;
     hipLaunchKernelGGL(mx_gmm_kernel<kGmm1Mx>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, h.offsets,
@@ -780,8 +790,8 @@ hipError_t launch_moe_gmm2(const ep_handle_t &h, const int64_t *recv_count, cons
   const int64_t blocks = persistent_grid(items * ntn);
   if (h.num_tokens == 0 || blocks == 0) return hipSuccess;
   const GemmArgs p{(const uint8_t *)a_buf, (const uint8_t *)a_buf + ga.scale_off, inter, (const uint8_t *)w2,
-                   (const uint8_t *)w2_scales, hidden, ntn, ntw, device_cus(), inter, (uint8_t *)out_buf, nullptr,
-                   hidden};
+                   (const uint8_t *)w2_scales, hidden, ntn, ntw, device_cus(), inter, h.num_experts * (hidden / 32),
+                   (uint8_t *)out_buf, nullptr, hidden};
   hipLaunchKernelGGL(mx_gmm_kernel<kGmm2>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, h.offsets, recv_count,
                      h.num_experts);
   return hipGetLastError();

@@ -354,7 +354,10 @@ ep_status_t ep_moe_packed_bytes(int32_t num_experts, int32_t rows, int32_t k, si
  * fragment, lane l = 32g + r holding K bytes [16g, 16g+16) of the group's
  * row r at 16l and K bytes [32+16g, 48+16g) at 1024 + 16l; for each group
  * and span of four K steps 256 scale bytes, lane l's four at 4l (step
- * 4t+u's K-block 2(4t+u)+g of row r, zero past the last step). */
+ * 4t+u's K-block 2(4t+u)+g of row r, zero past the last step).  Fragments
+ * are ordered by K step, then expert, then group (scale blocks by span,
+ * then expert, then group), so the GEMMs need the weights packed for
+ * exactly the handle's num_experts experts. */
 ep_status_t ep_moe_pack_weights(const void *codes, const void *scales, int32_t num_experts, int32_t rows,
                                 int32_t k, int32_t gate_up, void *packed_codes, void *packed_scales,
                                 void *stream);

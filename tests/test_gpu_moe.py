@@ -467,7 +467,8 @@ def _pack_reference(codes, scales, gate_up):
             for u in range(4):
                 if 4 * t + u < ks:
                     ps[:, j, t, :, u] = scales[:, rows, (4 * t + u) * 2 + g]
-    return pc.reshape(-1), ps.reshape(-1)
+    # step-major: K step (scale span) first, then expert, then group
+    return pc.transpose(2, 0, 1, 3, 4, 5).reshape(-1), ps.transpose(2, 0, 1, 3, 4).reshape(-1)
 
 
 @pytest.mark.parametrize("gate_up", [True, False])
