@@ -392,14 +392,27 @@ def pack_moe_weights(codes, scales, gate_up: bool, *, stream=None):
     return pc, ps
 
 
-def _check_moe_args(handle: ep_handle_t, recv_count, **bufs) -> None:
-    _check_args(*[(b, n, None, None, None) for n, b in bufs.items()],
+def _check_moe_args(handle: ep_handle_t, recv_count, weights, **bufs) -> None:
+    """weights: (codes, scales, rows, k, names) of packed weights, which must be
+    the 1-D uint8 tensors ep_moe_pack_weights fills for exactly the handle's
+    num_experts experts (the packing is step-major, so weights packed for
+    another expert count would be read at the wrong places).  Shapes the
+    library rejects anyway are left to its own message."""
+    codes, scales, rows, k, (cn, sn) = weights
+    try:
+        cb, sb = ep_moe_packed_bytes(handle.num_experts, rows, k)
+    except EpError:
+        cb = sb = None
+    _check_args((codes, cn, torch.uint8, None if cb is None else (cb,), None),
+                (scales, sn, torch.uint8, None if sb is None else (sb,), None),
+                *[(b, n, None, None, None) for n, b in bufs.items()],
                 (recv_count, "recv_count", torch.int64, None, handle.num_experts))
 
 
 def ep_moe_gmm1(handle: ep_handle_t, x_buf, hidden: int, inter: int, w1, w1_scales, out_quant, out_buf, *,
                 recv_count=None, x_buf_bytes=None, out_buf_bytes=None, stream=None) -> None:
-    _check_moe_args(handle, recv_count, x_buf=x_buf, w1=w1, w1_scales=w1_scales, out_buf=out_buf)
+    _check_moe_args(handle, recv_count, (w1, w1_scales, 2 * inter, hidden, ("w1", "w1_scales")), x_buf=x_buf,
+                    out_buf=out_buf)
     _check(_lib.ep_moe_gmm1(ctypes.byref(handle), _ptr(recv_count), _ptr(x_buf),
                             _nbytes(x_buf) if x_buf_bytes is None else x_buf_bytes, hidden, inter, _ptr(w1),
                             _ptr(w1_scales), _quant(out_quant), _ptr(out_buf),
@@ -408,7 +421,8 @@ def ep_moe_gmm1(handle: ep_handle_t, x_buf, hidden: int, inter: int, w1, w1_scal
 
 def ep_moe_gmm2(handle: ep_handle_t, a_buf, inter: int, hidden: int, w2, w2_scales, out_buf, *,
                 recv_count=None, a_buf_bytes=None, out_buf_bytes=None, stream=None) -> None:
-    _check_moe_args(handle, recv_count, a_buf=a_buf, w2=w2, w2_scales=w2_scales, out_buf=out_buf)
+    _check_moe_args(handle, recv_count, (w2, w2_scales, hidden, inter, ("w2", "w2_scales")), a_buf=a_buf,
+                    out_buf=out_buf)
     _check(_lib.ep_moe_gmm2(ctypes.byref(handle), _ptr(recv_count), _ptr(a_buf),
                             _nbytes(a_buf) if a_buf_bytes is None else a_buf_bytes, inter, hidden, _ptr(w2),
                             _ptr(w2_scales), _ptr(out_buf), _nbytes(out_buf) if out_buf_bytes is None else out_buf_bytes,

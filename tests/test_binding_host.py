@@ -142,3 +142,34 @@ def test_low_latency_wrappers_check_inputs(ep):
     idx = torch.zeros((T, K), dtype=torch.int64)
     _raises(ep, lambda: ep.low_latency_dispatch(x, idx, 8, E), "GPU tensor")
     _raises(ep, lambda: ep.low_latency_dispatch(x.float(), idx, 8, E), "x must be")
+
+
+def _gmm_args(ep, experts, inter=64, hidden=H):
+    cb, sb = ep.ep_moe_packed_bytes(experts, 2 * inter, hidden)
+    return torch.zeros(cb, dtype=torch.uint8), torch.zeros(sb, dtype=torch.uint8)
+
+
+GMM_BAD = [
+    ("w1", lambda ep: (_gmm_args(ep, E + 1)[0], _gmm_args(ep, E)[1])),       # packed for other experts
+    ("w1_scales", lambda ep: (_gmm_args(ep, E)[0], _gmm_args(ep, E - 1)[1])),
+    ("w1", lambda ep: (_gmm_args(ep, E)[0].view(torch.int8), _gmm_args(ep, E)[1])),
+    ("w1", lambda ep: (_gmm_args(ep, E)[0].view(2, -1), _gmm_args(ep, E)[1])),
+    ("GPU tensor", lambda ep: _gmm_args(ep, E)),                            # all right, but on the CPU
+]
+
+
+@pytest.mark.parametrize("name,make", GMM_BAD, ids=[f"{n}-{i}" for i, (n, _) in enumerate(GMM_BAD)])
+def test_gmm1_checks_packed_weights(ep, name, make):
+    """Packed weights must be exactly what ep_moe_pack_weights fills for the
+    handle's experts: the step-major packing puts expert e's fragments of K
+    step s at a place that depends on the expert count."""
+    w1, w1s = make(ep)
+    buf = torch.zeros(1 << 16, dtype=torch.uint8)
+    _raises(ep, lambda: ep.ep_moe_gmm1(_handle(ep), buf, H, 64, w1, w1s, "mxfp8", buf), name)
+
+
+def test_gmm2_checks_packed_weights(ep):
+    cb, sb = ep.ep_moe_packed_bytes(E + 2, H, 128)
+    buf = torch.zeros(1 << 16, dtype=torch.uint8)
+    _raises(ep, lambda: ep.ep_moe_gmm2(_handle(ep), buf, 128, H, torch.zeros(cb, dtype=torch.uint8),
+                                       torch.zeros(sb, dtype=torch.uint8), buf), "w2")
