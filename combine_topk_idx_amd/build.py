@@ -25,6 +25,11 @@ LIB = os.path.join(HERE, "libep.so")
 PROBE_LIB = os.path.join(HERE, "libep_probe.so")   # measurement probes of bench.py --probes
 PROBE_SOURCES = ["probes.hip"]
 BUILD = os.path.join(HERE, "_build")
+ROOT = os.path.dirname(HERE)
+# a plain C99 program that uses the library only through include/ep.h
+CONSUMER_SRC = os.path.join(ROOT, "tests", "c_abi", "ep_consumer.c")
+CONSUMER = os.path.join(ROOT, "tests", "c_abi", "ep_consumer")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 SOURCES = ["layout.hip", "dispatch.hip", "combine.hip", "moe.hip", "static_ws.hip", "ep_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -62,11 +67,28 @@ def _link(objs: list, out: str, extra: tuple = ()) -> None:
     os.replace(tmp, out)
 
 
+def build_consumer() -> str:
+    """Compiles tests/c_abi/ep_consumer.c with gcc as strict C99 against
+    include/ep.h (the HIP headers as system headers) and links it to the
+    in-tree libep.so, found at run time relative to the program."""
+    cmd = ["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-isystem", os.path.join(ROCM, "include"), CONSUMER_SRC,
+           "-L", HERE, "-lep", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../combine_topk_idx_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
+           "-o", CONSUMER + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on the C consumer:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(CONSUMER + ".tmp", CONSUMER)
+    return CONSUMER
+
+
 def build(verbose: bool = False, out: str = LIB, defines: tuple = (), host_asan: bool = False) -> str:
     """Compile every source and link the library (default: libep.so next to
     this file; ``defines`` are extra -D macros, e.g. launch-shape overrides
     from csrc/tuning.hpp); returns the library path.  The default build also
-    links the measurement probes of ``bench.py --probes`` (libep_probe.so).
+    links the measurement probes of ``bench.py --probes`` (libep_probe.so)
+    and the plain C user of the header, tests/c_abi/ep_consumer.
 
     host_asan: the host code (argument checks, handles, launch set-up) with
     AddressSanitizer, for the host-only ABI tests on a machine without a
@@ -83,6 +105,8 @@ def build(verbose: bool = False, out: str = LIB, defines: tuple = (), host_asan:
     _link([objs[s] for s in SOURCES], out, lflags)
     if out == LIB:
         _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, lflags)
+        if not host_asan:
+            build_consumer()
     if verbose:
         print(f"built {out}" + (f" and {PROBE_LIB}" if out == LIB else "") + (" (host ASan)" if host_asan else ""))
     return out

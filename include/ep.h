@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 3
+#define EP_ABI_VERSION 4
 
 typedef enum {
   EP_OK = 0,

@@ -41,7 +41,14 @@ def test_exports_every_declared_symbol(ep):
 
 
 def test_abi_version(ep):
-    assert ep.ep_abi_version() == 3
+    """The built library reports the version its header declares (4: the
+    packed expert weights became step-major)."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ep.h")).read()
+    declared = int(re.search(r"#define EP_ABI_VERSION (\d+)", hdr).group(1))
+    assert declared == 4
+    assert ep.ep_abi_version() == declared
 
 
 FAKE = 1 << 40          # 256-byte aligned, never dereferenced on the host
