@@ -17,9 +17,9 @@ import torch
 
 from combine_topk_idx_amd import workloads as W
 from oracle import backward as OB, dispatch as OD, layout as OL, quant as OQ
-from tests.hip_path import canary_buffer, recv_rows, run_layout, run_path, sample_tokens, to_dev
+from tests.hip_path import canary_buffer, recv_rows, run_layout, run_path, to_dev
 from tests.oracle_path import oracle_run
-from tests.test_gpu_parity import check_combine, check_layout
+from tests.test_gpu_parity import check_combine, check_layout, full_size_expected
 
 pytestmark = pytest.mark.gpu
 
@@ -75,18 +75,19 @@ def test_interleaved_matches_region_form_combine(ep):
     assert np.array_equal(da[rows], db[rows]) and np.array_equal(sa[rows], sb[rows])
 
 
-def test_interleaved_full_size_sampled(ep):
+def test_interleaved_full_size(ep):
+    """The prefill workload in the interleaved form at full size: the whole
+    layout, every routed row and every token of combine."""
     w = replace(W.WORKLOADS["prefill"], interleaved=True)
-    _announce(f"interleaved sampled prefill {w.mode}")
+    _announce(f"interleaved full-size prefill {w.mode}")
     inp = W.make_inputs(w)
     run = run_path(ep, w, inp)
-    toks = sample_tokens(w, inp["topk_idx"])
-    lay, rb, out = oracle_run(w, inp, None, tokens=toks)
+    lay, rb, out = full_size_expected(w, inp, None)
     check_layout(run, lay)
-    rows = sorted({int(r) for t in toks for r in lay.slot[t] if r >= 0})
-    data, scales = recv_rows(ep, run, w, rows)
-    assert np.array_equal(data, rb.data[rows]) and np.array_equal(scales, rb.scales[rows])
-    check_combine(w, run.out[toks], out)
+    R = lay.num_rows
+    data, scales = recv_rows(ep, run, w)
+    assert np.array_equal(data[:R], rb.data[:R]) and np.array_equal(scales[:R], rb.scales[:R])
+    check_combine(w, run.out, out)
 
 
 @pytest.mark.parametrize("mode", ["mxfp8", "fp8_b128_ue8m0", "int8_token"])

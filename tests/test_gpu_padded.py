@@ -21,9 +21,9 @@ import torch
 
 from combine_topk_idx_amd import workloads as W
 from oracle import layout as OL
-from tests.hip_path import run_path, recv_rows, sample_tokens, to_dev, bf16_bits
+from tests.hip_path import run_path, recv_rows, to_dev, bf16_bits
 from tests.oracle_path import oracle_run
-from tests.test_gpu_parity import check_combine, check_layout
+from tests.test_gpu_parity import check_combine, check_layout, full_size_expected
 
 pytestmark = pytest.mark.gpu
 
@@ -77,23 +77,25 @@ def test_padded_full(ep, name, align, cap):
 
 # full-size, multi-workgroup layout; the capacity case drops the Zipf
 # routing's hot experts down to 4x the mean
-SAMPLED = [("prefill", 128, 0), ("prefill", 1, 512), ("large", 64, 0)]
+FULL_SIZE = [("prefill", 128, 0), ("prefill", 1, 512), ("large", 64, 0)]
 
 
-@pytest.mark.parametrize("name,align,cap", SAMPLED)
-def test_padded_full_size_sampled(ep, name, align, cap):
+@pytest.mark.parametrize("name,align,cap", FULL_SIZE)
+def test_padded_full_size(ep, name, align, cap):
+    """Full size, multi-workgroup layout: the whole layout, every routed row
+    (padding rows hold canaries the oracle does not define) and every token
+    of combine."""
     w = replace(W.WORKLOADS[name], row_align=align, expert_capacity=cap, combine_input="identity")
-    _announce(f"padded sampled {name} align={align} cap={cap} rows={w.max_rows} {w.mode}")
+    _announce(f"padded full-size {name} align={align} cap={cap} rows={w.max_rows} {w.mode}")
     inp = W.make_inputs(w)
     run = run_path(ep, w, inp)
-    toks = sample_tokens(w, inp["topk_idx"])
-    lay, rb, out = oracle_run(w, inp, None, tokens=toks)
+    lay, rb, out = full_size_expected(w, inp, None)
     check_layout(run, lay)
-    rows = sorted({int(r) for t in toks for r in lay.slot[t] if r >= 0})
-    data, scales = recv_rows(ep, run, w, rows)
-    assert np.array_equal(data, rb.data[rows])
-    assert np.array_equal(scales, rb.scales[rows])
-    check_combine(w, run.out[toks], out)
+    rows = np.nonzero(lay.row_src >= 0)[0]
+    data, scales = recv_rows(ep, run, w)
+    assert np.array_equal(data[rows], rb.data[rows])
+    assert np.array_equal(scales[rows], rb.scales[rows])
+    check_combine(w, run.out, out)
     if cap:
         assert run.status & 2 and lay.count.max() == cap
 

@@ -7,13 +7,11 @@ combine input is bf16 and within 2e-2 relative error (per-row L2) when it is
 quantised -- and, because both sides perform the same float32 operations in
 the same order, also bit-exact, which is checked separately.
 
-Workloads with at most a few hundred tokens are compared in full; the
-4096- and 16384-token ones are compared in full for the layout and on a
-sample of tokens (first, last, random, and tokens of the busiest expert) for
-dispatch and combine, at full size and in the launch configuration the
-benchmark uses.  Where the combine input is a set of bf16 expert rows of its
-own (the 16384-token workload), combine is compared on every token: the
-oracle's combine of such rows costs well under a millisecond per token.
+Every workload is compared in full, the 4096- and 16384-token ones at full
+size and in the launch configuration the benchmark uses: the whole layout,
+every routed receive row (the oracle's row quantiser, about 10 ms per
+7168-wide row, runs in worker processes: tests/oracle_pool.py) and every
+token of combine.
 """
 
 import sys
@@ -23,8 +21,9 @@ import pytest
 import torch
 
 from combine_topk_idx_amd import workloads as W
-from oracle import codecs, quant as Q
-from tests.hip_path import run_path, recv_rows, sample_tokens
+from oracle import codecs, combine as C, layout as OL, quant as Q
+from tests.hip_path import run_path, recv_rows
+from tests.oracle_pool import dispatch_parallel
 from tests.oracle_path import oracle_combine_bf16_rows, oracle_run
 
 pytestmark = pytest.mark.gpu
@@ -98,23 +97,33 @@ def test_workload_full(ep, name):
     check_combine(w, run.out, out)
 
 
+def full_size_expected(w, inp, y):
+    """The oracle's layout, receive rows and combine output of a whole
+    full-size workload (rows quantised in worker processes)."""
+    lay = OL.layout(inp["topk_idx"], w.E, w.t_max, row_align=w.row_align, expert_capacity=w.expert_capacity)
+    rb = dispatch_parallel(inp["x"], lay, w.mode)
+    if w.combine_input == "normal":
+        out = oracle_combine_bf16_rows(w, inp, lay, y)
+    else:                                            # identity experts: combine reads the dispatched rows
+        assert w.combine_input == "identity"
+        out = C.combine(rb, lay, inp["topk_weights"])
+    return lay, rb, out
+
+
 @pytest.mark.parametrize("name", LARGE)
-def test_workload_full_size_sampled(ep, name):
+def test_workload_full_size(ep, name):
     w = W.WORKLOADS[name]
-    _announce(f"sampled parity {name} T={w.T} H={w.H} E={w.E} k={w.k} {w.mode}")
+    _announce(f"full-size parity {name} T={w.T} H={w.H} E={w.E} k={w.k} {w.mode}")
     inp = W.make_inputs(w)
     y = _expert_out(w)
     run = run_path(ep, w, inp, expert_out=y)
-    toks = sample_tokens(w, inp["topk_idx"])
-    lay, rb, out = oracle_run(w, inp, y, tokens=toks)
+    lay, rb, out = full_size_expected(w, inp, y)
     check_layout(run, lay)                          # whole layout, bit-exact
-    rows = sorted({int(r) for t in toks for r in lay.slot[t] if r >= 0})
-    data, scales = recv_rows(ep, run, w, rows)
-    assert np.array_equal(data, rb.data[rows])
-    assert np.array_equal(scales, rb.scales[rows])
-    check_combine(w, run.out[toks], out)
-    if w.combine_input == "normal":                  # every token's combine, against the oracle
-        check_combine(w, run.out, oracle_combine_bf16_rows(w, inp, lay, y))
+    R = lay.num_rows
+    data, scales = recv_rows(ep, run, w)
+    assert np.array_equal(data[:R], rb.data[:R])    # every routed row
+    assert np.array_equal(scales[:R], rb.scales[:R])
+    check_combine(w, run.out, out)                  # every token
     if name == "prefill":                            # Zipf: hot experts hold > 10x the mean
         assert lay.count.max() > 10 * lay.count.mean()
 

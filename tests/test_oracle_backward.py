@@ -90,3 +90,23 @@ def test_planted_wrong_weight_breaks_adjoint():
     shifted = np.roll(wts, 1, axis=1)                 # weight of another j
     rb = B.combine_backward(inp["x"], lay, "none", shifted)
     assert _adjoint_gap(inp, lay, rb.data, w, wts) > 2.0 ** -6
+
+
+@pytest.mark.parametrize("weighted", [True, False])
+def test_parallel_backward_helper_is_the_oracle_backward(weighted):
+    """tests/oracle_pool.backward_parallel (the full-size GPU test's expected
+    rows, quantised in worker processes) gives the oracle's combine backward
+    row for row."""
+    from tests.oracle_pool import backward_parallel
+    w = W.random_workload(91, 200, 256, 16, 4, "mxfp8", neg_frac=0.2)
+    inp = W.make_inputs(w)
+    grad = W.make_inputs(W.random_workload(92, 200, 256, 16, 4, "mxfp8"))["x"]
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    wts = inp["topk_weights"] if weighted else None
+    toks = list(range(0, 200, 3))
+    want = B.combine_backward(grad, lay, "mxfp8", wts, tokens=toks)
+    got = backward_parallel(grad, lay, "mxfp8", wts, toks, workers=2, chunk=17)
+    rows = sorted({int(r) for t in toks for r in lay.slot[t] if r >= 0})
+    assert sorted(got) == rows
+    for r in rows:
+        assert np.array_equal(got[r][0], want.data[r]) and np.array_equal(got[r][1], want.scales[r])

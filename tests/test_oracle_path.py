@@ -212,3 +212,18 @@ def test_planted_dropped_term_is_caught(monkeypatch):
     keff = _keff(inp["topk_idx"], w.E).astype(np.float64)
     ref = W.bf16_from_f32((codecs.bf16_bits_to_f32(inp["x"]).astype(np.float64) * keff[:, None]).astype(np.float32))
     assert not np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "fp8_b128", "int8_token"])
+def test_parallel_dispatch_helper_is_the_oracle_dispatch(mode):
+    """tests/oracle_pool.dispatch_parallel (the full-size GPU tests' expected
+    receive rows, quantised in worker processes) returns exactly the oracle's
+    dispatch: same codes and scales in every row, same defined rows."""
+    from tests.oracle_pool import dispatch_parallel
+    w = W.random_workload(77, 300, 256, 16, 4, mode, neg_frac=0.2)
+    inp = W.make_inputs(w)
+    lay = L.layout(inp["topk_idx"], w.E, w.T)
+    want = D.dispatch(inp["x"], lay, mode)
+    got = dispatch_parallel(inp["x"], lay, mode, workers=2)
+    assert got.num_rows == want.num_rows
+    assert np.array_equal(got.data, want.data) and np.array_equal(got.scales, want.scales)
