@@ -56,11 +56,18 @@ def read_slots(ep, res, w):
     return slot, offs
 
 
-def oracle_moe(w: W.MoeWorkload, inp: dict, *, out_mode="mxfp8", tokens=None, row_align=1, expert_capacity=0):
+def oracle_moe(w: W.MoeWorkload, inp: dict, *, out_mode="mxfp8", tokens=None, row_align=1, expert_capacity=0,
+               parallel=False):
     """Oracle run; with `tokens`, only the rows of those tokens go through the
-    MLP and only their combine rows are returned."""
+    MLP and only their combine rows are returned.  parallel: the dispatch's
+    row quantiser runs in worker processes (tests/oracle_pool.py, the same
+    rows as the oracle's dispatch) -- for full-size inputs."""
     lay = OL.layout(inp["topk_idx"], w.E_local, w.T, row_align=row_align, expert_capacity=expert_capacity)
-    rb = OD.dispatch(inp["x"], lay, "mxfp8")
+    if parallel:
+        from tests.oracle_pool import dispatch_parallel
+        rb = dispatch_parallel(inp["x"], lay, "mxfp8")
+    else:
+        rb = OD.dispatch(inp["x"], lay, "mxfp8")
     want_rows = None
     if tokens is not None:
         want_rows = {int(r) for t in tokens for r in lay.slot[t] if r >= 0}

@@ -12,7 +12,7 @@ import torch
 from combine_topk_idx_amd import workloads as W
 from oracle import backward as OB, layout as OL
 from tests.hip_path import DEV, canary_buffer, recv_rows, run_layout, sample_tokens, to_dev, HipRun
-from tests.oracle_pool import backward_parallel
+from tests.oracle_pool import backward_parallel, dispatch_parallel
 
 pytestmark = pytest.mark.gpu
 
@@ -82,6 +82,23 @@ def test_backward_full_size_sampled(ep):
     data, scales = recv_rows(ep, run, w, rows)
     assert np.array_equal(data, np.stack([want[r][0] for r in rows]))
     assert np.array_equal(scales, np.stack([want[r][1] for r in rows]))
+
+
+def test_backward_full_size_unweighted(ep):
+    """The large workload's routing at full size without weights, MXFP4 rows:
+    every routed row (the oracle's unweighted rows are its row quantiser on
+    grad[t], run in worker processes for all 16384 tokens)."""
+    print("\n[case] backward full size unweighted T=16384 H=7168 mxfp4", flush=True)
+    w = W.WORKLOADS["large"]
+    inp = W.make_inputs(w)
+    grad = W.make_expert_out(w, rows=w.T)
+    run = _run(ep, w, inp, grad, False)
+    lay = OL.layout(inp["topk_idx"], w.E, w.T)
+    want = dispatch_parallel(grad, lay, w.mode)
+    R = lay.num_rows
+    data, scales = recv_rows(ep, run, w)
+    assert np.array_equal(data[:R], want.data[:R])
+    assert np.array_equal(scales[:R], want.scales[:R])
 
 
 @pytest.mark.parametrize("mode", ["mxfp8", "mxfp4"])

@@ -35,7 +35,7 @@ import torch
 
 from combine_topk_idx_amd import workloads as W
 from oracle import codecs, dispatch as OD, moe as OM
-from tests.hip_path import DEV, canary_buffer, sample_tokens, to_dev, NAN_BF16
+from tests.hip_path import DEV, canary_buffer, to_dev, NAN_BF16
 from tests import moe_bounds as MB
 from tests.moe_path import gpu_moe, oracle_moe, read_slots
 
@@ -299,19 +299,19 @@ def test_capacity_padded_blocks(ep):
 
 
 @pytest.mark.parametrize("name", ["moe_share", "moe_share32"])
-def test_share_full_size_sampled(ep, name):
+def test_share_full_size(ep, name):
     """The share at full size (hidden 7168, intermediate 3072, 6 local
     experts; 1024 tokens, and 256 whose 1- and 2-fragment chunks put the
-    plan on mixed tile widths), sampled tokens through the whole path; every
-    routed row within the 2e-2 relative error of a quantised combine."""
+    plan on mixed tile widths), every token through the whole path: every
+    requantised row, GMM2 row and combine output within its derived bound,
+    and every routed token within the 2e-2 relative error of a quantised
+    combine."""
     w = W.MOE_WORKLOADS[name]
-    _announce(f"{name} full size, sampled tokens")
+    _announce(f"{name} full size, every token")
     inp = W.make_moe_inputs(w)
     res = gpu_moe(ep, w, inp)
-    toks = sample_tokens(W.Workload("s", w.T, w.H, w.E_local, w.k, "int64", "mxfp8", "uniform"), inp["topk_idx"],
-                         n=24, window=0, hot_cap=8)
-    lay, rb, per, out = oracle_moe(w, inp, tokens=toks)
-    check_chain(ep, w, inp, res, lay, rb, per, out, tokens=toks, row_rel=ROW_REL)
+    lay, rb, per, out = oracle_moe(w, inp, parallel=True)
+    check_chain(ep, w, inp, res, lay, rb, per, out, row_rel=ROW_REL)
 
 
 MANY = [
