@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly on a GPU machine if the library is missing; they are
+    # GPU tests fail loudly on a machine with a GPU if the library is missing; they are
     # only skipped where there is no GPU at all.
     try:
         import torch
