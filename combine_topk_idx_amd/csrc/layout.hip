@@ -30,6 +30,10 @@
 // wave, against about four for a second launch.)  Larger ones run in two
 // launches over 2048-pair chunks: rank (per-chunk counts and ranks), then
 // finalize (each workgroup redoes the small scan over chunk counts itself).
+// With more than 128 chunks (262144 pairs) that redone scan, which reads the
+// whole chunk-count table in every workgroup, would grow with the square
+// of the chunk count; a column-scan kernel between the two then turns the
+// table into prefixes once, and each finalize workgroup reads two rows.
 #include "common.hpp"
 #include "tuning.hpp"
 
@@ -46,6 +50,9 @@ constexpr int64_t kSingleMaxPairs = (int64_t)kSingleItems * kThreads;
 constexpr int64_t kSingleMaxRows = 65536;          // single workgroup also clears row_src tail
 constexpr int kMaxFillBlocks = 512;                // finalize workgroups beyond the chunk count
 constexpr int kHelperRows = 2048;                  // rows per clearing helper of the single-workgroup path
+// Above this many chunks the count table's columns are scanned by a kernel
+// of their own before finalize (three launches instead of two).
+constexpr int kColscanMinChunks = EP_LAYOUT_COLSCAN_MIN;
 
 // Expert of an id, or -1 for -1 / ids outside [-1, E) (which set `bad`).
 template <typename IdxT>
@@ -310,6 +317,7 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(const IdxT *__res
 constexpr int kTileInts = 8192;
 static_assert(kTileInts % kThreads == 0, "a tile is whole loads per thread");
 
+template <bool SCANNED>
 __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int align, int cap, int nblocks, int b,
                                                const int *__restrict__ hist, const uint32_t *__restrict__ bstat,
                                                int64_t *__restrict__ recv_count, int *__restrict__ cum,
@@ -333,8 +341,16 @@ __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int a
   if (b == 0)
     for (int i = threadIdx.x; i < nblocks; i += kThreads) bad |= bstat[i];
 
-  const int tile_rows = kTileInts / E;
   int tot = 0, pre = 0;
+  if constexpr (SCANNED) {
+    // hist holds inclusive prefixes down each expert's column (the column
+    // scan): chunk b's base is row b - 1, the totals are the last row
+    if (e < E && nblocks > 0) {
+      tot = hist[(int64_t)(nblocks - 1) * E + e];
+      pre = b == 0 ? 0 : (b < nblocks ? hist[(int64_t)(b - 1) * E + e] : tot);
+    }
+  } else {
+  const int tile_rows = kTileInts / E;
   // this thread's share of a tile (rows * E <= kTileInts ints) is loaded
   // whole before any of it is stored, so the loads are in flight together;
   // the next tile's share is loaded before the current tile is summed
@@ -370,6 +386,7 @@ __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int a
       }
     }
     __syncthreads();
+  }
   }
   int nrows;
   const int p = block_exclusive_scan(e < E ? block_rows(tot, align, cap) : 0, wsum, nrows);
@@ -411,6 +428,7 @@ __device__ __forceinline__ void finalize_chunk(int n, int E, int max_rows, int a
                   offs, kept);
 }
 
+template <bool SCANNED>
 __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
     int n, int E, int max_rows, int align, int cap, int nblocks, const int *__restrict__ hist,
     const uint32_t *__restrict__ bstat, int64_t *__restrict__ recv_count, int *__restrict__ cum,
@@ -421,8 +439,51 @@ __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
   __shared__ int kept[kMaxExperts];
   __shared__ int wsum[kWaves];
   __shared__ uint32_t sbad;
-  finalize_chunk(n, E, max_rows, align, cap, nblocks, blockIdx.x, hist, bstat, recv_count, cum, offsets, slot,
-                 row_src, status, tile, base, offs, kept, wsum, &sbad);
+  finalize_chunk<SCANNED>(n, E, max_rows, align, cap, nblocks, blockIdx.x, hist, bstat, recv_count, cum, offsets,
+                          slot, row_src, status, tile, base, offs, kept, wsum, &sbad);
+}
+
+// Column scan between the two passes of a layout with many chunks: the
+// chunk counts hist[b*E + e] become inclusive prefixes down each expert's
+// column, so that each finalize workgroup reads two rows of the table
+// instead of all of it (whose cost grows with the square of the chunk
+// count).  Workgroup g owns experts [64g, 64g + 64), one per lane, so every
+// load and store of a wave is one contiguous row piece; wave w owns the
+// chunks [w*L, (w+1)*L), L = ceil(nblocks / 16).  Each wave sums its
+// chunks, the waves' sums are added up through LDS in wave order, and a
+// second walk writes the prefixes in place.
+constexpr int kScanWaves = kThreads / kWave;          // row segments per column-scan workgroup
+constexpr int kScanBatch = 16;                        // loads in flight per lane
+__global__ __launch_bounds__(kThreads) void layout_colscan_kernel(int *__restrict__ hist, int nblocks, int E) {
+  __shared__ int part[kScanWaves][kWave];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int e = blockIdx.x * kWave + lane;
+  const bool on = e < E;
+  const int L = (nblocks + kScanWaves - 1) / kScanWaves;
+  const int b0 = min(w * L, nblocks), b1 = min(b0 + L, nblocks);
+  int s = 0;
+  for (int b = b0; b < b1; b += kScanBatch) {
+    int v[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) v[u] = on && b + u < b1 ? hist[(int64_t)(b + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) s += v[u];
+  }
+  part[w][lane] = s;
+  __syncthreads();
+  int run = 0;
+#pragma unroll
+  for (int i = 0; i < kScanWaves; ++i) run += i < w ? part[i][lane] : 0;
+  for (int b = b0; b < b1; b += kScanBatch) {
+    int v[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) v[u] = on && b + u < b1 ? hist[(int64_t)(b + u) * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      run += v[u];
+      if (on && b + u < b1) hist[(int64_t)(b + u) * E + e] = run;
+    }
+  }
 }
 
 template <typename IdxT>
@@ -453,8 +514,16 @@ hipError_t launch_typed(const IdxT *idx, int n, int32_t E, int max_rows, int ali
   if (nb > 0) {
     hipLaunchKernelGGL(layout_rank_kernel<IdxT>, dim3(nb), dim3(kThreads), 0, s, idx, n, E, hist, bstat, slot);
   }
-  hipLaunchKernelGGL(layout_finalize_kernel, dim3(grid), dim3(kThreads), 0, s, n, E, max_rows, align, cap, nb, hist,
-                     bstat, recv_count, cum, offsets, slot, row_src, status);
+  if (nb > kColscanMinChunks) {
+    // many chunks: scan the count table's columns once, then each finalize
+    // workgroup reads two of its rows
+    hipLaunchKernelGGL(layout_colscan_kernel, dim3((E + kWave - 1) / kWave), dim3(kThreads), 0, s, hist, nb, E);
+    hipLaunchKernelGGL(layout_finalize_kernel<true>, dim3(grid), dim3(kThreads), 0, s, n, E, max_rows, align, cap,
+                       nb, hist, bstat, recv_count, cum, offsets, slot, row_src, status);
+  } else {
+    hipLaunchKernelGGL(layout_finalize_kernel<false>, dim3(grid), dim3(kThreads), 0, s, n, E, max_rows, align, cap,
+                       nb, hist, bstat, recv_count, cum, offsets, slot, row_src, status);
+  }
   return hipGetLastError();
 }
 

@@ -36,3 +36,6 @@
 #ifndef EP_LAYOUT_ITEMS
 #define EP_LAYOUT_ITEMS 2         // pairs per thread of a multi-block layout chunk (chunk = 1024 * this)
 #endif
+#ifndef EP_LAYOUT_COLSCAN_MIN
+#define EP_LAYOUT_COLSCAN_MIN 128 // chunk counts above which the layout scans its count table in a kernel of its own
+#endif

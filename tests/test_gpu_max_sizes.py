@@ -73,3 +73,26 @@ def test_path_max_topk_and_experts(ep):
     assert np.array_equal(data[:R], rb.data[:R])
     assert np.array_equal(run.recv_weights[:R].cpu().numpy(), rb.weights[:R])
     check_combine(w, run.out, out)
+
+
+@pytest.mark.parametrize("T,align,cap", [(32768, 1, 0), (33024, 1, 0), (33024, 256, 0), (40000, 1, 160)],
+                         ids=["128chunks", "129chunks", "129chunks-align256", "157chunks-cap160"])
+def test_layout_around_column_scan(ep, T, align, cap):
+    """Both sides of the chunk count (128) above which the layout scans its
+    count table in a kernel of its own: 262144 pairs (two launches) and
+    264192 pairs (three), compact, aligned and overflowing capacity blocks,
+    against the oracle bit for bit."""
+    w = W.Workload("colscan", T, 32, 256, 8, "int64", "none", "zipf", neg_frac=0.05, seed=9200 + T,
+                   row_align=align, expert_capacity=cap)
+    _announce(f"layout T={w.T} k={w.k} E={w.E} align={align} cap={cap} ({w.T * w.k // 2048} chunks)")
+    inp = W.make_inputs(w)
+    h, ws, rc = run_layout(ep, w, inp["topk_idx"])
+    got = read_layout(ep, h, ws, rc, w)
+    lay = OL.layout(inp["topk_idx"], w.E, w.t_max, row_align=align, expert_capacity=cap)
+    assert np.array_equal(got["recv_count"], lay.count)
+    assert np.array_equal(got["offsets"], lay.offsets.astype(np.int32))
+    assert np.array_equal(got["slot"], lay.slot)
+    assert np.array_equal(got["row_src"], lay.row_src)
+    assert got["status"] == lay.status
+    if cap:
+        assert lay.status & 2
