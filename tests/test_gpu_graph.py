@@ -86,3 +86,39 @@ def test_graph_replays_match_eager(ep, name, fused):
         assert torch.equal(ws[slot_ptr: slot_ptr + 4 * w.T * w.k], ref["ws"]), f"replay {rep}: slots"
         assert torch.equal(recv[: R * dq], ref_rows), f"replay {rep}: receive rows"
         assert torch.equal(out.view(torch.int16), ref["out"].view(torch.int16)), f"replay {rep}: combine"
+
+
+@pytest.mark.parametrize("T", [16384, 33024], ids=["64chunks_two_launches", "129chunks_column_scan"])
+def test_graph_replays_multichunk_layout(ep, T):
+    """The multi-chunk layout (rank, then finalize; above 128 chunks with the
+    column scan between them, which rewrites the chunk-count table in place)
+    captured once and replayed over a workspace filled with garbage before
+    every replay: each replay must give the eager counts, offsets, slots and
+    row sources."""
+    print(f"\n[case] graph replay layout T={T} k=8 E=256", flush=True)
+    sys.stdout.flush()
+    w = W.Workload("gl", T, 32, 256, 8, "int64", "none", "zipf", neg_frac=0.05, seed=9300 + T)
+    inp = W.make_inputs(w)
+    idx = to_dev(inp["topk_idx"])
+    ws = torch.empty(ep.ep_workspace_bytes(w.t_max, w.k, w.E), dtype=torch.uint8, device=DEV)
+    rc = torch.empty(w.E, dtype=torch.int64, device=DEV)
+    ws.fill_(0xA5)
+    h = ep.ep_layout(idx, w.E, w.t_max, rc, ws)
+    torch.cuda.synchronize()
+    off = lambda p: p - ws.data_ptr()
+    views = [(off(h.offsets), 4 * (w.E + 1)), (off(h.slot), 4 * w.T * w.k), (off(h.row_src), 4 * w.max_rows)]
+    ref_rc = rc.clone()
+    ref = [ws[o: o + n].clone() for o, n in views]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ep.ep_layout(idx, w.E, w.t_max, rc, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        ws.fill_(0x5A + rep)
+        rc.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(rc, ref_rc), f"replay {rep}: counts"
+        for (o, n), r in zip(views, ref):
+            assert torch.equal(ws[o: o + n], r), f"replay {rep}: layout bytes at {o}"
