@@ -447,20 +447,23 @@ __global__ __launch_bounds__(kThreads) void layout_finalize_kernel(
 // chunk counts hist[b*E + e] become inclusive prefixes down each expert's
 // column, so that each finalize workgroup reads two rows of the table
 // instead of all of it (whose cost grows with the square of the chunk
-// count).  Workgroup g owns experts [64g, 64g + 64), one per lane, so every
-// load and store of a wave is one contiguous row piece; wave w owns the
-// chunks [w*L, (w+1)*L), L = ceil(nblocks / 16).  Each wave sums its
-// chunks, the waves' sums are added up through LDS in wave order, and a
-// second walk writes the prefixes in place.
-constexpr int kScanWaves = kThreads / kWave;          // row segments per column-scan workgroup
-constexpr int kScanBatch = 16;                        // loads in flight per lane
+// count).  Workgroup g owns 16 experts [16g, 16g + 16) and splits the
+// chunks into 64 runs of L = ceil(nblocks / 64): thread t handles expert
+// 16g + t % 16 over run t / 16, so the 16 threads of one run read one
+// contiguous 64-byte piece of a row.  Each thread sums its run, the runs'
+// sums are added up through LDS in run order, and a second walk writes the
+// prefixes in place.  (16 experts per workgroup spread the table's reads
+// over E / 16 CUs; one CU per 64 experts was limited by its own fetch.)
+constexpr int kScanCols = 16;                         // experts per column-scan workgroup
+constexpr int kScanRuns = kThreads / kScanCols;       // runs of chunks per expert
+constexpr int kScanBatch = 16;                        // loads in flight per thread
 __global__ __launch_bounds__(kThreads) void layout_colscan_kernel(int *__restrict__ hist, int nblocks, int E) {
-  __shared__ int part[kScanWaves][kWave];
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  const int e = blockIdx.x * kWave + lane;
+  __shared__ int part[kScanRuns][kScanCols];
+  const int c = threadIdx.x % kScanCols, run_id = threadIdx.x / kScanCols;
+  const int e = blockIdx.x * kScanCols + c;
   const bool on = e < E;
-  const int L = (nblocks + kScanWaves - 1) / kScanWaves;
-  const int b0 = min(w * L, nblocks), b1 = min(b0 + L, nblocks);
+  const int L = (nblocks + kScanRuns - 1) / kScanRuns;
+  const int b0 = min(run_id * L, nblocks), b1 = min(b0 + L, nblocks);
   int s = 0;
   for (int b = b0; b < b1; b += kScanBatch) {
     int v[kScanBatch];
@@ -469,11 +472,10 @@ __global__ __launch_bounds__(kThreads) void layout_colscan_kernel(int *__restric
 #pragma unroll
     for (int u = 0; u < kScanBatch; ++u) s += v[u];
   }
-  part[w][lane] = s;
+  part[run_id][c] = s;
   __syncthreads();
   int run = 0;
-#pragma unroll
-  for (int i = 0; i < kScanWaves; ++i) run += i < w ? part[i][lane] : 0;
+  for (int i = 0; i < run_id; ++i) run += part[i][c];
   for (int b = b0; b < b1; b += kScanBatch) {
     int v[kScanBatch];
 #pragma unroll
@@ -517,7 +519,8 @@ hipError_t launch_typed(const IdxT *idx, int n, int32_t E, int max_rows, int ali
   if (nb > kColscanMinChunks) {
     // many chunks: scan the count table's columns once, then each finalize
     // workgroup reads two of its rows
-    hipLaunchKernelGGL(layout_colscan_kernel, dim3((E + kWave - 1) / kWave), dim3(kThreads), 0, s, hist, nb, E);
+    hipLaunchKernelGGL(layout_colscan_kernel, dim3((E + kScanCols - 1) / kScanCols), dim3(kThreads), 0, s, hist, nb,
+                       E);
     hipLaunchKernelGGL(layout_finalize_kernel<true>, dim3(grid), dim3(kThreads), 0, s, n, E, max_rows, align, cap,
                        nb, hist, bstat, recv_count, cum, offsets, slot, row_src, status);
   } else {
